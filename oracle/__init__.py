@@ -1,0 +1,262 @@
+"""CPU oracle for the Stream-K GEMM path.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The product path (the HIP library and its
+Python binding in ``persistent_gemm_amd``) never calls it, and this module
+imports nothing from the product: the two share no code.  Inputs reach both
+sides as plain host bytes made by ``persistent_gemm_amd.inputs`` (a seeded
+generator that holds none of the arithmetic below).
+
+What the path computes, written out plainly (fp64 throughout):
+
+    D[m][n] = sigma * sum_{k=0}^{K-1} a(m,k) * b(n,k) + beta[n]
+    C[m][n] = RNE_bf16(D[m][n])
+
+Stream-K only changes *who* performs which MAC iterations of this sum and in
+which order the fp32 partial tiles are added; the value it aims at is this
+one.  Sources:
+
+* The contraction itself, with FP4 (MX) operands and a Stream-K split of the
+  K-loop: "Stream-k mxfp4 kernel" (ROCm/tritonBLAS pull request 74), the
+  author's description and the Copilot pull request overview.
+* bf16 / fp8 ``matmul`` and ``addmm`` checked against ``torch.mm`` /
+  ``torch.addmm`` (so alpha = beta = 1): "Fix StreamK Kernel Bias #67",
+  the review comments on the two correctness tests.
+* The bias runs along N (one value per output column), is broadcast over the
+  M rows, and is added once, after the partial tiles of a split tile have been
+  aggregated; in the quantized mode it is turned into fp32 before the add:
+  "Fix StreamK Kernel Bias #67", Motivation and Technical Details.
+* Element encodings are not on those pages.  E2M1 (FP4) and E8M0 (the shared
+  block scale, one per 32 consecutive K elements) follow the OCP Microscaling
+  Formats (MX) v1.0 specification; E4M3FN follows the OCP 8-bit Floating Point
+  (OFP8) specification; bf16 is the top half of an IEEE binary32.
+
+Readings where the pages are silent: the bf16 output is rounded once, to
+nearest-even, straight from the fp64 value (never through fp32, which would
+double-round); for fp8 the per-tensor scale is applied before the bias is
+added; the two FP4 codes of a byte hold the even K index in the low nibble.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against
+something other than itself (torch's own format conversions, closed forms,
+hand-worked sums, an exact-rational brute force and invariants).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "E2M1_VALUES",
+    "decode_e2m1",
+    "decode_e8m0",
+    "decode_e4m3fn",
+    "decode_bf16",
+    "unpack_fp4",
+    "mxfp4_operand",
+    "rne_bf16_from_double",
+    "bf16_to_double",
+    "operands",
+    "gemm",
+    "gemm_elements",
+    "abs_product_sums",
+    "accept",
+]
+
+# OCP MX v1.0, FP4 (E2M1): code bits are sign | exponent(2, bias 1) | mantissa(1).
+# Listed by code 0..15.
+E2M1_VALUES = np.array(
+    [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+     -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0],
+    dtype=np.float64,
+)
+
+
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """FP4 codes (uint8 in 0..15) -> fp64 values, by table lookup."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    if codes.size and int(codes.max()) > 15:
+        raise ValueError("E2M1 codes are 4-bit")
+    return E2M1_VALUES[codes]
+
+
+def decode_e8m0(e: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> 2**(e - 127); 0xFF is NaN (OCP MX v1.0)."""
+    e = np.asarray(e, dtype=np.int64)
+    v = np.ldexp(np.ones(e.shape, dtype=np.float64), (e - 127).astype(np.int32))
+    return np.where(e == 255, np.nan, v)
+
+
+def decode_e4m3fn(b: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN bytes -> fp64.  Exponent bias 7, no infinities, S.1111.111 is NaN."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    exp = (b >> 3) & 0xF
+    man = (b & 0x7).astype(np.float64)
+    normal = np.ldexp(1.0 + man / 8.0, (exp - 7).astype(np.int32))
+    subnormal = np.ldexp(man / 8.0, -6)
+    mag = np.where(exp == 0, subnormal, normal)
+    mag = np.where((exp == 15) & ((b & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def decode_bf16(u: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp64 (bf16 is the upper half of binary32)."""
+    u = np.ascontiguousarray(np.asarray(u, dtype=np.uint16))
+    return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+bf16_to_double = decode_bf16
+
+
+def unpack_fp4(packed: np.ndarray, K: int) -> np.ndarray:
+    """uint8[rows][K/2] -> codes uint8[rows][K]; element 2j is the low nibble of byte j."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    if packed.shape[1] != K // 2:
+        raise ValueError("packed FP4 rows must hold K/2 bytes")
+    codes = np.empty((rows, K), dtype=np.uint8)
+    codes[:, 0::2] = packed & 0x0F
+    codes[:, 1::2] = packed >> 4
+    return codes
+
+
+def mxfp4_operand(packed: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
+    """Decode an MXFP4 operand: value(r, k) = E2M1(code(r, k)) * 2**(scale[r][k // 32] - 127)."""
+    if K % 32:
+        raise ValueError("MXFP4 needs K to be a multiple of the 32-element scale block")
+    vals = decode_e2m1(unpack_fp4(packed, K))
+    sc = decode_e8m0(np.asarray(scales, dtype=np.uint8))
+    if sc.shape != (vals.shape[0], K // 32):
+        raise ValueError("MXFP4 scales must be [rows][K/32]")
+    return vals * np.repeat(sc, 32, axis=1)
+
+
+def rne_bf16_from_double(d: np.ndarray) -> np.ndarray:
+    """Round fp64 values once to the nearest bf16 (ties to even); return uint16 bit patterns.
+
+    quantum = 2**(max(floor(log2|d|), -126) - 7) is the bf16 spacing at |d| (the
+    subnormal spacing 2**-133 below 2**-126); rint() rounds half to even.
+    Results of magnitude >= 2**128 become +-inf; NaN becomes 0x7FC0.
+    """
+    d = np.asarray(d, dtype=np.float64)
+    out_shape = d.shape
+    d = d.reshape(-1)
+    res = np.zeros(d.shape, dtype=np.float64)
+    finite = np.isfinite(d)
+    nz = finite & (d != 0.0)
+    _, ex = np.frexp(d[nz])                     # d = f * 2**ex, 0.5 <= |f| < 1
+    e = ex.astype(np.int64) - 1                 # floor(log2 |d|)
+    q = np.ldexp(1.0, (np.maximum(e, -126) - 7).astype(np.int32))
+    r = np.rint(d[nz] / q) * q
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, r), r)
+    res[nz] = r
+    res[finite & (d == 0.0)] = d[finite & (d == 0.0)]      # keeps the sign of zero
+    res[np.isinf(d)] = d[np.isinf(d)]
+    bits = (res.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bits[np.isnan(d)] = 0x7FC0
+    return bits.reshape(out_shape)
+
+
+def operands(dtype: str, A, B, SA=None, SB=None, K: int | None = None):
+    """Decoded fp64 operands (a[M][K], b[N][K]) and sigma for one of the three input types.
+
+    dtype "mxfp4": A, B are uint8[rows][K/2] packed E2M1, SA, SB uint8[rows][K/32] E8M0.
+    dtype "bf16":  A, B are uint16[rows][K] bf16 bit patterns; sigma = 1.
+    dtype "fp8":   A, B are uint8[rows][K] E4M3FN; SA, SB are the per-tensor fp32
+                   scale factors (Python floats), sigma = SA * SB.
+    """
+    if dtype == "mxfp4":
+        if K is None:
+            K = 2 * np.asarray(A).shape[1]
+        return mxfp4_operand(A, SA, K), mxfp4_operand(B, SB, K), 1.0
+    if dtype == "bf16":
+        return decode_bf16(A), decode_bf16(B), 1.0
+    if dtype == "fp8":
+        sa = 1.0 if SA is None else float(np.float32(SA))
+        sb = 1.0 if SB is None else float(np.float32(SB))
+        return decode_e4m3fn(A), decode_e4m3fn(B), sa * sb
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _beta(bias, N: int) -> np.ndarray:
+    if bias is None:
+        return np.zeros(N, dtype=np.float64)
+    beta = decode_bf16(bias).reshape(-1)
+    if beta.shape[0] != N:
+        raise ValueError("bias must hold N values")
+    return beta
+
+
+def gemm(dtype: str, A, B, SA=None, SB=None, bias=None, K: int | None = None):
+    """Whole-output oracle.  Returns (C uint16[M][N] bf16 bits, D float64[M][N]).
+
+    The K-sum is one fp64 matrix product of the decoded operands (a library
+    primitive); for MXFP4 inputs every product and partial sum is exact in fp64.
+    """
+    a, b, sigma = operands(dtype, A, B, SA, SB, K)
+    D = sigma * (a @ b.T) + _beta(bias, b.shape[0])[None, :]
+    return rne_bf16_from_double(D), D
+
+
+def gemm_elements(dtype: str, A, B, rows, cols, SA=None, SB=None, bias=None, K: int | None = None):
+    """Oracle for sampled outputs (m, n) = (rows[i], cols[i]), one dot product each.
+
+    Returns (C uint16[count], D float64[count], S float64[count]) where S is the
+    error-bound sum |sigma| * sum_k |a(m,k) b(n,k)|.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    ur, ri = np.unique(rows, return_inverse=True)
+    uc, ci = np.unique(cols, return_inverse=True)
+    if dtype == "mxfp4":
+        if K is None:
+            K = 2 * np.asarray(A).shape[1]
+        a = mxfp4_operand(np.asarray(A)[ur], np.asarray(SA)[ur], K)
+        b = mxfp4_operand(np.asarray(B)[uc], np.asarray(SB)[uc], K)
+        sigma = 1.0
+    else:
+        a, b, sigma = operands(dtype, np.asarray(A)[ur], np.asarray(B)[uc], SA, SB, K)
+    full_n = np.asarray(B).shape[0]
+    beta = _beta(bias, full_n)[cols]
+    dots = np.einsum("ik,ik->i", a[ri], b[ci])
+    D = sigma * dots + beta
+    S = abs(sigma) * np.einsum("ik,ik->i", np.abs(a[ri]), np.abs(b[ci]))
+    return rne_bf16_from_double(D), D, S
+
+
+def abs_product_sums(dtype: str, A, B, SA=None, SB=None, K: int | None = None) -> np.ndarray:
+    """S[m][n] = |sigma| * sum_k |a(m,k) * b(n,k)|, the scale of the error bound."""
+    a, b, sigma = operands(dtype, A, B, SA, SB, K)
+    return abs(sigma) * (np.abs(a) @ np.abs(b).T)
+
+
+def _ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 at |x|: 2**(floor(log2|x|) - 7), and 2**-133 below 2**-126."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    safe = np.where(x > 0, x, 1.0)
+    _, ex = np.frexp(safe)
+    e = np.maximum(ex.astype(np.int64) - 1, -126)
+    return np.where(x >= 2.0 ** -126, np.ldexp(1.0, (e - 7).astype(np.int32)), 2.0 ** -133)
+
+
+def accept(C_test: np.ndarray, C_ref: np.ndarray, D: np.ndarray, S: np.ndarray | None) -> np.ndarray:
+    """Elementwise acceptance of a bf16 result against the oracle.
+
+    An element passes when its bits equal the oracle's (+0 and -0 count as
+    equal, any NaN matches NaN), or when |C_test - D| <= 2**-7 * S + ulp_bf16(max(|D|, |C_test|)).
+    S=None means bit equality only.  Returns a boolean array (True = pass).
+    """
+    C_test = np.asarray(C_test, dtype=np.uint16)
+    C_ref = np.asarray(C_ref, dtype=np.uint16)
+    same = (C_test == C_ref) | (((C_test | C_ref) & 0x7FFF) == 0)
+    t = decode_bf16(C_test)
+    r = decode_bf16(C_ref)
+    same |= np.isnan(t) & np.isnan(r)
+    if S is None:
+        return same
+    D = np.asarray(D, dtype=np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        err = np.abs(t - D)
+        bound = np.ldexp(np.asarray(S, dtype=np.float64), -7) + _ulp_bf16(np.maximum(np.abs(D), np.abs(t)))
+        ok = np.isfinite(err) & (err <= bound)
+    return same | ok

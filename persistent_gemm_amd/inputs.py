@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for the Stream-K GEMM workloads.
+
+This module only draws random bytes; it holds none of the GEMM arithmetic, so
+both the HIP path and the CPU oracle can consume what it makes.  Every draw
+uses one CPU ``torch.Generator`` in the fixed order A, A-scales, B, B-scales,
+bias, and returns plain numpy arrays of the exact bytes both sides read.
+
+Distributions (the workloads the Stream-K pages exercise, made synthetic):
+
+* MXFP4: every 4-bit E2M1 code (including -0, code 8) is equally likely; two
+  codes per byte with the even K index in the low nibble; one E8M0 scale byte
+  per 32 K-elements, uniform on {125, ..., 129} (exponents -2..2).
+* bf16: N(0, 1) in fp32, rounded to bf16 by torch.
+* fp8: N(0, 1) in fp32, clipped to +-448 and rounded to OCP E4M3FN by torch;
+  per-tensor fp32 scales (1.0 unless asked otherwise).
+* bias: N(0, 1) in fp32 rounded to bf16, one value per output column.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "mxfp4" | "bf16" | "fp8"
+    M: int
+    N: int
+    K: int
+    bias: bool
+    seed: int
+    grid_cap: int = 0     # 0 = every CU
+    tile: str | None = None
+    caps: tuple = field(default_factory=tuple)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+# The five synthetic workloads; the seed of each is fixed so that tests,
+# the bench and the oracle all see the same bytes.
+WORKLOADS = {
+    "mxfp4_addmm_256x256x512_g5": Workload(
+        "mxfp4_addmm_256x256x512_g5", "mxfp4", 256, 256, 512, True, 1000, grid_cap=5, tile="64x64"),
+    "bf16_addmm_4096": Workload("bf16_addmm_4096", "bf16", 4096, 4096, 4096, True, 1001),
+    "mxfp4_gemm_16x8192x8192": Workload("mxfp4_gemm_16x8192x8192", "mxfp4", 16, 8192, 8192, False, 1002),
+    "mxfp4_addmm_8192": Workload("mxfp4_addmm_8192", "mxfp4", 8192, 8192, 8192, True, 1003),
+    "fp8_gemm_4096_capsweep": Workload(
+        "fp8_gemm_4096_capsweep", "fp8", 4096, 4096, 4096, False, 1004, caps=(1, 32, 64, 128, 256)),
+}
+
+
+def _bf16_bits(x: torch.Tensor) -> np.ndarray:
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
+                scale_lo: int = 125, scale_hi: int = 129, fp8_scales=(1.0, 1.0)) -> dict:
+    """Draw one problem.  Returns a dict with keys A, B, SA, SB, bias (None if absent).
+
+    mxfp4: A uint8[M][K/2], B uint8[N][K/2], SA uint8[M][K/32], SB uint8[N][K/32].
+    bf16:  A uint16[M][K], B uint16[N][K] (bit patterns); SA = SB = None.
+    fp8:   A uint8[M][K], B uint8[N][K] (E4M3FN bytes); SA, SB python floats.
+    bias:  uint16[N] bf16 bit patterns, or None.
+    """
+    g = torch.Generator().manual_seed(seed)
+    out = {"dtype": dtype, "M": M, "N": N, "K": K}
+
+    def fp4(rows):
+        codes = torch.randint(0, 16, (rows, K), generator=g, dtype=torch.uint8)
+        return (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous().numpy()
+
+    def e8m0(rows):
+        return torch.randint(scale_lo, scale_hi + 1, (rows, K // 32), generator=g, dtype=torch.uint8).numpy()
+
+    if dtype == "mxfp4":
+        if K % 32:
+            raise ValueError("MXFP4 needs K % 32 == 0")
+        out["A"] = fp4(M)
+        out["SA"] = e8m0(M)
+        out["B"] = fp4(N)
+        out["SB"] = e8m0(N)
+    elif dtype == "bf16":
+        out["A"] = _bf16_bits(torch.randn(M, K, generator=g))
+        out["SA"] = None
+        out["B"] = _bf16_bits(torch.randn(N, K, generator=g))
+        out["SB"] = None
+    elif dtype == "fp8":
+        def e4m3(rows):
+            x = torch.randn(rows, K, generator=g).clamp(-448.0, 448.0)
+            return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out["A"] = e4m3(M)
+        out["SA"] = float(np.float32(fp8_scales[0]))
+        out["B"] = e4m3(N)
+        out["SB"] = float(np.float32(fp8_scales[1]))
+    else:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    out["bias"] = _bf16_bits(torch.randn(N, generator=g)) if bias else None
+    return out
+
+
+def integer_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int, lo: int = -8, hi: int = 8) -> dict:
+    """Small-integer operands (values in [lo, hi]) in the bf16 or fp8 encoding.
+
+    Every product and every partial sum of such inputs is an integer far below
+    2**24, so any fp32 summation order is exact.  The bias, if drawn, is an
+    integer in [-64, 64].
+    """
+    g = torch.Generator().manual_seed(seed)
+    out = {"dtype": dtype, "M": M, "N": N, "K": K}
+    a = torch.randint(lo, hi + 1, (M, K), generator=g).float()
+    b = torch.randint(lo, hi + 1, (N, K), generator=g).float()
+    if dtype == "bf16":
+        out["A"], out["B"] = _bf16_bits(a), _bf16_bits(b)
+        out["SA"] = out["SB"] = None
+    elif dtype == "fp8":
+        out["A"] = a.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out["B"] = b.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out["SA"] = out["SB"] = 1.0
+    else:
+        raise ValueError("integer_inputs covers bf16 and fp8")
+    out["bias"] = _bf16_bits(torch.randint(-64, 65, (N,), generator=g).float()) if bias else None
+    return out

@@ -1,0 +1,123 @@
+"""Exact-rational brute force used to pin the oracle on tiny problems.
+
+Written independently of ``oracle/``: every element is decoded from its bit
+fields (no lookup tables), every product and sum is an exact ``Fraction``, and
+the final rounding to bf16 is done on the exact rational by integer arithmetic.
+Only small shapes are practical (pure-Python loops).
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction
+
+
+def e2m1(code: int) -> Fraction:
+    """FP4 E2M1 from its fields: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0."""
+    s = -1 if code & 0b1000 else 1
+    e = (code >> 1) & 0b11
+    m = code & 1
+    if e == 0:
+        mag = Fraction(m, 2)                       # subnormal: 0.m * 2**(1-1)
+    else:
+        mag = Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+    return s * mag
+
+
+def e8m0(byte: int) -> Fraction:
+    if byte == 255:
+        raise ValueError("NaN scale")
+    return Fraction(2) ** (byte - 127)
+
+
+def e4m3fn(byte: int) -> Fraction:
+    s = -1 if byte & 0x80 else 1
+    e = (byte >> 3) & 0xF
+    m = byte & 0x7
+    if e == 15 and m == 7:
+        raise ValueError("NaN")
+    if e == 0:
+        mag = Fraction(m, 8) * Fraction(2) ** -6
+    else:
+        mag = Fraction(2) ** (e - 7) * (1 + Fraction(m, 8))
+    return s * mag
+
+
+def bf16(bits: int) -> Fraction:
+    s = -1 if bits & 0x8000 else 1
+    e = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    if e == 0xFF:
+        raise ValueError("inf/NaN")
+    if e == 0:
+        mag = Fraction(m) * Fraction(2) ** -133
+    else:
+        mag = Fraction(2) ** (e - 127) * (1 + Fraction(m, 128))
+    return s * mag
+
+
+def _floor_log2(x: Fraction) -> int:
+    """floor(log2 x) for x > 0, exactly."""
+    e = x.numerator.bit_length() - x.denominator.bit_length()
+    while Fraction(2) ** e > x:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= x:
+        e += 1
+    return e
+
+
+def round_bf16(x: Fraction) -> int:
+    """Nearest bf16 to the exact rational x, ties to an even mantissa; returns the bit pattern."""
+    if x == 0:
+        return 0
+    sign = 0x8000 if x < 0 else 0
+    a = abs(x)
+    e = max(_floor_log2(a), -126)
+    quantum = Fraction(2) ** (e - 7)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = fl * quantum
+    if v >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    if v < Fraction(2) ** -126:
+        return sign | int(v / Fraction(2) ** -133)
+    ev = _floor_log2(v)
+    mant = (v / Fraction(2) ** ev - 1) * 128
+    assert mant.denominator == 1
+    return sign | ((ev + 127) << 7) | int(mant)
+
+
+def gemm(dtype: str, A, B, SA, SB, bias, M: int, N: int, K: int):
+    """C[m][n] bits for D = sigma * sum_k a*b + bias[n], all exact."""
+    def a_val(m, k):
+        if dtype == "mxfp4":
+            byte = int(A[m][k // 2])
+            code = (byte >> 4) if (k & 1) else (byte & 0xF)
+            return e2m1(code) * e8m0(int(SA[m][k // 32]))
+        if dtype == "bf16":
+            return bf16(int(A[m][k]))
+        return e4m3fn(int(A[m][k]))
+
+    def b_val(n, k):
+        if dtype == "mxfp4":
+            byte = int(B[n][k // 2])
+            code = (byte >> 4) if (k & 1) else (byte & 0xF)
+            return e2m1(code) * e8m0(int(SB[n][k // 32]))
+        if dtype == "bf16":
+            return bf16(int(B[n][k]))
+        return e4m3fn(int(B[n][k]))
+
+    sigma = Fraction(1)
+    if dtype == "fp8":
+        sigma = Fraction(float(SA)) * Fraction(float(SB))
+    out = [[0] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            s = sum((a_val(m, k) * b_val(n, k) for k in range(K)), Fraction(0))
+            d = sigma * s
+            if bias is not None:
+                d += bf16(int(bias[n]))
+            out[m][n] = round_bf16(d)
+    return out

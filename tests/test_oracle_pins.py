@@ -1,0 +1,450 @@
+"""Pins for the CPU oracle: each checks it against something other than itself.
+
+* decoders against torch's own CPU format conversions (E4M3FN, E8M0, bf16);
+* E2M1 against its OCP bit-field definition;
+* bf16 rounding against torch's fp32->bf16 conversion, and against hand-built
+  doubles where rounding through fp32 first would give the wrong answer;
+* whole GEMMs against an exact-rational brute force (tests/bruteforce.py),
+  hand-worked sums, identity operands, the bias-broadcast property, integer
+  matrix products and algebraic invariants.
+
+``test_planted_mistakes_are_caught`` plants plausible mistakes in the oracle
+(on the CPU) and checks that at least one pin fails for each.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import bruteforce as bf
+import oracle
+from persistent_gemm_amd.inputs import integer_inputs, make_inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _pack(codes: np.ndarray) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _f32_to_bf16_torch(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- decoders
+
+def pin_e4m3fn_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    got = oracle.decode_e4m3fn(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+
+
+def pin_e8m0_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).float().double().numpy()
+    got = oracle.decode_e8m0(codes)
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(ref[:255], got[:255])
+
+
+def pin_bf16_decode_vs_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = oracle.decode_bf16(bits)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+
+
+def pin_e2m1_bitfields():
+    for code in range(16):
+        assert float(bf.e2m1(code)) == oracle.decode_e2m1(np.array([code]))[0]
+        assert np.signbit(oracle.decode_e2m1(np.array([code]))[0]) == bool(code & 8)
+
+
+# ---------------------------------------------------------------- rounding
+
+def pin_rne_vs_torch_on_floats():
+    rng = np.random.default_rng(7)
+    raw = rng.integers(0, 2**32, size=400_000, dtype=np.uint64).astype(np.uint32)
+    ties = (raw & 0xFFFF0000) | 0x8000            # exactly on a bf16 midpoint
+    near = (raw & 0xFFFF0000) | rng.choice(np.array([0x7FFF, 0x8001, 0x0001, 0xFFFF], np.uint32), raw.size)
+    for pat in (raw, ties, near):
+        f = pat.view(np.float32)
+        f = f[np.isfinite(f)]
+        assert np.array_equal(oracle.rne_bf16_from_double(f.astype(np.float64)), _f32_to_bf16_torch(f))
+
+
+def pin_rne_from_double_not_via_float():
+    # mid1 = 1 + 2**-8 lies halfway between bf16 1.0 (0x3F80) and 1 + 2**-7 (0x3F81).
+    mid1 = 1.0 + 2.0 ** -8
+    # mid2 = 1 + 3 * 2**-8 lies halfway between 0x3F81 and 0x3F82.
+    mid2 = 1.0 + 3 * 2.0 ** -8
+    cases = {
+        mid1: 0x3F80,                    # tie -> even
+        mid1 + 2.0 ** -40: 0x3F81,       # float32(x) == mid1 would tie to 0x3F80: wrong
+        mid1 - 2.0 ** -40: 0x3F80,
+        mid2: 0x3F82,                    # tie -> even mantissa (2)
+        mid2 - 2.0 ** -40: 0x3F81,       # float32(x) == mid2 would give 0x3F82: wrong
+        -(mid1 + 2.0 ** -40): 0xBF81,
+        257.0: 0x4380, 259.0: 0x4382, 258.0: 0x4381,
+    }
+    pairs = list(cases.items()) + [(0.0, 0x0000), (-0.0, 0x8000)]   # +-0 collide as dict keys
+    x = np.array([p[0] for p in pairs], dtype=np.float64)
+    want = np.array([p[1] for p in pairs], dtype=np.uint16)
+    assert np.array_equal(oracle.rne_bf16_from_double(x), want)
+
+
+def pin_rne_overflow_subnormal_nan():
+    max_bf16 = (2.0 - 2.0 ** -7) * 2.0 ** 127          # 0x7F7F
+    half_ulp = 2.0 ** (127 - 8)
+    cases = {
+        max_bf16: 0x7F7F,
+        max_bf16 + half_ulp * 0.999: 0x7F7F,
+        max_bf16 + half_ulp: 0x7F80,                       # tie, odd mantissa -> rounds up -> inf
+        2.0 ** 128: 0x7F80, -(2.0 ** 129): 0xFF80, float("inf"): 0x7F80,
+        2.0 ** -133: 0x0001,                               # smallest subnormal
+        1.5 * 2.0 ** -133: 0x0002,                         # tie -> even
+        2.0 ** -134: 0x0000,                               # tie between 0 and 2**-133 -> even (0)
+        2.0 ** -134 + 2.0 ** -160: 0x0001,
+        -(2.0 ** -134 + 2.0 ** -160): 0x8001,
+        2.0 ** -126: 0x0080,                               # smallest normal
+        2.0 ** -126 - 2.0 ** -134: 0x0080,                 # tie between 0x7F and 0x80 -> even (0x80)
+        1e-300: 0x0000,
+    }
+    x = np.array(list(cases.keys()), dtype=np.float64)
+    want = np.array(list(cases.values()), dtype=np.uint16)
+    assert np.array_equal(oracle.rne_bf16_from_double(x), want)
+    assert oracle.rne_bf16_from_double(np.array([np.nan]))[0] == 0x7FC0
+
+
+def pin_rne_vs_rational():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(3000) * np.ldexp(1.0, rng.integers(-140, 120, 3000))
+    got = oracle.rne_bf16_from_double(x)
+    from fractions import Fraction
+    want = np.array([bf.round_bf16(Fraction(float(v))) for v in x], dtype=np.uint16)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- whole GEMMs
+
+def _bruteforce_case(dtype, M, N, K, bias, seed):
+    if dtype == "fp8":
+        x = make_inputs(dtype, M, N, K, bias=bias, seed=seed, fp8_scales=(0.5, 3.0))
+    else:
+        x = make_inputs(dtype, M, N, K, bias=bias, seed=seed)
+    C, _ = oracle.gemm(dtype, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=K)
+    want = np.array(bf.gemm(dtype, x["A"], x["B"], x["SA"], x["SB"], x["bias"], M, N, K), dtype=np.uint16)
+    assert np.array_equal(C, want), (dtype, M, N, K, bias, seed)
+    rows = np.repeat(np.arange(M), N)
+    cols = np.tile(np.arange(N), M)
+    Ce, _, _ = oracle.gemm_elements(dtype, x["A"], x["B"], rows, cols, x["SA"], x["SB"], x["bias"], K=K)
+    assert np.array_equal(Ce.reshape(M, N), want)
+
+
+def pin_bruteforce_mxfp4():
+    for seed, (M, N, K) in enumerate([(1, 1, 32), (2, 3, 64), (3, 2, 96), (4, 4, 64)]):
+        for bias in (False, True):
+            _bruteforce_case("mxfp4", M, N, K, bias, 100 + seed)
+
+
+def pin_bruteforce_bf16():
+    for seed, (M, N, K) in enumerate([(1, 1, 8), (2, 3, 16), (3, 4, 40)]):
+        for bias in (False, True):
+            _bruteforce_case("bf16", M, N, K, bias, 200 + seed)
+
+
+def pin_bruteforce_fp8():
+    for seed, (M, N, K) in enumerate([(1, 2, 16), (3, 3, 32), (4, 2, 48)]):
+        for bias in (False, True):
+            _bruteforce_case("fp8", M, N, K, bias, 300 + seed)
+
+
+def _one_by_one(a_codes, b_codes, sa=127, sb=127, bias=None):
+    """MXFP4 with M = N = 1, K = 32 from explicit codes."""
+    A = _pack(np.array([a_codes], dtype=np.uint8))
+    B = _pack(np.array([b_codes], dtype=np.uint8))
+    SA = np.array([[sa]], dtype=np.uint8)
+    SB = np.array([[sb]], dtype=np.uint8)
+    bb = None if bias is None else _f32_to_bf16_torch(np.array([bias], np.float32))
+    C, D = oracle.gemm("mxfp4", A, B, SA, SB, bb, K=32)
+    return int(C[0, 0]), float(D[0, 0])
+
+
+def pin_handworked_mxfp4():
+    one, neg_one, six, two, one_half = 0x2, 0xA, 0x7, 0x4, 0x3
+    assert _one_by_one([one] * 32, [one] * 32) == (0x4200, 32.0)
+    assert _one_by_one([one] * 32, [one] * 32, sa=128) == (0x4280, 64.0)
+    assert _one_by_one([one] * 32, [one, neg_one] * 16)[1] == 0.0
+    assert _one_by_one([one] * 32, [one, neg_one] * 16, bias=0.5) == (0x3F00, 0.5)
+    assert _one_by_one([six] * 32, [six] * 32, sa=129, sb=129) == (0x4690, 18432.0)
+    a = [six] * 7 + [two, one] + [0] * 23
+    b = [six] * 7 + [two, one] + [0] * 23
+    assert _one_by_one(a, b) == (0x4380, 257.0)          # tie -> 256
+    b2 = [six] * 7 + [two, one_half] + [0] * 23
+    a2 = [six] * 7 + [two, two] + [0] * 23
+    assert _one_by_one(a2, b2) == (0x4382, 259.0)        # tie -> 260
+    # order of nibbles: code at k=1 sits in the high nibble of byte 0
+    a3 = [0] * 32
+    a3[1] = six
+    b3 = [0] * 32
+    b3[1] = two
+    assert _one_by_one(a3, b3) == (0x4140, 12.0)
+    # the scale of k in [32, 64) is the second scale byte
+    A = _pack(np.array([[0] * 32 + [one] * 32], np.uint8))
+    B = _pack(np.array([[0] * 32 + [one] * 32], np.uint8))
+    C, D = oracle.gemm("mxfp4", A, B, np.array([[120, 128]], np.uint8), np.array([[127, 127]], np.uint8), None, K=64)
+    assert D[0, 0] == 64.0 and C[0, 0] == 0x4280
+
+
+def pin_identity():
+    # MXFP4: A = I (code 1.0, scale 2**0) -> C[m][n] = b(n, m) exactly.
+    K = 64
+    x = make_inputs("mxfp4", 8, 24, K, bias=False, seed=5)
+    codes = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(codes, 0x2)
+    A = _pack(codes)
+    SA = np.full((K, K // 32), 127, np.uint8)
+    C, _ = oracle.gemm("mxfp4", A, x["B"], SA, x["SB"], None, K=K)
+    bvals = np.array([[float(bf.e2m1((int(x["B"][n][k // 2]) >> (4 * (k & 1))) & 0xF) * bf.e8m0(int(x["SB"][n][k // 32])))
+                       for k in range(K)] for n in range(24)], dtype=np.float32)
+    assert np.array_equal(C, _f32_to_bf16_torch(bvals.T))
+    # bf16: A = I -> C = B^T, bit for bit.
+    y = make_inputs("bf16", 4, 20, 32, bias=False, seed=6)
+    A = np.zeros((32, 32), np.uint16)
+    np.fill_diagonal(A, 0x3F80)
+    C, _ = oracle.gemm("bf16", A, y["B"], None, None, None)
+    assert np.array_equal(C, y["B"].T)
+    # fp8: A = I (0x38 = 1.0) -> C = bf16(e4m3 value of B)^T.
+    z = make_inputs("fp8", 4, 20, 32, bias=False, seed=7)
+    A = np.zeros((32, 32), np.uint8)
+    np.fill_diagonal(A, 0x38)
+    C, _ = oracle.gemm("fp8", A, z["B"], 1.0, 1.0, None)
+    bv = torch.from_numpy(z["B"]).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(C, _f32_to_bf16_torch(bv.T))
+
+
+def pin_bias_broadcast():
+    for dtype in ("mxfp4", "bf16", "fp8"):
+        x = make_inputs(dtype, 6, 40, 64, bias=True, seed=8)
+        A0 = np.zeros_like(x["A"])
+        C, _ = oracle.gemm(dtype, A0, x["B"], x["SA"], x["SB"], x["bias"], K=64)
+        assert np.array_equal(C, np.broadcast_to(x["bias"], C.shape))
+    for dtype in ("bf16", "fp8"):
+        y = integer_inputs(dtype, 5, 12, 16, bias=True, seed=9, lo=-3, hi=3)
+        Cb, Db = oracle.gemm(dtype, y["A"], y["B"], y["SA"], y["SB"], y["bias"])
+        Cn, Dn = oracle.gemm(dtype, y["A"], y["B"], y["SA"], y["SB"], None)
+        diff = oracle.decode_bf16(Cb) - oracle.decode_bf16(Cn)
+        bias = oracle.decode_bf16(y["bias"])
+        assert np.array_equal(diff, np.broadcast_to(bias, diff.shape))
+        assert np.array_equal(Db - Dn, np.broadcast_to(bias, Db.shape))
+
+
+def _mx_int(packed, scales, K):
+    """MXFP4 values times 2**3, as exact integers (scales restricted to >= 125)."""
+    out = np.zeros((packed.shape[0], K), np.int64)
+    for r in range(packed.shape[0]):
+        for k in range(K):
+            code = (int(packed[r][k // 2]) >> (4 * (k & 1))) & 0xF
+            v = bf.e2m1(code) * bf.e8m0(int(scales[r][k // 32])) * 8
+            assert v.denominator == 1
+            out[r, k] = int(v)
+    return out
+
+
+def pin_integer_matmul():
+    # MXFP4: 8 * a and 8 * b are integers, so 64 * D is an int64 matrix product.
+    x = make_inputs("mxfp4", 9, 7, 160, bias=False, seed=10)
+    _, D = oracle.gemm("mxfp4", x["A"], x["B"], x["SA"], x["SB"], None, K=160)
+    ref = _mx_int(x["A"], x["SA"], 160) @ _mx_int(x["B"], x["SB"], 160).T
+    assert np.array_equal(D * 64, ref.astype(np.float64))
+    # bf16 / fp8 small integers: D equals the int64 product plus the bias; C is torch's rounding of it.
+    for dtype in ("bf16", "fp8"):
+        y = integer_inputs(dtype, 11, 13, 64, bias=True, seed=12)
+        C, D = oracle.gemm(dtype, y["A"], y["B"], y["SA"], y["SB"], y["bias"])
+        if dtype == "bf16":
+            ai = torch.from_numpy(y["A"].view(np.int16)).view(torch.bfloat16).long().numpy()
+            bi = torch.from_numpy(y["B"].view(np.int16)).view(torch.bfloat16).long().numpy()
+        else:
+            ai = torch.from_numpy(y["A"]).view(torch.float8_e4m3fn).float().long().numpy()
+            bi = torch.from_numpy(y["B"]).view(torch.float8_e4m3fn).float().long().numpy()
+        bias = torch.from_numpy(y["bias"].view(np.int16)).view(torch.bfloat16).long().numpy()
+        ref = ai @ bi.T + bias[None, :]
+        assert np.array_equal(D, ref.astype(np.float64))
+        assert np.array_equal(C, _f32_to_bf16_torch(ref.astype(np.float32)))
+
+
+def pin_invariants_mxfp4():
+    K = 128
+    x = make_inputs("mxfp4", 6, 5, K, bias=False, seed=13)
+    C, D = oracle.gemm("mxfp4", x["A"], x["B"], x["SA"], x["SB"], None, K=K)
+    # one more in every A scale byte doubles the result exactly
+    C2, D2 = oracle.gemm("mxfp4", x["A"], x["B"], x["SA"] + 1, x["SB"], None, K=K)
+    assert np.array_equal(D2, 2 * D)
+    # permuting whole 32-wide K blocks (data and scales together) changes nothing
+    perm = np.array([2, 0, 3, 1])
+    Ab = x["A"].reshape(6, 4, 16)[:, perm].reshape(6, 64)
+    Bb = x["B"].reshape(5, 4, 16)[:, perm].reshape(5, 64)
+    C3, D3 = oracle.gemm("mxfp4", Ab, Bb, x["SA"][:, perm], x["SB"][:, perm], None, K=K)
+    assert np.array_equal(D3, D) and np.array_equal(C3, C)
+    # swapping the operands transposes the result
+    C4, _ = oracle.gemm("mxfp4", x["B"], x["A"], x["SB"], x["SA"], None, K=K)
+    assert np.array_equal(C4, C.T)
+    # permuting rows of A permutes rows of C
+    rp = np.array([3, 1, 5, 0, 2, 4])
+    C5, _ = oracle.gemm("mxfp4", x["A"][rp], x["B"], x["SA"][rp], x["SB"], None, K=K)
+    assert np.array_equal(C5, C[rp])
+    # shifting only the first K block's scale changes the value by exactly that block's part
+    SA6 = x["SA"].copy()
+    SA6[:, 0] += 1
+    _, D6 = oracle.gemm("mxfp4", x["A"], x["B"], SA6, x["SB"], None, K=K)
+    Afirst = x["A"].copy()
+    Afirst[:, 16:] = 0
+    _, Dfirst = oracle.gemm("mxfp4", Afirst, x["B"], x["SA"], x["SB"], None, K=K)
+    assert np.array_equal(D6 - D, Dfirst)
+
+
+def pin_accept():
+    x = make_inputs("bf16", 16, 24, 256, bias=True, seed=14)
+    C, D = oracle.gemm("bf16", x["A"], x["B"], None, None, x["bias"])
+    S = oracle.abs_product_sums("bf16", x["A"], x["B"])
+    assert oracle.accept(C, C, D, S).all()
+    assert oracle.accept(C, C, D, None).all()
+    # one bf16 ulp away: inside the bound, not bit-equal
+    C1 = C.copy()
+    C1[0, 0] ^= 1
+    assert oracle.accept(C1, C, D, S).all()
+    assert not oracle.accept(C1, C, D, None)[0, 0]
+    # far away: rejected
+    Cbad = C.copy()
+    Cbad[3, 4] = oracle.rne_bf16_from_double(np.array([D[3, 4] + 2 * S[3, 4] + 1.0]))[0]
+    assert not oracle.accept(Cbad, C, D, S)[3, 4]
+    # +0 and -0 count as equal
+    z = np.array([0x0000], np.uint16)
+    assert oracle.accept(np.array([0x8000], np.uint16), z, np.zeros(1), None).all()
+
+
+PINS = [
+    pin_e4m3fn_vs_torch, pin_e8m0_vs_torch, pin_bf16_decode_vs_torch, pin_e2m1_bitfields,
+    pin_rne_vs_torch_on_floats, pin_rne_from_double_not_via_float, pin_rne_overflow_subnormal_nan,
+    pin_rne_vs_rational, pin_bruteforce_mxfp4, pin_bruteforce_bf16, pin_bruteforce_fp8,
+    pin_handworked_mxfp4, pin_identity, pin_bias_broadcast, pin_integer_matmul,
+    pin_invariants_mxfp4, pin_accept,
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _mut_e2m1_entry(mp):
+    t = oracle.E2M1_VALUES.copy()
+    t[5] = 2.5
+    mp.setattr(oracle, "E2M1_VALUES", t)
+
+
+def _mut_nibble_order(mp):
+    # A consistent nibble swap in both operands permutes K inside one scale block
+    # and cannot change C; the plausible mistake is a swap in one operand only.
+    real = oracle.operands
+
+    def ops(dtype, A, B, SA=None, SB=None, K=None):
+        if dtype == "mxfp4":
+            A = np.asarray(A, np.uint8)
+            A = ((A >> 4) | (A << 4)).astype(np.uint8)
+        return real(dtype, A, B, SA, SB, K)
+    mp.setattr(oracle, "operands", ops)
+
+
+def _mut_scale_block(mp):
+    real = oracle.decode_e8m0
+
+    def shifted(e):
+        e = np.asarray(e)
+        return real(np.roll(e, 1, axis=-1) if e.ndim == 2 else e)
+    mp.setattr(oracle, "decode_e8m0", shifted)
+
+
+def _mut_drop_bias(mp):
+    mp.setattr(oracle, "_beta", lambda bias, N: np.zeros(N))
+
+
+def _mut_double_bias(mp):
+    real = oracle._beta
+    mp.setattr(oracle, "_beta", lambda bias, N: 2 * real(bias, N))
+
+
+def _mut_round_via_float(mp):
+    real = oracle.rne_bf16_from_double
+    mp.setattr(oracle, "rne_bf16_from_double",
+               lambda d: real(np.asarray(d, dtype=np.float64).astype(np.float32).astype(np.float64)))
+
+
+def _mut_round_truncate(mp):
+    def trunc(d):
+        d = np.asarray(d, dtype=np.float64)
+        return (d.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    mp.setattr(oracle, "rne_bf16_from_double", trunc)
+
+
+def _mut_e4m3_bias(mp):
+    real = oracle.decode_e4m3fn
+    mp.setattr(oracle, "decode_e4m3fn", lambda b: real(b) * 0.5)
+
+
+def _mut_fp8_sigma(mp):
+    real = oracle.operands
+
+    def ops(dtype, A, B, SA=None, SB=None, K=None):
+        a, b, s = real(dtype, A, B, SA, SB, K)
+        return a, b, 1.0
+    mp.setattr(oracle, "operands", ops)
+
+
+def _mut_transpose_b(mp):
+    real = oracle.operands
+
+    def ops(dtype, A, B, SA=None, SB=None, K=None):
+        a, b, s = real(dtype, A, B, SA, SB, K)
+        if b.shape[0] == b.shape[1]:
+            b = b.T.copy()
+        else:
+            b = b[::-1].copy()
+        return a, b, s
+    mp.setattr(oracle, "operands", ops)
+
+
+def _mut_bf16_decode(mp):
+    real = oracle.decode_bf16
+    mp.setattr(oracle, "decode_bf16", lambda u: real(np.asarray(u, np.uint16) ^ np.uint16(1)))
+
+
+MUTATIONS = [
+    _mut_e2m1_entry, _mut_nibble_order, _mut_scale_block, _mut_drop_bias, _mut_double_bias,
+    _mut_round_via_float, _mut_round_truncate, _mut_e4m3_bias, _mut_fp8_sigma, _mut_transpose_b,
+    _mut_bf16_decode,
+]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m.__name__ for m in MUTATIONS])
+def test_planted_mistakes_are_caught(mutation, monkeypatch):
+    mutation(monkeypatch)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught {mutation.__name__}"
