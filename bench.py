@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the Stream-K GEMM on one MI355X.
+
+One step is one call of the library on one synthetic problem with its inputs
+already resident in HBM.  The default workload is the 8192^3 MXFP4 addmm
+(E2M1 values with an E8M0 scale per 32 K elements, a bf16 bias along N, bf16
+output), the problem on which MXFP4 TFLOP/s and the fraction of the dense FP4
+MFMA peak are quoted.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cap C] [--no-cpu]
+
+The ``roofline`` object uses kernel durations measured here with HIP events on
+the launch stream; ``traffic`` comes from the rocprofv3 counter summary kept
+under profiles/ and is reported only while the kernel sources are the ones
+that summary was taken with.  ``cpu_baseline`` times the CPU oracle (test
+infrastructure, never the product path) on a bounded sample of the same
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 Stream-K GEMM TFLOP/s and % of dense FP4 MFMA peak, 1 MI355X"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"mxfp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "mxfp4_addmm_8192"
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "persistent_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str, tag: str):
+    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(w) -> int:
+    """Each operand, scale, bias and output element once."""
+    M, N, K = w.M, w.N, w.K
+    if w.dtype == "mxfp4":
+        b = (M + N) * (K // 2) + (M + N) * (K // 32)
+    elif w.dtype == "bf16":
+        b = (M + N) * K * 2
+    else:
+        b = (M + N) * K + 8
+    return b + (2 * N if w.bias else 0) + 2 * M * N
+
+
+def cpu_baseline(w, x, budget_s: float = 12.0) -> dict:
+    """The oracle on the first R rows of the workload (all N columns, full K)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+
+    def sample(rows):
+        sub = dict(x)
+        sub["A"] = x["A"][:rows]
+        if w.dtype == "mxfp4":
+            sub["SA"] = x["SA"][:rows]
+        t0 = time.perf_counter()
+        oracle.gemm(w.dtype, sub["A"], sub["B"], sub["SA"], sub["SB"], sub["bias"], K=w.K)
+        return time.perf_counter() - t0
+
+    rows = min(64, w.M)
+    t = sample(rows)
+    if t < budget_s / 4 and rows < w.M:
+        rows = int(min(w.M, max(rows, rows * budget_s / max(t, 1e-3) * 0.8)))
+        rows = max(1, rows // 16 * 16) if rows >= 16 else rows
+        t = sample(rows)
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle (fp64 numpy, decode + product + bf16 rounding) on rows 0..{rows - 1} of A "
+                      f"({rows}x{w.N}x{w.K}), {t:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cap", type=int, default=None, help="grid cap (default: the workload's)")
+    ap.add_argument("--tile", default=None, help="tile override, e.g. 256x256")
+    ap.add_argument("--policy", default="hybrid", choices=["hybrid", "sk", "dp"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--rotate", type=int, default=0, help="rotate over this many input copies (defeats the MALL)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import persistent_gemm_amd as pg
+    from persistent_gemm_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    cap = w.grid_cap if args.cap is None else args.cap
+    tile = None
+    if args.tile:
+        tile = tuple(int(v) for v in args.tile.lower().split("x"))
+    elif w.tile:
+        tile = tuple(int(v) for v in w.tile.split("x"))
+    policy = {"hybrid": pg.HYBRID, "sk": pg.PURE_SK, "dp": pg.PURE_DP}[args.policy]
+
+    x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        d = {}
+        if w.dtype == "mxfp4":
+            for k in ("A", "B", "SA", "SB"):
+                d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
+        elif w.dtype == "bf16":
+            for k in ("A", "B"):
+                d[k] = torch.from_numpy(x[k].view(np.int16)).view(torch.bfloat16).to(dev)
+            d["SA"] = d["SB"] = None
+        else:
+            for k in ("A", "B"):
+                d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
+            d["SA"] = torch.tensor([x["SA"]], dtype=torch.float32, device=dev)
+            d["SB"] = torch.tensor([x["SB"]], dtype=torch.float32, device=dev)
+        d["bias"] = None if x["bias"] is None else torch.from_numpy(x["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return d
+
+    copies = [to_dev(x)]
+    for i in range(1, max(1, args.rotate)):
+        copies.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in copies[0].items()})
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    p = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=cap, policy=policy, tile=tile)
+
+    def step(i):
+        d = copies[i % len(copies)]
+        pg.gemm_ex(w.dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap, policy=policy, tile=tile)
+
+    for i in range(args.warmup):
+        step(i)
+    pg.check()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pg.check()
+
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kern_s = float(np.mean(kern_ms)) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    flops = float(w.flops)
+    value = flops / (ms_per_step / 1e3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    eff_peak = peak * (p.grid / 256.0 if args.workload.startswith("fp8_gemm_4096_cap") else 1.0)
+    achieved = flops / avg_kern_s / 1e12
+    tag = "" if cap == w.grid_cap and tile is None and policy == pg.HYBRID else f"_cap{cap}"
+    traffic = traffic_for(args.workload, tag)
+    out = {
+        "metric": METRIC if w.dtype == "mxfp4" else f"{w.dtype} Stream-K GEMM TFLOP/s, 1 MI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
+                   "tile": f"{p.tile_m}x{p.tile_n}x{p.tile_k}", "policy": args.policy, "grid": p.grid,
+                   "sk_tiles": p.sk_tiles, "tiles": p.tiles, "parallelism": "stream-k, 1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": eff_peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / eff_peak, 4), "traffic": traffic,
+                     "kernel_ms": {"mean": round(float(np.mean(kern_ms)), 5), "min": round(float(np.min(kern_ms)), 5),
+                                   "median": round(float(np.median(kern_ms)), 5),
+                                   "max": round(float(np.max(kern_ms)), 5)},
+                     "algorithmic_bytes": algorithmic_bytes(w),
+                     "hbm_gbs_at_algorithmic_bytes": round(algorithmic_bytes(w) / avg_kern_s / 1e9, 1)},
+    }
+    if w.dtype == "mxfp4" and w.M <= 16:
+        ab = algorithmic_bytes(w)
+        out["roofline"].update({"bound": "hbm", "achieved": round(ab / avg_kern_s / 1e9, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(ab / avg_kern_s / 1e9 / PEAK_HBM_GBS, 4)})
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,211 @@
+/*
+ * sk_gemm.h -- Stream-K GEMM for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * Every entry point computes, for m < M and n < N,
+ *
+ *     C[m][n] = RNE_bf16( sigma * sum_{k<K} a(m,k) * b(n,k) + bias[n] )
+ *
+ * with one persistent launch of at most grid_cap workgroups, in which each
+ * workgroup owns a contiguous range of K-loop MAC iterations that may span
+ * several output tiles ("Stream-k mxfp4 kernel", tritonBLAS pull request 74:
+ * description and pull request overview).  A tile whose iterations are split
+ * between workgroups is finished by its owner after it has added the fp32
+ * partial tiles of the other workgroups in a fixed order, so the bits of C do
+ * not depend on timing.  The bias, when present, runs along N, is broadcast
+ * over the M rows and is added exactly once, after that aggregation ("Fix
+ * StreamK Kernel Bias #67", Motivation and Technical Details).  The grid cap
+ * mirrors a persistent GEMM confined to a chosen number of compute units
+ * ("SM-constraint-GEMM by triton persistent kernel", description and Nsys
+ * Results: a cap above the device's unit count is clamped to it).
+ *
+ * Layouts (all row-major, the K index contiguous):
+ *   MXFP4  A uint8[M][K/2], B uint8[N][K/2]: two OCP E2M1 codes per byte, the
+ *          even K index in the low nibble.  A_scale uint8[M][K/32],
+ *          B_scale uint8[N][K/32]: OCP E8M0 (value 2^(e-127)), one per 32
+ *          consecutive K elements starting at k = 0.  E8M0 0xFF (NaN) is
+ *          undefined input.  sigma = 1.
+ *   bf16   A uint16[M][K], B uint16[N][K] (bf16 bit patterns).  sigma = 1.
+ *   fp8    A uint8[M][K], B uint8[N][K], OCP E4M3FN.  A_scale / B_scale are
+ *          device pointers to one fp32 each (per-tensor), NULL meaning 1.0;
+ *          sigma = A_scale * B_scale, applied to the fp32 sum before the bias
+ *          (the bias is converted to fp32 for the add).
+ *   bias   bf16[N] bit patterns, or NULL.
+ *   C      bf16[M][N] bit patterns, written in full (every element).
+ * B is stored N x K (the transpose of the usual K x N), so A and B are read
+ * the same way.  C must not overlap any input.
+ *
+ * Precision: fp32 accumulation.  The one rounding to bf16 is round-to-
+ * nearest-even of the fp32 value sigma*acc (+) bias taken exactly (the sum is
+ * carried with its rounding error, so bias addition does not double-round).
+ *
+ * Ownership and asynchrony: all tensor pointers are device pointers owned by
+ * the caller and must stay valid until the stream has passed the launch.
+ * Calls enqueue on `stream` (a hipStream_t; NULL is the default stream) and
+ * return without waiting.  The library owns its scratch (fp32 partial tiles,
+ * lock flags, an error word), kept per (device, stream), grown on demand and
+ * freed by sk_release_workspace().  Device-side failures (a workgroup that
+ * waited past its spin limit) are reported by sk_check().
+ *
+ * Errors: every call returns an sk_status and never aborts.  Arguments are
+ * checked before anything is launched:
+ *   SK_ERR_ARG          a required pointer is NULL, M, N or K < 1, a size is
+ *                       beyond the supported range (M, N < 2^31, K <= 2^21),
+ *                       C overlaps an input, bf16 given scales, an unknown
+ *                       dtype / policy, or sk_addmm without a bias;
+ *   SK_ERR_ALIGN        MXFP4 K not a multiple of 32, fp8 K not a multiple of
+ *                       16, bf16 K not a multiple of 8 (a row of A or B must
+ *                       be a whole number of 16-byte chunks), or A, B, C not
+ *                       16-byte aligned, or bias not 2-byte aligned;
+ *   SK_ERR_UNSUPPORTED  the current device is not gfx950, or a tile override
+ *                       names no compiled kernel for that dtype;
+ *   SK_ERR_HIP          a HIP runtime call failed;
+ *   SK_ERR_NOMEM        scratch could not be allocated;
+ *   SK_ERR_TIMEOUT      (sk_check only) a workgroup gave up waiting for a
+ *                       partial tile; the affected output tiles are unwritten.
+ */
+#ifndef SK_GEMM_H
+#define SK_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sk_status {
+  SK_OK = 0,
+  SK_ERR_ARG = 1,
+  SK_ERR_ALIGN = 2,
+  SK_ERR_UNSUPPORTED = 3,
+  SK_ERR_HIP = 4,
+  SK_ERR_NOMEM = 5,
+  SK_ERR_TIMEOUT = 6
+} sk_status;
+
+typedef enum sk_dtype { SK_MXFP4 = 0, SK_BF16 = 1, SK_FP8_E4M3 = 2 } sk_dtype;
+
+/* How output tiles are divided between the persistent workgroups.
+ * HYBRID: whole tiles are dealt out round-robin ("data-parallel tail"), and
+ *   only the tiles that would leave the last round unbalanced -- the
+ *   remainder plus one full round -- are shared out by MAC iteration
+ *   (Stream-K head); no head when the tile count is a multiple of the grid.
+ * PURE_SK: every tile is shared out by MAC iteration.
+ * PURE_DP: whole tiles round-robin, no iteration splitting (the "Persistent"
+ *   path that the Stream-K switch turns off in "Fix StreamK Kernel Bias #67",
+ *   Improve StreamK Testing). */
+typedef enum sk_policy { SK_POLICY_HYBRID = 0, SK_POLICY_PURE_SK = 1, SK_POLICY_PURE_DP = 2 } sk_policy;
+
+/* sk_gemm_args.debug_flags bits (tests only). */
+#define SK_DEBUG_DELAY 1u       /* each workgroup sleeps a seeded pseudo-random time before publishing its partial */
+#define SK_DEBUG_DROP_SIGNAL 2u /* workgroup drop_signal_wg never publishes its partial tile's flag */
+
+/* MXFP4: A, B packed E2M1; A_scale, B_scale E8M0 (required).  bias may be NULL. */
+sk_status sk_gemm_mxfp4(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
+                        const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
+
+/* bf16 x bf16 -> bf16.  bias may be NULL. */
+sk_status sk_gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                       int grid_cap, void* stream);
+
+/* fp8 (E4M3FN) with per-tensor fp32 scales (device pointers to one float each, NULL = 1.0).  bias may be NULL. */
+sk_status sk_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* A_scale, const float* B_scale,
+                      const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
+
+/* addmm(bias, A, B) = the dtype's GEMM with a bias that is required (alpha = beta = 1).
+ * A_scale / B_scale as for that dtype (NULL for bf16). */
+sk_status sk_addmm(sk_dtype dtype, const void* bias, const void* A, const void* B, const void* A_scale,
+                   const void* B_scale, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
+
+/* Full-control entry point: the same kernels with a chosen policy and tile, plus test hooks.
+ * Zero-initialise and fill the fields you need. */
+typedef struct sk_gemm_args {
+  int32_t dtype;            /* sk_dtype */
+  int32_t policy;           /* sk_policy */
+  const void* A;
+  const void* B;
+  const void* A_scale;      /* MXFP4: uint8 [M][K/32]; fp8: device float* or NULL; bf16: NULL */
+  const void* B_scale;
+  const void* bias;         /* bf16[N] or NULL */
+  void* C;                  /* bf16[M][N] */
+  int64_t M, N, K;
+  int32_t grid_cap;         /* <= 0: every compute unit */
+  int32_t tile_m, tile_n;   /* 0, 0: automatic choice; else one of the compiled tiles of that dtype */
+  void* stream;             /* hipStream_t */
+  uint32_t debug_flags;     /* SK_DEBUG_* (tests only) */
+  uint32_t delay_seed;      /* with SK_DEBUG_DELAY */
+  int32_t drop_signal_wg;   /* with SK_DEBUG_DROP_SIGNAL */
+  int32_t reserved;
+  uint64_t spin_limit_ticks;/* owner wait limit in ticks of the 100 MHz device clock; 0 = 2e8 (2 s) */
+} sk_gemm_args;
+
+sk_status sk_gemm_ex(const sk_gemm_args* args);
+
+/* The partition a call would use (host-only; no device work).  num_cus = 0 asks the current device. */
+typedef struct sk_plan_query {
+  int32_t dtype, policy;
+  int64_t M, N, K;
+  int32_t grid_cap;
+  int32_t tile_m, tile_n;
+  int32_t num_cus;
+} sk_plan_query;
+
+typedef struct sk_plan_info {
+  int32_t tile_m, tile_n, tile_k;   /* output tile and K elements per MAC iteration */
+  int32_t tiles_m, tiles_n;
+  int64_t tiles;                    /* T */
+  int32_t iters_per_tile;           /* I = ceil(K / tile_k) */
+  int32_t grid;                     /* G, persistent workgroups launched */
+  int32_t policy;
+  int32_t variant;                  /* index of the compiled kernel */
+  int64_t sk_tiles;                 /* tiles [0, sk_tiles) are shared by iteration */
+  int64_t sk_iters;                 /* S = sk_tiles * I */
+  int64_t iters_per_wg;             /* q = S / G */
+  int64_t iters_extra;              /* r = S % G: workgroups w < r get q + 1 iterations */
+  int64_t scratch_bytes;            /* fp32 partial-tile scratch this call needs */
+  int32_t threads;                  /* threads per workgroup */
+  int32_t lds_bytes;                /* LDS per workgroup */
+} sk_plan_info;
+
+sk_status sk_plan(const sk_plan_query* q, sk_plan_info* out);
+
+/* Stream-K iteration range [begin, end) of workgroup wg under plan p (host-only). */
+sk_status sk_plan_wg_range(const sk_plan_info* p, int32_t wg, int64_t* begin, int64_t* end);
+
+/* One unit of a workgroup's work: MAC iterations [k0, k1) of output tile `tile`.
+ * mode 0: finish the tile (epilogue); 1: publish the fp32 partial for the tile's
+ * finisher; 2: add the partials of workgroups first .. wg-1 (descending), then finish. */
+typedef struct sk_work_item {
+  int64_t tile;
+  int32_t k0, k1;
+  int32_t mode;
+  int32_t first;
+} sk_work_item;
+
+/* The ordered work list the kernel runs for workgroup wg under plan p (host-only; the
+ * kernel walks the same list).  Writes at most max_items items; *count gets the total. */
+sk_status sk_plan_wg_work(const sk_plan_info* p, int32_t wg, sk_work_item* items, int32_t max_items,
+                          int32_t* count);
+
+/* Waits for `stream`, then reports (and clears) a device-side timeout recorded in this
+ * device/stream's scratch since the last check. */
+sk_status sk_check(void* stream);
+
+/* Waits for every stream that has scratch, then frees all scratch of every device. */
+void sk_release_workspace(void);
+
+/* Test hook: fill the current device/stream's scratch (grown to at least scratch_bytes) with
+ * NaN partials and stale lock values, so a following call must not depend on their contents. */
+sk_status sk_debug_poison_workspace(void* stream, int64_t scratch_bytes);
+
+/* Number of compiled kernels, and the shape of kernel `index` (host-only). */
+int32_t sk_num_variants(void);
+sk_status sk_variant_info(int32_t index, int32_t* dtype, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k,
+                          int32_t* threads, int32_t* lds_bytes);
+
+const char* sk_status_string(sk_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SK_GEMM_H */

@@ -1,1 +1,348 @@
-"""persistent_gemm_amd: a Stream-K GEMM for MI355X (gfx950) behind a small C ABI."""
+"""persistent_gemm_amd: a Stream-K GEMM for MI355X (gfx950) behind a small C ABI.
+
+This module is a thin ctypes binding over ``libskgemm.so`` (built from
+``persistent_gemm_amd/csrc`` by ``persistent_gemm_amd/build.py``): it checks
+tensor shapes and dtypes, passes device pointers and the current HIP stream,
+and turns status codes into exceptions.  Every step of the GEMM runs in the
+library's HIP kernels; there is no fallback.  PyTorch supplies device memory
+and streams only.
+
+Entry points mirror ``include/sk_gemm.h``:
+``gemm_mxfp4``, ``gemm_bf16``, ``gemm_fp8``, ``addmm`` and ``gemm_ex`` (policy,
+tile and test hooks), plus ``plan``, ``plan_wg_range``, ``check``,
+``release_workspace``, ``poison_workspace`` and ``variants``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "SkError", "MXFP4", "BF16", "FP8", "HYBRID", "PURE_SK", "PURE_DP", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
+    "library_path", "load", "gemm_mxfp4", "gemm_bf16", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
+    "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
+]
+
+MXFP4, BF16, FP8 = 0, 1, 2
+HYBRID, PURE_SK, PURE_DP = 0, 1, 2
+DEBUG_DELAY, DEBUG_DROP_SIGNAL = 1, 2
+
+_STATUS = {0: "SK_OK", 1: "SK_ERR_ARG", 2: "SK_ERR_ALIGN", 3: "SK_ERR_UNSUPPORTED", 4: "SK_ERR_HIP",
+           5: "SK_ERR_NOMEM", 6: "SK_ERR_TIMEOUT"}
+_DTYPES = {"mxfp4": MXFP4, "bf16": BF16, "fp8": FP8}
+
+
+class SkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        super().__init__(f"{where}: {self.name}")
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("policy", ctypes.c_int32),
+        ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
+        ("A_scale", ctypes.c_void_p), ("B_scale", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p), ("C", ctypes.c_void_p),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("grid_cap", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+        ("stream", ctypes.c_void_p),
+        ("debug_flags", ctypes.c_uint32), ("delay_seed", ctypes.c_uint32),
+        ("drop_signal_wg", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("spin_limit_ticks", ctypes.c_uint64),
+    ]
+
+
+class _PlanQuery(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("policy", ctypes.c_int32),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("grid_cap", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+    ]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+        ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
+        ("tiles", ctypes.c_int64), ("iters_per_tile", ctypes.c_int32), ("grid", ctypes.c_int32),
+        ("policy", ctypes.c_int32), ("variant", ctypes.c_int32),
+        ("sk_tiles", ctypes.c_int64), ("sk_iters", ctypes.c_int64),
+        ("iters_per_wg", ctypes.c_int64), ("iters_extra", ctypes.c_int64),
+        ("scratch_bytes", ctypes.c_int64), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+    ]
+
+
+class _WorkItem(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int64), ("k0", ctypes.c_int32), ("k1", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("first", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Plan:
+    tile_m: int
+    tile_n: int
+    tile_k: int
+    tiles_m: int
+    tiles_n: int
+    tiles: int
+    iters_per_tile: int
+    grid: int
+    policy: int
+    variant: int
+    sk_tiles: int
+    sk_iters: int
+    iters_per_wg: int
+    iters_extra: int
+    scratch_bytes: int
+    threads: int
+    lds_bytes: int
+    _raw: object = None
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskgemm.so")
+
+
+def load():
+    """Load libskgemm.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python persistent_gemm_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.sk_gemm_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.sk_gemm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.sk_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.sk_addmm.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.sk_gemm_ex.argtypes = [ctypes.POINTER(_Args)]
+    lib.sk_plan.argtypes = [ctypes.POINTER(_PlanQuery), ctypes.POINTER(_PlanInfo)]
+    lib.sk_plan_wg_range.argtypes = [ctypes.POINTER(_PlanInfo), ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.sk_plan_wg_work.argtypes = [ctypes.POINTER(_PlanInfo), ctypes.c_int32, ctypes.POINTER(_WorkItem),
+                                    ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.sk_check.argtypes = [vp]
+    lib.sk_release_workspace.argtypes = []
+    lib.sk_release_workspace.restype = None
+    lib.sk_debug_poison_workspace.argtypes = [vp, i64]
+    lib.sk_num_variants.argtypes = []
+    lib.sk_variant_info.argtypes = [ctypes.c_int32] + [ctypes.POINTER(ctypes.c_int32)] * 6
+    lib.sk_status_string.argtypes = [ctypes.c_int]
+    lib.sk_status_string.restype = ctypes.c_char_p
+    for name in ("sk_gemm_mxfp4", "sk_gemm_bf16", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
+                 "sk_plan_wg_range", "sk_plan_wg_work", "sk_check", "sk_debug_poison_workspace", "sk_variant_info"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.sk_num_variants.restype = ctypes.c_int32
+    _LIB = lib
+    return lib
+
+
+def _ok(status: int, where: str):
+    if status != 0:
+        raise SkError(status, where)
+
+
+# ---------------------------------------------------------------- tensor marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, name, dtypes, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _out(C, M, N, device):
+    torch = _torch()
+    if C is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    _need(C, "C", (torch.bfloat16, torch.int16, torch.uint16), (M, N), device)
+    return C
+
+
+def _marshal(dtype, A, B, A_scale, B_scale, bias, C):
+    """Checks tensors for one dtype; returns (M, N, K, C)."""
+    torch = _torch()
+    dev = A.device
+    if dtype == MXFP4:
+        M, kh = A.shape
+        N = B.shape[0]
+        K = 2 * kh
+        _need(A, "A", (torch.uint8,), (M, kh), dev)
+        _need(B, "B", (torch.uint8,), (N, kh), dev)
+        _need(A_scale, "A_scale", (torch.uint8,), (M, K // 32), dev)
+        _need(B_scale, "B_scale", (torch.uint8,), (N, K // 32), dev)
+    elif dtype == BF16:
+        M, K = A.shape
+        N = B.shape[0]
+        _need(A, "A", (torch.bfloat16, torch.int16, torch.uint16), (M, K), dev)
+        _need(B, "B", (torch.bfloat16, torch.int16, torch.uint16), (N, K), dev)
+        if A_scale is not None or B_scale is not None:
+            raise ValueError("bf16 takes no scales")
+    elif dtype == FP8:
+        M, K = A.shape
+        N = B.shape[0]
+        _need(A, "A", (torch.float8_e4m3fn, torch.uint8), (M, K), dev)
+        _need(B, "B", (torch.float8_e4m3fn, torch.uint8), (N, K), dev)
+        for s, nm in ((A_scale, "A_scale"), (B_scale, "B_scale")):
+            if s is not None:
+                _need(s, nm, (torch.float32,), tuple(s.shape), dev)
+                if s.numel() != 1:
+                    raise ValueError(f"{nm} must hold one fp32 value")
+    else:
+        raise ValueError(f"unknown dtype {dtype}")
+    if bias is not None:
+        _need(bias, "bias", (torch.bfloat16, torch.int16, torch.uint16), (N,), dev)
+    C = _out(C, M, N, dev)
+    return M, N, K, C
+
+
+def _dt(dtype):
+    return _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def gemm_mxfp4(A, B, A_scale, B_scale, bias=None, C=None, grid_cap=0, stream=None):
+    """C = A . B^T (+ bias) for packed MXFP4 operands; returns C (bf16 [M, N])."""
+    M, N, K, C = _marshal(MXFP4, A, B, A_scale, B_scale, bias, C)
+    _ok(load().sk_gemm_mxfp4(_ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale), _ptr(bias), _ptr(C), M, N, K,
+                             int(grid_cap), _stream(A, stream)), "sk_gemm_mxfp4")
+    return C
+
+
+def gemm_bf16(A, B, bias=None, C=None, grid_cap=0, stream=None):
+    M, N, K, C = _marshal(BF16, A, B, None, None, bias, C)
+    _ok(load().sk_gemm_bf16(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K, int(grid_cap), _stream(A, stream)),
+        "sk_gemm_bf16")
+    return C
+
+
+def gemm_fp8(A, B, A_scale=None, B_scale=None, bias=None, C=None, grid_cap=0, stream=None):
+    M, N, K, C = _marshal(FP8, A, B, A_scale, B_scale, bias, C)
+    _ok(load().sk_gemm_fp8(_ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale), _ptr(bias), _ptr(C), M, N, K,
+                           int(grid_cap), _stream(A, stream)), "sk_gemm_fp8")
+    return C
+
+
+def addmm(dtype, bias, A, B, A_scale=None, B_scale=None, C=None, grid_cap=0, stream=None):
+    """addmm(bias, A, B): the dtype's GEMM with a required bias (alpha = beta = 1)."""
+    d = _dt(dtype)
+    M, N, K, C = _marshal(d, A, B, A_scale, B_scale, bias, C)
+    _ok(load().sk_addmm(d, _ptr(bias), _ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale), _ptr(C), M, N, K,
+                        int(grid_cap), _stream(A, stream)), "sk_addmm")
+    return C
+
+
+def gemm_ex(dtype, A, B, A_scale=None, B_scale=None, bias=None, C=None, *, grid_cap=0, policy=HYBRID,
+            tile=None, stream=None, debug_flags=0, delay_seed=0, drop_signal_wg=-1, spin_limit_ticks=0):
+    """The same kernels with an explicit policy / tile and the test hooks of sk_gemm_ex."""
+    d = _dt(dtype)
+    M, N, K, C = _marshal(d, A, B, A_scale, B_scale, bias, C)
+    a = _Args()
+    a.dtype, a.policy = d, int(policy)
+    a.A, a.B, a.A_scale, a.B_scale = _ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale)
+    a.bias, a.C = _ptr(bias), _ptr(C)
+    a.M, a.N, a.K = M, N, K
+    a.grid_cap = int(grid_cap)
+    a.tile_m, a.tile_n = (0, 0) if tile is None else (int(tile[0]), int(tile[1]))
+    a.stream = _stream(A, stream)
+    a.debug_flags, a.delay_seed = int(debug_flags), int(delay_seed)
+    a.drop_signal_wg, a.spin_limit_ticks = int(drop_signal_wg), int(spin_limit_ticks)
+    _ok(load().sk_gemm_ex(ctypes.byref(a)), "sk_gemm_ex")
+    return C
+
+
+def plan(dtype, M, N, K, *, grid_cap=0, policy=HYBRID, tile=None, num_cus=0) -> Plan:
+    """The partition a call would use (host-only; num_cus=0 asks the current device)."""
+    q = _PlanQuery()
+    q.dtype, q.policy = _dt(dtype), int(policy)
+    q.M, q.N, q.K = int(M), int(N), int(K)
+    q.grid_cap = int(grid_cap)
+    q.tile_m, q.tile_n = (0, 0) if tile is None else (int(tile[0]), int(tile[1]))
+    q.num_cus = int(num_cus)
+    info = _PlanInfo()
+    _ok(load().sk_plan(ctypes.byref(q), ctypes.byref(info)), "sk_plan")
+    vals = {f: getattr(info, f) for f, _ in _PlanInfo._fields_}
+    return Plan(**vals, _raw=info)
+
+
+def plan_wg_range(p: Plan, wg: int):
+    b, e = ctypes.c_int64(), ctypes.c_int64()
+    _ok(load().sk_plan_wg_range(ctypes.byref(p._raw), int(wg), ctypes.byref(b), ctypes.byref(e)),
+        "sk_plan_wg_range")
+    return b.value, e.value
+
+
+def plan_wg_work(p: Plan, wg: int):
+    """Ordered work list of workgroup wg: tuples (tile, k0, k1, mode, first); mode 0 whole, 1 contributor, 2 owner."""
+    lib = load()
+    n = ctypes.c_int32()
+    _ok(lib.sk_plan_wg_work(ctypes.byref(p._raw), int(wg), None, 0, ctypes.byref(n)), "sk_plan_wg_work")
+    buf = (_WorkItem * max(n.value, 1))()
+    _ok(lib.sk_plan_wg_work(ctypes.byref(p._raw), int(wg), buf, n.value, ctypes.byref(n)), "sk_plan_wg_work")
+    return [(x.tile, x.k0, x.k1, x.mode, x.first) for x in buf[:n.value]]
+
+
+def check(stream=None):
+    """Waits for the stream; raises SkError(SK_ERR_TIMEOUT) if a workgroup gave up waiting."""
+    if stream is None:
+        torch = _torch()
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _ok(load().sk_check(stream), "sk_check")
+
+
+def release_workspace():
+    load().sk_release_workspace()
+
+
+def poison_workspace(scratch_bytes: int, stream=None):
+    if stream is None:
+        torch = _torch()
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _ok(load().sk_debug_poison_workspace(stream, int(scratch_bytes)), "sk_debug_poison_workspace")
+
+
+def variants():
+    """Compiled kernel shapes: list of dicts (dtype, tile_m, tile_n, tile_k, threads, lds_bytes)."""
+    lib = load()
+    out = []
+    for i in range(lib.sk_num_variants()):
+        v = [ctypes.c_int32() for _ in range(6)]
+        _ok(lib.sk_variant_info(i, *[ctypes.byref(x) for x in v]), "sk_variant_info")
+        out.append(dict(zip(("dtype", "tile_m", "tile_n", "tile_k", "threads", "lds_bytes"), [x.value for x in v])))
+    return out

@@ -1,0 +1,485 @@
+// C ABI of the Stream-K GEMM library: argument checks, the Stream-K planner,
+// per-(device, stream) scratch, and the launch.
+//
+// The scratch (fp32 partial tiles P, lock flags, an error word) is owned here
+// and cached per device *and* stream, never shared between devices: a single
+// global buffer on the default device breaks calls made on another GPU
+// ("Stream-k mxfp4 kernel", Copilot comment on the global Stream-K scratch
+// buffers).  The flags carry a per-launch epoch, so their old contents never
+// matter (freshly allocated lock buffers may hold anything).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/sk_gemm.h"
+#include "sk_common.h"
+
+namespace {
+
+using sk::KArgs;
+using sk::Variant;
+
+constexpr int64_t kMaxMN = (int64_t)1 << 31;
+constexpr int64_t kMaxK = (int64_t)1 << 21;
+constexpr uint64_t kDefaultSpin = 200000000ull;  // 2 s of the 100 MHz device clock
+
+struct DeviceInfo {
+  bool ok = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+
+struct Workspace {
+  int device = -1;
+  hipStream_t stream = nullptr;
+  float* P = nullptr;
+  size_t p_bytes = 0;
+  uint32_t* flags = nullptr;  // kMaxGrid locks, then the error word
+  uint32_t epoch = 0;         // last epoch used
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, uintptr_t>, Workspace*> g_ws;
+std::map<int, DeviceInfo> g_dev;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dtype_ok(int d) { return d == SK_MXFP4 || d == SK_BF16 || d == SK_FP8_E4M3; }
+
+// Bytes of one row of A or B for K elements.
+int64_t row_bytes(int dtype, int64_t K) {
+  switch (dtype) {
+    case SK_MXFP4: return K / 2;
+    case SK_BF16: return 2 * K;
+    default: return K;
+  }
+}
+
+sk_status device_info(int* dev_out, DeviceInfo* info) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SK_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_dev.find(dev);
+  if (it == g_dev.end()) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return SK_ERR_HIP;
+    DeviceInfo d;
+    d.ok = true;
+    d.gfx950 = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    d.cus = p.multiProcessorCount;
+    it = g_dev.emplace(dev, d).first;
+  }
+  *dev_out = dev;
+  *info = it->second;
+  return SK_OK;
+}
+
+// Kernel shape: an explicit (tile_m, tile_n), else a choice by problem shape.
+int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n) {
+  const int nv = sk::num_variants();
+  auto find = [&](int bm, int bn) {
+    for (int i = 0; i < nv; ++i) {
+      const Variant* v = sk::variant(i);
+      if (v->dtype == dtype && v->bm == bm && v->bn == bn) return i;
+    }
+    return -1;
+  };
+  if (tile_m > 0 || tile_n > 0) return find(tile_m, tile_n);
+  if (M <= 16) {
+    int i = find(16, 256);
+    if (i >= 0) return i;
+  }
+  if (M <= 64 && N <= 64) {
+    int i = find(64, 64);
+    if (i >= 0) return i;
+  }
+  if (M * N <= (int64_t)2048 * 2048) {
+    int i = find(128, 128);
+    if (i >= 0) return i;
+  }
+  return find(256, 256);
+}
+
+sk_status make_plan(int dtype, int policy, int64_t M, int64_t N, int64_t K, int grid_cap, int tile_m, int tile_n,
+                    int num_cus, sk_plan_info* p) {
+  if (!dtype_ok(dtype)) return SK_ERR_ARG;
+  if (policy < SK_POLICY_HYBRID || policy > SK_POLICY_PURE_DP) return SK_ERR_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxMN || N >= kMaxMN || K > kMaxK) return SK_ERR_ARG;
+  if (num_cus < 1) return SK_ERR_ARG;
+  const int vi = pick_variant(dtype, M, N, tile_m, tile_n);
+  if (vi < 0) return SK_ERR_UNSUPPORTED;
+  const Variant* v = sk::variant(vi);
+  std::memset(p, 0, sizeof(*p));
+  p->tile_m = v->bm;
+  p->tile_n = v->bn;
+  p->tile_k = v->bk;
+  p->tiles_m = (int32_t)cdiv(M, v->bm);
+  p->tiles_n = (int32_t)cdiv(N, v->bn);
+  p->tiles = (int64_t)p->tiles_m * p->tiles_n;
+  p->iters_per_tile = (int32_t)cdiv(K, v->bk);
+  p->policy = policy;
+  p->variant = vi;
+  p->threads = v->threads;
+  p->lds_bytes = v->lds;
+  int64_t cap = grid_cap <= 0 ? num_cus : (grid_cap < num_cus ? grid_cap : num_cus);
+  if (cap > sk::kMaxGrid) cap = sk::kMaxGrid;
+  const int64_t T = p->tiles, I = p->iters_per_tile;
+  int64_t G, sk_tiles;
+  if (policy == SK_POLICY_PURE_DP) {
+    G = cap < T ? cap : T;
+    sk_tiles = 0;
+  } else if (policy == SK_POLICY_PURE_SK) {
+    G = cap < T * I ? cap : T * I;
+    sk_tiles = T;
+  } else {
+    if (T >= cap) {
+      G = cap;
+      const int64_t rem = T % G;
+      sk_tiles = rem == 0 ? 0 : rem + G;
+      if (sk_tiles > T) sk_tiles = T;
+    } else {
+      G = cap < T * I ? cap : T * I;
+      sk_tiles = T;
+    }
+  }
+  p->grid = (int32_t)G;
+  p->sk_tiles = sk_tiles;
+  p->sk_iters = sk_tiles * I;
+  p->iters_per_wg = p->sk_iters / G;
+  p->iters_extra = p->sk_iters % G;
+  p->scratch_bytes = sk_tiles > 0 ? G * (int64_t)v->bm * v->bn * (int64_t)sizeof(float) : 0;
+  return SK_OK;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+sk_status validate(const sk_gemm_args& g) {
+  if (!dtype_ok(g.dtype)) return SK_ERR_ARG;
+  if (g.policy < SK_POLICY_HYBRID || g.policy > SK_POLICY_PURE_DP) return SK_ERR_ARG;
+  if (!g.A || !g.B || !g.C) return SK_ERR_ARG;
+  if (g.M < 1 || g.N < 1 || g.K < 1 || g.M >= kMaxMN || g.N >= kMaxMN || g.K > kMaxK) return SK_ERR_ARG;
+  if (g.dtype == SK_MXFP4 && (!g.A_scale || !g.B_scale)) return SK_ERR_ARG;
+  if (g.dtype == SK_BF16 && (g.A_scale || g.B_scale)) return SK_ERR_ARG;
+  if (g.dtype == SK_MXFP4 && g.K % 32) return SK_ERR_ALIGN;
+  if (g.dtype == SK_FP8_E4M3 && g.K % 16) return SK_ERR_ALIGN;
+  if (g.dtype == SK_BF16 && g.K % 8) return SK_ERR_ALIGN;
+  if (((uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)g.C) & 15) return SK_ERR_ALIGN;
+  if (g.bias && ((uintptr_t)g.bias & 1)) return SK_ERR_ALIGN;
+  if (g.dtype == SK_FP8_E4M3 && (((uintptr_t)g.A_scale | (uintptr_t)g.B_scale) & 3)) return SK_ERR_ALIGN;
+  const int64_t rb = row_bytes(g.dtype, g.K);
+  const int64_t c_bytes = g.M * g.N * 2;
+  const int64_t sbytes = g.dtype == SK_MXFP4 ? g.K / 32 : (g.dtype == SK_FP8_E4M3 ? 4 : 0);
+  if (overlaps(g.C, c_bytes, g.A, g.M * rb) || overlaps(g.C, c_bytes, g.B, g.N * rb) ||
+      overlaps(g.C, c_bytes, g.bias, g.N * 2) ||
+      overlaps(g.C, c_bytes, g.A_scale, g.dtype == SK_MXFP4 ? g.M * sbytes : sbytes) ||
+      overlaps(g.C, c_bytes, g.B_scale, g.dtype == SK_MXFP4 ? g.N * sbytes : sbytes))
+    return SK_ERR_ARG;
+  return SK_OK;
+}
+
+// Scratch of (device, stream), grown to p_bytes; called with g_mu unlocked.
+sk_status get_workspace(int dev, hipStream_t stream, size_t p_bytes, Workspace** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const auto key = std::make_pair(dev, (uintptr_t)stream);
+  Workspace*& ws = g_ws[key];
+  if (!ws) {
+    Workspace* w = new Workspace();
+    w->device = dev;
+    w->stream = stream;
+    if (hipMalloc((void**)&w->flags, sk::kFlagWords * sizeof(uint32_t)) != hipSuccess) {
+      delete w;
+      g_ws.erase(key);
+      return SK_ERR_NOMEM;
+    }
+    if (hipMemset(w->flags, 0, sk::kFlagWords * sizeof(uint32_t)) != hipSuccess) {
+      hipFree(w->flags);
+      delete w;
+      g_ws.erase(key);
+      return SK_ERR_HIP;
+    }
+    ws = w;
+  }
+  if (p_bytes > ws->p_bytes) {
+    // The old buffer may still be read by work queued on this stream.
+    if (ws->P) {
+      if (hipStreamSynchronize(stream) != hipSuccess) return SK_ERR_HIP;
+      hipFree(ws->P);
+      ws->P = nullptr;
+      ws->p_bytes = 0;
+    }
+    size_t want = p_bytes;
+    if (hipMalloc((void**)&ws->P, want) != hipSuccess) {
+      ws->P = nullptr;
+      return SK_ERR_NOMEM;
+    }
+    ws->p_bytes = want;
+  }
+  *out = ws;
+  return SK_OK;
+}
+
+// Next epoch of a workspace; restarts the flags when the counter would wrap.
+sk_status next_epoch(Workspace* ws, uint32_t* epoch) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (ws->epoch == 0xFFFFFFFFu) {
+    if (hipMemsetAsync(ws->flags, 0, sk::kMaxGrid * sizeof(uint32_t), ws->stream) != hipSuccess) return SK_ERR_HIP;
+    ws->epoch = 0;
+  }
+  *epoch = ++ws->epoch;
+  return SK_OK;
+}
+
+sk_status run(const sk_gemm_args& g) {
+  sk_status st = validate(g);
+  if (st != SK_OK) return st;
+  int dev = 0;
+  DeviceInfo info;
+  st = device_info(&dev, &info);
+  if (st != SK_OK) return st;
+  if (!info.gfx950) return SK_ERR_UNSUPPORTED;
+  sk_plan_info p;
+  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, info.cus, &p);
+  if (st != SK_OK) return st;
+  hipStream_t stream = (hipStream_t)g.stream;
+  Workspace* ws = nullptr;
+  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, &ws);
+  if (st != SK_OK) return st;
+  uint32_t epoch = 0;
+  st = next_epoch(ws, &epoch);
+  if (st != SK_OK) return st;
+
+  const Variant* v = sk::variant(p.variant);
+  KArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.A = (const uint8_t*)g.A;
+  a.B = (const uint8_t*)g.B;
+  if (g.dtype == SK_MXFP4) {
+    a.SA = (const uint8_t*)g.A_scale;
+    a.SB = (const uint8_t*)g.B_scale;
+  } else if (g.dtype == SK_FP8_E4M3) {
+    a.fsa = (const float*)g.A_scale;
+    a.fsb = (const float*)g.B_scale;
+  }
+  a.bias = (const uint16_t*)g.bias;
+  a.C = (uint16_t*)g.C;
+  a.P = ws->P;
+  a.locks = ws->flags;
+  a.err = ws->flags + sk::kErrIndex;
+  a.M = g.M;
+  a.N = g.N;
+  a.K = g.K;
+  a.row_bytes = row_bytes(g.dtype, g.K);
+  a.a_pitch = a.row_bytes;
+  a.b_pitch = a.row_bytes;
+  a.s_pitch = g.dtype == SK_MXFP4 ? g.K / 32 : 0;
+  a.tiles = p.tiles;
+  a.sk_tiles = p.sk_tiles;
+  a.q = p.iters_per_wg;
+  a.r = p.iters_extra;
+  a.tiles_m = p.tiles_m;
+  a.tiles_n = p.tiles_n;
+  a.iters = p.iters_per_tile;
+  a.G = p.grid;
+  a.epoch = epoch;
+  const int spr = v->kb / 16;
+  a.scale_fast = (g.dtype == SK_MXFP4 && a.s_pitch % spr == 0 && a.s_pitch % 8 == 0 &&
+                  ((uintptr_t)g.A_scale % 8) == 0 && ((uintptr_t)g.B_scale % 8) == 0)
+                     ? 1u
+                     : 0u;
+  a.spin_limit = g.spin_limit_ticks ? g.spin_limit_ticks : kDefaultSpin;
+  a.drop_wg = (g.debug_flags & SK_DEBUG_DROP_SIGNAL) ? g.drop_signal_wg : -1;
+  a.delay_seed = (g.debug_flags & SK_DEBUG_DELAY) ? (g.delay_seed ? g.delay_seed : 1u) : 0u;
+  if (v->launch(p.grid, a, stream) != hipSuccess) return SK_ERR_HIP;
+  return SK_OK;
+}
+
+sk_gemm_args base_args(int dtype, const void* A, const void* B, const void* sa, const void* sb, const void* bias,
+                       void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream) {
+  sk_gemm_args g;
+  std::memset(&g, 0, sizeof(g));
+  g.dtype = dtype;
+  g.policy = SK_POLICY_HYBRID;
+  g.A = A;
+  g.B = B;
+  g.A_scale = sa;
+  g.B_scale = sb;
+  g.bias = bias;
+  g.C = C;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.grid_cap = grid_cap;
+  g.stream = stream;
+  g.drop_signal_wg = -1;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+sk_status sk_gemm_mxfp4(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
+                        const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream) {
+  return run(base_args(SK_MXFP4, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
+}
+
+sk_status sk_gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                       int grid_cap, void* stream) {
+  return run(base_args(SK_BF16, A, B, nullptr, nullptr, bias, C, M, N, K, grid_cap, stream));
+}
+
+sk_status sk_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* A_scale, const float* B_scale,
+                      const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream) {
+  return run(base_args(SK_FP8_E4M3, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
+}
+
+sk_status sk_addmm(sk_dtype dtype, const void* bias, const void* A, const void* B, const void* A_scale,
+                   const void* B_scale, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream) {
+  if (!bias) return SK_ERR_ARG;
+  return run(base_args((int)dtype, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
+}
+
+sk_status sk_gemm_ex(const sk_gemm_args* args) {
+  if (!args) return SK_ERR_ARG;
+  return run(*args);
+}
+
+sk_status sk_plan(const sk_plan_query* q, sk_plan_info* out) {
+  if (!q || !out) return SK_ERR_ARG;
+  int cus = q->num_cus;
+  if (cus <= 0) {
+    int dev = 0;
+    DeviceInfo info;
+    sk_status st = device_info(&dev, &info);
+    if (st != SK_OK) return st;
+    cus = info.cus;
+  }
+  return make_plan(q->dtype, q->policy, q->M, q->N, q->K, q->grid_cap, q->tile_m, q->tile_n, cus, out);
+}
+
+sk_status sk_plan_wg_range(const sk_plan_info* p, int32_t wg, int64_t* begin, int64_t* end) {
+  if (!p || !begin || !end || wg < 0 || wg >= p->grid) return SK_ERR_ARG;
+  if (p->sk_tiles == 0) {
+    *begin = *end = 0;
+    return SK_OK;
+  }
+  *begin = sk::sk_begin(wg, p->iters_per_wg, p->iters_extra);
+  *end = sk::sk_begin(wg + 1, p->iters_per_wg, p->iters_extra);
+  return SK_OK;
+}
+
+sk_status sk_plan_wg_work(const sk_plan_info* p, int32_t wg, sk_work_item* items, int32_t max_items,
+                          int32_t* count) {
+  if (!p || !count || wg < 0 || wg >= p->grid || max_items < 0 || (max_items > 0 && !items)) return SK_ERR_ARG;
+  sk::WorkIter work(wg, p->sk_tiles, p->tiles, p->iters_per_tile, p->iters_per_wg, p->iters_extra, p->grid);
+  sk::WorkItem it;
+  int32_t n = 0;
+  while (work.next(it)) {
+    if (n < max_items) {
+      items[n].tile = it.tile;
+      items[n].k0 = it.k0;
+      items[n].k1 = it.k1;
+      items[n].mode = it.mode;
+      items[n].first = it.first;
+    }
+    ++n;
+  }
+  *count = n;
+  return SK_OK;
+}
+
+sk_status sk_check(void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SK_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SK_ERR_HIP;
+  Workspace* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_ws.find(std::make_pair(dev, (uintptr_t)stream));
+    if (it == g_ws.end()) return SK_OK;
+    ws = it->second;
+  }
+  uint32_t err = 0;
+  if (hipMemcpy(&err, ws->flags + sk::kErrIndex, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return SK_ERR_HIP;
+  if (err) {
+    if (hipMemset(ws->flags + sk::kErrIndex, 0, sizeof(uint32_t)) != hipSuccess) return SK_ERR_HIP;
+    return SK_ERR_TIMEOUT;
+  }
+  return SK_OK;
+}
+
+void sk_release_workspace(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_ws) {
+    Workspace* ws = kv.second;
+    if (!ws) continue;
+    hipSetDevice(ws->device);
+    hipStreamSynchronize(ws->stream);
+    if (ws->P) hipFree(ws->P);
+    if (ws->flags) hipFree(ws->flags);
+    delete ws;
+  }
+  g_ws.clear();
+  if (have_cur) hipSetDevice(cur);
+}
+
+sk_status sk_debug_poison_workspace(void* stream, int64_t scratch_bytes) {
+  int dev = 0;
+  DeviceInfo info;
+  sk_status st = device_info(&dev, &info);
+  if (st != SK_OK) return st;
+  Workspace* ws = nullptr;
+  st = get_workspace(dev, (hipStream_t)stream, scratch_bytes > 0 ? (size_t)scratch_bytes : 0, &ws);
+  if (st != SK_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (ws->P && hipMemsetAsync(ws->P, 0xFF, ws->p_bytes, s) != hipSuccess) return SK_ERR_HIP;  // all-ones = NaN
+  // Stale flags: the current epoch, which the next launch (epoch + 1) must not accept.
+  std::vector<uint32_t> stale(sk::kMaxGrid, ws->epoch);
+  if (hipMemcpyAsync(ws->flags, stale.data(), stale.size() * sizeof(uint32_t), hipMemcpyHostToDevice, s) != hipSuccess)
+    return SK_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SK_ERR_HIP;
+  return SK_OK;
+}
+
+int32_t sk_num_variants(void) { return sk::num_variants(); }
+
+sk_status sk_variant_info(int32_t index, int32_t* dtype, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k,
+                          int32_t* threads, int32_t* lds_bytes) {
+  const Variant* v = sk::variant(index);
+  if (!v) return SK_ERR_ARG;
+  if (dtype) *dtype = v->dtype;
+  if (tile_m) *tile_m = v->bm;
+  if (tile_n) *tile_n = v->bn;
+  if (tile_k) *tile_k = v->bk;
+  if (threads) *threads = v->threads;
+  if (lds_bytes) *lds_bytes = v->lds;
+  return SK_OK;
+}
+
+const char* sk_status_string(sk_status s) {
+  switch (s) {
+    case SK_OK: return "ok";
+    case SK_ERR_ARG: return "invalid argument";
+    case SK_ERR_ALIGN: return "misaligned size or pointer";
+    case SK_ERR_UNSUPPORTED: return "unsupported device or tile";
+    case SK_ERR_HIP: return "HIP runtime error";
+    case SK_ERR_NOMEM: return "out of device memory";
+    case SK_ERR_TIMEOUT: return "a workgroup timed out waiting for a partial tile";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

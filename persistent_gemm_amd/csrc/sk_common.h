@@ -1,0 +1,162 @@
+// Shared between the host side (planner, launch) and the device side (kernel).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sk {
+
+enum : int { DT_MXFP4 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+// Lock flags per scratch area; the grid never exceeds this many workgroups.
+constexpr int kMaxGrid = 1024;
+// Index of the device error word inside the flag array.
+constexpr int kErrIndex = kMaxGrid;
+constexpr int kFlagWords = kMaxGrid + 64;
+
+// Everything one launch needs.  Pointers are device pointers.
+struct KArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  const uint8_t* SA;        // MXFP4 block scales of A, [M][K/32]
+  const uint8_t* SB;        // MXFP4 block scales of B, [N][K/32]
+  const float* fsa;         // fp8 per-tensor scale of A (NULL = 1)
+  const float* fsb;         // fp8 per-tensor scale of B (NULL = 1)
+  const uint16_t* bias;     // bf16[N] or NULL
+  uint16_t* C;              // bf16[M][N]
+  float* P;                 // fp32 partial tiles, one BM*BN slot per workgroup
+  uint32_t* locks;          // one flag per workgroup; flag == epoch means "partial published"
+  uint32_t* err;            // set to 1 when a wait gives up
+  int64_t M, N, K;
+  int64_t a_pitch;          // bytes per row of A
+  int64_t b_pitch;          // bytes per row of B
+  int64_t s_pitch;          // bytes per row of the MXFP4 scales (K/32)
+  int64_t row_bytes;        // bytes of K data per row (== a_pitch == b_pitch)
+  int64_t tiles;            // T
+  int64_t sk_tiles;         // tiles [0, sk_tiles) are split by MAC iteration
+  int64_t q, r;             // Stream-K iterations S = q*G + r
+  int32_t tiles_m, tiles_n;
+  int32_t iters;            // I, MAC iterations (k-steps) per tile
+  int32_t G;                // persistent workgroups
+  uint32_t epoch;           // this launch's flag value
+  uint32_t scale_fast;      // 1: every k-step of scales is whole and 8-byte aligned
+  uint64_t spin_limit;      // ticks of the 100 MHz realtime counter
+  int32_t drop_wg;          // test hook: this workgroup never publishes (-1: none)
+  uint32_t delay_seed;      // test hook: nonzero = seeded sleeps before publishing
+};
+
+// Stream-K partition of S = q*G + r MAC iterations: workgroup w owns
+// [begin(w), begin(w+1)), the first r workgroups getting one extra iteration.
+__host__ __device__ inline int64_t sk_begin(int64_t w, int64_t q, int64_t r) {
+  return w * q + (w < r ? w : r);
+}
+
+// The workgroup whose range holds iteration x (x < S).
+__host__ __device__ inline int64_t sk_owner_of(int64_t x, int64_t q, int64_t r) {
+  const int64_t big = r * (q + 1);
+  if (x < big) return x / (q + 1);
+  return r + (x - big) / q;  // q > 0 here, because x < S
+}
+
+// One unit of work of a workgroup: MAC iterations [k0, k1) of one tile.
+enum : int { WORK_WHOLE = 0, WORK_CONTRIB = 1, WORK_OWNER = 2 };
+struct WorkItem {
+  int64_t tile;
+  int32_t k0, k1;
+  int32_t mode;       // WORK_WHOLE: finish the tile; WORK_CONTRIB: publish a partial;
+                      // WORK_OWNER: add the partials of workgroups [first, w) then finish
+  int32_t first;      // WORK_OWNER only: lowest contributing workgroup
+};
+
+// The work of workgroup w, in the order it is done:
+//   1. the contributor segment, when w's Stream-K range ends inside a tile;
+//   2. the whole tiles inside the range;
+//   3. the owned split tile, when the range starts inside a tile and reaches its end;
+//   4. the data-parallel tiles sk_tiles + w + j*G.
+// Contributions come first and owners wait only on lower workgroups, so no
+// workgroup ever waits on one that could be waiting on it.
+struct WorkIter {
+  int64_t s, e, I, tf, tl, whole, whole_end, dp, tiles, q, r;
+  int32_t G, phase;
+  bool contrib, owner;
+
+  __host__ __device__ WorkIter(int64_t w, int64_t sk_tiles, int64_t tiles_, int64_t iters, int64_t q_, int64_t r_,
+                               int32_t G_) {
+    I = iters;
+    q = q_;
+    r = r_;
+    G = G_;
+    tiles = tiles_;
+    s = e = 0;
+    if (sk_tiles > 0) {
+      s = sk_begin(w, q, r);
+      e = sk_begin(w + 1, q, r);
+    }
+    const bool any = s < e;
+    tf = any ? s / I : 0;
+    tl = any ? (e - 1) / I : 0;
+    contrib = any && (e % I) != 0;
+    owner = any && (s % I) != 0 && (tf < tl || (e % I) == 0);
+    whole = any ? ((s % I) ? tf + 1 : tf) : 0;
+    whole_end = any ? ((e % I) ? tl : tl + 1) : 0;
+    dp = sk_tiles + w;
+    phase = 0;
+  }
+
+  __host__ __device__ bool next(WorkItem& it) {
+    for (;;) {
+      it.k0 = 0;
+      it.k1 = (int32_t)I;
+      it.first = -1;
+      if (phase == 0) {
+        phase = 1;
+        if (!contrib) continue;
+        it.tile = tl;
+        it.k0 = (int32_t)((s > tl * I ? s : tl * I) - tl * I);
+        it.k1 = (int32_t)(e - tl * I);
+        it.mode = WORK_CONTRIB;
+        return true;
+      }
+      if (phase == 1) {
+        if (whole >= whole_end) {
+          phase = 2;
+          continue;
+        }
+        it.tile = whole++;
+        it.mode = WORK_WHOLE;
+        return true;
+      }
+      if (phase == 2) {
+        phase = 3;
+        if (!owner) continue;
+        it.tile = tf;
+        it.k0 = (int32_t)(s - tf * I);
+        it.mode = WORK_OWNER;
+        it.first = (int32_t)sk_owner_of(tf * I, q, r);
+        return true;
+      }
+      if (dp >= tiles) return false;
+      it.tile = dp;
+      dp += G;
+      it.mode = WORK_WHOLE;
+      return true;
+    }
+  }
+};
+
+// One compiled kernel shape.
+struct Variant {
+  int dtype;
+  int bm, bn;       // output tile
+  int kb;           // bytes of each operand row per MAC iteration
+  int bk;           // K elements per MAC iteration
+  int mfma;         // 32 (32x32 MFMA) or 16 (16x16 MFMA)
+  int threads;
+  int lds;
+  hipError_t (*launch)(int grid, const KArgs& a, hipStream_t s);
+};
+
+int num_variants();
+const Variant* variant(int index);
+
+}  // namespace sk

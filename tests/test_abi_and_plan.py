@@ -1,0 +1,203 @@
+"""Host-side tests of the C ABI (no GPU): exported symbols, argument checks,
+and the Stream-K planner / work lists that the kernel walks."""
+
+from __future__ import annotations
+
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import persistent_gemm_amd as pg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sk_gemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pg.load()
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_variants_table():
+    v = pg.variants()
+    shapes = {(x["dtype"], x["tile_m"], x["tile_n"]) for x in v}
+    for need in [(pg.MXFP4, 256, 256), (pg.MXFP4, 64, 64), (pg.MXFP4, 16, 256), (pg.BF16, 256, 256),
+                 (pg.BF16, 128, 192), (pg.FP8, 256, 256)]:
+        assert need in shapes
+    for x in v:
+        assert x["threads"] == 256 and 0 < x["lds_bytes"] <= 160 * 1024
+
+
+# ---------------------------------------------------------------- argument checks (host only)
+
+def _args(**kw):
+    a = pg._Args()
+    a.dtype, a.policy = pg.MXFP4, pg.HYBRID
+    a.A, a.B, a.A_scale, a.B_scale, a.C = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    a.M, a.N, a.K = 64, 64, 128
+    a.drop_signal_wg = -1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), 1), (dict(B=None), 1), (dict(C=None), 1), (dict(A_scale=None), 1),
+    (dict(M=0), 1), (dict(N=-3), 1), (dict(K=0), 1), (dict(K=(1 << 21) + 32), 1), (dict(M=1 << 31), 1),
+    (dict(dtype=7), 1), (dict(policy=9), 1),
+    (dict(K=48), 2), (dict(A=0x10008), 2), (dict(C=0x50002), 2), (dict(bias=0x60001), 2),
+    (dict(C=0x10000 + 64), 1),                        # C overlaps A
+    (dict(dtype=pg.BF16, K=12, A_scale=None, B_scale=None), 2),
+    (dict(dtype=pg.BF16), 1),                         # bf16 takes no scales
+    (dict(dtype=pg.FP8, K=24), 2),
+    (dict(dtype=pg.FP8, A_scale=0x30002), 2),
+])
+def test_argument_checks(kw, status):
+    a = _args(**kw)
+    assert pg.load().sk_gemm_ex(ctypes.byref(a)) == status
+
+
+def test_addmm_requires_bias():
+    lib = pg.load()
+    assert lib.sk_addmm(0, None, 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 64, 64, 128, 0, None) == 1
+
+
+def test_status_strings():
+    lib = pg.load()
+    for s in range(7):
+        assert lib.sk_status_string(s)
+    assert lib.sk_check  # exported
+
+
+# ---------------------------------------------------------------- planner
+
+def test_plan_worked_mxfp4_64x64_grid5():
+    # 256 x 256 x 512 MXFP4 on 64 x 64 tiles with 128 K per iteration and 5 workgroups.
+    p = pg.plan("mxfp4", 256, 256, 512, grid_cap=5, tile=(64, 64), num_cus=256)
+    assert (p.tiles, p.iters_per_tile, p.grid) == (16, 4, 5)
+    assert (p.sk_tiles, p.sk_iters, p.iters_per_wg, p.iters_extra) == (6, 24, 4, 4)
+    assert [pg.plan_wg_range(p, w) for w in range(5)] == [(0, 5), (5, 10), (10, 15), (15, 20), (20, 24)]
+    # tiles 1, 2, 3 are split; the holder of the last iteration finishes each one
+    assert pg.plan_wg_work(p, 1) == [(2, 0, 2, 1, -1), (1, 1, 4, 2, 0), (7, 0, 4, 0, -1), (12, 0, 4, 0, -1)]
+    ps = pg.plan("mxfp4", 256, 256, 512, grid_cap=5, tile=(64, 64), num_cus=256, policy=pg.PURE_SK)
+    assert [pg.plan_wg_range(ps, w) for w in range(5)] == [(0, 13), (13, 26), (26, 39), (39, 52), (52, 64)]
+
+
+def test_plan_worked_large():
+    # 4096^3 bf16 on 256 x 256 tiles: 256 tiles on 256 CUs -> no Stream-K head.
+    p = pg.plan("bf16", 4096, 4096, 4096, num_cus=256)
+    assert (p.tile_m, p.tile_n, p.tiles, p.grid, p.sk_tiles) == (256, 256, 256, 256, 0)
+    # 128 x 192 tiles: 32 x 22 = 704 tiles -> head of 192 + 256 tiles, tail of 256 (one round).
+    p = pg.plan("bf16", 4096, 4096, 4096, tile=(128, 192), num_cus=256)
+    assert (p.tiles, p.sk_tiles, p.tiles - p.sk_tiles) == (704, 448, 256)
+    # 8192^3 MXFP4: 1024 tiles, four data-parallel rounds, no head.
+    p = pg.plan("mxfp4", 8192, 8192, 8192, num_cus=256)
+    assert (p.tiles, p.iters_per_tile, p.sk_tiles, p.grid) == (1024, 32, 0, 256)
+    # skinny 16 x 8192 x 8192 MXFP4: 32 tiles of 16 x 256, all Stream-K, 8 workgroups per tile.
+    p = pg.plan("mxfp4", 16, 8192, 8192, num_cus=256)
+    assert (p.tile_m, p.tile_n, p.tiles, p.sk_tiles, p.grid, p.iters_per_wg, p.iters_extra) == \
+        (16, 256, 32, 32, 256, 4, 0)
+    # the cap clamps to the CU count
+    assert pg.plan("fp8", 4096, 4096, 4096, grid_cap=300, num_cus=256).grid == 256
+    assert pg.plan("fp8", 4096, 4096, 4096, grid_cap=32, num_cus=256).grid == 32
+
+
+def _check_plan(p, cap):
+    T, I, G = p.tiles, p.iters_per_tile, p.grid
+    assert 1 <= G <= cap
+    work = [pg.plan_wg_work(p, w) for w in range(G)]
+    covered = {}
+    finished = {}
+    contrib_of = {}
+    for w, items in enumerate(work):
+        modes = [m for (_, _, _, m, _) in items]
+        assert modes.count(1) <= 1 and (1 not in modes or modes[0] == 1)
+        assert modes.count(2) <= 1
+        for (t, k0, k1, m, first) in items:
+            assert 0 <= t < T and 0 <= k0 < k1 <= I
+            for k in range(k0, k1):
+                assert (t, k) not in covered, (t, k)
+                covered[(t, k)] = w
+            if m == 1:
+                contrib_of[w] = (t, k0, k1)
+            else:
+                assert t not in finished
+                finished[t] = (w, k0, m, first)
+    assert len(covered) == T * I
+    assert sorted(finished) == list(range(T))
+    for t, (w, k0, m, first) in finished.items():
+        if m == 0:
+            assert k0 == 0
+            continue
+        assert 0 <= first < w and k0 > 0
+        expect = 0
+        for v in range(first, w):                # contributors, in K order
+            ct, c0, c1 = contrib_of[v]
+            assert ct == t and c0 == expect
+            expect = c1
+        assert expect == k0
+    return work
+
+
+def _dispatch_completes(work, slots):
+    """Resident-slot model: workgroups start in id order when a slot is free and run their items
+    in order; an owner item waits until all its contributors have published."""
+    G = len(work)
+    published = set()
+    pos = [0] * G
+    running, next_wg, done = [], 0, 0
+    while done < G:
+        while len(running) < slots and next_wg < G:
+            running.append(next_wg)
+            next_wg += 1
+        progressed = False
+        for w in list(running):
+            items = work[w]
+            while pos[w] < len(items):
+                t, k0, k1, m, first = items[pos[w]]
+                if m == 2 and not all(v in published for v in range(first, w)):
+                    break
+                if m == 1:
+                    published.add(w)
+                pos[w] += 1
+                progressed = True
+            if pos[w] == len(items):
+                running.remove(w)
+                done += 1
+                progressed = True
+        if not progressed:
+            return False
+    return True
+
+
+def test_plan_invariants_exhaustive():
+    n = 0
+    for tm, tn, I, cap, pol in itertools.product(range(1, 5), range(1, 4), range(1, 6), [1, 2, 3, 5, 7, 11, 16],
+                                                 [pg.HYBRID, pg.PURE_SK, pg.PURE_DP]):
+        p = pg.plan("mxfp4", 64 * tm, 64 * tn, 128 * I, grid_cap=cap, policy=pol, tile=(64, 64), num_cus=256)
+        work = _check_plan(p, cap)
+        for slots in (1, 2, max(1, p.grid // 2), p.grid):
+            assert _dispatch_completes(work, slots), (tm, tn, I, cap, pol, slots)
+        n += 1
+    assert n > 1000
+
+
+def test_plan_ragged_and_hybrid_shapes():
+    for (M, N, K, cap) in [(100, 72, 96, 5), (300, 130, 1000 // 32 * 32, 17), (16, 8192, 8192, 256),
+                           (4096, 4096, 4096, 256), (8192, 8192, 8192, 256), (1000, 3000, 2048, 256)]:
+        for pol in (pg.HYBRID, pg.PURE_SK, pg.PURE_DP):
+            p = pg.plan("mxfp4", M, N, K, grid_cap=cap, policy=pol, num_cus=256)
+            assert p.tiles_m == -(-M // p.tile_m) and p.iters_per_tile == -(-K // p.tile_k)
+            if p.tiles * p.iters_per_tile <= 20000:
+                _check_plan(p, cap)

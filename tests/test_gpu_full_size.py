@@ -1,0 +1,86 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+bench times (default tile and policy), plus the other tiles worth checking."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import persistent_gemm_amd as pg
+from persistent_gemm_amd.inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_util import assert_bitexact, assert_within_bound, device_inputs, oracle_full, run, say
+
+
+def _wl(name):
+    w = WORKLOADS[name]
+    return w, make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
+
+
+def test_skinny_mxfp4_16x8192x8192_bitexact():
+    w, x = _wl("mxfp4_gemm_16x8192x8192")
+    d = device_inputs(x)
+    C, _ = oracle_full(x)
+    for tile, policy, g in [(None, pg.HYBRID, 0), ((16, 128), pg.HYBRID, 0), ((16, 256), pg.PURE_SK, 100),
+                            ((16, 256), pg.PURE_DP, 0), ((64, 64), pg.HYBRID, 0)]:
+        say(f"skinny 16x8192x8192 tile {tile} policy {policy} grid {g}")
+        assert_bitexact(run(d, tile=tile, policy=policy, grid_cap=g), C, f"{tile} {policy} {g}")
+
+
+def test_large_mxfp4_addmm_8192_sampled_bitexact():
+    w, x = _wl("mxfp4_addmm_8192")
+    d = device_inputs(x)
+    say("8192^3 mxfp4 addmm, default plan")
+    got = run(d)
+    rng = np.random.default_rng(0)
+    # a 128 x 128 block spanning a tile corner, the last rows/cols, and random samples
+    rows = np.concatenate([np.repeat(np.arange(192, 320), 128), np.repeat(np.arange(8064, 8192), 2),
+                           rng.integers(0, 8192, 30000)])
+    cols = np.concatenate([np.tile(np.arange(192, 320), 128), np.tile([0, 8191], 128),
+                           rng.integers(0, 8192, 30000)])
+    Cs, _, _ = oracle.gemm_elements("mxfp4", x["A"], x["B"], rows, cols, x["SA"], x["SB"], x["bias"], K=w.K)
+    sub = got[rows, cols]
+    ok = oracle.accept(sub, Cs, None, None)
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} sampled elements differ"
+    for tile, policy, g in [((128, 128), pg.HYBRID, 0), ((256, 256), pg.PURE_SK, 0), ((256, 256), pg.HYBRID, 200)]:
+        say(f"8192^3 tile {tile} policy {policy} grid {g}")
+        again = run(d, tile=tile, policy=policy, grid_cap=g)
+        assert np.array_equal(again, got), f"{tile} {policy} {g} differs from the default plan"
+
+
+@pytest.fixture(scope="module")
+def bf16_4096():
+    w, x = _wl("bf16_addmm_4096")
+    C, D = oracle_full(x)
+    S = oracle.abs_product_sums("bf16", x["A"], x["B"])
+    return w, x, device_inputs(x), C, D, S
+
+
+@pytest.mark.parametrize("tile", [None, (128, 192), (128, 128)])
+def test_bf16_addmm_4096_within_bound(bf16_4096, tile):
+    w, x, d, C, D, S = bf16_4096
+    say(f"bf16 4096^3 addmm tile {tile}")
+    first = run(d, tile=tile)
+    assert_within_bound(first, C, D, S, f"tile {tile}")
+    assert np.array_equal(run(d, tile=tile), first)
+
+
+def test_fp8_4096_cap_sweep_within_bound():
+    w, x = _wl("fp8_gemm_4096_capsweep")
+    d = device_inputs(x)
+    C, D = oracle_full(x)
+    S = oracle.abs_product_sums("fp8", x["A"], x["B"], x["SA"], x["SB"])
+    results = {}
+    for cap in w.caps:
+        say(f"fp8 4096^3 cap {cap}")
+        got = run(d, grid_cap=cap)
+        assert_within_bound(got, C, D, S, f"cap {cap}")
+        results[cap] = got
+    # every cap divides the 256 tiles: the same whole-tile partition, the same bits
+    for cap in w.caps:
+        assert np.array_equal(results[cap], results[256])

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+MXFP4 inputs make every fp32 partial sum exact (products are multiples of
+2**-6 below 576, sums stay far below 2**18), so MXFP4 results must match the
+oracle bit for bit at every grid size, policy and tile.  bf16 / fp8 inputs
+with small integer values are exact too; random bf16 / fp8 inputs are held
+to |err| <= 2**-7 * sum|a*b| + one bf16 ulp, and must repeat bit for bit.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import persistent_gemm_amd as pg
+from persistent_gemm_amd.inputs import WORKLOADS, integer_inputs, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_util import assert_bitexact, assert_within_bound, device_inputs, oracle_full, run, say
+
+
+def _wl(name, bias=None):
+    w = WORKLOADS[name]
+    return make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias if bias is None else bias, seed=w.seed)
+
+
+# ---------------------------------------------------------------- the small MXFP4 addmm (grid of 5)
+
+@pytest.fixture(scope="module")
+def small():
+    x = _wl("mxfp4_addmm_256x256x512_g5")
+    C, D = oracle_full(x)
+    return x, device_inputs(x), C
+
+
+@pytest.mark.parametrize("policy", [pg.HYBRID, pg.PURE_SK, pg.PURE_DP])
+def test_small_mxfp4_addmm_grid5(small, policy):
+    x, d, C = small
+    say(f"small mxfp4 addmm 256x256x512 tile 64x64 grid 5 policy {policy}")
+    got = run(d, grid_cap=5, tile=(64, 64), policy=policy)
+    assert_bitexact(got, C, f"policy {policy}")
+
+
+def test_small_mxfp4_grid_sweep(small):
+    x, d, C = small
+    for policy in (pg.HYBRID, pg.PURE_SK, pg.PURE_DP):
+        for g in (1, 2, 3, 4, 5, 7, 8, 16, 31, 64, 128, 255, 256):
+            say(f"grid sweep policy {policy} grid {g}")
+            got = run(d, grid_cap=g, tile=(64, 64), policy=policy)
+            assert_bitexact(got, C, f"policy {policy} grid {g}")
+
+
+def test_small_mxfp4_other_tiles(small):
+    x, d, C = small
+    for tile in [(16, 256), (16, 128), (128, 128), (256, 256), None]:
+        for g in (3, 5, 256):
+            say(f"tile {tile} grid {g}")
+            got = run(d, grid_cap=g, tile=tile, policy=pg.PURE_SK)
+            assert_bitexact(got, C, f"tile {tile} grid {g}")
+
+
+# ---------------------------------------------------------------- ragged shapes and edges
+
+RAGGED = [(1, 1, 32), (100, 72, 96), (33, 300, 1056), (257, 129, 544), (16, 520, 4096), (515, 260, 288)]
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_mxfp4_ragged(M, N, K):
+    x = make_inputs("mxfp4", M, N, K, bias=True, seed=M * 7 + N * 3 + K)
+    d = device_inputs(x)
+    C, _ = oracle_full(x)
+    Cn, _ = oracle_full(x, bias=False)
+    for tile in [None, (64, 64), (16, 256), (128, 128), (256, 256)]:
+        for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 7), (pg.PURE_DP, 3), (pg.PURE_SK, 256)]:
+            say(f"mxfp4 {M}x{N}x{K} tile {tile} policy {policy} grid {g}")
+            assert_bitexact(run(d, grid_cap=g, tile=tile, policy=policy), C, f"{M}x{N}x{K} {tile} {policy} {g}")
+        assert_bitexact(run(d, bias=False, tile=tile, policy=pg.PURE_SK, grid_cap=5), Cn, f"no bias {tile}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 16), (100, 72, 96), (300, 200, 512), (64, 384, 1040)])
+def test_integer_inputs_exact(dtype, M, N, K):
+    x = integer_inputs(dtype, M, N, K, bias=True, seed=M + N + K)
+    d = device_inputs(x)
+    C, _ = oracle_full(x)
+    tiles = [None, (64, 64), (128, 128), (256, 256)] + ([(128, 192)] if dtype == "bf16" else [(16, 256)])
+    for tile in tiles:
+        for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 5), (pg.PURE_DP, 2)]:
+            say(f"{dtype} integers {M}x{N}x{K} tile {tile} policy {policy} grid {g}")
+            assert_bitexact(run(d, grid_cap=g, tile=tile, policy=policy), C, f"{dtype} {tile} {policy} {g}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_random_within_bound_and_repeatable(dtype):
+    M, N, K = 513, 388, 1056
+    kw = {"fp8_scales": (0.5, 3.0)} if dtype == "fp8" else {}
+    x = make_inputs(dtype, M, N, K, bias=True, seed=77, **kw)
+    d = device_inputs(x)
+    C, D = oracle_full(x)
+    S = oracle.abs_product_sums(dtype, x["A"], x["B"], x["SA"], x["SB"])
+    for tile in [None, (64, 64), (128, 128), (256, 256)]:
+        for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 9)]:
+            say(f"{dtype} random {M}x{N}x{K} tile {tile} policy {policy} grid {g}")
+            first = run(d, grid_cap=g, tile=tile, policy=policy)
+            assert_within_bound(first, C, D, S, f"{dtype} {tile} {policy}")
+            for _ in range(2):
+                assert np.array_equal(run(d, grid_cap=g, tile=tile, policy=policy), first)
+
+
+# ---------------------------------------------------------------- fixup protocol
+
+def test_bias_added_exactly_once_on_split_tiles():
+    # A = 0 and a bias of 1024: a missing or doubled bias on a split tile shows as 0 or 2048.
+    x = make_inputs("mxfp4", 192, 256, 1024, bias=False, seed=5)
+    x["A"] = np.zeros_like(x["A"])
+    x["bias"] = np.full(256, 0x4480, np.uint16)            # bf16 1024.0
+    d = device_inputs(x)
+    for g in (2, 3, 7, 13, 64):
+        say(f"bias once grid {g}")
+        got = run(d, grid_cap=g, tile=(64, 64), policy=pg.PURE_SK)
+        assert (got == 0x4480).all()
+    y = make_inputs("mxfp4", 192, 256, 1024, bias=True, seed=6)
+    C, _ = oracle_full(y)
+    dy = device_inputs(y)
+    for g in (2, 3, 7, 13, 64):
+        assert_bitexact(run(dy, grid_cap=g, tile=(64, 64), policy=pg.PURE_SK), C, f"grid {g}")
+
+
+def test_poisoned_scratch_and_stale_flags(small):
+    x, d, C = small
+    p = pg.plan("mxfp4", 256, 256, 512, grid_cap=7, tile=(64, 64), policy=pg.PURE_SK)
+    for _ in range(3):
+        say("poison then run")
+        pg.poison_workspace(p.scratch_bytes)
+        assert_bitexact(run(d, grid_cap=7, tile=(64, 64), policy=pg.PURE_SK), C, "after poison")
+
+
+def test_delayed_publication_keeps_bits(small):
+    x, d, C = small
+    for seed in (1, 2, 3, 99):
+        say(f"delay seed {seed}")
+        got = run(d, grid_cap=7, tile=(64, 64), policy=pg.PURE_SK, debug_flags=pg.DEBUG_DELAY, delay_seed=seed)
+        assert_bitexact(got, C, f"delay seed {seed}")
+    y = make_inputs("bf16", 300, 260, 2048, bias=True, seed=8)
+    dy = device_inputs(y)
+    ref = run(dy, grid_cap=11, tile=(64, 64), policy=pg.PURE_SK)
+    for seed in (4, 5):
+        got = run(dy, grid_cap=11, tile=(64, 64), policy=pg.PURE_SK, debug_flags=pg.DEBUG_DELAY, delay_seed=seed)
+        assert np.array_equal(got, ref)
+
+
+def test_timeout_is_reported_and_recovers(small):
+    x, d, C = small
+    p = pg.plan("mxfp4", 256, 256, 512, grid_cap=5, tile=(64, 64), policy=pg.PURE_SK)
+    # find a workgroup that publishes a partial
+    w = next(w for w in range(p.grid) if any(m == 1 for (_, _, _, m, _) in pg.plan_wg_work(p, w)))
+    say(f"drop signal of workgroup {w}, 1 ms spin limit")
+    pg.gemm_ex("mxfp4", d["A"], d["B"], d["SA"], d["SB"], d["bias"], grid_cap=5, tile=(64, 64),
+               policy=pg.PURE_SK, debug_flags=pg.DEBUG_DROP_SIGNAL, drop_signal_wg=w, spin_limit_ticks=100_000)
+    with pytest.raises(pg.SkError) as e:
+        pg.check()
+    assert e.value.name == "SK_ERR_TIMEOUT"
+    pg.check()                                   # cleared
+    assert_bitexact(run(d, grid_cap=5, tile=(64, 64), policy=pg.PURE_SK), C, "after timeout")
+
+
+def test_two_streams_keep_separate_scratch():
+    xs = [make_inputs("mxfp4", 256, 320, 1024, bias=True, seed=s) for s in (11, 12)]
+    ds = [device_inputs(x) for x in xs]
+    Cs = [oracle_full(x)[0] for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        for d, s in zip(ds, streams):
+            with torch.cuda.stream(s):
+                outs.append(pg.gemm_ex("mxfp4", d["A"], d["B"], d["SA"], d["SB"], d["bias"], grid_cap=9,
+                                       tile=(64, 64), policy=pg.PURE_SK, stream=s))
+    for s in streams:
+        pg.check(s)
+    torch.cuda.synchronize()
+    for i, out in enumerate(outs):
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert_bitexact(got, Cs[i % 2], f"stream result {i}")
+
+
+# ---------------------------------------------------------------- entry points
+
+def test_entry_points_agree(small):
+    x, d, C = small
+    say("entry points")
+    c1 = pg.gemm_mxfp4(d["A"], d["B"], d["SA"], d["SB"], d["bias"], grid_cap=5)
+    c2 = pg.addmm("mxfp4", d["bias"], d["A"], d["B"], d["SA"], d["SB"], grid_cap=5)
+    pg.check()
+    for c in (c1, c2):
+        assert_bitexact(c.view(torch.int16).cpu().numpy().view(np.uint16), C, "entry point")
+    y = integer_inputs("bf16", 130, 70, 136, bias=True, seed=3)
+    dy = device_inputs(y)
+    Cy, _ = oracle_full(y)
+    for c in (pg.gemm_bf16(dy["A"], dy["B"], dy["bias"]), pg.addmm("bf16", dy["bias"], dy["A"], dy["B"])):
+        pg.check()
+        assert_bitexact(c.view(torch.int16).cpu().numpy().view(np.uint16), Cy, "bf16 entry point")
+    z = integer_inputs("fp8", 130, 70, 144, bias=True, seed=4)
+    dz = device_inputs(z)
+    Cz, _ = oracle_full(z)
+    for c in (pg.gemm_fp8(dz["A"], dz["B"], dz["SA"], dz["SB"], dz["bias"]),
+              pg.addmm("fp8", dz["bias"], dz["A"], dz["B"], dz["SA"], dz["SB"])):
+        pg.check()
+        assert_bitexact(c.view(torch.int16).cpu().numpy().view(np.uint16), Cz, "fp8 entry point")
+
+
+def test_errors_are_status_codes(small):
+    x, d, C = small
+    out = torch.empty(256 * 256 + 1, dtype=torch.int16, device="cuda")
+    lib = pg.load()
+    s = torch.cuda.current_stream().cuda_stream
+    # C one element into an allocation: not 16-byte aligned
+    st = lib.sk_gemm_mxfp4(d["A"].data_ptr(), d["B"].data_ptr(), d["SA"].data_ptr(), d["SB"].data_ptr(),
+                           None, out.data_ptr() + 2, 256, 256, 512, 0, s)
+    assert st == 2
+    st = lib.sk_gemm_mxfp4(d["A"].data_ptr(), d["B"].data_ptr(), None, d["SB"].data_ptr(),
+                           None, out.data_ptr(), 256, 256, 512, 0, s)
+    assert st == 1
+    st = lib.sk_gemm_mxfp4(d["A"].data_ptr(), d["B"].data_ptr(), d["SA"].data_ptr(), d["SB"].data_ptr(),
+                           None, d["A"].data_ptr(), 256, 256, 512, 0, s)
+    assert st == 1
+    pg.check()
