@@ -49,7 +49,8 @@
  * Errors: every call returns an sk_status and never aborts.  Arguments are
  * checked before anything is launched:
  *   SK_ERR_ARG          a required pointer is NULL, M, N or K < 1, a size is
- *                       beyond the supported range (M, N < 2^31, K <= 2^21),
+ *                       beyond the supported range (M < 2^31, N <= 2^22,
+ *                       K <= 2^21, tiles * MAC iterations per tile < 2^31),
  *                       C overlaps an input, bf16 given scales, an unknown
  *                       dtype / policy, or sk_addmm without a bias;
  *   SK_ERR_ALIGN        MXFP4 K not a multiple of 32, fp8 K not a multiple of

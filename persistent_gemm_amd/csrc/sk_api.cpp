@@ -26,8 +26,10 @@ namespace {
 using sk::KArgs;
 using sk::Variant;
 
-constexpr int64_t kMaxMN = (int64_t)1 << 31;
-constexpr int64_t kMaxK = (int64_t)1 << 21;
+using sk::kMaxIters;
+using sk::kMaxK;
+using sk::kMaxM;
+using sk::kMaxN;
 constexpr uint64_t kDefaultSpin = 200000000ull;  // 2 s of the 100 MHz device clock
 
 struct DeviceInfo {
@@ -111,7 +113,7 @@ sk_status make_plan(int dtype, int policy, int64_t M, int64_t N, int64_t K, int 
                     int num_cus, sk_plan_info* p) {
   if (!dtype_ok(dtype)) return SK_ERR_ARG;
   if (policy < SK_POLICY_HYBRID || policy > SK_POLICY_PURE_DP) return SK_ERR_ARG;
-  if (M < 1 || N < 1 || K < 1 || M >= kMaxMN || N >= kMaxMN || K > kMaxK) return SK_ERR_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxM || N > kMaxN || K > kMaxK) return SK_ERR_ARG;
   if (num_cus < 1) return SK_ERR_ARG;
   const int vi = pick_variant(dtype, M, N, tile_m, tile_n);
   if (vi < 0) return SK_ERR_UNSUPPORTED;
@@ -131,6 +133,7 @@ sk_status make_plan(int dtype, int policy, int64_t M, int64_t N, int64_t K, int 
   int64_t cap = grid_cap <= 0 ? num_cus : (grid_cap < num_cus ? grid_cap : num_cus);
   if (cap > sk::kMaxGrid) cap = sk::kMaxGrid;
   const int64_t T = p->tiles, I = p->iters_per_tile;
+  if (T * I > kMaxIters) return SK_ERR_ARG;
   int64_t G, sk_tiles;
   if (policy == SK_POLICY_PURE_DP) {
     G = cap < T ? cap : T;
@@ -168,7 +171,7 @@ sk_status validate(const sk_gemm_args& g) {
   if (!dtype_ok(g.dtype)) return SK_ERR_ARG;
   if (g.policy < SK_POLICY_HYBRID || g.policy > SK_POLICY_PURE_DP) return SK_ERR_ARG;
   if (!g.A || !g.B || !g.C) return SK_ERR_ARG;
-  if (g.M < 1 || g.N < 1 || g.K < 1 || g.M >= kMaxMN || g.N >= kMaxMN || g.K > kMaxK) return SK_ERR_ARG;
+  if (g.M < 1 || g.N < 1 || g.K < 1 || g.M >= kMaxM || g.N > kMaxN || g.K > kMaxK) return SK_ERR_ARG;
   if (g.dtype == SK_MXFP4 && (!g.A_scale || !g.B_scale)) return SK_ERR_ARG;
   if (g.dtype == SK_BF16 && (g.A_scale || g.B_scale)) return SK_ERR_ARG;
   if (g.dtype == SK_MXFP4 && g.K % 32) return SK_ERR_ALIGN;
@@ -276,17 +279,15 @@ sk_status run(const sk_gemm_args& g) {
   a.P = ws->P;
   a.locks = ws->flags;
   a.err = ws->flags + sk::kErrIndex;
-  a.M = g.M;
-  a.N = g.N;
-  a.K = g.K;
-  a.row_bytes = row_bytes(g.dtype, g.K);
-  a.a_pitch = a.row_bytes;
-  a.b_pitch = a.row_bytes;
-  a.s_pitch = g.dtype == SK_MXFP4 ? g.K / 32 : 0;
-  a.tiles = p.tiles;
-  a.sk_tiles = p.sk_tiles;
-  a.q = p.iters_per_wg;
-  a.r = p.iters_extra;
+  a.M = (int32_t)g.M;
+  a.N = (int32_t)g.N;
+  a.K = (int32_t)g.K;
+  a.row_bytes = (int32_t)row_bytes(g.dtype, g.K);
+  a.s_pitch = g.dtype == SK_MXFP4 ? (int32_t)(g.K / 32) : 0;
+  a.tiles = (int32_t)p.tiles;
+  a.sk_tiles = (int32_t)p.sk_tiles;
+  a.q = (int32_t)p.iters_per_wg;
+  a.r = (int32_t)p.iters_extra;
   a.tiles_m = p.tiles_m;
   a.tiles_n = p.tiles_n;
   a.iters = p.iters_per_tile;
@@ -374,15 +375,16 @@ sk_status sk_plan_wg_range(const sk_plan_info* p, int32_t wg, int64_t* begin, in
     *begin = *end = 0;
     return SK_OK;
   }
-  *begin = sk::sk_begin(wg, p->iters_per_wg, p->iters_extra);
-  *end = sk::sk_begin(wg + 1, p->iters_per_wg, p->iters_extra);
+  *begin = sk::sk_begin(wg, (int32_t)p->iters_per_wg, (int32_t)p->iters_extra);
+  *end = sk::sk_begin(wg + 1, (int32_t)p->iters_per_wg, (int32_t)p->iters_extra);
   return SK_OK;
 }
 
 sk_status sk_plan_wg_work(const sk_plan_info* p, int32_t wg, sk_work_item* items, int32_t max_items,
                           int32_t* count) {
   if (!p || !count || wg < 0 || wg >= p->grid || max_items < 0 || (max_items > 0 && !items)) return SK_ERR_ARG;
-  sk::WorkIter work(wg, p->sk_tiles, p->tiles, p->iters_per_tile, p->iters_per_wg, p->iters_extra, p->grid);
+  sk::WorkIter work(wg, (int32_t)p->sk_tiles, (int32_t)p->tiles, p->iters_per_tile, (int32_t)p->iters_per_wg,
+                    (int32_t)p->iters_extra, p->grid);
   sk::WorkItem it;
   int32_t n = 0;
   while (work.next(it)) {

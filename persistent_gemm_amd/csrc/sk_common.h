@@ -14,6 +14,14 @@ constexpr int kMaxGrid = 1024;
 constexpr int kErrIndex = kMaxGrid;
 constexpr int kFlagWords = kMaxGrid + 64;
 
+// Size limits that keep every in-kernel index and byte offset in 32 bits:
+// a 256-row slab of C (256 * N * 2 bytes), of A or B (256 * row bytes) and
+// the Stream-K iteration count (tiles * iterations per tile) stay below 2^31.
+constexpr int64_t kMaxM = (int64_t)1 << 31;
+constexpr int64_t kMaxN = (int64_t)1 << 22;
+constexpr int64_t kMaxK = (int64_t)1 << 21;
+constexpr int64_t kMaxIters = ((int64_t)1 << 31) - 1;
+
 // Everything one launch needs.  Pointers are device pointers.
 struct KArgs {
   const uint8_t* A;
@@ -27,33 +35,31 @@ struct KArgs {
   float* P;                 // fp32 partial tiles, one BM*BN slot per workgroup
   uint32_t* locks;          // one flag per workgroup; flag == epoch means "partial published"
   uint32_t* err;            // set to 1 when a wait gives up
-  int64_t M, N, K;
-  int64_t a_pitch;          // bytes per row of A
-  int64_t b_pitch;          // bytes per row of B
-  int64_t s_pitch;          // bytes per row of the MXFP4 scales (K/32)
-  int64_t row_bytes;        // bytes of K data per row (== a_pitch == b_pitch)
-  int64_t tiles;            // T
-  int64_t sk_tiles;         // tiles [0, sk_tiles) are split by MAC iteration
-  int64_t q, r;             // Stream-K iterations S = q*G + r
+  uint64_t spin_limit;      // ticks of the 100 MHz realtime counter
+  int32_t M, N, K;
+  int32_t row_bytes;        // bytes of K data per row of A and of B (their pitch)
+  int32_t s_pitch;          // bytes per row of the MXFP4 scales (K/32)
+  int32_t tiles;            // T
+  int32_t sk_tiles;         // tiles [0, sk_tiles) are split by MAC iteration
+  int32_t q, r;             // Stream-K iterations S = q*G + r
   int32_t tiles_m, tiles_n;
   int32_t iters;            // I, MAC iterations (k-steps) per tile
   int32_t G;                // persistent workgroups
   uint32_t epoch;           // this launch's flag value
   uint32_t scale_fast;      // 1: every k-step of scales is whole and 8-byte aligned
-  uint64_t spin_limit;      // ticks of the 100 MHz realtime counter
   int32_t drop_wg;          // test hook: this workgroup never publishes (-1: none)
   uint32_t delay_seed;      // test hook: nonzero = seeded sleeps before publishing
 };
 
 // Stream-K partition of S = q*G + r MAC iterations: workgroup w owns
 // [begin(w), begin(w+1)), the first r workgroups getting one extra iteration.
-__host__ __device__ inline int64_t sk_begin(int64_t w, int64_t q, int64_t r) {
+__host__ __device__ inline int32_t sk_begin(int32_t w, int32_t q, int32_t r) {
   return w * q + (w < r ? w : r);
 }
 
 // The workgroup whose range holds iteration x (x < S).
-__host__ __device__ inline int64_t sk_owner_of(int64_t x, int64_t q, int64_t r) {
-  const int64_t big = r * (q + 1);
+__host__ __device__ inline int32_t sk_owner_of(int32_t x, int32_t q, int32_t r) {
+  const int32_t big = r * (q + 1);
   if (x < big) return x / (q + 1);
   return r + (x - big) / q;  // q > 0 here, because x < S
 }
@@ -61,7 +67,7 @@ __host__ __device__ inline int64_t sk_owner_of(int64_t x, int64_t q, int64_t r) 
 // One unit of work of a workgroup: MAC iterations [k0, k1) of one tile.
 enum : int { WORK_WHOLE = 0, WORK_CONTRIB = 1, WORK_OWNER = 2 };
 struct WorkItem {
-  int64_t tile;
+  int32_t tile;
   int32_t k0, k1;
   int32_t mode;       // WORK_WHOLE: finish the tile; WORK_CONTRIB: publish a partial;
                       // WORK_OWNER: add the partials of workgroups [first, w) then finish
@@ -76,11 +82,10 @@ struct WorkItem {
 // Contributions come first and owners wait only on lower workgroups, so no
 // workgroup ever waits on one that could be waiting on it.
 struct WorkIter {
-  int64_t s, e, I, tf, tl, whole, whole_end, dp, tiles, q, r;
-  int32_t G, phase;
+  int32_t s, e, I, tf, tl, whole, whole_end, dp, tiles, q, r, G, phase;
   bool contrib, owner;
 
-  __host__ __device__ WorkIter(int64_t w, int64_t sk_tiles, int64_t tiles_, int64_t iters, int64_t q_, int64_t r_,
+  __host__ __device__ WorkIter(int32_t w, int32_t sk_tiles, int32_t tiles_, int32_t iters, int32_t q_, int32_t r_,
                                int32_t G_) {
     I = iters;
     q = q_;
@@ -106,14 +111,14 @@ struct WorkIter {
   __host__ __device__ bool next(WorkItem& it) {
     for (;;) {
       it.k0 = 0;
-      it.k1 = (int32_t)I;
+      it.k1 = I;
       it.first = -1;
       if (phase == 0) {
         phase = 1;
         if (!contrib) continue;
         it.tile = tl;
-        it.k0 = (int32_t)((s > tl * I ? s : tl * I) - tl * I);
-        it.k1 = (int32_t)(e - tl * I);
+        it.k0 = (s > tl * I ? s : tl * I) - tl * I;
+        it.k1 = e - tl * I;
         it.mode = WORK_CONTRIB;
         return true;
       }
@@ -130,9 +135,9 @@ struct WorkIter {
         phase = 3;
         if (!owner) continue;
         it.tile = tf;
-        it.k0 = (int32_t)(s - tf * I);
+        it.k0 = s - tf * I;
         it.mode = WORK_OWNER;
-        it.first = (int32_t)sk_owner_of(tf * I, q, r);
+        it.first = sk_owner_of(tf * I, q, r);
         return true;
       }
       if (dp >= tiles) return false;

@@ -1,7 +1,7 @@
 // Stream-K GEMM kernels for gfx950 (MI355X).
 //
 // One persistent kernel template serves MXFP4, bf16 and fp8.  Each of the G
-// workgroups (256 threads = 4 wave64) runs, in order:
+// workgroups (256 threads = 4 wave64) walks its work list (WorkIter):
 //   1. its Stream-K contributor segment, if its iteration range ends inside a
 //      tile: the fp32 partial goes to its scratch slot P[w], then flag w is
 //      released with this launch's epoch;
@@ -16,11 +16,14 @@
 // publish their partial first thing, so the wait graph has no cycle even when
 // the grid is larger than what fits on the device at once.
 //
-// Per MAC iteration (k-step) each operand row contributes KB bytes (128 for the
-// big tiles: 256 FP4, 128 fp8 or 64 bf16 values).  A and B k-slices are loaded
-// with 16-byte buffer loads (out-of-range chunks read as zero), staged through
-// registers into a double-buffered LDS tile (16-byte chunks XOR-swizzled by row
-// to spread LDS banks), and consumed by MFMA:
+// Main loop.  Per MAC iteration (k-step) each operand row contributes KB bytes
+// (64 or 128: 128 or 256 FP4 values, 64 or 128 fp8, 32 or 64 bf16).  The A and
+// B k-slices are copied straight from HBM into LDS with 16-byte direct-to-LDS
+// buffer loads (one wave instruction fills one 1 KiB row group; rows and K
+// chunks past the matrix read as zero) into a ring of STAGES buffers, issued
+// STAGES-1 k-steps ahead of use.  MXFP4 scale bytes go the same way (dword
+// loads) when every k-step of scales is whole and aligned, else through
+// registers one k-step ahead.  Operands are consumed by MFMA:
 //   MXFP4: v_mfma_scale_f32_{32x32x64,16x16x128}_f8f6f4 with E2M1 operands and
 //          the E8M0 block scales as the per-lane scale operands;
 //   fp8:   the same instruction with E4M3 operands and unit block scales; the
@@ -49,10 +52,13 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer resource word 3 for gfx9-family raw (untyped) buffers.
 constexpr int kRsrcWord3 = 0x00020000;
-// Any offset at or past 2^31 lies beyond every resource built here: reads 0.
+// Any offset at or past 2^31 lies beyond every resource built here: reads 0,
+// writes are dropped.
 constexpr uint32_t kOob = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -67,9 +73,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int DT_, int BM_, int BN_, int KB_, int MF_, int WM_, int WN_>
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+template <int DT_, int BM_, int BN_, int KB_, int MF_, int WM_, int WN_, int STAGES_>
 struct Cfg {
   static constexpr int DT = DT_, BM = BM_, BN = BN_, KB = KB_, MF = MF_, WM = WM_, WN = WN_;
+  static constexpr int STAGES = STAGES_;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // per-wave tile
@@ -78,29 +87,62 @@ struct Cfg {
   static constexpr int LB = KB / NG;                   // bytes per lane per row per k-step
   static constexpr int U = DT == DT_FP8 ? 32 : 16;     // bytes per lane per MFMA
   static constexpr int NU = LB / U;                    // MFMAs per block per k-step
-  static constexpr int CPR = KB / 16;                  // 16-byte chunks per row per k-step
+  static constexpr int NCH = U / 16;                   // 16-byte chunks per lane per MFMA
   static constexpr int SPR = DT == DT_MXFP4 ? KB / 16 : 0;  // scale bytes per row per k-step
   static constexpr int BK = DT == DT_MXFP4 ? 2 * KB : (DT == DT_BF16 ? KB / 2 : KB);
   static constexpr int ACC = MF == 32 ? 16 : 4;        // fp32 accumulators per block per lane
+
+  // LDS image of one operand k-slice: rows of KB bytes, one after another.  The
+  // 16-byte chunks of row r are stored permuted: slot p holds chunk p ^ swz(r),
+  // with swz taking bits of r mod 16 (see swz()).  A direct-to-LDS load of one
+  // wave fills RG = 1024/KB whole rows, eight (or four) consecutive lanes
+  // reading one contiguous row segment from memory; and 16 lanes that read the
+  // same chunk of 16 consecutive rows hit 16 different 16-byte bank groups.
+  static constexpr int RG = 1024 / KB;
+  static constexpr int CPR = KB / 16;                  // chunks per row
+  static constexpr int A_GROUPS = BM / RG, B_GROUPS = BN / RG;
+  // Scale bytes of a k-step, [row][SPR], filled by dword loads of 64 lanes
+  // (256 bytes per instruction), so each area is a whole number of 256 B.
+  static constexpr int SA_INST = DT == DT_MXFP4 ? cdiv(BM * SPR, 256) : 0;
+  static constexpr int SB_INST = DT == DT_MXFP4 ? cdiv(BN * SPR, 256) : 0;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * KB;
   static constexpr int SA_OFF = (BM + BN) * KB;
-  static constexpr int SB_OFF = SA_OFF + BM * SPR;
-  static constexpr int STAGE = ((BM + BN) * (KB + SPR) + 15) / 16 * 16;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int A_CH = BM * CPR, B_CH = BN * CPR;
-  static constexpr int A_PT = (A_CH + NT - 1) / NT, B_PT = (B_CH + NT - 1) / NT;
-  static constexpr int SA_PT = DT == DT_MXFP4 ? (BM + NT - 1) / NT : 0;
-  static constexpr int SB_PT = DT == DT_MXFP4 ? (BN + NT - 1) / NT : 0;
-  static constexpr int P_SLOT = BM * BN;                // floats per scratch slot
-  static constexpr int P_WAVE = FM * FN * ACC * 64;     // floats per wave in a slot
+  static constexpr int SB_OFF = SA_OFF + SA_INST * 256;
+  static constexpr int STAGE = SB_OFF + SB_INST * 256;
+  static constexpr int LDS = STAGES * STAGE;
+  // Direct loads per wave per k-step; a wave with nothing left repeats a
+  // group (same bytes to the same place), so every wave issues the same count.
+  static constexpr int A_PT = cdiv(A_GROUPS, NW), B_PT = cdiv(B_GROUPS, NW);
+  static constexpr int SA_PT = cdiv(SA_INST, NW), SB_PT = cdiv(SB_INST, NW);
+  static constexpr int LOADS_PER_STAGE = A_PT + B_PT;             // data only
+  static constexpr int LOADS_PER_STAGE_S = A_PT + B_PT + SA_PT + SB_PT;
+  // Register path for scales (ragged or unaligned K): one row per thread.
+  static constexpr int SAR_PT = DT == DT_MXFP4 ? cdiv(BM, NT) : 0;
+  static constexpr int SBR_PT = DT == DT_MXFP4 ? cdiv(BN, NT) : 0;
+  static constexpr int P_SLOT = BM * BN;                // floats per scratch slot (row-major tile)
+  // Output staging: one MFMA block row of every wave at a time, fp32, row-major
+  // [WM*MF rows][BN + PADC]; the padding puts the lanes of one ds_write on
+  // distinct banks (rows 4 apart are written together).
+  static constexpr int PADC = MF == 32 ? 8 : 4;
+  static constexpr int SROWS = WM * MF;
+  static constexpr int RS = BN + PADC;                  // staging row stride in floats
+  static constexpr int STAGING = SROWS * RS * 4;
+  static constexpr int Q_PER_ROW = BN / 4;              // 4-float groups per staged row
+  static constexpr int Q_PASSES = SROWS * Q_PER_ROW / NT;
 
   static_assert(MF == 32 || MF == 16, "MFMA shape");
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be whole MFMA blocks");
   static_assert(LB % U == 0 && NU >= 1, "k-step must give each lane whole MFMA operands");
-  static_assert(KB % 16 == 0 && (CPR & (CPR - 1)) == 0, "k-step is a power-of-two number of chunks");
+  static_assert(KB == 64 || KB == 128, "k-step bytes per row");
+  static_assert(BM % RG == 0 && BN % RG == 0, "row groups tile the operands");
+  static_assert(MF % 16 == 0, "MFMA blocks cover whole 16-row swizzle periods");
   static_assert(DT != DT_MXFP4 || SPR == 4 || SPR == 8, "scale bytes per row per k-step");
+  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+  static_assert((STAGES - 2) * LOADS_PER_STAGE_S <= 63, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(STAGING <= LDS, "output staging reuses the operand stages");
+  static_assert((SROWS * Q_PER_ROW) % NT == 0, "whole passes over the staged rows");
 };
 
 template <class C>
@@ -150,23 +192,53 @@ __device__ __forceinline__ void mfma(typename Acc<C>::T& acc, const v4u* a, cons
 // bf16 nearest-even of the exact value t + bias, where t and bias are fp32.
 // s = fl(t + bias) carries an error e (TwoSum).  Rounding s to bf16 gives the
 // right answer unless s sits exactly on a bf16 midpoint while e != 0: then the
-// exact sum lies on e's side of the midpoint.
-__device__ __forceinline__ uint16_t round_sum_bf16(float t, float bias) {
+// exact sum lies on e's side of the midpoint.  Branch-free (selects only).
+__device__ __forceinline__ uint32_t round_sum_bf16(float t, float bias) {
 #pragma clang fp contract(off)
   const float s = t + bias;
   const float bv = s - t;
   const float av = s - bv;
   const float e = (t - av) + (bias - bv);
   const uint32_t u = __float_as_uint(s);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u & 0x007fffffu) ? (uint16_t)0x7fc0 : (uint16_t)(u >> 16);
-  if ((u & 0xffffu) == 0x8000u && e != 0.0f) {
-    const uint32_t low = u >> 16;                       // neighbour nearer zero
-    return (uint16_t)(((e > 0.0f) == (s > 0.0f)) ? low + 1 : low);
-  }
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const bool tie = (u & 0xffffu) == 0x8000u && e != 0.0f;
+  const uint32_t toward = (u >> 16) + (((e > 0.0f) == (s > 0.0f)) ? 1u : 0u);
+  const uint32_t r = tie ? toward : rne;
+  return (u & 0x7fffffffu) > 0x7f800000u ? 0x7fc0u : r;
+}
+
+// bf16 nearest-even of an fp32 value (no addend).
+__device__ __forceinline__ uint32_t round_bf16(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? 0x7fc0u : rne;
 }
 
 __device__ __forceinline__ float bf16_to_float(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Index of this thread's wave; the same for all its lanes, which the compiler
+// cannot infer from threadIdx, so it is made explicitly uniform.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Workgroup barrier for the main loop.  __syncthreads() also waits for every
+// outstanding global load (vmcnt(0)), which would drain the direct-to-LDS
+// loads issued for later stages; here each wave has already waited for the
+// loads of the stage about to be read, so only LDS traffic must settle.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, MAX] (the count is an immediate).
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  static_for<MAX + 1>([&](auto c) {
+    constexpr int k = decltype(c)::value;
+    if (n == k) {
+      if constexpr (k == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(k) : "memory");
+    }
+  });
+}
 
 // ---------------------------------------------------------------- the kernel body
 
@@ -174,33 +246,58 @@ template <class C>
 struct Kernel {
   static constexpr int NT = C::NT;
 
-  // Register staging for one k-step of global loads.
-  struct Stage {
-    v4u a[C::A_PT];
-    v4u b[C::B_PT];
-    v2u sa[C::SA_PT > 0 ? C::SA_PT : 1];
-    v2u sb[C::SB_PT > 0 ? C::SB_PT : 1];
-  };
-
   struct TileCtx {
     __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
-    int64_t m0, n0;
   };
 
-  static __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & (C::CPR - 1)); }
+  // Per-lane 32-bit buffer offsets of this wave's direct-to-LDS loads, fixed
+  // for a launch.  Lane j of a data load fills slot j % CPR of row
+  // (group*RG + j / CPR), so it fetches that row's chunk (j % CPR) ^ swz(row);
+  // lane j of a scale load takes the (j % DPR)-th scale dword of row
+  // (inst*64/DPR + j / DPR).  Rows past M or N lie outside the tile's buffer
+  // resource and read as zero.
+  static constexpr int DPR = C::SPR / 4 > 0 ? C::SPR / 4 : 1;   // scale dwords per row
+  struct LoadOffs {
+    uint32_t a[C::A_PT];     // lane's row offset plus chunk offset, per load
+    uint32_t b[C::B_PT];
+    uint32_t ca[C::A_PT];    // lane's chunk byte offset inside the k-step, per load
+    uint32_t cb[C::B_PT];
+    uint32_t sa[C::SA_PT > 0 ? C::SA_PT : 1];
+    uint32_t sb[C::SB_PT > 0 ? C::SB_PT : 1];
+  };
+  // Scale bytes of one k-step through registers (the fallback path).
+  struct ScaleRegs {
+    v2u sa[C::SAR_PT > 0 ? C::SAR_PT : 1];
+    v2u sb[C::SBR_PT > 0 ? C::SBR_PT : 1];
+  };
+  struct Ops {
+    v4u a[C::FM][C::NCH];
+    v4u b[C::FN][C::NCH];
+  };
+  struct Scales {
+    int a[C::FM];
+    int b[C::FN];
+  };
+  struct LdsPtrs {
+    const lds_u8* a;                 // lane's row in block 0 of its A rows
+    const lds_u8* b;
+    int slot[C::NU * C::NCH];        // byte offset of the lane's chunk for (sub-step, half)
+    int sa, sb;                      // byte offsets of the lane's block-0 scale words inside a stage
+  };
 
-  static __device__ __forceinline__ TileCtx tile_ctx(const KArgs& a, int64_t tile) {
+  static __device__ __forceinline__ lds_u8* stage_ptr(lds_u8* smem, int s) { return smem + s * C::STAGE; }
+
+  static __device__ __forceinline__ TileCtx tile_ctx(const KArgs& a, int tile) {
     TileCtx t;
-    const int64_t tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
-    t.m0 = tm * C::BM;
-    t.n0 = tn * C::BN;
-    const int64_t rows_a = min((int64_t)C::BM, a.M - t.m0);
-    const int64_t rows_b = min((int64_t)C::BN, a.N - t.n0);
-    t.ra = make_rsrc(a.A + t.m0 * a.a_pitch, (uint32_t)(rows_a * a.a_pitch));
-    t.rb = make_rsrc(a.B + t.n0 * a.b_pitch, (uint32_t)(rows_b * a.b_pitch));
+    const int tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int rows_a = min(C::BM, a.M - m0);
+    const int rows_b = min(C::BN, a.N - n0);
+    t.ra = make_rsrc(a.A + (int64_t)m0 * a.row_bytes, (uint32_t)(rows_a * a.row_bytes));
+    t.rb = make_rsrc(a.B + (int64_t)n0 * a.row_bytes, (uint32_t)(rows_b * a.row_bytes));
     if constexpr (C::DT == DT_MXFP4) {
-      t.rsa = make_rsrc(a.SA + t.m0 * a.s_pitch, (uint32_t)(rows_a * a.s_pitch));
-      t.rsb = make_rsrc(a.SB + t.n0 * a.s_pitch, (uint32_t)(rows_b * a.s_pitch));
+      t.rsa = make_rsrc(a.SA + (int64_t)m0 * a.s_pitch, (uint32_t)(rows_a * a.s_pitch));
+      t.rsb = make_rsrc(a.SB + (int64_t)n0 * a.s_pitch, (uint32_t)(rows_b * a.s_pitch));
     } else {
       t.rsa = t.ra;
       t.rsb = t.rb;
@@ -208,18 +305,88 @@ struct Kernel {
     return t;
   }
 
-  // 8 scale bytes of one row for k-step ks; bytes past K/32 read as 127 (x1) so
-  // that they never turn the zero padding into NaN.
-  static __device__ __forceinline__ v2u load_scales(const KArgs& a, __amdgpu_buffer_rsrc_t rs, int row, int ks) {
-    const uint32_t off = (uint32_t)(row * a.s_pitch) + (uint32_t)(ks * C::SPR);
-    if (a.scale_fast) {
-      if constexpr (C::SPR == 8) return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
-      else return v2u{__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0), 0u};
+  static __device__ __forceinline__ LoadOffs load_offsets(const KArgs& a) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int rr = lane / C::CPR, p = lane % C::CPR;
+    LoadOffs o;
+#pragma unroll
+    for (int i = 0; i < C::A_PT; ++i) {
+      const int row = ((wave + i * C::NW) % C::A_GROUPS) * C::RG + rr;
+      o.ca[i] = (uint32_t)((p ^ swz(row)) * 16);
+      o.a[i] = (uint32_t)row * (uint32_t)a.row_bytes + o.ca[i];
     }
+#pragma unroll
+    for (int i = 0; i < C::B_PT; ++i) {
+      const int row = ((wave + i * C::NW) % C::B_GROUPS) * C::RG + rr;
+      o.cb[i] = (uint32_t)((p ^ swz(row)) * 16);
+      o.b[i] = (uint32_t)row * (uint32_t)a.row_bytes + o.cb[i];
+    }
+    if constexpr (C::DT == DT_MXFP4) {
+      const int d = lane % DPR, r = lane / DPR;
+#pragma unroll
+      for (int i = 0; i < C::SA_PT; ++i) {
+        const int row = ((wave + i * C::NW) % C::SA_INST) * (64 / DPR) + r;
+        o.sa[i] = row < C::BM ? (uint32_t)(row * a.s_pitch + d * 4) : kOob;
+      }
+#pragma unroll
+      for (int i = 0; i < C::SB_PT; ++i) {
+        const int row = ((wave + i * C::NW) % C::SB_INST) * (64 / DPR) + r;
+        o.sb[i] = row < C::BN ? (uint32_t)(row * a.s_pitch + d * 4) : kOob;
+      }
+    }
+    return o;
+  }
+
+  // Issue the direct-to-LDS loads of k-step ks into stage `st`.  The k-step's
+  // byte offset rides in the uniform soffset (all bounds checks use the lane
+  // offset alone); in a ragged last k-step, chunks past the end of the row
+  // point outside the buffer and read as zero.
+  static __device__ __forceinline__ void issue(const KArgs& a, const TileCtx& t, const LoadOffs& o, int ks,
+                                               lds_u8* st, bool scales_direct) {
+    const int wave = wave_id();
+    const uint32_t kbyte = (uint32_t)ks * C::KB;
+    const bool ragged = kbyte + C::KB > (uint32_t)a.row_bytes;
+#pragma unroll
+    for (int i = 0; i < C::A_PT; ++i) {
+      const int grp = (wave + i * C::NW) % C::A_GROUPS;
+      const bool kin = !ragged || kbyte + o.ca[i] < (uint32_t)a.row_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.ra, (lds_void*)(st + C::A_OFF + grp * 1024), 16,
+                                               kin ? o.a[i] : kOob, kbyte, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PT; ++i) {
+      const int grp = (wave + i * C::NW) % C::B_GROUPS;
+      const bool kin = !ragged || kbyte + o.cb[i] < (uint32_t)a.row_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rb, (lds_void*)(st + C::B_OFF + grp * 1024), 16,
+                                               kin ? o.b[i] : kOob, kbyte, 0, 0);
+    }
+    if constexpr (C::DT == DT_MXFP4) {
+      if (scales_direct) {
+        const uint32_t sbyte = (uint32_t)ks * C::SPR;
+#pragma unroll
+        for (int i = 0; i < C::SA_PT; ++i) {
+          const int ins = (wave + i * C::NW) % C::SA_INST;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rsa, (lds_void*)(st + C::SA_OFF + ins * 256), 4, o.sa[i],
+                                                   sbyte, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::SB_PT; ++i) {
+          const int ins = (wave + i * C::NW) % C::SB_INST;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rsb, (lds_void*)(st + C::SB_OFF + ins * 256), 4, o.sb[i],
+                                                   sbyte, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Fallback for scales: SPR bytes of one row for k-step ks with byte loads;
+  // bytes past K/32 read as 127 (x1) so they never turn zero padding into NaN.
+  static __device__ __forceinline__ v2u load_scale_row(const KArgs& a, __amdgpu_buffer_rsrc_t rs, int row, int ks) {
+    const uint32_t off = (uint32_t)(row * a.s_pitch) + (uint32_t)(ks * C::SPR);
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < C::SPR; ++j) {
-      const bool in = (int64_t)ks * C::SPR + j < a.s_pitch;
+      const bool in = ks * C::SPR + j < a.s_pitch;
       uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? off + j : kOob, 0, 0);
       if (!in) v = 127u;
       w[j >> 2] |= v << (8 * (j & 3));
@@ -227,186 +394,187 @@ struct Kernel {
     return v2u{w[0], w[1]};
   }
 
-  static __device__ __forceinline__ void gload(const KArgs& a, const TileCtx& t, int ks, Stage& st) {
-    const int tid = threadIdx.x;
-    const int64_t kbyte = (int64_t)ks * C::KB;
-#pragma unroll
-    for (int i = 0; i < C::A_PT; ++i) {
-      const int id = tid + i * NT;
-      if (C::A_CH % NT == 0 || id < C::A_CH) {
-        const int row = id / C::CPR, c = id % C::CPR;
-        const bool in = kbyte + c * 16 < a.row_bytes;
-        const uint32_t off = in ? (uint32_t)(row * a.a_pitch + kbyte + c * 16) : kOob;
-        st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(t.ra, off, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PT; ++i) {
-      const int id = tid + i * NT;
-      if (C::B_CH % NT == 0 || id < C::B_CH) {
-        const int row = id / C::CPR, c = id % C::CPR;
-        const bool in = kbyte + c * 16 < a.row_bytes;
-        const uint32_t off = in ? (uint32_t)(row * a.b_pitch + kbyte + c * 16) : kOob;
-        st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(t.rb, off, 0, 0);
-      }
-    }
+  static __device__ __forceinline__ void load_scale_regs(const KArgs& a, const TileCtx& t, int ks, ScaleRegs& r) {
     if constexpr (C::DT == DT_MXFP4) {
+      const int tid = threadIdx.x;
 #pragma unroll
-      for (int i = 0; i < C::SA_PT; ++i) {
+      for (int i = 0; i < C::SAR_PT; ++i) {
         const int row = tid + i * NT;
-        if (C::BM % NT == 0 || row < C::BM) st.sa[i] = load_scales(a, t.rsa, row, ks);
+        if (C::BM % NT == 0 || row < C::BM) r.sa[i] = load_scale_row(a, t.rsa, row, ks);
       }
 #pragma unroll
-      for (int i = 0; i < C::SB_PT; ++i) {
+      for (int i = 0; i < C::SBR_PT; ++i) {
         const int row = tid + i * NT;
-        if (C::BN % NT == 0 || row < C::BN) st.sb[i] = load_scales(a, t.rsb, row, ks);
+        if (C::BN % NT == 0 || row < C::BN) r.sb[i] = load_scale_row(a, t.rsb, row, ks);
       }
     }
   }
 
-  static __device__ __forceinline__ void sstore(uint8_t* stage, const Stage& st) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < C::A_PT; ++i) {
-      const int id = tid + i * NT;
-      if (C::A_CH % NT == 0 || id < C::A_CH) {
-        const int row = id / C::CPR, c = id % C::CPR;
-        *(v4u*)(stage + C::A_OFF + row * C::KB + swz(row, c) * 16) = st.a[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PT; ++i) {
-      const int id = tid + i * NT;
-      if (C::B_CH % NT == 0 || id < C::B_CH) {
-        const int row = id / C::CPR, c = id % C::CPR;
-        *(v4u*)(stage + C::B_OFF + row * C::KB + swz(row, c) * 16) = st.b[i];
-      }
-    }
+  static __device__ __forceinline__ void store_scale_regs(lds_u8* st, const ScaleRegs& r) {
     if constexpr (C::DT == DT_MXFP4) {
+      const int tid = threadIdx.x;
 #pragma unroll
-      for (int i = 0; i < C::SA_PT; ++i) {
+      for (int i = 0; i < C::SAR_PT; ++i) {
         const int row = tid + i * NT;
         if (C::BM % NT == 0 || row < C::BM) {
-          if constexpr (C::SPR == 8) *(v2u*)(stage + C::SA_OFF + row * 8) = st.sa[i];
-          else *(uint32_t*)(stage + C::SA_OFF + row * 4) = st.sa[i][0];
+          if constexpr (C::SPR == 8) *(__attribute__((address_space(3))) v2u*)(st + C::SA_OFF + row * 8) = r.sa[i];
+          else *(__attribute__((address_space(3))) uint32_t*)(st + C::SA_OFF + row * 4) = r.sa[i][0];
         }
       }
 #pragma unroll
-      for (int i = 0; i < C::SB_PT; ++i) {
+      for (int i = 0; i < C::SBR_PT; ++i) {
         const int row = tid + i * NT;
         if (C::BN % NT == 0 || row < C::BN) {
-          if constexpr (C::SPR == 8) *(v2u*)(stage + C::SB_OFF + row * 8) = st.sb[i];
-          else *(uint32_t*)(stage + C::SB_OFF + row * 4) = st.sb[i][0];
+          if constexpr (C::SPR == 8) *(__attribute__((address_space(3))) v2u*)(st + C::SB_OFF + row * 8) = r.sb[i];
+          else *(__attribute__((address_space(3))) uint32_t*)(st + C::SB_OFF + row * 4) = r.sb[i][0];
         }
       }
     }
   }
 
-  // Lane's NU scale bytes of one operand row, packed little-endian.
-  static __device__ __forceinline__ int lane_scales(const uint8_t* base, int row, int g) {
-    const uint8_t* p = base + row * C::SPR + g * C::NU;
-    if constexpr (C::NU == 4) return *(const int*)p;
-    else if constexpr (C::NU == 2) return (int)*(const uint16_t*)p;
+  // Chunk permutation of row r: for 128-byte rows, rows 2k and 2k+1 share the
+  // value k (mod 8) and sit on opposite halves of the banks; for 64-byte rows,
+  // rows 4k..4k+3 share k (mod 4) and fill the four bank quarters.
+  static __device__ __forceinline__ constexpr int swz(int r) {
+    return C::KB == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+  }
+
+  static __device__ __forceinline__ LdsPtrs lds_ptrs(const lds_u8* smem) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int lr = lane % C::MF, g = lane / C::MF;
+    LdsPtrs p;
+    // Block rows start at multiples of 16, so the lane's permutation is swz(lr).
+    const int x = swz(lr);
+#pragma unroll
+    for (int k = 0; k < C::NU * C::NCH; ++k) p.slot[k] = ((g * (C::LB / 16) + k) ^ x) * 16;
+    p.a = smem + C::A_OFF + (wm * C::WTM + lr) * C::KB;
+    p.b = smem + C::B_OFF + (wn * C::WTN + lr) * C::KB;
+    p.sa = C::SA_OFF + (wm * C::WTM + lr) * C::SPR + g * C::NU;
+    p.sb = C::SB_OFF + (wn * C::WTN + lr) * C::SPR + g * C::NU;
+    return p;
+  }
+
+  static __device__ __forceinline__ int scale_word(const lds_u8* p) {
+    if constexpr (C::NU == 4) return *(const __attribute__((address_space(3))) int*)p;
+    else if constexpr (C::NU == 2) return (int)*(const __attribute__((address_space(3))) uint16_t*)p;
     else return (int)*p;
   }
 
-  static __device__ __forceinline__ void compute(const uint8_t* stage, Acc<C>& acc) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / C::WN, wn = wave % C::WN;
-    const int lr = lane % C::MF, g = lane / C::MF;
-    int sa[C::FM], sb[C::FN];
+  static __device__ __forceinline__ void read_scales(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
     if constexpr (C::DT == DT_MXFP4) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) sa[i] = lane_scales(stage + C::SA_OFF, wm * C::WTM + i * C::MF + lr, g);
+      for (int i = 0; i < C::FM; ++i) sc.a[i] = scale_word(st + p.sa + i * C::MF * C::SPR);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) sb[j] = lane_scales(stage + C::SB_OFF, wn * C::WTN + j * C::MF + lr, g);
+      for (int j = 0; j < C::FN; ++j) sc.b[j] = scale_word(st + p.sb + j * C::MF * C::SPR);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) sa[i] = 0x7f7f7f7f;   // unit E8M0 block scales
+      for (int i = 0; i < C::FM; ++i) sc.a[i] = 0x7f7f7f7f;   // unit E8M0 block scales
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) sb[j] = 0x7f7f7f7f;
+      for (int j = 0; j < C::FN; ++j) sc.b[j] = 0x7f7f7f7f;
     }
-    static_for<C::NU>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      constexpr int NCH = C::U / 16;
-      v4u av[C::FM][NCH], bv[C::FN][NCH];
+  }
+
+  // LDS operands of sub-step U (one MFMA K slice) of the stage at byte offset `so`.
+  template <int U>
+  static __device__ __forceinline__ void read_ops(int so, const LdsPtrs& p, Ops& o) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int row = wm * C::WTM + i * C::MF + lr;
-#pragma unroll
-        for (int h = 0; h < NCH; ++h) {
-          const int c = (g * C::LB + u * C::U) / 16 + h;
-          av[i][h] = *(const v4u*)(stage + C::A_OFF + row * C::KB + swz(row, c) * 16);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int row = wn * C::WTN + j * C::MF + lr;
-#pragma unroll
-        for (int h = 0; h < NCH; ++h) {
-          const int c = (g * C::LB + u * C::U) / 16 + h;
-          bv[j][h] = *(const v4u*)(stage + C::B_OFF + row * C::KB + swz(row, c) * 16);
-        }
-      }
+    for (int h = 0; h < C::NCH; ++h) {
+      const int off = so + p.slot[U * C::NCH + h];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
+        o.a[i][h] = *(const __attribute__((address_space(3))) v4u*)(p.a + off + i * C::MF * C::KB);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) mfma<C, (C::DT == DT_MXFP4 ? u : 0)>(acc.v[i][j], av[i], bv[j], sa[i], sb[j]);
-    });
+      for (int j = 0; j < C::FN; ++j)
+        o.b[j][h] = *(const __attribute__((address_space(3))) v4u*)(p.b + off + j * C::MF * C::KB);
+    }
+  }
+
+  template <int U>
+  static __device__ __forceinline__ void mfmas(const Ops& o, const Scales& sc, Acc<C>& acc) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) mfma<C, (C::DT == DT_MXFP4 ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
+  }
+
+  // Program-order anchor for the accumulators: MFMAs count as side-effect-free,
+  // so without this the compiler moves all of a k-step's MFMAs behind its LDS
+  // reads and barrier.  An empty volatile asm that reads and rewrites every
+  // accumulator (kept in AGPRs) and clobbers memory pins both in place.
+  static __device__ __forceinline__ void anchor(Acc<C>& acc) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) asm volatile("" : "+a"(acc.v[i][j])::"memory");
   }
 
   // MAC iterations [k0, k1) of one tile into acc (which the caller zeroed).
-  static __device__ __forceinline__ void mac(const KArgs& a, int64_t tile, int k0, int k1, Acc<C>& acc,
-                                             uint8_t* smem) {
+  //
+  // k-step j of the segment lives in stage j % STAGES; its loads are issued
+  // STAGES-1 k-steps before it is used.  Inside a k-step the operands of
+  // sub-step u+1 are read from LDS before the MFMAs of sub-step u are issued;
+  // at the last sub-step the next stage is published (its loads have landed --
+  // vmcnt counts only the loads of the stages after it -- and a barrier), and
+  // its first operands are read so they overlap the k-step's last MFMAs.
+  static __device__ __forceinline__ void mac(const KArgs& a, int tile, int k0, int k1, Acc<C>& acc,
+                                             lds_u8* smem, const LoadOffs& lo, const LdsPtrs& lp) {
+    constexpr int S = C::STAGES;
     const TileCtx t = tile_ctx(a, tile);
-    Stage st;
-    gload(a, t, k0, st);
-    sstore(smem, st);
-    __syncthreads();
-    for (int ks = k0; ks < k1; ++ks) {
-      uint8_t* cur = smem + ((ks - k0) & 1) * C::STAGE;
-      uint8_t* nxt = smem + (((ks - k0) & 1) ^ 1) * C::STAGE;
-      const bool more = ks + 1 < k1;
-      if (more) gload(a, t, ks + 1, st);
-      compute(cur, acc);
-      if (more) sstore(nxt, st);
-      __syncthreads();
+    const bool direct = C::DT != DT_MXFP4 || a.scale_fast != 0;
+    const int n = k1 - k0;
+    const int per_stage = direct ? C::LOADS_PER_STAGE_S : C::LOADS_PER_STAGE;
+    ScaleRegs sr;
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+      if (p < n) issue(a, t, lo, k0 + p, stage_ptr(smem, p), direct);
+    if (!direct) {
+      load_scale_regs(a, t, k0, sr);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      store_scale_regs(stage_ptr(smem, 0), sr);
+    } else {
+      wait_vmcnt<(S - 2) * C::LOADS_PER_STAGE_S>(min(S - 2, n - 1) * per_stage);
     }
-  }
-
-  static __device__ __forceinline__ float* slot(const KArgs& a, int w) {
-    return a.P + (int64_t)w * C::P_SLOT + (threadIdx.x >> 6) * C::P_WAVE;
-  }
-
-  static __device__ __forceinline__ void store_partial(const KArgs& a, int w, const Acc<C>& acc) {
-    float* p = slot(a, w);
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int q = 0; q < C::ACC / 4; ++q) {
-          v4f v;
-          v[0] = acc.v[i][j][4 * q + 0]; v[1] = acc.v[i][j][4 * q + 1];
-          v[2] = acc.v[i][j][4 * q + 2]; v[3] = acc.v[i][j][4 * q + 3];
-          *(v4f*)(p + (((i * C::FN + j) * (C::ACC / 4) + q) * 64 + lane) * 4) = v;
+    lds_barrier();
+    Ops o0, o1;
+    Scales sc0, sc1;
+    read_scales(stage_ptr(smem, 0), lp, sc0);
+    read_ops<0>(0, lp, o0);
+    for (int j = 0; j < n; ++j) {
+      const int cur = j % S;
+      const int nxt = (j + 1) % S;
+      const bool more = j + 1 < n;
+      if (j + S - 1 < n) issue(a, t, lo, k0 + j + S - 1, stage_ptr(smem, (j + S - 1) % S), direct);
+      if (!direct && more) load_scale_regs(a, t, k0 + j + 1, sr);
+      static_for<C::NU>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        Ops& now = (u & 1) ? o1 : o0;
+        Ops& nxo = (u & 1) ? o0 : o1;
+        if constexpr (u + 1 < C::NU) {
+          read_ops<u + 1>(cur * C::STAGE, lp, nxo);
+          mfmas<u>(now, sc0, acc);
+        } else {
+          if (more) {
+            if (direct) {
+              // stages issued after k-step j+1: up to k-step min(j+S-1, n-1)
+              wait_vmcnt<(S - 2) * C::LOADS_PER_STAGE_S>(min(S - 2, n - 2 - j) * per_stage);
+            } else {
+              asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+              store_scale_regs(stage_ptr(smem, nxt), sr);
+            }
+          }
+          lds_barrier();
+          if (more) {
+            read_scales(stage_ptr(smem, nxt), lp, sc1);
+            read_ops<0>(nxt * C::STAGE, lp, nxo);
+          }
+          mfmas<u>(now, sc0, acc);
+          sc0 = sc1;
+          if constexpr ((C::NU & 1) == 1) o0 = o1;   // sub-step 0 always starts in o0
         }
-  }
-
-  static __device__ __forceinline__ void add_partial(const KArgs& a, int w, Acc<C>& acc) {
-    const float* p = slot(a, w);
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int q = 0; q < C::ACC / 4; ++q) {
-          const v4f v = *(const v4f*)(p + (((i * C::FN + j) * (C::ACC / 4) + q) * 64 + lane) * 4);
-          acc.v[i][j][4 * q + 0] += v[0]; acc.v[i][j][4 * q + 1] += v[1];
-          acc.v[i][j][4 * q + 2] += v[2]; acc.v[i][j][4 * q + 3] += v[3];
-        }
+        anchor(acc);
+      });
+    }
   }
 
   // Publish this workgroup's partial: every thread's stores become visible at
@@ -440,72 +608,138 @@ struct Kernel {
       *s_flag = ok;
     }
     __syncthreads();
-    const int ok = *s_flag;
+    // The flag is the same for every lane; saying so keeps the work loop (and
+    // every buffer descriptor derived from it) wave-uniform.
+    const int ok = __builtin_amdgcn_readfirstlane(*s_flag);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __syncthreads();
     return ok != 0;
   }
 
-  static __device__ __forceinline__ void epilogue(const KArgs& a, int64_t tile, const Acc<C>& acc) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Emits a finished tile or a partial one, through LDS, one MFMA block row of
+  // every wave at a time: the accumulators are written to the staging area
+  // (row-major fp32), then each thread takes 4 consecutive columns of a row.
+  //   contrib: the 4 floats go to this workgroup's scratch slot P[w], a
+  //            row-major BM x BN fp32 tile.
+  //   final:   the partials of workgroups w-1, w-2, ..., first (if any) are
+  //            added in that order, then sigma, the bias and one rounding to
+  //            bf16; 8-byte stores of 4 bf16 (element stores at the N edge or
+  //            when N is not a multiple of 4).
+  // The staging area overlays the operand stages, which are idle here.
+  static __device__ __forceinline__ void drain(const KArgs& a, int tile, const Acc<C>& acc, lds_u8* smem,
+                                               bool contrib, int w, int first) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int lr = lane % C::MF, g = lane / C::MF;
-    const int64_t tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
-    const int64_t m0 = tm * C::BM + wm * C::WTM, n0 = tn * C::BN + wn * C::WTN;
+    const int tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int rows = min(C::BM, a.M - m0);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C + (int64_t)m0 * a.N, (uint32_t)rows * (uint32_t)a.N * 2u);
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias, a.bias ? (uint32_t)(a.N * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.P, 0x7fffffffu);
     float sigma = 1.0f;
     if constexpr (C::DT == DT_FP8) {
       const float x = a.fsa ? *a.fsa : 1.0f;
       const float y = a.fsb ? *a.fsb : 1.0f;
       sigma = x * y;
     }
+    const bool plain = a.bias == nullptr;
+    const bool vec = (a.N & 3) == 0;
+    // this thread's 4-column group (fixed for the tile) and its bias
+    const int qcol = (tid % C::Q_PER_ROW) * 4;
+    const int col = n0 + qcol;
+    float bias4[4];
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int64_t col = n0 + j * C::MF + lr;
-      const bool col_ok = col < a.N;
-      const float bias = (a.bias && col_ok) ? bf16_to_float(a.bias[col]) : 0.0f;
+    for (int k = 0; k < 4; ++k) {
+      const bool ok = !plain && col + k < a.N;
+      bias4[k] = bf16_to_float((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbias, ok ? (uint32_t)(col + k) * 2 : kOob, 0, 0));
+    }
+    // where this lane writes its accumulators in the staging rows
+    const int wrow = wm * C::MF + 4 * g;          // + (MF == 32 ? 8*(e/4) + e%4 : e)
+    const int wcol = wn * C::WTN + lr;            // + j*MF
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
+    for (int i = 0; i < C::FM; ++i) {
+      lds_barrier();                               // staging (or the last stage) is free
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
         for (int e = 0; e < C::ACC; ++e) {
-          const int r = C::MF == 32 ? 8 * (e / 4) + 4 * g + (e % 4) : 4 * g + e;
-          const int64_t row = m0 + i * C::MF + r;
-          if (col_ok && row < a.M) {
-            float t = acc.v[i][j][e];
-            if constexpr (C::DT == DT_FP8) t = t * sigma;
-            a.C[row * a.N + col] = round_sum_bf16(t, bias);
-          }
+          const int r = wrow + (C::MF == 32 ? 8 * (e / 4) + (e % 4) : e);
+          *(__attribute__((address_space(3))) float*)(smem + (r * C::RS + wcol + j * C::MF) * 4) = acc.v[i][j][e];
+        }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int pz = 0; pz < C::Q_PASSES; ++pz) {
+        const int idx = pz * C::NT + tid;
+        const int srow = idx / C::Q_PER_ROW;       // staged row: wave row srow / MF, block row i
+        const v4f x0 = *(const __attribute__((address_space(3))) v4f*)(smem + (srow * C::RS + qcol) * 4);
+        const int trow = (srow / C::MF) * C::WTM + i * C::MF + (srow % C::MF);   // row inside the tile
+        const uint32_t poff = (uint32_t)(trow * C::BN + qcol) * 4u;
+        if (contrib) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x0), rp,
+                                                 (uint32_t)w * (C::P_SLOT * 4u) + poff, 0, 0);
+          continue;
+        }
+        v4f x = x0;
+        for (int v = w - 1; v >= first; --v) {
+          const v4u p = __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)v * (C::P_SLOT * 4u) + poff, 0, 0);
+          x[0] += __uint_as_float(p[0]);
+          x[1] += __uint_as_float(p[1]);
+          x[2] += __uint_as_float(p[2]);
+          x[3] += __uint_as_float(p[3]);
+        }
+        uint32_t h[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float v = x[k];
+          if constexpr (C::DT == DT_FP8) v = v * sigma;
+          h[k] = plain ? round_bf16(v) : round_sum_bf16(v, bias4[k]);
+        }
+        const uint32_t coff = ((uint32_t)trow * (uint32_t)a.N + (uint32_t)col) * 2u;
+        if (vec && col + 4 <= a.N) {
+          __builtin_amdgcn_raw_buffer_store_b64(v2u{h[0] | (h[1] << 16), h[2] | (h[3] << 16)}, rc, coff, 0, 0);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h[k], rc, col + k < a.N ? coff + 2u * k : kOob, 0, 0);
         }
       }
     }
+    lds_barrier();                                 // staging free for the next tile's loads
   }
 
-  static __device__ void run(const KArgs& a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+  static __device__ __forceinline__ void run(const KArgs& a) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::LDS];
     __shared__ int s_flag;
+    lds_u8* smem = (lds_u8*)smem_raw;
     const int w = blockIdx.x;
+    const LoadOffs lo = load_offsets(a);
+    const LdsPtrs lp = lds_ptrs(smem);
     Acc<C> acc;
     WorkIter work(w, a.sk_tiles, a.tiles, a.iters, a.q, a.r, a.G);
     WorkItem it;
     while (work.next(it)) {
       acc.zero();
-      mac(a, it.tile, it.k0, it.k1, acc, smem);
+      mac(a, it.tile, it.k0, it.k1, acc, smem, lo, lp);
       if (it.mode == WORK_CONTRIB) {
-        store_partial(a, w, acc);
+        drain(a, it.tile, acc, smem, true, w, w);
         publish(a, w);
         continue;
       }
-      bool ok = true;
+      int first = w;
       if (it.mode == WORK_OWNER) {
-        // Partials are added in descending workgroup order, a fixed order.
+        // wait for every contributor; their partials are then added in
+        // descending workgroup order, a fixed order
         for (int v = w - 1; v >= it.first; --v) {
           if (!wait_for(a, v, &s_flag)) {
-            ok = false;
+            first = -1;
             break;
           }
-          add_partial(a, v, acc);
         }
+        if (first == w) first = it.first;
       }
-      if (ok) epilogue(a, it.tile, acc);
+      if (first >= 0) drain(a, it.tile, acc, smem, false, w, first);
     }
   }
 };
@@ -522,29 +756,30 @@ hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-#define SK_VARIANT(DT, BM, BN, KB, MF, WM, WN, OCC)                                                     \
+#define SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST) Cfg<DT, BM, BN, KB, MF, WM, WN, ST>
+#define SK_VARIANT(DT, BM, BN, KB, MF, WM, WN, ST, OCC)                                                   \
   Variant {                                                                                              \
-    DT, BM, BN, KB, Cfg<DT, BM, BN, KB, MF, WM, WN>::BK, MF, Cfg<DT, BM, BN, KB, MF, WM, WN>::NT,       \
-        Cfg<DT, BM, BN, KB, MF, WM, WN>::LDS, &launch_variant<Cfg<DT, BM, BN, KB, MF, WM, WN>, OCC>     \
+    DT, BM, BN, KB, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::BK, MF, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NT, \
+        SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::LDS, &launch_variant<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC> \
   }
 
 static const Variant kVariants[] = {
     // MXFP4
-    SK_VARIANT(DT_MXFP4, 256, 256, 128, 32, 2, 2, 1),
-    SK_VARIANT(DT_MXFP4, 128, 128, 128, 32, 2, 2, 1),
-    SK_VARIANT(DT_MXFP4, 64, 64, 64, 32, 2, 2, 2),
-    SK_VARIANT(DT_MXFP4, 16, 256, 128, 16, 1, 4, 1),
-    SK_VARIANT(DT_MXFP4, 16, 128, 128, 16, 1, 4, 1),
+    SK_VARIANT(DT_MXFP4, 256, 256, 64, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_MXFP4, 128, 128, 128, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_MXFP4, 64, 64, 64, 32, 2, 2, 4, 2),
+    SK_VARIANT(DT_MXFP4, 16, 256, 64, 16, 1, 4, 4, 1),
+    SK_VARIANT(DT_MXFP4, 16, 128, 64, 16, 1, 4, 4, 1),
     // bf16
-    SK_VARIANT(DT_BF16, 256, 256, 128, 32, 2, 2, 1),
-    SK_VARIANT(DT_BF16, 128, 128, 128, 32, 2, 2, 1),
-    SK_VARIANT(DT_BF16, 128, 192, 128, 32, 2, 2, 1),
-    SK_VARIANT(DT_BF16, 64, 64, 64, 32, 2, 2, 2),
+    SK_VARIANT(DT_BF16, 256, 256, 64, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_BF16, 128, 128, 128, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_BF16, 128, 192, 128, 32, 2, 2, 3, 1),
+    SK_VARIANT(DT_BF16, 64, 64, 64, 32, 2, 2, 4, 2),
     // fp8
-    SK_VARIANT(DT_FP8, 256, 256, 128, 32, 2, 2, 1),
-    SK_VARIANT(DT_FP8, 128, 128, 128, 32, 2, 2, 1),
-    SK_VARIANT(DT_FP8, 64, 64, 64, 32, 2, 2, 2),
-    SK_VARIANT(DT_FP8, 16, 256, 128, 16, 1, 4, 1),
+    SK_VARIANT(DT_FP8, 256, 256, 64, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_FP8, 128, 128, 128, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_FP8, 64, 64, 64, 32, 2, 2, 4, 2),
+    SK_VARIANT(DT_FP8, 16, 256, 128, 16, 1, 4, 3, 1),
 };
 
 int num_variants() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }

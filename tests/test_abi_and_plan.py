@@ -103,11 +103,12 @@ def test_plan_worked_large():
     assert (p.tiles, p.sk_tiles, p.tiles - p.sk_tiles) == (704, 448, 256)
     # 8192^3 MXFP4: 1024 tiles, four data-parallel rounds, no head.
     p = pg.plan("mxfp4", 8192, 8192, 8192, num_cus=256)
-    assert (p.tiles, p.iters_per_tile, p.sk_tiles, p.grid) == (1024, 32, 0, 256)
+    assert (p.tiles, p.iters_per_tile, p.sk_tiles, p.grid) == (1024, 8192 // p.tile_k, 0, 256)
     # skinny 16 x 8192 x 8192 MXFP4: 32 tiles of 16 x 256, all Stream-K, 8 workgroups per tile.
     p = pg.plan("mxfp4", 16, 8192, 8192, num_cus=256)
+    I = 8192 // p.tile_k
     assert (p.tile_m, p.tile_n, p.tiles, p.sk_tiles, p.grid, p.iters_per_wg, p.iters_extra) == \
-        (16, 256, 32, 32, 256, 4, 0)
+        (16, 256, 32, 32, 256, 32 * I // 256, 0)
     # the cap clamps to the CU count
     assert pg.plan("fp8", 4096, 4096, 4096, grid_cap=300, num_cus=256).grid == 256
     assert pg.plan("fp8", 4096, 4096, 4096, grid_cap=32, num_cus=256).grid == 32
