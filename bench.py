@@ -111,6 +111,7 @@ def main() -> int:
     ap.add_argument("--cap", type=int, default=None, help="grid cap (default: the workload's)")
     ap.add_argument("--tile", default=None, help="tile override, e.g. 256x256")
     ap.add_argument("--policy", default="hybrid", choices=["hybrid", "sk", "dp"])
+    ap.add_argument("--variant", type=int, default=None, help="compiled kernel index (default: automatic)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate", type=int, default=0, help="rotate over this many input copies (defeats the MALL)")
     args = ap.parse_args()
@@ -159,11 +160,12 @@ def main() -> int:
     for i in range(1, max(1, args.rotate)):
         copies.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in copies[0].items()})
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
-    p = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=cap, policy=policy, tile=tile)
+    p = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=cap, policy=policy, tile=tile, variant=args.variant)
 
     def step(i):
         d = copies[i % len(copies)]
-        pg.gemm_ex(w.dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap, policy=policy, tile=tile)
+        pg.gemm_ex(w.dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap, policy=policy, tile=tile,
+                   variant=args.variant)
 
     for i in range(args.warmup):
         step(i)
@@ -207,7 +209,8 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
-                   "tile": f"{p.tile_m}x{p.tile_n}x{p.tile_k}", "policy": args.policy, "grid": p.grid,
+                   "tile": f"{p.tile_m}x{p.tile_n}x{p.tile_k}", "threads": p.threads, "variant": p.variant,
+                   "policy": args.policy, "grid": p.grid,
                    "sk_tiles": p.sk_tiles, "tiles": p.tiles, "parallelism": "stream-k, 1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": eff_peak, "unit": "TFLOP/s",
                      "frac": round(achieved / eff_peak, 4), "traffic": traffic,

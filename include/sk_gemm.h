@@ -135,7 +135,8 @@ typedef struct sk_gemm_args {
   uint32_t debug_flags;     /* SK_DEBUG_* (tests only) */
   uint32_t delay_seed;      /* with SK_DEBUG_DELAY */
   int32_t drop_signal_wg;   /* with SK_DEBUG_DROP_SIGNAL */
-  int32_t reserved;
+  int32_t variant;          /* 0: automatic; k > 0: compiled kernel k-1 (see sk_variant_info), which must
+                               match dtype (SK_ERR_UNSUPPORTED otherwise); overrides tile_m, tile_n */
   uint64_t spin_limit_ticks;/* owner wait limit in ticks of the 100 MHz device clock; 0 = 2e8 (2 s) */
 } sk_gemm_args;
 
@@ -148,6 +149,7 @@ typedef struct sk_plan_query {
   int32_t grid_cap;
   int32_t tile_m, tile_n;
   int32_t num_cus;
+  int32_t variant;          /* as in sk_gemm_args */
 } sk_plan_query;
 
 typedef struct sk_plan_info {

@@ -51,7 +51,7 @@ class _Args(ctypes.Structure):
         ("grid_cap", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
         ("stream", ctypes.c_void_p),
         ("debug_flags", ctypes.c_uint32), ("delay_seed", ctypes.c_uint32),
-        ("drop_signal_wg", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("drop_signal_wg", ctypes.c_int32), ("variant", ctypes.c_int32),
         ("spin_limit_ticks", ctypes.c_uint64),
     ]
 
@@ -61,7 +61,7 @@ class _PlanQuery(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("policy", ctypes.c_int32),
         ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
         ("grid_cap", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-        ("num_cus", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32), ("variant", ctypes.c_int32),
     ]
 
 
@@ -265,7 +265,8 @@ def addmm(dtype, bias, A, B, A_scale=None, B_scale=None, C=None, grid_cap=0, str
 
 
 def gemm_ex(dtype, A, B, A_scale=None, B_scale=None, bias=None, C=None, *, grid_cap=0, policy=HYBRID,
-            tile=None, stream=None, debug_flags=0, delay_seed=0, drop_signal_wg=-1, spin_limit_ticks=0):
+            tile=None, stream=None, debug_flags=0, delay_seed=0, drop_signal_wg=-1, spin_limit_ticks=0,
+            variant=None):
     """The same kernels with an explicit policy / tile and the test hooks of sk_gemm_ex."""
     d = _dt(dtype)
     M, N, K, C = _marshal(d, A, B, A_scale, B_scale, bias, C)
@@ -279,11 +280,12 @@ def gemm_ex(dtype, A, B, A_scale=None, B_scale=None, bias=None, C=None, *, grid_
     a.stream = _stream(A, stream)
     a.debug_flags, a.delay_seed = int(debug_flags), int(delay_seed)
     a.drop_signal_wg, a.spin_limit_ticks = int(drop_signal_wg), int(spin_limit_ticks)
+    a.variant = 0 if variant is None else int(variant) + 1
     _ok(load().sk_gemm_ex(ctypes.byref(a)), "sk_gemm_ex")
     return C
 
 
-def plan(dtype, M, N, K, *, grid_cap=0, policy=HYBRID, tile=None, num_cus=0) -> Plan:
+def plan(dtype, M, N, K, *, grid_cap=0, policy=HYBRID, tile=None, num_cus=0, variant=None) -> Plan:
     """The partition a call would use (host-only; num_cus=0 asks the current device)."""
     q = _PlanQuery()
     q.dtype, q.policy = _dt(dtype), int(policy)
@@ -291,6 +293,7 @@ def plan(dtype, M, N, K, *, grid_cap=0, policy=HYBRID, tile=None, num_cus=0) -> 
     q.grid_cap = int(grid_cap)
     q.tile_m, q.tile_n = (0, 0) if tile is None else (int(tile[0]), int(tile[1]))
     q.num_cus = int(num_cus)
+    q.variant = 0 if variant is None else int(variant) + 1
     info = _PlanInfo()
     _ok(load().sk_plan(ctypes.byref(q), ctypes.byref(info)), "sk_plan")
     vals = {f: getattr(info, f) for f, _ in _PlanInfo._fields_}

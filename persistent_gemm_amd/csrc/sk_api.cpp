@@ -84,8 +84,12 @@ sk_status device_info(int* dev_out, DeviceInfo* info) {
 }
 
 // Kernel shape: an explicit (tile_m, tile_n), else a choice by problem shape.
-int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n) {
+int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n, int forced) {
   const int nv = sk::num_variants();
+  if (forced > 0) {
+    const Variant* v = sk::variant(forced - 1);
+    return (v && v->dtype == dtype) ? forced - 1 : -1;
+  }
   auto find = [&](int bm, int bn) {
     for (int i = 0; i < nv; ++i) {
       const Variant* v = sk::variant(i);
@@ -110,12 +114,13 @@ int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n) {
 }
 
 sk_status make_plan(int dtype, int policy, int64_t M, int64_t N, int64_t K, int grid_cap, int tile_m, int tile_n,
-                    int num_cus, sk_plan_info* p) {
+                    int forced, int num_cus, sk_plan_info* p) {
   if (!dtype_ok(dtype)) return SK_ERR_ARG;
   if (policy < SK_POLICY_HYBRID || policy > SK_POLICY_PURE_DP) return SK_ERR_ARG;
   if (M < 1 || N < 1 || K < 1 || M >= kMaxM || N > kMaxN || K > kMaxK) return SK_ERR_ARG;
   if (num_cus < 1) return SK_ERR_ARG;
-  const int vi = pick_variant(dtype, M, N, tile_m, tile_n);
+  if (forced < 0) return SK_ERR_ARG;
+  const int vi = pick_variant(dtype, M, N, tile_m, tile_n, forced);
   if (vi < 0) return SK_ERR_UNSUPPORTED;
   const Variant* v = sk::variant(vi);
   std::memset(p, 0, sizeof(*p));
@@ -252,7 +257,7 @@ sk_status run(const sk_gemm_args& g) {
   if (st != SK_OK) return st;
   if (!info.gfx950) return SK_ERR_UNSUPPORTED;
   sk_plan_info p;
-  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, info.cus, &p);
+  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, info.cus, &p);
   if (st != SK_OK) return st;
   hipStream_t stream = (hipStream_t)g.stream;
   Workspace* ws = nullptr;
@@ -366,7 +371,7 @@ sk_status sk_plan(const sk_plan_query* q, sk_plan_info* out) {
     if (st != SK_OK) return st;
     cus = info.cus;
   }
-  return make_plan(q->dtype, q->policy, q->M, q->N, q->K, q->grid_cap, q->tile_m, q->tile_n, cus, out);
+  return make_plan(q->dtype, q->policy, q->M, q->N, q->K, q->grid_cap, q->tile_m, q->tile_n, q->variant, cus, out);
 }
 
 sk_status sk_plan_wg_range(const sk_plan_info* p, int32_t wg, int64_t* begin, int64_t* end) {

@@ -109,43 +109,42 @@ struct WorkIter {
   }
 
   __host__ __device__ bool next(WorkItem& it) {
-    for (;;) {
-      it.k0 = 0;
-      it.k1 = I;
-      it.first = -1;
-      if (phase == 0) {
-        phase = 1;
-        if (!contrib) continue;
+    it.k0 = 0;
+    it.k1 = I;
+    it.first = -1;
+    if (phase == 0) {
+      phase = 1;
+      if (contrib) {
         it.tile = tl;
         it.k0 = (s > tl * I ? s : tl * I) - tl * I;
         it.k1 = e - tl * I;
         it.mode = WORK_CONTRIB;
         return true;
       }
-      if (phase == 1) {
-        if (whole >= whole_end) {
-          phase = 2;
-          continue;
-        }
+    }
+    if (phase == 1) {
+      if (whole < whole_end) {
         it.tile = whole++;
         it.mode = WORK_WHOLE;
         return true;
       }
-      if (phase == 2) {
-        phase = 3;
-        if (!owner) continue;
+      phase = 2;
+    }
+    if (phase == 2) {
+      phase = 3;
+      if (owner) {
         it.tile = tf;
         it.k0 = s - tf * I;
         it.mode = WORK_OWNER;
         it.first = sk_owner_of(tf * I, q, r);
         return true;
       }
-      if (dp >= tiles) return false;
-      it.tile = dp;
-      dp += G;
-      it.mode = WORK_WHOLE;
-      return true;
     }
+    if (dp >= tiles) return false;
+    it.tile = dp;
+    dp += G;
+    it.mode = WORK_WHOLE;
+    return true;
   }
 };
 

@@ -1,7 +1,7 @@
 // Stream-K GEMM kernels for gfx950 (MI355X).
 //
 // One persistent kernel template serves MXFP4, bf16 and fp8.  Each of the G
-// workgroups (256 threads = 4 wave64) walks its work list (WorkIter):
+// workgroups (4 or 8 wave64) walks its work list (WorkIter):
 //   1. its Stream-K contributor segment, if its iteration range ends inside a
 //      tile: the fp32 partial goes to its scratch slot P[w], then flag w is
 //      released with this launch's epoch;
@@ -34,7 +34,16 @@
 // scale block, whose E8M0 byte is picked by op_sel from the lane's scale word.
 // Every lane takes LB = KB / (64 / MF) contiguous bytes of a row per k-step,
 // so the K order inside a k-step is permuted identically for A and B (the sum
-// is unchanged) and each lane's scale bytes are contiguous in memory.
+// is unchanged) and each lane's scale bytes are contiguous in memory.  Each
+// MFMA block is computed transposed (B block as the first operand), so a lane
+// ends with runs of four consecutive output columns of one row.
+//
+// The whole work list of a workgroup is one stream of k-steps through the
+// stage ring: loads for the next work item are issued while the current one
+// is being finished, so HBM traffic does not stop at tile boundaries.  A tile
+// is finished from registers: partials are stored and summed in register
+// order (each wave store is one contiguous 1 KiB run), and the output is
+// rounded and written as 8-byte runs of four bf16.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -120,16 +129,11 @@ struct Cfg {
   // Register path for scales (ragged or unaligned K): one row per thread.
   static constexpr int SAR_PT = DT == DT_MXFP4 ? cdiv(BM, NT) : 0;
   static constexpr int SBR_PT = DT == DT_MXFP4 ? cdiv(BN, NT) : 0;
-  static constexpr int P_SLOT = BM * BN;                // floats per scratch slot (row-major tile)
-  // Output staging: one MFMA block row of every wave at a time, fp32, row-major
-  // [WM*MF rows][BN + PADC]; the padding puts the lanes of one ds_write on
-  // distinct banks (rows 4 apart are written together).
-  static constexpr int PADC = MF == 32 ? 8 : 4;
-  static constexpr int SROWS = WM * MF;
-  static constexpr int RS = BN + PADC;                  // staging row stride in floats
-  static constexpr int STAGING = SROWS * RS * 4;
-  static constexpr int Q_PER_ROW = BN / 4;              // 4-float groups per staged row
-  static constexpr int Q_PASSES = SROWS * Q_PER_ROW / NT;
+  static constexpr int P_SLOT = BM * BN;                // floats per scratch slot
+  static constexpr int P_WAVE = FM * FN * ACC * 64;     // floats per wave in a slot
+  static constexpr int NQ = ACC / 4;                    // 4-column runs per block per lane
+  static constexpr int BIAS_OFF = STAGES * STAGE;       // bf16 bias of the current tile
+  static constexpr int LDS_TOTAL = BIAS_OFF + BN * 2;
 
   static_assert(MF == 32 || MF == 16, "MFMA shape");
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be whole MFMA blocks");
@@ -140,9 +144,8 @@ struct Cfg {
   static_assert(DT != DT_MXFP4 || SPR == 4 || SPR == 8, "scale bytes per row per k-step");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
   static_assert((STAGES - 2) * LOADS_PER_STAGE_S <= 63, "vmcnt range");
-  static_assert(LDS <= 160 * 1024, "LDS");
-  static_assert(STAGING <= LDS, "output staging reuses the operand stages");
-  static_assert((SROWS * Q_PER_ROW) % NT == 0, "whole passes over the staged rows");
+  static_assert(LDS_TOTAL <= 160 * 1024, "LDS");
+  static_assert(BN <= NT, "one bias element per thread");
 };
 
 template <class C>
@@ -159,15 +162,18 @@ struct Acc {
 
 // ---------------------------------------------------------------- MFMA wrappers
 
+// One MFMA block of C, computed as the transposed product (B block x A block):
+// lane l then holds C row (l % MF) and, for each accumulator quad, four
+// consecutive columns, which the epilogue stores as one 8-byte run.
 template <class C, int OP>
 __device__ __forceinline__ void mfma(typename Acc<C>::T& acc, const v4u* a, const v4u* b, int sa, int sb) {
   if constexpr (C::DT == DT_BF16) {
     v8bf va = __builtin_bit_cast(v8bf, a[0]);
     v8bf vb = __builtin_bit_cast(v8bf, b[0]);
     if constexpr (C::MF == 32)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, va, acc, 0, 0, 0);
     else
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, vb, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, va, acc, 0, 0, 0);
   } else {
     v8i va, vb;
     va[0] = a[0][0]; va[1] = a[0][1]; va[2] = a[0][2]; va[3] = a[0][3];
@@ -181,9 +187,9 @@ __device__ __forceinline__ void mfma(typename Acc<C>::T& acc, const v4u* a, cons
     }
     constexpr int fmt = C::DT == DT_FP8 ? 0 : 4;   // 0 = E4M3, 4 = E2M1
     if constexpr (C::MF == 32)
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, fmt, fmt, OP, sa, OP, sb);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc, fmt, fmt, OP, sb, OP, sa);
     else
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, acc, fmt, fmt, OP, sa, OP, sb);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vb, va, acc, fmt, fmt, OP, sb, OP, sa);
   }
 }
 
@@ -220,12 +226,30 @@ __device__ __forceinline__ float bf16_to_float(uint16_t h) { return __uint_as_fl
 // cannot infer from threadIdx, so it is made explicitly uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// The launch arguments, read afresh from the kernel argument segment at each
+// call.  Outside the main loop every argument is fetched where it is used
+// instead of being held in scalar registers for the whole kernel (the
+// arguments alone would take half of them).  The empty asm hides the pointer's
+// origin, so the loads are neither merged nor hoisted; they stay scalar loads.
+__device__ __forceinline__ const KArgs& kargs() {
+  const __attribute__((address_space(4))) uint8_t* p =
+      (const __attribute__((address_space(4))) uint8_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const KArgs*)p;
+}
+
 // Workgroup barrier for the main loop.  __syncthreads() also waits for every
 // outstanding global load (vmcnt(0)), which would drain the direct-to-LDS
 // loads issued for later stages; here each wave has already waited for the
 // loads of the stage about to be read, so only LDS traffic must settle.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // s_waitcnt vmcnt(n) for a run-time n in [0, MAX] (the count is an immediate).
@@ -341,22 +365,22 @@ struct Kernel {
   // byte offset rides in the uniform soffset (all bounds checks use the lane
   // offset alone); in a ragged last k-step, chunks past the end of the row
   // point outside the buffer and read as zero.
-  static __device__ __forceinline__ void issue(const KArgs& a, const TileCtx& t, const LoadOffs& o, int ks,
+  static __device__ __forceinline__ void issue(int row_bytes, const TileCtx& t, const LoadOffs& o, int ks,
                                                lds_u8* st, bool scales_direct) {
     const int wave = wave_id();
     const uint32_t kbyte = (uint32_t)ks * C::KB;
-    const bool ragged = kbyte + C::KB > (uint32_t)a.row_bytes;
+    const bool ragged = kbyte + C::KB > (uint32_t)row_bytes;
 #pragma unroll
     for (int i = 0; i < C::A_PT; ++i) {
       const int grp = (wave + i * C::NW) % C::A_GROUPS;
-      const bool kin = !ragged || kbyte + o.ca[i] < (uint32_t)a.row_bytes;
+      const bool kin = !ragged || kbyte + o.ca[i] < (uint32_t)row_bytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(t.ra, (lds_void*)(st + C::A_OFF + grp * 1024), 16,
                                                kin ? o.a[i] : kOob, kbyte, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::B_PT; ++i) {
       const int grp = (wave + i * C::NW) % C::B_GROUPS;
-      const bool kin = !ragged || kbyte + o.cb[i] < (uint32_t)a.row_bytes;
+      const bool kin = !ragged || kbyte + o.cb[i] < (uint32_t)row_bytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rb, (lds_void*)(st + C::B_OFF + grp * 1024), 16,
                                                kin ? o.b[i] : kOob, kbyte, 0, 0);
     }
@@ -381,12 +405,12 @@ struct Kernel {
 
   // Fallback for scales: SPR bytes of one row for k-step ks with byte loads;
   // bytes past K/32 read as 127 (x1) so they never turn zero padding into NaN.
-  static __device__ __forceinline__ v2u load_scale_row(const KArgs& a, __amdgpu_buffer_rsrc_t rs, int row, int ks) {
-    const uint32_t off = (uint32_t)(row * a.s_pitch) + (uint32_t)(ks * C::SPR);
+  static __device__ __forceinline__ v2u load_scale_row(int s_pitch, __amdgpu_buffer_rsrc_t rs, int row, int ks) {
+    const uint32_t off = (uint32_t)(row * s_pitch) + (uint32_t)(ks * C::SPR);
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < C::SPR; ++j) {
-      const bool in = ks * C::SPR + j < a.s_pitch;
+      const bool in = ks * C::SPR + j < s_pitch;
       uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? off + j : kOob, 0, 0);
       if (!in) v = 127u;
       w[j >> 2] |= v << (8 * (j & 3));
@@ -394,18 +418,18 @@ struct Kernel {
     return v2u{w[0], w[1]};
   }
 
-  static __device__ __forceinline__ void load_scale_regs(const KArgs& a, const TileCtx& t, int ks, ScaleRegs& r) {
+  static __device__ __forceinline__ void load_scale_regs(int s_pitch, const TileCtx& t, int ks, ScaleRegs& r) {
     if constexpr (C::DT == DT_MXFP4) {
       const int tid = threadIdx.x;
 #pragma unroll
       for (int i = 0; i < C::SAR_PT; ++i) {
         const int row = tid + i * NT;
-        if (C::BM % NT == 0 || row < C::BM) r.sa[i] = load_scale_row(a, t.rsa, row, ks);
+        if (C::BM % NT == 0 || row < C::BM) r.sa[i] = load_scale_row(s_pitch, t.rsa, row, ks);
       }
 #pragma unroll
       for (int i = 0; i < C::SBR_PT; ++i) {
         const int row = tid + i * NT;
-        if (C::BN % NT == 0 || row < C::BN) r.sb[i] = load_scale_row(a, t.rsb, row, ks);
+        if (C::BN % NT == 0 || row < C::BN) r.sb[i] = load_scale_row(s_pitch, t.rsb, row, ks);
       }
     }
   }
@@ -509,74 +533,6 @@ struct Kernel {
       for (int j = 0; j < C::FN; ++j) asm volatile("" : "+a"(acc.v[i][j])::"memory");
   }
 
-  // MAC iterations [k0, k1) of one tile into acc (which the caller zeroed).
-  //
-  // k-step j of the segment lives in stage j % STAGES; its loads are issued
-  // STAGES-1 k-steps before it is used.  Inside a k-step the operands of
-  // sub-step u+1 are read from LDS before the MFMAs of sub-step u are issued;
-  // at the last sub-step the next stage is published (its loads have landed --
-  // vmcnt counts only the loads of the stages after it -- and a barrier), and
-  // its first operands are read so they overlap the k-step's last MFMAs.
-  static __device__ __forceinline__ void mac(const KArgs& a, int tile, int k0, int k1, Acc<C>& acc,
-                                             lds_u8* smem, const LoadOffs& lo, const LdsPtrs& lp) {
-    constexpr int S = C::STAGES;
-    const TileCtx t = tile_ctx(a, tile);
-    const bool direct = C::DT != DT_MXFP4 || a.scale_fast != 0;
-    const int n = k1 - k0;
-    const int per_stage = direct ? C::LOADS_PER_STAGE_S : C::LOADS_PER_STAGE;
-    ScaleRegs sr;
-#pragma unroll
-    for (int p = 0; p < S - 1; ++p)
-      if (p < n) issue(a, t, lo, k0 + p, stage_ptr(smem, p), direct);
-    if (!direct) {
-      load_scale_regs(a, t, k0, sr);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      store_scale_regs(stage_ptr(smem, 0), sr);
-    } else {
-      wait_vmcnt<(S - 2) * C::LOADS_PER_STAGE_S>(min(S - 2, n - 1) * per_stage);
-    }
-    lds_barrier();
-    Ops o0, o1;
-    Scales sc0, sc1;
-    read_scales(stage_ptr(smem, 0), lp, sc0);
-    read_ops<0>(0, lp, o0);
-    for (int j = 0; j < n; ++j) {
-      const int cur = j % S;
-      const int nxt = (j + 1) % S;
-      const bool more = j + 1 < n;
-      if (j + S - 1 < n) issue(a, t, lo, k0 + j + S - 1, stage_ptr(smem, (j + S - 1) % S), direct);
-      if (!direct && more) load_scale_regs(a, t, k0 + j + 1, sr);
-      static_for<C::NU>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        Ops& now = (u & 1) ? o1 : o0;
-        Ops& nxo = (u & 1) ? o0 : o1;
-        if constexpr (u + 1 < C::NU) {
-          read_ops<u + 1>(cur * C::STAGE, lp, nxo);
-          mfmas<u>(now, sc0, acc);
-        } else {
-          if (more) {
-            if (direct) {
-              // stages issued after k-step j+1: up to k-step min(j+S-1, n-1)
-              wait_vmcnt<(S - 2) * C::LOADS_PER_STAGE_S>(min(S - 2, n - 2 - j) * per_stage);
-            } else {
-              asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-              store_scale_regs(stage_ptr(smem, nxt), sr);
-            }
-          }
-          lds_barrier();
-          if (more) {
-            read_scales(stage_ptr(smem, nxt), lp, sc1);
-            read_ops<0>(nxt * C::STAGE, lp, nxo);
-          }
-          mfmas<u>(now, sc0, acc);
-          sc0 = sc1;
-          if constexpr ((C::NU & 1) == 1) o0 = o1;   // sub-step 0 always starts in o0
-        }
-        anchor(acc);
-      });
-    }
-  }
-
   // Publish this workgroup's partial: every thread's stores become visible at
   // device scope before the flag does.
   static __device__ __forceinline__ void publish(const KArgs& a, int w) {
@@ -616,26 +572,72 @@ struct Kernel {
     return ok != 0;
   }
 
-  // Emits a finished tile or a partial one, through LDS, one MFMA block row of
-  // every wave at a time: the accumulators are written to the staging area
-  // (row-major fp32), then each thread takes 4 consecutive columns of a row.
-  //   contrib: the 4 floats go to this workgroup's scratch slot P[w], a
-  //            row-major BM x BN fp32 tile.
-  //   final:   the partials of workgroups w-1, w-2, ..., first (if any) are
-  //            added in that order, then sigma, the bias and one rounding to
-  //            bf16; 8-byte stores of 4 bf16 (element stores at the N edge or
-  //            when N is not a multiple of 4).
-  // The staging area overlays the operand stages, which are idle here.
-  static __device__ __forceinline__ void drain(const KArgs& a, int tile, const Acc<C>& acc, lds_u8* smem,
-                                               bool contrib, int w, int first) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  // Scratch slot of workgroup w in accumulator (register) order, so that each
+  // store or load of a wave is one contiguous 1 KiB run:
+  // [wave][block][accumulator quad][lane][4 floats].
+  static __device__ __forceinline__ uint32_t slot_off(int w) {
+    return (uint32_t)w * (uint32_t)(C::P_SLOT * 4) +
+           (uint32_t)(wave_id() * C::P_WAVE + (threadIdx.x & 63) * 4) * 4u;
+  }
+
+  // Four accumulators (one run of four output columns) copied out of AGPRs.
+  // The explicit reads keep the accumulators in AGPRs for their whole life;
+  // left to itself the register allocator moves some of them to VGPRs for
+  // the epilogue's arithmetic and then runs out of VGPRs in the main loop.
+  template <class T>
+  static __device__ __forceinline__ v4f read_run(const T& blk, int q) {
+    v4f r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float x;
+      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(blk[4 * q + k]));
+      r[k] = x;
+    }
+    return r;
+  }
+
+  // A VALU read of an MFMA result needs wait states after the MFMA (up to 18
+  // for the 16-pass shapes) that the hardware does not enforce.  The compiler
+  // inserts them for its own reads but not for the inline-asm reads above, so
+  // every path that reads accumulators starts with this.
+  static __device__ __forceinline__ void mfma_read_hazard() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  }
+
+  static __device__ __forceinline__ uint32_t run_off(int i, int j, int q) {
+    return (uint32_t)(((i * C::FN + j) * C::NQ + q) * 1024);
+  }
+
+  static __device__ __forceinline__ void store_partial(const KArgs& a, int w, const Acc<C>& acc) {
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.P, 0x7fffffffu);
+    const uint32_t base = slot_off(w);
+    mfma_read_hazard();
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < C::NQ; ++q) {
+          const v4f v = read_run(acc.v[i][j], q);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rp, base + run_off(i, j, q), 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  }
+
+  // Finishes one tile: C = round(sigma * (acc + P[w-1] + ... + P[first]) + bias),
+  // the partials of the lower workgroups added in descending order (none when
+  // first >= w), straight from registers.  Each lane holds, per block and run,
+  // four consecutive columns of one row, which go out as one 8-byte store of
+  // four bf16.  The tile's bias was staged in LDS (as -0 when there is none).
+  static __device__ __forceinline__ void epilogue(const KArgs& a, int tile, const Acc<C>& acc, const lds_u8* smem,
+                                                  int w, int first) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int lr = lane % C::MF, g = lane / C::MF;
     const int tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
     const int m0 = tm * C::BM, n0 = tn * C::BN;
     const int rows = min(C::BM, a.M - m0);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C + (int64_t)m0 * a.N, (uint32_t)rows * (uint32_t)a.N * 2u);
-    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias, a.bias ? (uint32_t)(a.N * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.P, 0x7fffffffu);
     float sigma = 1.0f;
     if constexpr (C::DT == DT_FP8) {
@@ -643,103 +645,275 @@ struct Kernel {
       const float y = a.fsb ? *a.fsb : 1.0f;
       sigma = x * y;
     }
-    const bool plain = a.bias == nullptr;
-    const bool vec = (a.N & 3) == 0;
-    // this thread's 4-column group (fixed for the tile) and its bias
-    const int qcol = (tid % C::Q_PER_ROW) * 4;
-    const int col = n0 + qcol;
-    float bias4[4];
+    const int N = a.N;
+    // Either every 4-column run is whole and 8-byte aligned (N % 4 == 0 and an
+    // 8-aligned C), so a run lies entirely inside or outside the matrix, or
+    // elements are stored one by one.
+    const bool vec = (N & 3) == 0 && ((uintptr_t)a.C & 7) == 0;
+    mfma_read_hazard();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const bool ok = !plain && col + k < a.N;
-      bias4[k] = bf16_to_float((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbias, ok ? (uint32_t)(col + k) * 2 : kOob, 0, 0));
-    }
-    // where this lane writes its accumulators in the staging rows
-    const int wrow = wm * C::MF + 4 * g;          // + (MF == 32 ? 8*(e/4) + e%4 : e)
-    const int wcol = wn * C::WTN + lr;            // + j*MF
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      lds_barrier();                               // staging (or the last stage) is free
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
+        v4f x[C::NQ];
 #pragma unroll
-        for (int e = 0; e < C::ACC; ++e) {
-          const int r = wrow + (C::MF == 32 ? 8 * (e / 4) + (e % 4) : e);
-          *(__attribute__((address_space(3))) float*)(smem + (r * C::RS + wcol + j * C::MF) * 4) = acc.v[i][j][e];
-        }
-      }
-      lds_barrier();
-#pragma unroll
-      for (int pz = 0; pz < C::Q_PASSES; ++pz) {
-        const int idx = pz * C::NT + tid;
-        const int srow = idx / C::Q_PER_ROW;       // staged row: wave row srow / MF, block row i
-        const v4f x0 = *(const __attribute__((address_space(3))) v4f*)(smem + (srow * C::RS + qcol) * 4);
-        const int trow = (srow / C::MF) * C::WTM + i * C::MF + (srow % C::MF);   // row inside the tile
-        const uint32_t poff = (uint32_t)(trow * C::BN + qcol) * 4u;
-        if (contrib) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x0), rp,
-                                                 (uint32_t)w * (C::P_SLOT * 4u) + poff, 0, 0);
-          continue;
-        }
-        v4f x = x0;
+        for (int q = 0; q < C::NQ; ++q) x[q] = read_run(acc.v[i][j], q);
         for (int v = w - 1; v >= first; --v) {
-          const v4u p = __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)v * (C::P_SLOT * 4u) + poff, 0, 0);
-          x[0] += __uint_as_float(p[0]);
-          x[1] += __uint_as_float(p[1]);
-          x[2] += __uint_as_float(p[2]);
-          x[3] += __uint_as_float(p[3]);
-        }
-        uint32_t h[4];
+          const uint32_t base = slot_off(v);
+          v4u p[C::NQ];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float v = x[k];
-          if constexpr (C::DT == DT_FP8) v = v * sigma;
-          h[k] = plain ? round_bf16(v) : round_sum_bf16(v, bias4[k]);
-        }
-        const uint32_t coff = ((uint32_t)trow * (uint32_t)a.N + (uint32_t)col) * 2u;
-        if (vec && col + 4 <= a.N) {
-          __builtin_amdgcn_raw_buffer_store_b64(v2u{h[0] | (h[1] << 16), h[2] | (h[3] << 16)}, rc, coff, 0, 0);
-        } else {
+          for (int q = 0; q < C::NQ; ++q) p[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, base + run_off(i, j, q), 0, 0);
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h[k], rc, col + k < a.N ? coff + 2u * k : kOob, 0, 0);
+          for (int q = 0; q < C::NQ; ++q) x[q] += __builtin_bit_cast(v4f, p[q]);
         }
-      }
-    }
-    lds_barrier();                                 // staging free for the next tile's loads
-  }
-
-  static __device__ __forceinline__ void run(const KArgs& a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::LDS];
-    __shared__ int s_flag;
-    lds_u8* smem = (lds_u8*)smem_raw;
-    const int w = blockIdx.x;
-    const LoadOffs lo = load_offsets(a);
-    const LdsPtrs lp = lds_ptrs(smem);
-    Acc<C> acc;
-    WorkIter work(w, a.sk_tiles, a.tiles, a.iters, a.q, a.r, a.G);
-    WorkItem it;
-    while (work.next(it)) {
-      acc.zero();
-      mac(a, it.tile, it.k0, it.k1, acc, smem, lo, lp);
-      if (it.mode == WORK_CONTRIB) {
-        drain(a, it.tile, acc, smem, true, w, w);
-        publish(a, w);
-        continue;
-      }
-      int first = w;
-      if (it.mode == WORK_OWNER) {
-        // wait for every contributor; their partials are then added in
-        // descending workgroup order, a fixed order
-        for (int v = w - 1; v >= it.first; --v) {
-          if (!wait_for(a, v, &s_flag)) {
-            first = -1;
-            break;
+        const uint32_t row = (uint32_t)(wm * C::WTM + i * C::MF + lr);     // inside the tile
+#pragma unroll
+        for (int q = 0; q < C::NQ; ++q) {
+          const int tcol = wn * C::WTN + j * C::MF + (C::MF == 32 ? 8 * q + 4 * g : 4 * g);
+          const int col = n0 + tcol;
+          const v2u bb = *(const __attribute__((address_space(3))) v2u*)(smem + C::BIAS_OFF + tcol * 2);
+          const float b4[4] = {__uint_as_float(bb[0] << 16), __uint_as_float(bb[0] & 0xffff0000u),
+                               __uint_as_float(bb[1] << 16), __uint_as_float(bb[1] & 0xffff0000u)};
+          uint32_t h[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float v = x[q][k];
+            if constexpr (C::DT == DT_FP8) v = v * sigma;
+            h[k] = round_sum_bf16(v, b4[k]);
+          }
+          const uint32_t coff = (row * (uint32_t)N + (uint32_t)col) * 2u;
+          if (vec) {
+            __builtin_amdgcn_raw_buffer_store_b64(v2u{h[0] | (h[1] << 16), h[2] | (h[3] << 16)}, rc,
+                                                  col < N ? coff : kOob, 0, 0);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h[k], rc, col + k < N ? coff + 2u * k : kOob, 0, 0);
           }
         }
-        if (first == w) first = it.first;
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (first >= 0) drain(a, it.tile, acc, smem, false, w, first);
+  }
+
+  // Position in a workgroup's work list: the WorkIter fields that change as
+  // it is walked.  The rest is recomputed from the launch arguments at each
+  // step, which keeps two cursors down to six scalar registers.
+  struct Cursor {
+    int32_t phase, whole, dp;
+  };
+
+  static __device__ __forceinline__ Cursor cursor_begin(int w) {
+    const KArgs& a = kargs();
+    const WorkIter it(w, a.sk_tiles, a.tiles, a.iters, a.q, a.r, a.G);
+    return Cursor{it.phase, it.whole, it.dp};
+  }
+
+  // Next work item of workgroup w; the item is the same for every lane, and
+  // saying so keeps everything derived from it (tile origins, buffer
+  // descriptors) in scalar registers.
+  static __device__ __forceinline__ bool advance(int w, Cursor& c, WorkItem& x) {
+    const KArgs& a = kargs();
+    WorkIter it(w, a.sk_tiles, a.tiles, a.iters, a.q, a.r, a.G);
+    it.phase = c.phase;
+    it.whole = c.whole;
+    it.dp = c.dp;
+    const bool more = it.next(x);
+    c.phase = __builtin_amdgcn_readfirstlane(it.phase);
+    c.whole = __builtin_amdgcn_readfirstlane(it.whole);
+    c.dp = __builtin_amdgcn_readfirstlane(it.dp);
+    x.tile = __builtin_amdgcn_readfirstlane(x.tile);
+    x.k0 = __builtin_amdgcn_readfirstlane(x.k0);
+    x.k1 = __builtin_amdgcn_readfirstlane(x.k1);
+    x.mode = __builtin_amdgcn_readfirstlane(x.mode);
+    x.first = __builtin_amdgcn_readfirstlane(x.first);
+    return more;
+  }
+
+  // Runs the workgroup's whole work list as one stream of k-steps through a
+  // ring of STAGES LDS buffers: k-step c (counted over the whole list) lives
+  // in stage c % STAGES and its loads are issued STAGES-1 k-steps ahead, also
+  // across item boundaries, so the next tile's operands are on their way while
+  // a tile is being finished.  Inside a k-step the operands of sub-step u+1
+  // are read from LDS before the MFMAs of sub-step u; at the last sub-step the
+  // next stage is published (its loads have landed and a barrier) and, inside
+  // an item, its first operands are read, overlapping the k-step's last MFMAs.
+  template <bool DIRECT>
+  static __device__ __forceinline__ void run_list(lds_u8* smem, int* s_flag) {
+    constexpr int S = C::STAGES;
+    constexpr int PER_STAGE = DIRECT ? C::LOADS_PER_STAGE_S : C::LOADS_PER_STAGE;
+    const int w = blockIdx.x;
+    const int tid = threadIdx.x;
+    const LoadOffs lo = load_offsets(kargs());
+    const LdsPtrs lp = lds_ptrs(smem);
+    const int row_bytes = kargs().row_bytes;
+    const int s_pitch = kargs().s_pitch;
+
+    // Two cursors over the same work list: one issues loads, one computes.
+    Cursor ci = cursor_begin(w);
+    Cursor cc = ci;
+    WorkItem ii, ic;
+    bool have_i = advance(w, ci, ii);
+    if (!have_i) return;
+    advance(w, cc, ic);
+    int ki = ii.k0, ki_end = ii.k1;
+    TileCtx ti = tile_ctx(kargs(), ii.tile);
+    int issued = 0;   // k-steps issued so far
+    int done = 0;     // k-steps computed so far
+
+    // Scales through registers (when they cannot go straight to LDS): loaded
+    // with the k-step's data, written to its stage at the end of the k-step
+    // being computed meanwhile (before that k-step's closing barrier).
+    ScaleRegs sr;
+    int sr_stage = -1;
+    auto flush_scales = [&]() {
+      if constexpr (!DIRECT) {
+        if (sr_stage >= 0) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          store_scale_regs(stage_ptr(smem, sr_stage), sr);
+          sr_stage = -1;
+        }
+      }
+    };
+    auto issue_next = [&]() {
+      if (!have_i) return;
+      lds_u8* st = stage_ptr(smem, issued % S);
+      issue(row_bytes, ti, lo, ki, st, DIRECT);
+      if constexpr (!DIRECT) {
+        load_scale_regs(s_pitch, ti, ki, sr);
+        sr_stage = issued % S;
+      }
+      ++issued;
+      if (++ki == ki_end) {
+        WorkItem x;
+        have_i = advance(w, ci, x);
+        if (have_i) {
+          ki = x.k0;
+          ki_end = x.k1;
+          ti = tile_ctx(kargs(), x.tile);
+        }
+      }
+    };
+    // The loads of stage done+1 have landed once no more than the loads of
+    // the stages after it are outstanding (loads complete in issue order;
+    // anything else outstanding is younger and only makes the wait longer).
+    auto wait_next = [&]() {
+      if constexpr (DIRECT) {
+        const int later = issued - done - 2;
+        if constexpr (S == 4) {
+          if (later >= 2) wait_vmcnt_n<2 * PER_STAGE>();
+          else if (later == 1) wait_vmcnt_n<PER_STAGE>();
+          else wait_vmcnt_n<0>();
+        } else if constexpr (S == 3) {
+          if (later >= 1) wait_vmcnt_n<PER_STAGE>();
+          else wait_vmcnt_n<0>();
+        } else {
+          wait_vmcnt_n<0>();
+        }
+      }
+    };
+    // this tile's bias element (one per thread), staged in LDS before the epilogue
+    auto load_bias = [&](int tile) -> uint32_t {
+      const KArgs& a = kargs();
+      const int tn = tile % a.tiles_n;
+      const int col = tn * C::BN + tid;
+      if (a.bias == nullptr) return 0x8000u;   // -0: adding it changes nothing, not even a zero's sign
+      const bool ok = tid < C::BN && col < a.N;
+      return __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(a.bias, (uint32_t)(a.N * 2)), ok ? (uint32_t)col * 2 : kOob,
+                                                 0, 0);
+    };
+
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p) {
+      issue_next();
+      flush_scales();
+    }
+    uint32_t bias_h = load_bias(ic.tile);
+    // stage 0 landed: everything but the loads of the stages after it (and the bias load)
+    if constexpr (DIRECT) {
+      if (issued >= 3) wait_vmcnt_n<2 * PER_STAGE>();
+      else if (issued == 2) wait_vmcnt_n<PER_STAGE>();
+      else wait_vmcnt_n<0>();
+    }
+    lds_barrier();
+    for (;;) {
+      // stage done % S is visible to every wave; start the item's first k-step
+      Ops o0, o1;
+      Scales sc0, sc1;
+      read_scales(stage_ptr(smem, done % S), lp, sc0);
+      read_ops<0>((done % S) * C::STAGE, lp, o0);
+      Acc<C> acc;
+      acc.zero();
+      int n = ic.k1 - ic.k0;   // at least one k-step per item
+      do {
+        const int cur = done % S;
+        const int nxt = (done + 1) % S;
+        issue_next();
+        const bool more = done + 1 < issued;   // another k-step follows (in this or a later item)
+        const bool inside = n > 1;             // ... in this item
+        static_for<C::NU>([&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          Ops& now = (u & 1) ? o1 : o0;
+          Ops& nxo = (u & 1) ? o0 : o1;
+          if constexpr (u + 1 < C::NU) {
+            read_ops<u + 1>(cur * C::STAGE, lp, nxo);
+            mfmas<u>(now, sc0, acc);
+          } else {
+            flush_scales();
+            if (more) wait_next();
+            lds_barrier();
+            // The next item's first operands are read after this item is
+            // finished, so that they do not occupy registers during its end.
+            if (inside) {
+              read_scales(stage_ptr(smem, nxt), lp, sc1);
+              read_ops<0>(nxt * C::STAGE, lp, nxo);
+            }
+            mfmas<u>(now, sc0, acc);
+            sc0 = sc1;
+            if constexpr ((C::NU & 1) == 1) o0 = o1;   // sub-step 0 always starts in o0
+          }
+          anchor(acc);
+        });
+        ++done;
+      } while (--n > 0);
+
+      // ---- the item is complete
+      if (ic.mode == WORK_CONTRIB) {
+        store_partial(kargs(), w, acc);
+        publish(kargs(), w);
+      } else {
+        bool ok = true;
+        int first = w;   // lowest contributing workgroup (w: none)
+        if (ic.mode == WORK_OWNER) {
+          // every contributor has published before any partial is read
+          first = ic.first;
+          for (int v = w - 1; v >= first; --v)
+            if (!wait_for(kargs(), v, s_flag)) {
+              ok = false;
+              break;
+            }
+        }
+        if (ok) {
+          lds_barrier();   // every wave is done with the previous tile's bias
+          if (tid < C::BN) *(__attribute__((address_space(3))) uint16_t*)(smem + C::BIAS_OFF + tid * 2) = (uint16_t)bias_h;
+          lds_barrier();
+          epilogue(kargs(), ic.tile, acc, smem, w, first);
+        }
+      }
+      if (!advance(w, cc, ic)) break;
+      bias_h = load_bias(ic.tile);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  static __device__ __forceinline__ void run() {
+    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::LDS_TOTAL];
+    __shared__ int s_flag;
+    lds_u8* smem = (lds_u8*)smem_raw;
+    if constexpr (C::DT == DT_MXFP4) {
+      if (kargs().scale_fast) run_list<true>(smem, &s_flag);
+      else run_list<false>(smem, &s_flag);
+    } else {
+      run_list<true>(smem, &s_flag);
     }
   }
 };
@@ -747,7 +921,8 @@ struct Kernel {
 template <class C, int OCC>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void sk_gemm_kernel(KArgs a) {
-  Kernel<C>::run(a);
+  (void)a;   // read through kargs()
+  Kernel<C>::run();
 }
 
 template <class C, int OCC>
@@ -760,22 +935,25 @@ hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
 #define SK_VARIANT(DT, BM, BN, KB, MF, WM, WN, ST, OCC)                                                   \
   Variant {                                                                                              \
     DT, BM, BN, KB, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::BK, MF, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NT, \
-        SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::LDS, &launch_variant<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC> \
+        SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::LDS_TOTAL, &launch_variant<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC> \
   }
 
 static const Variant kVariants[] = {
     // MXFP4
+    SK_VARIANT(DT_MXFP4, 256, 256, 64, 32, 2, 4, 4, 2),
     SK_VARIANT(DT_MXFP4, 256, 256, 64, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_MXFP4, 128, 128, 128, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_MXFP4, 64, 64, 64, 32, 2, 2, 4, 2),
     SK_VARIANT(DT_MXFP4, 16, 256, 64, 16, 1, 4, 4, 1),
     SK_VARIANT(DT_MXFP4, 16, 128, 64, 16, 1, 4, 4, 1),
     // bf16
+    SK_VARIANT(DT_BF16, 256, 256, 64, 32, 2, 4, 4, 2),
     SK_VARIANT(DT_BF16, 256, 256, 64, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_BF16, 128, 128, 128, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_BF16, 128, 192, 128, 32, 2, 2, 3, 1),
     SK_VARIANT(DT_BF16, 64, 64, 64, 32, 2, 2, 4, 2),
     // fp8
+    SK_VARIANT(DT_FP8, 256, 256, 64, 32, 2, 4, 4, 2),
     SK_VARIANT(DT_FP8, 256, 256, 64, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_FP8, 128, 128, 128, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_FP8, 64, 64, 64, 32, 2, 2, 4, 2),
