@@ -13,8 +13,12 @@ The ``roofline`` object uses kernel durations measured here with HIP events on
 the launch stream; ``traffic`` comes from the rocprofv3 counter summary kept
 under profiles/ and is reported only while the kernel sources are the ones
 that summary was taken with.  ``cpu_baseline`` times the CPU oracle (test
-infrastructure, never the product path) on a bounded sample of the same
-workload.
+infrastructure, never the product path) on the same workload, whole, repeated
+for at least ten seconds.
+
+    python bench.py --copy-calibration MIB          # plain device copy (counter reference)
+    python bench.py --traffic-summary F W CF CW --copy-calibration MIB
+                                                    # rocprofv3 --pmc CSVs -> profiles/traffic_<workload>.json
 """
 
 from __future__ import annotations
@@ -60,6 +64,65 @@ def traffic_for(workload: str, tag: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _pmc_per_dispatch(csv_dir: str, counter: str, match) -> list:
+    """Per-dispatch totals of one rocprofv3 --pmc counter (CSV output) for kernels whose name passes `match`."""
+    import csv
+    import glob
+    per = {}
+    for f in sorted(glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter or not match(r["Kernel_Name"]):
+                    continue
+                key = (f, r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def traffic_summary(args) -> int:
+    """HBM bytes per launch of the GEMM kernel from FETCH_SIZE / WRITE_SIZE runs, each
+    scaled by what the same counter reads for a plain device copy of known size."""
+    fetch_dir, write_dir, copy_fetch_dir, copy_write_dir = args.traffic_summary
+    is_gemm = lambda name: "sk_gemm_kernel" in name
+    is_copy = lambda name: "copyBuffer" in name   # the HIP runtime's device-to-device copy kernel
+    copy_bytes = args.copy_calibration * (1 << 20)
+    out = {"workload": args.workload, "source_hash": source_hash(), "copy_bytes": copy_bytes}
+    for name, gdir, cdir in (("fetch", fetch_dir, copy_fetch_dir), ("write", write_dir, copy_write_dir)):
+        counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
+        g = _pmc_per_dispatch(gdir, counter, is_gemm)
+        c = _pmc_per_dispatch(cdir, counter, is_copy)
+        if not g or not c:
+            print(f"no {counter} dispatches found (gemm {len(g)}, copy {len(c)})", file=sys.stderr)
+            return 1
+        g_kib, c_kib = float(np.mean(g)), float(np.mean(c))
+        factor = copy_bytes / (c_kib * 1024.0)
+        out[name] = {"counter": counter, "gemm_kib_per_dispatch": g_kib, "gemm_dispatches": len(g),
+                     "copy_kib_per_dispatch": c_kib, "copy_dispatches": len(c), "scale": factor,
+                     "bytes_per_launch": g_kib * 1024.0 * factor}
+    out["hbm_bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    from persistent_gemm_amd.inputs import WORKLOADS
+    out["algorithmic_bytes"] = algorithmic_bytes(WORKLOADS[args.workload])
+    path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
+def copy_calibration(args) -> int:
+    """A plain device-to-device copy of known size (the reference for the HBM byte counters)."""
+    import torch
+    n = args.copy_calibration * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 256)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup + args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": args.warmup + args.steps}), flush=True)
+    return 0
+
+
 def algorithmic_bytes(w) -> int:
     """Each operand, scale, bias and output element once."""
     M, N, K = w.M, w.N, w.K
@@ -72,34 +135,25 @@ def algorithmic_bytes(w) -> int:
     return b + (2 * N if w.bias else 0) + 2 * M * N
 
 
-def cpu_baseline(w, x, budget_s: float = 12.0) -> dict:
-    """The oracle on the first R rows of the workload (all N columns, full K)."""
+def cpu_baseline(w, x, budget_s: float = 10.0) -> dict:
+    """The oracle on the whole workload, repeated until budget_s of CPU time has passed."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # threadpoolctl missing: report the affinity set
         threads = len(os.sched_getaffinity(0))
-
-    def sample(rows):
-        sub = dict(x)
-        sub["A"] = x["A"][:rows]
-        if w.dtype == "mxfp4":
-            sub["SA"] = x["SA"][:rows]
-        t0 = time.perf_counter()
-        oracle.gemm(w.dtype, sub["A"], sub["B"], sub["SA"], sub["SB"], sub["bias"], K=w.K)
-        return time.perf_counter() - t0
-
-    rows = min(64, w.M)
-    t = sample(rows)
-    if t < budget_s / 4 and rows < w.M:
-        rows = int(min(w.M, max(rows, rows * budget_s / max(t, 1e-3) * 0.8)))
-        rows = max(1, rows // 16 * 16) if rows >= 16 else rows
-        t = sample(rows)
-    flops = 2.0 * rows * w.N * w.K
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm(w.dtype, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=w.K)
+        runs += 1
+        t = time.perf_counter() - t0
+        if t >= budget_s:
+            break
+    flops = 2.0 * w.M * w.N * w.K * runs
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle (fp64 numpy, decode + product + bf16 rounding) on rows 0..{rows - 1} of A "
-                      f"({rows}x{w.N}x{w.K}), {t:.2f} s"}
+            "sample": f"the whole {w.M}x{w.N}x{w.K} problem, {runs} oracle run(s) in {t:.1f} s (fp64 numpy: "
+                      f"decode, one matrix product with {threads} BLAS threads, bf16 rounding)"}
 
 
 def main() -> int:
@@ -114,12 +168,24 @@ def main() -> int:
     ap.add_argument("--variant", type=int, default=None, help="compiled kernel index (default: automatic)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate", type=int, default=0, help="rotate over this many input copies (defeats the MALL)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB instead (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV output (no GPU)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        if args.copy_calibration <= 0:
+            ap.error("--traffic-summary needs --copy-calibration MIB (the copy size of the calibration runs)")
+        return traffic_summary(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         return 2
+
+    if args.copy_calibration > 0:
+        return copy_calibration(args)
 
     import torch
 
@@ -193,7 +259,8 @@ def main() -> int:
     peak = PEAK_TFLOPS[w.dtype]
     eff_peak = peak * (p.grid / 256.0 if args.workload.startswith("fp8_gemm_4096_cap") else 1.0)
     achieved = flops / avg_kern_s / 1e12
-    tag = "" if cap == w.grid_cap and tile is None and policy == pg.HYBRID else f"_cap{cap}"
+    default_launch = args.cap is None and args.tile is None and policy == pg.HYBRID and args.variant is None
+    tag = "" if default_launch else "_nondefault"
     traffic = traffic_for(args.workload, tag)
     out = {
         "metric": METRIC if w.dtype == "mxfp4" else f"{w.dtype} Stream-K GEMM TFLOP/s, 1 MI355X",

@@ -939,9 +939,9 @@ hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
   }
 
 static const Variant kVariants[] = {
-    // MXFP4
-    SK_VARIANT(DT_MXFP4, 256, 256, 64, 32, 2, 4, 4, 2),
+    // MXFP4 (the first variant of a tile shape is the automatic choice for it)
     SK_VARIANT(DT_MXFP4, 256, 256, 64, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_MXFP4, 256, 256, 64, 32, 2, 4, 4, 2),
     SK_VARIANT(DT_MXFP4, 128, 128, 128, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_MXFP4, 64, 64, 64, 32, 2, 2, 4, 2),
     SK_VARIANT(DT_MXFP4, 16, 256, 64, 16, 1, 4, 4, 1),

@@ -111,6 +111,42 @@ def test_random_within_bound_and_repeatable(dtype):
                 assert np.array_equal(run(d, grid_cap=g, tile=tile, policy=policy), first)
 
 
+# ---------------------------------------------------------------- every compiled kernel
+
+_DTYPES = {0: "mxfp4", 1: "bf16", 2: "fp8"}
+
+
+def _num_variants():
+    try:
+        return len(pg.variants())
+    except Exception:  # library not built: the load error surfaces in every other test
+        return 1
+
+
+@pytest.mark.parametrize("index", range(_num_variants()))
+def test_every_variant_exact(index):
+    """Each compiled kernel, chosen by index, on exact inputs spanning several
+    tiles with ragged M, N and K tails, under all three policies.  N is once a
+    multiple of 4 (8-byte output runs) and once not (element stores); for
+    MXFP4 one K keeps the scales on the direct-to-LDS path, the other (K/32
+    not a multiple of 8) sends them through registers."""
+    v = pg.variants()[index]
+    dtype, bm, bn = _DTYPES[v["dtype"]], v["tile_m"], v["tile_n"]
+    M = 2 * bm + 7
+    ragged_k = {"mxfp4": 448, "bf16": 200, "fp8": 208}[dtype]   # K % 32, % 8, % 16 are what the ABI requires
+    for N, K in [(2 * bn + 12, 512 if dtype == "mxfp4" else 256), (bn + 13, ragged_k)]:
+        if dtype == "mxfp4":
+            x = make_inputs(dtype, M, N, K, bias=True, seed=3000 + index)
+        else:
+            x = integer_inputs(dtype, M, N, K, bias=True, seed=3000 + index)
+        d = device_inputs(x)
+        C, _ = oracle_full(x)
+        for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 7), (pg.PURE_DP, 3)]:
+            say(f"variant {index} ({dtype} {bm}x{bn}, {v['threads']} threads) {M}x{N}x{K} policy {policy} grid {g}")
+            got = run(d, grid_cap=g, policy=policy, variant=index)
+            assert_bitexact(got, C, f"variant {index} {M}x{N}x{K} policy {policy} grid {g}")
+
+
 # ---------------------------------------------------------------- fixup protocol
 
 def test_bias_added_exactly_once_on_split_tiles():
