@@ -14,6 +14,8 @@
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -180,26 +182,41 @@ def _one_by_one(a_codes, b_codes, sa=127, sb=127, bias=None):
     return int(C[0, 0]), float(D[0, 0])
 
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _runs(spec):
+    """'2*3,10*1' -> [2, 2, 2, 10] (E2M1 codes for k = 0, 1, ...)."""
+    out = []
+    for part in spec.split(","):
+        code, count = part.split("*")
+        out += [int(code)] * int(count)
+    return out
+
+
+def golden_handworked():
+    """Cases of tests/golden/mxfp4_1x1x32_handworked.txt (worked by hand from the formats)."""
+    cases = []
+    with open(os.path.join(GOLDEN, "mxfp4_1x1x32_handworked.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, a, b, sa, sb, bias, total, bits = line.split()
+            cases.append((name, _runs(a), _runs(b), int(sa), int(sb), None if bias == "none" else float(bias),
+                          float(total), int(bits, 16)))
+    return cases
+
+
 def pin_handworked_mxfp4():
-    one, neg_one, six, two, one_half = 0x2, 0xA, 0x7, 0x4, 0x3
-    assert _one_by_one([one] * 32, [one] * 32) == (0x4200, 32.0)
-    assert _one_by_one([one] * 32, [one] * 32, sa=128) == (0x4280, 64.0)
-    assert _one_by_one([one] * 32, [one, neg_one] * 16)[1] == 0.0
-    assert _one_by_one([one] * 32, [one, neg_one] * 16, bias=0.5) == (0x3F00, 0.5)
-    assert _one_by_one([six] * 32, [six] * 32, sa=129, sb=129) == (0x4690, 18432.0)
-    a = [six] * 7 + [two, one] + [0] * 23
-    b = [six] * 7 + [two, one] + [0] * 23
-    assert _one_by_one(a, b) == (0x4380, 257.0)          # tie -> 256
-    b2 = [six] * 7 + [two, one_half] + [0] * 23
-    a2 = [six] * 7 + [two, two] + [0] * 23
-    assert _one_by_one(a2, b2) == (0x4382, 259.0)        # tie -> 260
-    # order of nibbles: code at k=1 sits in the high nibble of byte 0
-    a3 = [0] * 32
-    a3[1] = six
-    b3 = [0] * 32
-    b3[1] = two
-    assert _one_by_one(a3, b3) == (0x4140, 12.0)
-    # the scale of k in [32, 64) is the second scale byte
+    cases = golden_handworked()
+    assert len(cases) == 8
+    for name, a, b, sa, sb, bias, total, bits in cases:
+        assert len(a) == 32 and len(b) == 32, name
+        got = _one_by_one(a, b, sa=sa, sb=sb, bias=bias)
+        assert got == (bits, total), f"{name}: oracle gives {got}, worked by hand {(bits, total)}"
+    # the scale of k in [32, 64) is the second scale byte (K = 64, outside the 1x1x32 file)
+    one = 0x2
     A = _pack(np.array([[0] * 32 + [one] * 32], np.uint8))
     B = _pack(np.array([[0] * 32 + [one] * 32], np.uint8))
     C, D = oracle.gemm("mxfp4", A, B, np.array([[120, 128]], np.uint8), np.array([[127, 127]], np.uint8), None, K=64)
