@@ -74,6 +74,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// A raw buffer resource as four words (for the inline-asm loads below):
+// base address, no stride, `bytes` records, raw-buffer flags.
+__device__ __forceinline__ v4u rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return v4u{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const v4u& r) {
+  const uint64_t b = ((uint64_t)r[1] << 32) | r[0];
+  return make_rsrc((const void*)(uintptr_t)b, r[2]);
+}
+
+// Direct-to-LDS buffer loads (the lane's bytes land at LDS address m0 +
+// lane * size), written as inline asm on purpose: the compiler, seeing an LDS
+// write it cannot tell apart from the stage being read, would otherwise put
+// an s_waitcnt vmcnt(0) before every later LDS read, draining the loads issued
+// for the stages ahead.  The kernel waits for each stage with explicit vmcnt
+// counts instead.  One wait state separates the m0 write from its use.
+__device__ __forceinline__ void dma_load16(const v4u& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+               :: "v"(voff), "s"(lds), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_load4(const v4u& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, %3 offen lds"
+               :: "v"(voff), "s"(lds), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (N > 0) {
@@ -132,6 +159,12 @@ struct Cfg {
   static constexpr int P_SLOT = BM * BN;                // floats per scratch slot
   static constexpr int P_WAVE = FM * FN * ACC * 64;     // floats per wave in a slot
   static constexpr int NQ = ACC / 4;                    // 4-column runs per block per lane
+  // Output staging (epilogue): per wave, MF rows x SC columns of bf16 in the
+  // stage freed by a tile's last k-step, read back as 16-byte row chunks.
+  static constexpr int SC = WTN % 64 == 0 ? 64 : 32;
+  static constexpr int SCH = SC / 8;                    // 16-byte chunks per staged row
+  static constexpr int SRP = 64 / SCH;                  // staged rows per wave store
+  static constexpr int STG_WAVE = MF * SC * 2;
   static constexpr int BIAS_OFF = STAGES * STAGE;       // bf16 bias of the current tile
   static constexpr int LDS_TOTAL = BIAS_OFF + BN * 2;
 
@@ -146,6 +179,8 @@ struct Cfg {
   static_assert((STAGES - 2) * LOADS_PER_STAGE_S <= 63, "vmcnt range");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS");
   static_assert(BN <= NT, "one bias element per thread");
+  static_assert(NW * STG_WAVE <= STAGE, "output staging fits in one stage");
+  static_assert(WTN % SC == 0 && SC % MF == 0 && MF % SRP == 0, "output staging windows");
 };
 
 template <class C>
@@ -222,6 +257,33 @@ __device__ __forceinline__ uint32_t round_bf16(float s) {
 
 __device__ __forceinline__ float bf16_to_float(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Four outputs bf16(t[k] + bias[k]), correctly rounded, as two packed words.
+// The fp32 sum s = fl(t + bias) rounds to the same bf16 as the exact sum
+// unless s is itself a bf16 midpoint (every bf16 rounding boundary is an
+// fp32 value, so an exact sum on the other side of one would have that
+// boundary as its nearest fp32).  So the hardware conversion of s is used,
+// and the exact path (round_sum_bf16) only for a run holding a midpoint.
+__device__ __forceinline__ v2u round_run(const float t[4], const float b[4]) {
+  float s[4];
+  bool tie = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    s[k] = t[k] + b[k];
+    tie |= (__float_as_uint(s[k]) & 0xffffu) == 0x8000u;
+  }
+  v2u h;
+  h[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{s[0], s[1]}), v2bf));
+  h[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{s[2], s[3]}), v2bf));
+  if (tie) {
+    h[0] = round_sum_bf16(t[0], b[0]) | (round_sum_bf16(t[1], b[1]) << 16);
+    h[1] = round_sum_bf16(t[2], b[2]) | (round_sum_bf16(t[3], b[3]) << 16);
+  }
+  return h;
+}
+
 // Index of this thread's wave; the same for all its lanes, which the compiler
 // cannot infer from threadIdx, so it is made explicitly uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -271,7 +333,7 @@ struct Kernel {
   static constexpr int NT = C::NT;
 
   struct TileCtx {
-    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+    v4u ra, rb, rsa, rsb;   // A, B and (MXFP4) their scales, from the tile's first row
   };
 
   // Per-lane 32-bit buffer offsets of this wave's direct-to-LDS loads, fixed
@@ -317,11 +379,11 @@ struct Kernel {
     const int m0 = tm * C::BM, n0 = tn * C::BN;
     const int rows_a = min(C::BM, a.M - m0);
     const int rows_b = min(C::BN, a.N - n0);
-    t.ra = make_rsrc(a.A + (int64_t)m0 * a.row_bytes, (uint32_t)(rows_a * a.row_bytes));
-    t.rb = make_rsrc(a.B + (int64_t)n0 * a.row_bytes, (uint32_t)(rows_b * a.row_bytes));
+    t.ra = rsrc_words(a.A + (int64_t)m0 * a.row_bytes, (uint32_t)(rows_a * a.row_bytes));
+    t.rb = rsrc_words(a.B + (int64_t)n0 * a.row_bytes, (uint32_t)(rows_b * a.row_bytes));
     if constexpr (C::DT == DT_MXFP4) {
-      t.rsa = make_rsrc(a.SA + (int64_t)m0 * a.s_pitch, (uint32_t)(rows_a * a.s_pitch));
-      t.rsb = make_rsrc(a.SB + (int64_t)n0 * a.s_pitch, (uint32_t)(rows_b * a.s_pitch));
+      t.rsa = rsrc_words(a.SA + (int64_t)m0 * a.s_pitch, (uint32_t)(rows_a * a.s_pitch));
+      t.rsb = rsrc_words(a.SB + (int64_t)n0 * a.s_pitch, (uint32_t)(rows_b * a.s_pitch));
     } else {
       t.rsa = t.ra;
       t.rsb = t.rb;
@@ -374,15 +436,13 @@ struct Kernel {
     for (int i = 0; i < C::A_PT; ++i) {
       const int grp = (wave + i * C::NW) % C::A_GROUPS;
       const bool kin = !ragged || kbyte + o.ca[i] < (uint32_t)row_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.ra, (lds_void*)(st + C::A_OFF + grp * 1024), 16,
-                                               kin ? o.a[i] : kOob, kbyte, 0, 0);
+      dma_load16(t.ra, kin ? o.a[i] : kOob, kbyte, (uint32_t)(uintptr_t)(st + C::A_OFF + grp * 1024));
     }
 #pragma unroll
     for (int i = 0; i < C::B_PT; ++i) {
       const int grp = (wave + i * C::NW) % C::B_GROUPS;
       const bool kin = !ragged || kbyte + o.cb[i] < (uint32_t)row_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rb, (lds_void*)(st + C::B_OFF + grp * 1024), 16,
-                                               kin ? o.b[i] : kOob, kbyte, 0, 0);
+      dma_load16(t.rb, kin ? o.b[i] : kOob, kbyte, (uint32_t)(uintptr_t)(st + C::B_OFF + grp * 1024));
     }
     if constexpr (C::DT == DT_MXFP4) {
       if (scales_direct) {
@@ -390,14 +450,12 @@ struct Kernel {
 #pragma unroll
         for (int i = 0; i < C::SA_PT; ++i) {
           const int ins = (wave + i * C::NW) % C::SA_INST;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rsa, (lds_void*)(st + C::SA_OFF + ins * 256), 4, o.sa[i],
-                                                   sbyte, 0, 0);
+          dma_load4(t.rsa, o.sa[i], sbyte, (uint32_t)(uintptr_t)(st + C::SA_OFF + ins * 256));
         }
 #pragma unroll
         for (int i = 0; i < C::SB_PT; ++i) {
           const int ins = (wave + i * C::NW) % C::SB_INST;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rsb, (lds_void*)(st + C::SB_OFF + ins * 256), 4, o.sb[i],
-                                                   sbyte, 0, 0);
+          dma_load4(t.rsb, o.sb[i], sbyte, (uint32_t)(uintptr_t)(st + C::SB_OFF + ins * 256));
         }
       }
     }
@@ -424,12 +482,12 @@ struct Kernel {
 #pragma unroll
       for (int i = 0; i < C::SAR_PT; ++i) {
         const int row = tid + i * NT;
-        if (C::BM % NT == 0 || row < C::BM) r.sa[i] = load_scale_row(s_pitch, t.rsa, row, ks);
+        if (C::BM % NT == 0 || row < C::BM) r.sa[i] = load_scale_row(s_pitch, rsrc_of(t.rsa), row, ks);
       }
 #pragma unroll
       for (int i = 0; i < C::SBR_PT; ++i) {
         const int row = tid + i * NT;
-        if (C::BN % NT == 0 || row < C::BN) r.sb[i] = load_scale_row(s_pitch, t.rsb, row, ks);
+        if (C::BN % NT == 0 || row < C::BN) r.sb[i] = load_scale_row(s_pitch, rsrc_of(t.rsb), row, ks);
       }
     }
   }
@@ -626,11 +684,15 @@ struct Kernel {
 
   // Finishes one tile: C = round(sigma * (acc + P[w-1] + ... + P[first]) + bias),
   // the partials of the lower workgroups added in descending order (none when
-  // first >= w), straight from registers.  Each lane holds, per block and run,
-  // four consecutive columns of one row, which go out as one 8-byte store of
-  // four bf16.  The tile's bias was staged in LDS (as -0 when there is none).
+  // first >= w).  Each lane holds, per block and run, four consecutive
+  // columns of one row.  When N % 8 == 0 the wave rounds MF rows x SC columns
+  // at a time into its part of the LDS stage `stg` (free while a tile is
+  // finished) and writes them back as 16-byte pieces of whole rows, so each
+  // store instruction fills entire 128-byte lines; otherwise elements are
+  // stored one by one.  The tile's bias was staged in LDS (as -0 when there
+  // is none).
   static __device__ __forceinline__ void epilogue(const KArgs& a, int tile, const Acc<C>& acc, const lds_u8* smem,
-                                                  int w, int first) {
+                                                  lds_u8* stg, int w, int first) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int lr = lane % C::MF, g = lane / C::MF;
@@ -646,53 +708,89 @@ struct Kernel {
       sigma = x * y;
     }
     const int N = a.N;
-    // Either every 4-column run is whole and 8-byte aligned (N % 4 == 0 and an
-    // 8-aligned C), so a run lies entirely inside or outside the matrix, or
-    // elements are stored one by one.
-    const bool vec = (N & 3) == 0 && ((uintptr_t)a.C & 7) == 0;
+    const bool staged = (N & 7) == 0;
+    lds_u8* sw = stg + wave * C::STG_WAVE;
     mfma_read_hazard();
+
+    // the rounded run (block i, j; run q) of this lane, partials included
+    auto run_bits = [&](int j, int q, const v4f& xq) -> v2u {
+      const int tcol = wn * C::WTN + j * C::MF + (C::MF == 32 ? 8 * q + 4 * g : 4 * g);
+      const v2u bb = *(const __attribute__((address_space(3))) v2u*)(smem + C::BIAS_OFF + tcol * 2);
+      const float b4[4] = {__uint_as_float(bb[0] << 16), __uint_as_float(bb[0] & 0xffff0000u),
+                           __uint_as_float(bb[1] << 16), __uint_as_float(bb[1] & 0xffff0000u)};
+      float t[4];
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+      for (int k = 0; k < 4; ++k) t[k] = C::DT == DT_FP8 ? xq[k] * sigma : xq[k];
+      return round_run(t, b4);
+    };
+    auto block_sums = [&](const typename Acc<C>::T& blk, int i, int j, v4f x[C::NQ]) {
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        v4f x[C::NQ];
+      for (int q = 0; q < C::NQ; ++q) x[q] = read_run(blk, q);
+      for (int v = w - 1; v >= first; --v) {
+        const uint32_t base = slot_off(v);
+        v4u p[C::NQ];
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q) x[q] = read_run(acc.v[i][j], q);
-        for (int v = w - 1; v >= first; --v) {
-          const uint32_t base = slot_off(v);
-          v4u p[C::NQ];
+        for (int q = 0; q < C::NQ; ++q) p[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, base + run_off(i, j, q), 0, 0);
 #pragma unroll
-          for (int q = 0; q < C::NQ; ++q) p[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, base + run_off(i, j, q), 0, 0);
+        for (int q = 0; q < C::NQ; ++q) x[q] += __builtin_bit_cast(v4f, p[q]);
+      }
+    };
+
+    // compile-time block indices throughout: accumulators are only ever
+    // indexed by constants (a dynamic index would move them to scratch)
+    static_for<C::FM>([&](auto ic_) {
+      constexpr int i = decltype(ic_)::value;
+      const uint32_t row0 = (uint32_t)(wm * C::WTM + i * C::MF);     // first row of the block row, in the tile
+      if (staged) {
+        static_for<C::WTN / C::SC>([&](auto cwc) {
+          constexpr int cw = decltype(cwc)::value;
+          static_for<C::SC / C::MF>([&](auto jjc) {
+            constexpr int jj = decltype(jjc)::value;
+            constexpr int j = cw * (C::SC / C::MF) + jj;
+            v4f x[C::NQ];
+            block_sums(acc.v[i][j], i, j, x);
 #pragma unroll
-          for (int q = 0; q < C::NQ; ++q) x[q] += __builtin_bit_cast(v4f, p[q]);
-        }
-        const uint32_t row = (uint32_t)(wm * C::WTM + i * C::MF + lr);     // inside the tile
+            for (int q = 0; q < C::NQ; ++q) {
+              const v2u h = run_bits(j, q, x[q]);
+              const int c = jj * C::MF + (C::MF == 32 ? 8 * q + 4 * g : 4 * g);   // column in the window
+              const int off = lr * (C::SC * 2) + (((c >> 3) ^ (lr % C::SCH)) << 4) + (((c >> 2) & 1) << 3);
+              *(__attribute__((address_space(3))) v2u*)(sw + off) = h;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+          // every lane's writes land before any lane's reads (one wave's LDS
+          // operations execute in order; this keeps the compiler from moving
+          // them across each other)
+          asm volatile("" ::: "memory");
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q) {
-          const int tcol = wn * C::WTN + j * C::MF + (C::MF == 32 ? 8 * q + 4 * g : 4 * g);
-          const int col = n0 + tcol;
-          const v2u bb = *(const __attribute__((address_space(3))) v2u*)(smem + C::BIAS_OFF + tcol * 2);
-          const float b4[4] = {__uint_as_float(bb[0] << 16), __uint_as_float(bb[0] & 0xffff0000u),
-                               __uint_as_float(bb[1] << 16), __uint_as_float(bb[1] & 0xffff0000u)};
-          uint32_t h[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            float v = x[q][k];
-            if constexpr (C::DT == DT_FP8) v = v * sigma;
-            h[k] = round_sum_bf16(v, b4[k]);
+          for (int ps = 0; ps < C::MF / C::SRP; ++ps) {
+            const int r = ps * C::SRP + lane / C::SCH, ch = lane % C::SCH;
+            const v4u d = *(const __attribute__((address_space(3))) v4u*)(sw + r * (C::SC * 2) + ((ch ^ (r % C::SCH)) << 4));
+            const int col = n0 + wn * C::WTN + cw * C::SC + ch * 8;
+            const uint32_t coff = col < N ? ((row0 + r) * (uint32_t)N + (uint32_t)col) * 2u : kOob;
+            __builtin_amdgcn_raw_buffer_store_b128(d, rc, coff, 0, 0);
           }
-          const uint32_t coff = (row * (uint32_t)N + (uint32_t)col) * 2u;
-          if (vec) {
-            __builtin_amdgcn_raw_buffer_store_b64(v2u{h[0] | (h[1] << 16), h[2] | (h[3] << 16)}, rc,
-                                                  col < N ? coff : kOob, 0, 0);
-          } else {
+          asm volatile("" ::: "memory");
+        });
+      } else {
+        static_for<C::FN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          v4f x[C::NQ];
+          block_sums(acc.v[i][j], i, j, x);
+#pragma unroll
+          for (int q = 0; q < C::NQ; ++q) {
+            const v2u h = run_bits(j, q, x[q]);
+            const int col = n0 + wn * C::WTN + j * C::MF + (C::MF == 32 ? 8 * q + 4 * g : 4 * g);
+            const uint32_t coff = ((row0 + lr) * (uint32_t)N + (uint32_t)col) * 2u;
+            const uint32_t hv[4] = {h[0] & 0xffffu, h[0] >> 16, h[1] & 0xffffu, h[1] >> 16};
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h[k], rc, col + k < N ? coff + 2u * k : kOob, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv[k], rc, col + k < N ? coff + 2u * k : kOob, 0, 0);
           }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
+    });
   }
 
   // Position in a workgroup's work list: the WorkIter fields that change as
@@ -896,7 +994,9 @@ struct Kernel {
           lds_barrier();   // every wave is done with the previous tile's bias
           if (tid < C::BN) *(__attribute__((address_space(3))) uint16_t*)(smem + C::BIAS_OFF + tid * 2) = (uint16_t)bias_h;
           lds_barrier();
-          epilogue(kargs(), ic.tile, acc, smem, w, first);
+          // the stage of the item's last k-step is free until the next k-step issues into it
+          epilogue(kargs(), ic.tile, acc, smem, stage_ptr(smem, (done + S - 1) % S), w, first);
+          lds_barrier();   // ... which must wait until every wave is done staging output there
         }
       }
       if (!advance(w, cc, ic)) break;
