@@ -42,15 +42,18 @@
  * the caller and must stay valid until the stream has passed the launch.
  * Calls enqueue on `stream` (a hipStream_t; NULL is the default stream) and
  * return without waiting.  The library owns its scratch (fp32 partial tiles,
- * lock flags, an error word), kept per (device, stream), grown on demand and
- * freed by sk_release_workspace().  Device-side failures (a workgroup that
+ * lock flags, an error word, and for MXFP4 a k-step-major copy of the two
+ * scale arrays that a small kernel writes before the GEMM on the same
+ * stream), kept per (device, stream), grown on demand and freed by
+ * sk_release_workspace().  Device-side failures (a workgroup that
  * waited past its spin limit) are reported by sk_check().
  *
  * Errors: every call returns an sk_status and never aborts.  Arguments are
  * checked before anything is launched:
  *   SK_ERR_ARG          a required pointer is NULL, M, N or K < 1, a size is
  *                       beyond the supported range (M < 2^31, N <= 2^22,
- *                       K <= 2^21, tiles * MAC iterations per tile < 2^31),
+ *                       K <= 2^21, tiles * MAC iterations per tile < 2^31;
+ *                       MXFP4: M * K / 32 and N * K / 32 below 2^31),
  *                       C overlaps an input, bf16 given scales, an unknown
  *                       dtype / policy, or sk_addmm without a bias;
  *   SK_ERR_ALIGN        MXFP4 K not a multiple of 32, fp8 K not a multiple of

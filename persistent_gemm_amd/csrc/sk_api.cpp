@@ -43,6 +43,8 @@ struct Workspace {
   hipStream_t stream = nullptr;
   float* P = nullptr;
   size_t p_bytes = 0;
+  uint8_t* S = nullptr;       // MXFP4 scales of A and B, k-step-major
+  size_t s_bytes = 0;
   uint32_t* flags = nullptr;  // kMaxGrid locks, then the error word
   uint32_t epoch = 0;         // last epoch used
 };
@@ -196,8 +198,27 @@ sk_status validate(const sk_gemm_args& g) {
   return SK_OK;
 }
 
-// Scratch of (device, stream), grown to p_bytes; called with g_mu unlocked.
-sk_status get_workspace(int dev, hipStream_t stream, size_t p_bytes, Workspace** out) {
+// Grows one workspace buffer; work queued on the stream may still read the old one.
+template <class T>
+sk_status grow(hipStream_t stream, T** buf, size_t* have, size_t want) {
+  if (want <= *have) return SK_OK;
+  if (*buf) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return SK_ERR_HIP;
+    hipFree(*buf);
+    *buf = nullptr;
+    *have = 0;
+  }
+  if (hipMalloc((void**)buf, want) != hipSuccess) {
+    *buf = nullptr;
+    return SK_ERR_NOMEM;
+  }
+  *have = want;
+  return SK_OK;
+}
+
+// Scratch of (device, stream), grown to p_bytes of partial tiles and s_bytes
+// of re-laid scales; called with g_mu unlocked.
+sk_status get_workspace(int dev, hipStream_t stream, size_t p_bytes, size_t s_bytes, Workspace** out) {
   std::lock_guard<std::mutex> lk(g_mu);
   const auto key = std::make_pair(dev, (uintptr_t)stream);
   Workspace*& ws = g_ws[key];
@@ -218,21 +239,10 @@ sk_status get_workspace(int dev, hipStream_t stream, size_t p_bytes, Workspace**
     }
     ws = w;
   }
-  if (p_bytes > ws->p_bytes) {
-    // The old buffer may still be read by work queued on this stream.
-    if (ws->P) {
-      if (hipStreamSynchronize(stream) != hipSuccess) return SK_ERR_HIP;
-      hipFree(ws->P);
-      ws->P = nullptr;
-      ws->p_bytes = 0;
-    }
-    size_t want = p_bytes;
-    if (hipMalloc((void**)&ws->P, want) != hipSuccess) {
-      ws->P = nullptr;
-      return SK_ERR_NOMEM;
-    }
-    ws->p_bytes = want;
-  }
+  sk_status st = grow(stream, &ws->P, &ws->p_bytes, p_bytes);
+  if (st != SK_OK) return st;
+  st = grow(stream, &ws->S, &ws->s_bytes, s_bytes);
+  if (st != SK_OK) return st;
   *out = ws;
   return SK_OK;
 }
@@ -260,21 +270,40 @@ sk_status run(const sk_gemm_args& g) {
   st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, info.cus, &p);
   if (st != SK_OK) return st;
   hipStream_t stream = (hipStream_t)g.stream;
+  const Variant* v = sk::variant(p.variant);
+  // MXFP4 scales are read from a k-step-major copy: one k-step's scales of a
+  // tile are then one contiguous block (row-major scales would put each row's
+  // 4 or 8 bytes in a different cache line).  Every offset into the copy must
+  // fit in 32 bits.
+  const int64_t spr = v->kb / 16, ksteps = p.iters_per_tile;
+  int64_t sa_bytes = 0, sb_bytes = 0;
+  if (g.dtype == SK_MXFP4) {
+    sa_bytes = ksteps * g.M * spr;
+    sb_bytes = ksteps * g.N * spr;
+    if (sa_bytes >= ((int64_t)1 << 31) || sb_bytes >= ((int64_t)1 << 31)) return SK_ERR_ARG;
+  }
+  const int64_t sb_at = (sa_bytes + 255) / 256 * 256;
   Workspace* ws = nullptr;
-  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, &ws);
+  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, (size_t)(sb_at + sb_bytes), &ws);
   if (st != SK_OK) return st;
   uint32_t epoch = 0;
   st = next_epoch(ws, &epoch);
   if (st != SK_OK) return st;
 
-  const Variant* v = sk::variant(p.variant);
   KArgs a;
   std::memset(&a, 0, sizeof(a));
   a.A = (const uint8_t*)g.A;
   a.B = (const uint8_t*)g.B;
   if (g.dtype == SK_MXFP4) {
-    a.SA = (const uint8_t*)g.A_scale;
-    a.SB = (const uint8_t*)g.B_scale;
+    if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, ws->S, (int)g.M, (int)(g.K / 32), (int)ksteps, (int)spr,
+                                  stream) != hipSuccess ||
+        sk::launch_scale_relayout((const uint8_t*)g.B_scale, ws->S + sb_at, (int)g.N, (int)(g.K / 32), (int)ksteps,
+                                  (int)spr, stream) != hipSuccess)
+      return SK_ERR_HIP;
+    a.SA = ws->S;
+    a.SB = ws->S + sb_at;
+    a.sa_kstride = (uint32_t)(g.M * spr);
+    a.sb_kstride = (uint32_t)(g.N * spr);
   } else if (g.dtype == SK_FP8_E4M3) {
     a.fsa = (const float*)g.A_scale;
     a.fsb = (const float*)g.B_scale;
@@ -288,7 +317,6 @@ sk_status run(const sk_gemm_args& g) {
   a.N = (int32_t)g.N;
   a.K = (int32_t)g.K;
   a.row_bytes = (int32_t)row_bytes(g.dtype, g.K);
-  a.s_pitch = g.dtype == SK_MXFP4 ? (int32_t)(g.K / 32) : 0;
   a.tiles = (int32_t)p.tiles;
   a.sk_tiles = (int32_t)p.sk_tiles;
   a.q = (int32_t)p.iters_per_wg;
@@ -298,11 +326,6 @@ sk_status run(const sk_gemm_args& g) {
   a.iters = p.iters_per_tile;
   a.G = p.grid;
   a.epoch = epoch;
-  const int spr = v->kb / 16;
-  a.scale_fast = (g.dtype == SK_MXFP4 && a.s_pitch % spr == 0 && a.s_pitch % 8 == 0 &&
-                  ((uintptr_t)g.A_scale % 8) == 0 && ((uintptr_t)g.B_scale % 8) == 0)
-                     ? 1u
-                     : 0u;
   a.spin_limit = g.spin_limit_ticks ? g.spin_limit_ticks : kDefaultSpin;
   a.drop_wg = (g.debug_flags & SK_DEBUG_DROP_SIGNAL) ? g.drop_signal_wg : -1;
   a.delay_seed = (g.debug_flags & SK_DEBUG_DELAY) ? (g.delay_seed ? g.delay_seed : 1u) : 0u;
@@ -436,6 +459,7 @@ void sk_release_workspace(void) {
     hipSetDevice(ws->device);
     hipStreamSynchronize(ws->stream);
     if (ws->P) hipFree(ws->P);
+    if (ws->S) hipFree(ws->S);
     if (ws->flags) hipFree(ws->flags);
     delete ws;
   }
@@ -449,7 +473,7 @@ sk_status sk_debug_poison_workspace(void* stream, int64_t scratch_bytes) {
   sk_status st = device_info(&dev, &info);
   if (st != SK_OK) return st;
   Workspace* ws = nullptr;
-  st = get_workspace(dev, (hipStream_t)stream, scratch_bytes > 0 ? (size_t)scratch_bytes : 0, &ws);
+  st = get_workspace(dev, (hipStream_t)stream, scratch_bytes > 0 ? (size_t)scratch_bytes : 0, 0, &ws);
   if (st != SK_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (ws->P && hipMemsetAsync(ws->P, 0xFF, ws->p_bytes, s) != hipSuccess) return SK_ERR_HIP;  // all-ones = NaN

@@ -26,8 +26,8 @@ constexpr int64_t kMaxIters = ((int64_t)1 << 31) - 1;
 struct KArgs {
   const uint8_t* A;
   const uint8_t* B;
-  const uint8_t* SA;        // MXFP4 block scales of A, [M][K/32]
-  const uint8_t* SB;        // MXFP4 block scales of B, [N][K/32]
+  const uint8_t* SA;        // MXFP4 block scales of A, k-step-major: [k-step][M][SPR]
+  const uint8_t* SB;        // MXFP4 block scales of B, k-step-major: [k-step][N][SPR]
   const float* fsa;         // fp8 per-tensor scale of A (NULL = 1)
   const float* fsb;         // fp8 per-tensor scale of B (NULL = 1)
   const uint16_t* bias;     // bf16[N] or NULL
@@ -38,7 +38,8 @@ struct KArgs {
   uint64_t spin_limit;      // ticks of the 100 MHz realtime counter
   int32_t M, N, K;
   int32_t row_bytes;        // bytes of K data per row of A and of B (their pitch)
-  int32_t s_pitch;          // bytes per row of the MXFP4 scales (K/32)
+  uint32_t sa_kstride;      // bytes per k-step block of SA (M * SPR) and of SB (N * SPR)
+  uint32_t sb_kstride;
   int32_t tiles;            // T
   int32_t sk_tiles;         // tiles [0, sk_tiles) are split by MAC iteration
   int32_t q, r;             // Stream-K iterations S = q*G + r
@@ -46,7 +47,6 @@ struct KArgs {
   int32_t iters;            // I, MAC iterations (k-steps) per tile
   int32_t G;                // persistent workgroups
   uint32_t epoch;           // this launch's flag value
-  uint32_t scale_fast;      // 1: every k-step of scales is whole and 8-byte aligned
   int32_t drop_wg;          // test hook: this workgroup never publishes (-1: none)
   uint32_t delay_seed;      // test hook: nonzero = seeded sleeps before publishing
 };
@@ -162,5 +162,10 @@ struct Variant {
 
 int num_variants();
 const Variant* variant(int index);
+
+// Copies MXFP4 scales [rows][s_pitch] into the k-step-major layout the GEMM
+// reads: dst[ks][r][0..spr) = src[r][ks*spr ...], padded with 127 (x1).
+hipError_t launch_scale_relayout(const uint8_t* src, uint8_t* dst, int rows, int s_pitch, int ksteps, int spr,
+                                 hipStream_t s);
 
 }  // namespace sk

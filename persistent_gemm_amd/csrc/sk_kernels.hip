@@ -22,8 +22,9 @@
 // buffer loads (one wave instruction fills one 1 KiB row group; rows and K
 // chunks past the matrix read as zero) into a ring of STAGES buffers, issued
 // STAGES-1 k-steps ahead of use.  MXFP4 scale bytes go the same way (dword
-// loads) when every k-step of scales is whole and aligned, else through
-// registers one k-step ahead.  Operands are consumed by MFMA:
+// loads) from a k-step-major copy of the scales that a small pass before the
+// GEMM writes (sk_scale_relayout below), so that one k-step's scales of a
+// tile are one contiguous block.  Operands are consumed by MFMA:
 //   MXFP4: v_mfma_scale_f32_{32x32x64,16x16x128}_f8f6f4 with E2M1 operands and
 //          the E8M0 block scales as the per-lane scale operands;
 //   fp8:   the same instruction with E4M3 operands and unit block scales; the
@@ -79,6 +80,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ v4u rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   return v4u{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
+}
+
+// The same resource with its base moved up by `off` bytes.  (The range check
+// covers the SGPR offset too, so offsets past the records cannot ride there.)
+__device__ __forceinline__ v4u rsrc_plus(const v4u& r, uint32_t off) {
+  const uint64_t b = (((uint64_t)(r[1] & 0xffffu) << 32) | r[0]) + off;
+  return v4u{(uint32_t)b, (r[1] & 0xffff0000u) | ((uint32_t)(b >> 32) & 0xffffu), r[2], r[3]};
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const v4u& r) {
@@ -151,11 +159,7 @@ struct Cfg {
   // group (same bytes to the same place), so every wave issues the same count.
   static constexpr int A_PT = cdiv(A_GROUPS, NW), B_PT = cdiv(B_GROUPS, NW);
   static constexpr int SA_PT = cdiv(SA_INST, NW), SB_PT = cdiv(SB_INST, NW);
-  static constexpr int LOADS_PER_STAGE = A_PT + B_PT;             // data only
   static constexpr int LOADS_PER_STAGE_S = A_PT + B_PT + SA_PT + SB_PT;
-  // Register path for scales (ragged or unaligned K): one row per thread.
-  static constexpr int SAR_PT = DT == DT_MXFP4 ? cdiv(BM, NT) : 0;
-  static constexpr int SBR_PT = DT == DT_MXFP4 ? cdiv(BN, NT) : 0;
   static constexpr int P_SLOT = BM * BN;                // floats per scratch slot
   static constexpr int P_WAVE = FM * FN * ACC * 64;     // floats per wave in a slot
   static constexpr int NQ = ACC / 4;                    // 4-column runs per block per lane
@@ -339,10 +343,9 @@ struct Kernel {
   // Per-lane 32-bit buffer offsets of this wave's direct-to-LDS loads, fixed
   // for a launch.  Lane j of a data load fills slot j % CPR of row
   // (group*RG + j / CPR), so it fetches that row's chunk (j % CPR) ^ swz(row);
-  // lane j of a scale load takes the (j % DPR)-th scale dword of row
-  // (inst*64/DPR + j / DPR).  Rows past M or N lie outside the tile's buffer
+  // lane j of a scale load takes bytes [inst*256 + 4j, +4) of the k-step's
+  // scale block ([row][SPR]).  Rows past M or N lie outside the tile's buffer
   // resource and read as zero.
-  static constexpr int DPR = C::SPR / 4 > 0 ? C::SPR / 4 : 1;   // scale dwords per row
   struct LoadOffs {
     uint32_t a[C::A_PT];     // lane's row offset plus chunk offset, per load
     uint32_t b[C::B_PT];
@@ -350,11 +353,6 @@ struct Kernel {
     uint32_t cb[C::B_PT];
     uint32_t sa[C::SA_PT > 0 ? C::SA_PT : 1];
     uint32_t sb[C::SB_PT > 0 ? C::SB_PT : 1];
-  };
-  // Scale bytes of one k-step through registers (the fallback path).
-  struct ScaleRegs {
-    v2u sa[C::SAR_PT > 0 ? C::SAR_PT : 1];
-    v2u sb[C::SBR_PT > 0 ? C::SBR_PT : 1];
   };
   struct Ops {
     v4u a[C::FM][C::NCH];
@@ -382,8 +380,10 @@ struct Kernel {
     t.ra = rsrc_words(a.A + (int64_t)m0 * a.row_bytes, (uint32_t)(rows_a * a.row_bytes));
     t.rb = rsrc_words(a.B + (int64_t)n0 * a.row_bytes, (uint32_t)(rows_b * a.row_bytes));
     if constexpr (C::DT == DT_MXFP4) {
-      t.rsa = rsrc_words(a.SA + (int64_t)m0 * a.s_pitch, (uint32_t)(rows_a * a.s_pitch));
-      t.rsb = rsrc_words(a.SB + (int64_t)n0 * a.s_pitch, (uint32_t)(rows_b * a.s_pitch));
+      // k-step-major scales: k-step ks of row r at SA + ks * sa_kstride + r * SPR
+      // (the k-step's block is reached by moving the base, see rsrc_plus)
+      t.rsa = rsrc_words(a.SA + (int64_t)m0 * C::SPR, (uint32_t)(rows_a * C::SPR));
+      t.rsb = rsrc_words(a.SB + (int64_t)n0 * C::SPR, (uint32_t)(rows_b * C::SPR));
     } else {
       t.rsa = t.ra;
       t.rsb = t.rb;
@@ -408,110 +408,19 @@ struct Kernel {
       o.b[i] = (uint32_t)row * (uint32_t)a.row_bytes + o.cb[i];
     }
     if constexpr (C::DT == DT_MXFP4) {
-      const int d = lane % DPR, r = lane / DPR;
+      // the k-step's scale bytes of the tile's rows are contiguous ([row][SPR])
 #pragma unroll
       for (int i = 0; i < C::SA_PT; ++i) {
-        const int row = ((wave + i * C::NW) % C::SA_INST) * (64 / DPR) + r;
-        o.sa[i] = row < C::BM ? (uint32_t)(row * a.s_pitch + d * 4) : kOob;
+        const int byte = ((wave + i * C::NW) % C::SA_INST) * 256 + lane * 4;
+        o.sa[i] = byte < C::BM * C::SPR ? (uint32_t)byte : kOob;
       }
 #pragma unroll
       for (int i = 0; i < C::SB_PT; ++i) {
-        const int row = ((wave + i * C::NW) % C::SB_INST) * (64 / DPR) + r;
-        o.sb[i] = row < C::BN ? (uint32_t)(row * a.s_pitch + d * 4) : kOob;
+        const int byte = ((wave + i * C::NW) % C::SB_INST) * 256 + lane * 4;
+        o.sb[i] = byte < C::BN * C::SPR ? (uint32_t)byte : kOob;
       }
     }
     return o;
-  }
-
-  // Issue the direct-to-LDS loads of k-step ks into stage `st`.  The k-step's
-  // byte offset rides in the uniform soffset (all bounds checks use the lane
-  // offset alone); in a ragged last k-step, chunks past the end of the row
-  // point outside the buffer and read as zero.
-  static __device__ __forceinline__ void issue(int row_bytes, const TileCtx& t, const LoadOffs& o, int ks,
-                                               lds_u8* st, bool scales_direct) {
-    const int wave = wave_id();
-    const uint32_t kbyte = (uint32_t)ks * C::KB;
-    const bool ragged = kbyte + C::KB > (uint32_t)row_bytes;
-#pragma unroll
-    for (int i = 0; i < C::A_PT; ++i) {
-      const int grp = (wave + i * C::NW) % C::A_GROUPS;
-      const bool kin = !ragged || kbyte + o.ca[i] < (uint32_t)row_bytes;
-      dma_load16(t.ra, kin ? o.a[i] : kOob, kbyte, (uint32_t)(uintptr_t)(st + C::A_OFF + grp * 1024));
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PT; ++i) {
-      const int grp = (wave + i * C::NW) % C::B_GROUPS;
-      const bool kin = !ragged || kbyte + o.cb[i] < (uint32_t)row_bytes;
-      dma_load16(t.rb, kin ? o.b[i] : kOob, kbyte, (uint32_t)(uintptr_t)(st + C::B_OFF + grp * 1024));
-    }
-    if constexpr (C::DT == DT_MXFP4) {
-      if (scales_direct) {
-        const uint32_t sbyte = (uint32_t)ks * C::SPR;
-#pragma unroll
-        for (int i = 0; i < C::SA_PT; ++i) {
-          const int ins = (wave + i * C::NW) % C::SA_INST;
-          dma_load4(t.rsa, o.sa[i], sbyte, (uint32_t)(uintptr_t)(st + C::SA_OFF + ins * 256));
-        }
-#pragma unroll
-        for (int i = 0; i < C::SB_PT; ++i) {
-          const int ins = (wave + i * C::NW) % C::SB_INST;
-          dma_load4(t.rsb, o.sb[i], sbyte, (uint32_t)(uintptr_t)(st + C::SB_OFF + ins * 256));
-        }
-      }
-    }
-  }
-
-  // Fallback for scales: SPR bytes of one row for k-step ks with byte loads;
-  // bytes past K/32 read as 127 (x1) so they never turn zero padding into NaN.
-  static __device__ __forceinline__ v2u load_scale_row(int s_pitch, __amdgpu_buffer_rsrc_t rs, int row, int ks) {
-    const uint32_t off = (uint32_t)(row * s_pitch) + (uint32_t)(ks * C::SPR);
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < C::SPR; ++j) {
-      const bool in = ks * C::SPR + j < s_pitch;
-      uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? off + j : kOob, 0, 0);
-      if (!in) v = 127u;
-      w[j >> 2] |= v << (8 * (j & 3));
-    }
-    return v2u{w[0], w[1]};
-  }
-
-  static __device__ __forceinline__ void load_scale_regs(int s_pitch, const TileCtx& t, int ks, ScaleRegs& r) {
-    if constexpr (C::DT == DT_MXFP4) {
-      const int tid = threadIdx.x;
-#pragma unroll
-      for (int i = 0; i < C::SAR_PT; ++i) {
-        const int row = tid + i * NT;
-        if (C::BM % NT == 0 || row < C::BM) r.sa[i] = load_scale_row(s_pitch, rsrc_of(t.rsa), row, ks);
-      }
-#pragma unroll
-      for (int i = 0; i < C::SBR_PT; ++i) {
-        const int row = tid + i * NT;
-        if (C::BN % NT == 0 || row < C::BN) r.sb[i] = load_scale_row(s_pitch, rsrc_of(t.rsb), row, ks);
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void store_scale_regs(lds_u8* st, const ScaleRegs& r) {
-    if constexpr (C::DT == DT_MXFP4) {
-      const int tid = threadIdx.x;
-#pragma unroll
-      for (int i = 0; i < C::SAR_PT; ++i) {
-        const int row = tid + i * NT;
-        if (C::BM % NT == 0 || row < C::BM) {
-          if constexpr (C::SPR == 8) *(__attribute__((address_space(3))) v2u*)(st + C::SA_OFF + row * 8) = r.sa[i];
-          else *(__attribute__((address_space(3))) uint32_t*)(st + C::SA_OFF + row * 4) = r.sa[i][0];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < C::SBR_PT; ++i) {
-        const int row = tid + i * NT;
-        if (C::BN % NT == 0 || row < C::BN) {
-          if constexpr (C::SPR == 8) *(__attribute__((address_space(3))) v2u*)(st + C::SB_OFF + row * 8) = r.sb[i];
-          else *(__attribute__((address_space(3))) uint32_t*)(st + C::SB_OFF + row * 4) = r.sb[i][0];
-        }
-      }
-    }
   }
 
   // Chunk permutation of row r: for 128-byte rows, rows 2k and 2k+1 share the
@@ -569,6 +478,92 @@ struct Kernel {
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
         o.b[j][h] = *(const __attribute__((address_space(3))) v4u*)(p.b + off + j * C::MF * C::KB);
+    }
+  }
+
+  // The operand reads of one sub-step, one at a time, A and B blocks
+  // interleaved (A0, B0, A1, B1, ...) so that the first MFMAs of a sub-step
+  // find their operands first.
+  static constexpr int NRD = (C::FM + C::FN) * C::NCH;   // operand reads per sub-step
+  static constexpr int NSR = C::FM + C::FN;              // scale reads per stage
+  struct ReadDesc {
+    bool a;
+    int blk, h;
+  };
+  static constexpr ReadDesc read_desc(int r) {
+    const int h = r % C::NCH;
+    int k = r / C::NCH;
+    const int m = C::FM > C::FN ? C::FM : C::FN;
+    for (int t = 0; t < m; ++t) {
+      if (t < C::FM) {
+        if (k == 0) return ReadDesc{true, t, h};
+        --k;
+      }
+      if (t < C::FN) {
+        if (k == 0) return ReadDesc{false, t, h};
+        --k;
+      }
+    }
+    return ReadDesc{true, 0, 0};
+  }
+  template <int U, int R>
+  static __device__ __forceinline__ void read_op(int so, const LdsPtrs& p, Ops& o) {
+    constexpr ReadDesc d = read_desc(R);
+    const int off = so + p.slot[U * C::NCH + d.h];
+    if constexpr (d.a)
+      o.a[d.blk][d.h] = *(const __attribute__((address_space(3))) v4u*)(p.a + off + d.blk * C::MF * C::KB);
+    else
+      o.b[d.blk][d.h] = *(const __attribute__((address_space(3))) v4u*)(p.b + off + d.blk * C::MF * C::KB);
+  }
+  template <int R>
+  static __device__ __forceinline__ void read_scale(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
+    if constexpr (C::DT == DT_MXFP4) {
+      if constexpr (R < C::FM) sc.a[R] = scale_word(st + p.sa + R * C::MF * C::SPR);
+      else sc.b[R - C::FM] = scale_word(st + p.sb + (R - C::FM) * C::MF * C::SPR);
+    } else {
+      if constexpr (R < C::FM) sc.a[R] = 0x7f7f7f7f;
+      else sc.b[R - C::FM] = 0x7f7f7f7f;
+    }
+  }
+  template <int U, int B>
+  static __device__ __forceinline__ void mfma_one(const Ops& o, const Scales& sc, Acc<C>& acc) {
+    constexpr int i = B / C::FN, j = B % C::FN;
+    mfma<C, (C::DT == DT_MXFP4 ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
+  }
+
+  // One direct-to-LDS load of a k-step, by its index P among the k-step's
+  // LOADS_PER_STAGE_S loads (A row groups, then B, then the two scale areas).
+  // d.valid false issues the same load with every lane out of range: it
+  // writes zeros into a stage nobody reads, so that every k-step issues the
+  // same number of loads.
+  struct DmaCtx {
+    TileCtx t;
+    uint32_t kbyte;       // the k-step's byte offset in a row of A or B
+    v4u rsa, rsb;         // the k-step's scale blocks
+    uint32_t lds;         // LDS address of the target stage
+    bool valid, ragged;
+  };
+  template <int P>
+  static __device__ __forceinline__ void dma_piece(const DmaCtx& d, const LoadOffs& o, int row_bytes) {
+    const int wave = wave_id();
+    if constexpr (P < C::A_PT) {
+      constexpr int i = P;
+      const int grp = (wave + i * C::NW) % C::A_GROUPS;
+      const bool kin = d.valid && (!d.ragged || d.kbyte + o.ca[i] < (uint32_t)row_bytes);
+      dma_load16(d.t.ra, kin ? o.a[i] : kOob, d.kbyte, d.lds + C::A_OFF + grp * 1024);
+    } else if constexpr (P < C::A_PT + C::B_PT) {
+      constexpr int i = P - C::A_PT;
+      const int grp = (wave + i * C::NW) % C::B_GROUPS;
+      const bool kin = d.valid && (!d.ragged || d.kbyte + o.cb[i] < (uint32_t)row_bytes);
+      dma_load16(d.t.rb, kin ? o.b[i] : kOob, d.kbyte, d.lds + C::B_OFF + grp * 1024);
+    } else if constexpr (P < C::A_PT + C::B_PT + C::SA_PT) {
+      constexpr int i = P - C::A_PT - C::B_PT;
+      const int ins = (wave + i * C::NW) % C::SA_INST;
+      dma_load4(d.rsa, d.valid ? o.sa[i] : kOob, 0u, d.lds + C::SA_OFF + ins * 256);
+    } else {
+      constexpr int i = P - C::A_PT - C::B_PT - C::SA_PT;
+      const int ins = (wave + i * C::NW) % C::SB_INST;
+      dma_load4(d.rsb, d.valid ? o.sb[i] : kOob, 0u, d.lds + C::SB_OFF + ins * 256);
     }
   }
 
@@ -831,20 +826,16 @@ struct Kernel {
   // ring of STAGES LDS buffers: k-step c (counted over the whole list) lives
   // in stage c % STAGES and its loads are issued STAGES-1 k-steps ahead, also
   // across item boundaries, so the next tile's operands are on their way while
-  // a tile is being finished.  Inside a k-step the operands of sub-step u+1
-  // are read from LDS before the MFMAs of sub-step u; at the last sub-step the
-  // next stage is published (its loads have landed and a barrier) and, inside
-  // an item, its first operands are read, overlapping the k-step's last MFMAs.
-  template <bool DIRECT>
+  // a tile is being finished.
   static __device__ __forceinline__ void run_list(lds_u8* smem, int* s_flag) {
     constexpr int S = C::STAGES;
-    constexpr int PER_STAGE = DIRECT ? C::LOADS_PER_STAGE_S : C::LOADS_PER_STAGE;
+    constexpr int PER_STAGE = C::LOADS_PER_STAGE_S;
     const int w = blockIdx.x;
     const int tid = threadIdx.x;
     const LoadOffs lo = load_offsets(kargs());
     const LdsPtrs lp = lds_ptrs(smem);
     const int row_bytes = kargs().row_bytes;
-    const int s_pitch = kargs().s_pitch;
+    const uint32_t sa_kstride = kargs().sa_kstride, sb_kstride = kargs().sb_kstride;
 
     // Two cursors over the same work list: one issues loads, one computes.
     Cursor ci = cursor_begin(w);
@@ -858,57 +849,6 @@ struct Kernel {
     int issued = 0;   // k-steps issued so far
     int done = 0;     // k-steps computed so far
 
-    // Scales through registers (when they cannot go straight to LDS): loaded
-    // with the k-step's data, written to its stage at the end of the k-step
-    // being computed meanwhile (before that k-step's closing barrier).
-    ScaleRegs sr;
-    int sr_stage = -1;
-    auto flush_scales = [&]() {
-      if constexpr (!DIRECT) {
-        if (sr_stage >= 0) {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          store_scale_regs(stage_ptr(smem, sr_stage), sr);
-          sr_stage = -1;
-        }
-      }
-    };
-    auto issue_next = [&]() {
-      if (!have_i) return;
-      lds_u8* st = stage_ptr(smem, issued % S);
-      issue(row_bytes, ti, lo, ki, st, DIRECT);
-      if constexpr (!DIRECT) {
-        load_scale_regs(s_pitch, ti, ki, sr);
-        sr_stage = issued % S;
-      }
-      ++issued;
-      if (++ki == ki_end) {
-        WorkItem x;
-        have_i = advance(w, ci, x);
-        if (have_i) {
-          ki = x.k0;
-          ki_end = x.k1;
-          ti = tile_ctx(kargs(), x.tile);
-        }
-      }
-    };
-    // The loads of stage done+1 have landed once no more than the loads of
-    // the stages after it are outstanding (loads complete in issue order;
-    // anything else outstanding is younger and only makes the wait longer).
-    auto wait_next = [&]() {
-      if constexpr (DIRECT) {
-        const int later = issued - done - 2;
-        if constexpr (S == 4) {
-          if (later >= 2) wait_vmcnt_n<2 * PER_STAGE>();
-          else if (later == 1) wait_vmcnt_n<PER_STAGE>();
-          else wait_vmcnt_n<0>();
-        } else if constexpr (S == 3) {
-          if (later >= 1) wait_vmcnt_n<PER_STAGE>();
-          else wait_vmcnt_n<0>();
-        } else {
-          wait_vmcnt_n<0>();
-        }
-      }
-    };
     // this tile's bias element (one per thread), staged in LDS before the epilogue
     auto load_bias = [&](int tile) -> uint32_t {
       const KArgs& a = kargs();
@@ -920,57 +860,121 @@ struct Kernel {
                                                  0, 0);
     };
 
-#pragma unroll
-    for (int p = 0; p < S - 1; ++p) {
-      issue_next();
-      flush_scales();
-    }
+    // ---- the direct path: one fixed, interleaved schedule per k-step.
+    // k-step d reads stage d % S and issues the loads of k-step d + S - 1 (or
+    // same-count dummies past the end of the list) into stage (d + S - 1) % S,
+    // which the barrier of k-step d - 1 freed.  Because every k-step issues
+    // PER_STAGE loads, the loads of stage d + 1 have landed once at most
+    // (S - 2) * PER_STAGE loads are outstanding (loads complete in issue
+    // order; other outstanding operations are younger and only lengthen the
+    // wait).  Slot b of a sub-step is its b-th MFMA; the k-step's loads go
+    // after the slots before the barrier, the next sub-step's operand reads
+    // after the first slots of each sub-step, and the barrier that publishes
+    // stage d + 1 sits half-way through the last sub-step, after which that
+    // stage's scales and first operands are read (inside an item) between the
+    // remaining MFMAs.  sched_barrier(0) between slots keeps this order.
+    auto dma_ctx = [&]() -> DmaCtx {
+      DmaCtx d;
+      d.t = ti;
+      d.valid = have_i;
+      d.kbyte = have_i ? (uint32_t)ki * C::KB : 0u;
+      if constexpr (C::DT == DT_MXFP4) {
+        d.rsa = rsrc_plus(ti.rsa, have_i ? (uint32_t)ki * sa_kstride : 0u);
+        d.rsb = rsrc_plus(ti.rsb, have_i ? (uint32_t)ki * sb_kstride : 0u);
+      }
+      d.ragged = d.kbyte + C::KB > (uint32_t)row_bytes;
+      d.lds = (uint32_t)(uintptr_t)stage_ptr(smem, issued % S);
+      return d;
+    };
+    auto advance_issue = [&]() {
+      ++issued;
+      if (have_i && ++ki == ki_end) {
+        WorkItem x;
+        have_i = advance(w, ci, x);
+        if (have_i) {
+          ki = x.k0;
+          ki_end = x.k1;
+          ti = tile_ctx(kargs(), x.tile);
+        }
+      }
+    };
+    constexpr int NB = C::FM * C::FN;                     // MFMA slots per sub-step
+    constexpr int HB = NB / 2;                            // slots of the last sub-step before the barrier
+    constexpr int PRE = (C::NU - 1) * NB + HB;            // slots before the barrier
+    constexpr int POST = NB - HB;
+    auto kstep_interleaved = [&](int d, Ops& o0, Ops& o1, Scales& sc0, Scales& sc1, Acc<C>& acc) {
+      const int cur = d % S, nxt = (d + 1) % S;
+      const DmaCtx dc = dma_ctx();
+      if constexpr (PRE == 0) {
+        static_for<PER_STAGE>([&](auto pc) { dma_piece<decltype(pc)::value>(dc, lo, row_bytes); });
+      }
+      static_for<C::NU>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        Ops& now = (u & 1) ? o1 : o0;
+        Ops& nxo = (u & 1) ? o0 : o1;
+        constexpr bool last = u + 1 == C::NU;
+        static_for<(last ? HB : NB)>([&](auto bc) {
+          constexpr int b = decltype(bc)::value;
+          constexpr int slot = u * NB + b;                // among the PRE slots
+          mfma_one<u, b>(now, sc0, acc);
+          if constexpr (!last) {
+            static_for<NRD>([&](auto rc) {
+              constexpr int r = decltype(rc)::value;
+              if constexpr (r * NB / NRD == b) read_op<u + 1, r>(cur * C::STAGE, lp, nxo);
+            });
+          }
+          static_for<PER_STAGE>([&](auto pc) {
+            constexpr int pp = decltype(pc)::value;
+            if constexpr (pp * PRE / PER_STAGE == slot) dma_piece<pp>(dc, lo, row_bytes);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (last) {
+          wait_vmcnt_n<(S - 2) * PER_STAGE>();
+          lds_barrier();
+          // The next k-step's scales and first operands, also when it belongs
+          // to the next item (the stage is the same either way).
+          static_for<POST>([&](auto bc) {
+            constexpr int b = decltype(bc)::value;
+            mfma_one<u, HB + b>(now, sc0, acc);
+            static_for<NSR + NRD>([&](auto rc) {
+              constexpr int r = decltype(rc)::value;
+              if constexpr (r * POST / (NSR + NRD) == b) {
+                if constexpr (r < NSR) read_scale<r>(stage_ptr(smem, nxt), lp, sc1);
+                else read_op<0, r - NSR>(nxt * C::STAGE, lp, nxo);
+              }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+          });
+          sc0 = sc1;
+          if constexpr ((C::NU & 1) == 1) o0 = o1;   // sub-step 0 always starts in o0
+        }
+        anchor(acc);
+      });
+      advance_issue();
+    };
+
+    static_for<S - 1>([&](auto) {
+      const DmaCtx dc = dma_ctx();
+      static_for<PER_STAGE>([&](auto pc) { dma_piece<decltype(pc)::value>(dc, lo, row_bytes); });
+      advance_issue();
+    });
     uint32_t bias_h = load_bias(ic.tile);
     // stage 0 landed: everything but the loads of the stages after it (and the bias load)
-    if constexpr (DIRECT) {
-      if (issued >= 3) wait_vmcnt_n<2 * PER_STAGE>();
-      else if (issued == 2) wait_vmcnt_n<PER_STAGE>();
-      else wait_vmcnt_n<0>();
-    }
+    wait_vmcnt_n<(S - 2) * PER_STAGE>();
     lds_barrier();
+    // Operands of the next k-step: each k-step reads the next one's scales
+    // and first operands (also across items), so they are read here once.
+    Ops o0, o1;
+    Scales sc0, sc1;
+    read_scales(stage_ptr(smem, 0), lp, sc0);
+    read_ops<0>(0, lp, o0);
     for (;;) {
-      // stage done % S is visible to every wave; start the item's first k-step
-      Ops o0, o1;
-      Scales sc0, sc1;
-      read_scales(stage_ptr(smem, done % S), lp, sc0);
-      read_ops<0>((done % S) * C::STAGE, lp, o0);
       Acc<C> acc;
       acc.zero();
       int n = ic.k1 - ic.k0;   // at least one k-step per item
       do {
-        const int cur = done % S;
-        const int nxt = (done + 1) % S;
-        issue_next();
-        const bool more = done + 1 < issued;   // another k-step follows (in this or a later item)
-        const bool inside = n > 1;             // ... in this item
-        static_for<C::NU>([&](auto uc) {
-          constexpr int u = decltype(uc)::value;
-          Ops& now = (u & 1) ? o1 : o0;
-          Ops& nxo = (u & 1) ? o0 : o1;
-          if constexpr (u + 1 < C::NU) {
-            read_ops<u + 1>(cur * C::STAGE, lp, nxo);
-            mfmas<u>(now, sc0, acc);
-          } else {
-            flush_scales();
-            if (more) wait_next();
-            lds_barrier();
-            // The next item's first operands are read after this item is
-            // finished, so that they do not occupy registers during its end.
-            if (inside) {
-              read_scales(stage_ptr(smem, nxt), lp, sc1);
-              read_ops<0>(nxt * C::STAGE, lp, nxo);
-            }
-            mfmas<u>(now, sc0, acc);
-            sc0 = sc1;
-            if constexpr ((C::NU & 1) == 1) o0 = o1;   // sub-step 0 always starts in o0
-          }
-          anchor(acc);
-        });
+        kstep_interleaved(done, o0, o1, sc0, sc1, acc);
         ++done;
       } while (--n > 0);
 
@@ -1009,12 +1013,7 @@ struct Kernel {
     __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::LDS_TOTAL];
     __shared__ int s_flag;
     lds_u8* smem = (lds_u8*)smem_raw;
-    if constexpr (C::DT == DT_MXFP4) {
-      if (kargs().scale_fast) run_list<true>(smem, &s_flag);
-      else run_list<false>(smem, &s_flag);
-    } else {
-      run_list<true>(smem, &s_flag);
-    }
+    run_list(smem, &s_flag);
   }
 };
 
@@ -1028,6 +1027,74 @@ void sk_gemm_kernel(KArgs a) {
 template <class C, int OCC>
 hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((sk_gemm_kernel<C, OCC>), dim3(grid), dim3(C::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- MXFP4 scale re-layout
+
+// dst[ks][r][j] = src[r][ks * SPR + j] for r < rows, ks < ksteps, j < SPR,
+// with 127 (a scale of 1) where ks * SPR + j >= s_pitch (a ragged last
+// k-step), so that every k-step's scales of consecutive rows are one
+// contiguous block.  Each workgroup moves a 64-row x 64-k-step tile through
+// LDS: read along rows (the source's contiguous direction; 16-byte loads when
+// rows are 16-byte aligned), written as SPR-byte items along rows.
+template <int SPR>
+__global__ __launch_bounds__(256) void sk_scale_relayout(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                         int rows, int s_pitch, int ksteps, int vec16) {
+  typedef typename std::conditional<SPR == 4, uint32_t, v2u>::type Item;
+  constexpr int RB = 64 * SPR;                 // bytes of one row's 64 k-steps
+  __shared__ Item tile[64 * 64];               // [k][r]
+  const int r0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  uint8_t* t8 = (uint8_t*)tile;
+  if (vec16) {
+    // s_pitch % 16 == 0: a 16-byte piece is wholly inside the row or past its end
+    constexpr int PR = RB / 16, NP = 64 * PR / 256;
+    v4u v[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pc = tid + i * 256, r = pc / PR, q = pc % PR;
+      const int row = r0 + r, col = k0 * SPR + q * 16;
+      v[i] = v4u{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
+      if (row < rows && col < s_pitch) v[i] = *(const v4u*)(src + (int64_t)row * s_pitch + col);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pc = tid + i * 256, r = pc / PR, q = pc % PR;
+#pragma unroll
+      for (int e = 0; e < 16 / SPR; ++e) {
+        const int k = q * (16 / SPR) + e;
+        if constexpr (SPR == 4) tile[k * 64 + r] = v[i][e];
+        else tile[k * 64 + r] = v2u{v[i][2 * e], v[i][2 * e + 1]};
+      }
+    }
+  } else {
+    constexpr int NB = 64 * RB / 256;
+#pragma unroll 8
+    for (int i = 0; i < NB; ++i) {
+      const int b = tid + i * 256, r = b / RB, c = b % RB;
+      const int row = r0 + r, col = k0 * SPR + c;
+      uint8_t x = 127;
+      if (row < rows && col < s_pitch) x = src[(int64_t)row * s_pitch + col];
+      t8[((c / SPR) * 64 + r) * SPR + c % SPR] = x;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 64 * 64 / 256; ++i) {
+    const int p = tid + i * 256, k = p / 64, r = p % 64;
+    const int ks = k0 + k, row = r0 + r;
+    if (ks < ksteps && row < rows) *(Item*)(dst + ((int64_t)ks * rows + row) * SPR) = tile[p];
+  }
+}
+
+hipError_t launch_scale_relayout(const uint8_t* src, uint8_t* dst, int rows, int s_pitch, int ksteps, int spr,
+                                 hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((ksteps + 63) / 64));
+  const int vec16 = (s_pitch % 16 == 0 && ((uintptr_t)src & 15) == 0) ? 1 : 0;
+  if (spr == 4) hipLaunchKernelGGL(sk_scale_relayout<4>, grid, dim3(256), 0, s, src, dst, rows, s_pitch, ksteps, vec16);
+  else if (spr == 8) hipLaunchKernelGGL(sk_scale_relayout<8>, grid, dim3(256), 0, s, src, dst, rows, s_pitch, ksteps, vec16);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
