@@ -234,57 +234,46 @@ __device__ __forceinline__ void mfma(typename Acc<C>::T& acc, const v4u* a, cons
 
 // ---------------------------------------------------------------- epilogue rounding
 
-// bf16 nearest-even of the exact value t + bias, where t and bias are fp32.
-// s = fl(t + bias) carries an error e (TwoSum).  Rounding s to bf16 gives the
-// right answer unless s sits exactly on a bf16 midpoint while e != 0: then the
-// exact sum lies on e's side of the midpoint.  Branch-free (selects only).
-__device__ __forceinline__ uint32_t round_sum_bf16(float t, float bias) {
-#pragma clang fp contract(off)
-  const float s = t + bias;
-  const float bv = s - t;
-  const float av = s - bv;
-  const float e = (t - av) + (bias - bv);
-  const uint32_t u = __float_as_uint(s);
-  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const bool tie = (u & 0xffffu) == 0x8000u && e != 0.0f;
-  const uint32_t toward = (u >> 16) + (((e > 0.0f) == (s > 0.0f)) ? 1u : 0u);
-  const uint32_t r = tie ? toward : rne;
-  return (u & 0x7fffffffu) > 0x7f800000u ? 0x7fc0u : r;
-}
-
-// bf16 nearest-even of an fp32 value (no addend).
-__device__ __forceinline__ uint32_t round_bf16(float s) {
-  const uint32_t u = __float_as_uint(s);
-  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  return (u & 0x7fffffffu) > 0x7f800000u ? 0x7fc0u : rne;
-}
-
-__device__ __forceinline__ float bf16_to_float(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-// Four outputs bf16(t[k] + bias[k]), correctly rounded, as two packed words.
-// The fp32 sum s = fl(t + bias) rounds to the same bf16 as the exact sum
-// unless s is itself a bf16 midpoint (every bf16 rounding boundary is an
-// fp32 value, so an exact sum on the other side of one would have that
-// boundary as its nearest fp32).  So the hardware conversion of s is used,
-// and the exact path (round_sum_bf16) only for a run holding a midpoint.
+// Four outputs bf16(t[k] + b[k]) of the exact sums, correctly rounded to
+// nearest-even, as two packed words.  Each sum is taken twice, rounded toward
+// -inf and toward +inf (the wave's fp32 rounding mode is switched around the
+// adds and restored to nearest-even).  Of the two, the one with an odd last
+// bit is the sum rounded to odd (both are the sum when it is exact), and an
+// fp32 rounded to odd carries more than two bits beyond bf16, so converting
+// it to bf16 to nearest-even gives the correctly rounded result; NaN, infinity
+// and signed zeros come out as the nearest-even sum would give them.  The
+// adds are inline asm so that no compiler-scheduled float operation can fall
+// between the mode switches; each switch is followed by the two wait states
+// a mode change needs before a VALU instruction.
 __device__ __forceinline__ v2u round_run(const float t[4], const float b[4]) {
-  float s[4];
-  bool tie = false;
+  float dn[4], up[4];
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 2\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32 %0, %8, %12\n\t"
+      "v_add_f32 %1, %9, %13\n\t"
+      "v_add_f32 %2, %10, %14\n\t"
+      "v_add_f32 %3, %11, %15\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 1\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32 %4, %8, %12\n\t"
+      "v_add_f32 %5, %9, %13\n\t"
+      "v_add_f32 %6, %10, %14\n\t"
+      "v_add_f32 %7, %11, %15\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+      "s_nop 1"
+      : "=&v"(dn[0]), "=&v"(dn[1]), "=&v"(dn[2]), "=&v"(dn[3]), "=&v"(up[0]), "=&v"(up[1]), "=&v"(up[2]),
+        "=&v"(up[3])
+      : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+  float o[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    s[k] = t[k] + b[k];
-    tie |= (__float_as_uint(s[k]) & 0xffffu) == 0x8000u;
-  }
+  for (int k = 0; k < 4; ++k) o[k] = (__float_as_uint(dn[k]) & 1u) ? dn[k] : up[k];
   v2u h;
-  h[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{s[0], s[1]}), v2bf));
-  h[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{s[2], s[3]}), v2bf));
-  if (tie) {
-    h[0] = round_sum_bf16(t[0], b[0]) | (round_sum_bf16(t[1], b[1]) << 16);
-    h[1] = round_sum_bf16(t[2], b[2]) | (round_sum_bf16(t[3], b[3]) << 16);
-  }
+  h[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{o[0], o[1]}), v2bf));
+  h[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{o[2], o[3]}), v2bf));
   return h;
 }
 
@@ -705,12 +694,26 @@ struct Kernel {
     const int N = a.N;
     const bool staged = (N & 7) == 0;
     lds_u8* sw = stg + wave * C::STG_WAVE;
+    // The bias of every column this lane touches (the same for all block
+    // rows), read from LDS once: FN blocks x NQ runs of four bf16.
+    v2u bias[C::FN][C::NQ];
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < C::NQ; ++q) {
+        const int tcol = wn * C::WTN + j * C::MF + (C::MF == 32 ? 8 * q + 4 * g : 4 * g);
+        bias[j][q] = *(const __attribute__((address_space(3))) v2u*)(smem + C::BIAS_OFF + tcol * 2);
+      }
+    // Byte offset in C of this lane's first staged chunk (row wm*WTM + lane/SCH
+    // of the tile, column n0 + wn*WTN + 8*(lane%SCH)); each store adds a uniform
+    // offset.  Its column, to test against N.
+    const int lcol = n0 + wn * C::WTN + (lane % C::SCH) * 8;
+    const uint32_t lane_c = ((uint32_t)(wm * C::WTM + lane / C::SCH) * (uint32_t)N + (uint32_t)lcol) * 2u;
     mfma_read_hazard();
 
     // the rounded run (block i, j; run q) of this lane, partials included
     auto run_bits = [&](int j, int q, const v4f& xq) -> v2u {
-      const int tcol = wn * C::WTN + j * C::MF + (C::MF == 32 ? 8 * q + 4 * g : 4 * g);
-      const v2u bb = *(const __attribute__((address_space(3))) v2u*)(smem + C::BIAS_OFF + tcol * 2);
+      const v2u bb = bias[j][q];
       const float b4[4] = {__uint_as_float(bb[0] << 16), __uint_as_float(bb[0] & 0xffff0000u),
                            __uint_as_float(bb[1] << 16), __uint_as_float(bb[1] & 0xffff0000u)};
       float t[4];
@@ -757,13 +760,18 @@ struct Kernel {
           // operations execute in order; this keeps the compiler from moving
           // them across each other)
           asm volatile("" ::: "memory");
+          constexpr int PS = C::MF / C::SRP;
+          v4u d[PS];
 #pragma unroll
-          for (int ps = 0; ps < C::MF / C::SRP; ++ps) {
+          for (int ps = 0; ps < PS; ++ps) {
             const int r = ps * C::SRP + lane / C::SCH, ch = lane % C::SCH;
-            const v4u d = *(const __attribute__((address_space(3))) v4u*)(sw + r * (C::SC * 2) + ((ch ^ (r % C::SCH)) << 4));
-            const int col = n0 + wn * C::WTN + cw * C::SC + ch * 8;
-            const uint32_t coff = col < N ? ((row0 + r) * (uint32_t)N + (uint32_t)col) * 2u : kOob;
-            __builtin_amdgcn_raw_buffer_store_b128(d, rc, coff, 0, 0);
+            d[ps] = *(const __attribute__((address_space(3))) v4u*)(sw + r * (C::SC * 2) + ((ch ^ (r % C::SCH)) << 4));
+          }
+          const bool col_ok = lcol + cw * C::SC < N;
+#pragma unroll
+          for (int ps = 0; ps < PS; ++ps) {
+            const uint32_t up = ((uint32_t)(i * C::MF + ps * C::SRP) * (uint32_t)N + (uint32_t)(cw * C::SC)) * 2u;
+            __builtin_amdgcn_raw_buffer_store_b128(d[ps], rc, col_ok ? lane_c + up : kOob, 0, 0);
           }
           asm volatile("" ::: "memory");
         });
