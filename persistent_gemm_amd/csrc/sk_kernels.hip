@@ -514,9 +514,77 @@ struct Kernel {
       else sc.b[R - C::FM] = 0x7f7f7f7f;
     }
   }
+  // MFMA order inside a sub-step, in "shells" that follow the read order:
+  // once A_t and B_t are in, every block (i, j) with max(i, j) == t can go.
+  struct BlockIJ {
+    int i, j;
+  };
+  static constexpr BlockIJ block_of(int b) {
+    const int m = C::FM > C::FN ? C::FM : C::FN;
+    for (int t = 0; t < m; ++t) {
+      for (int j = 0; j < t; ++j)
+        if (t < C::FM && j < C::FN) {
+          if (b == 0) return BlockIJ{t, j};
+          --b;
+        }
+      for (int i = 0; i < t; ++i)
+        if (i < C::FM && t < C::FN) {
+          if (b == 0) return BlockIJ{i, t};
+          --b;
+        }
+      if (t < C::FM && t < C::FN) {
+        if (b == 0) return BlockIJ{t, t};
+        --b;
+      }
+    }
+    return BlockIJ{0, 0};
+  }
+  // Reads after the barrier, in the order the next k-step's first MFMAs need
+  // them: for each t, A_t's scales and operand, then B_t's (R < NSR + NRD).
+  struct PostRead {
+    bool scale, a;
+    int blk, h;
+  };
+  static constexpr PostRead post_read(int r) {
+    const int m = C::FM > C::FN ? C::FM : C::FN;
+    for (int t = 0; t < m; ++t) {
+      if (t < C::FM) {
+        if (r == 0) return PostRead{true, true, t, 0};
+        --r;
+        for (int h = 0; h < C::NCH; ++h) {
+          if (r == 0) return PostRead{false, true, t, h};
+          --r;
+        }
+      }
+      if (t < C::FN) {
+        if (r == 0) return PostRead{true, false, t, 0};
+        --r;
+        for (int h = 0; h < C::NCH; ++h) {
+          if (r == 0) return PostRead{false, false, t, h};
+          --r;
+        }
+      }
+    }
+    return PostRead{true, true, 0, 0};
+  }
+  template <int R>
+  static __device__ __forceinline__ void post_read_one(const lds_u8* st, int so, const LdsPtrs& p, Scales& sc, Ops& o) {
+    constexpr PostRead d = post_read(R);
+    if constexpr (d.scale) {
+      read_scale<d.a ? d.blk : C::FM + d.blk>(st, p, sc);
+    } else {
+      const int off = so + p.slot[d.h];
+      if constexpr (d.a)
+        o.a[d.blk][d.h] = *(const __attribute__((address_space(3))) v4u*)(p.a + off + d.blk * C::MF * C::KB);
+      else
+        o.b[d.blk][d.h] = *(const __attribute__((address_space(3))) v4u*)(p.b + off + d.blk * C::MF * C::KB);
+    }
+  }
+
   template <int U, int B>
   static __device__ __forceinline__ void mfma_one(const Ops& o, const Scales& sc, Acc<C>& acc) {
-    constexpr int i = B / C::FN, j = B % C::FN;
+    constexpr BlockIJ bij = block_of(B);
+    constexpr int i = bij.i, j = bij.j;
     mfma<C, (C::DT == DT_MXFP4 ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
   }
 
@@ -575,8 +643,16 @@ struct Kernel {
       for (int j = 0; j < C::FN; ++j) asm volatile("" : "+a"(acc.v[i][j])::"memory");
   }
 
-  // Publish this workgroup's partial: every thread's stores become visible at
-  // device scope before the flag does.
+  // Partial tiles and flags move between workgroups on different XCDs, whose
+  // L2 caches are not coherent with each other.  Rather than agent-scope
+  // fences (which write back or invalidate a whole L2, costly for every other
+  // workgroup sharing it), only these accesses are made device-coherent: the
+  // partials are stored and loaded with the device-scope cache policy (sc1),
+  // and the flags are device-scope atomics.
+  static constexpr int kDeviceScope = 16;   // buffer cache policy: sc1
+
+  // Publish this workgroup's partial: every thread's device-scope stores have
+  // completed (the barrier waits for them) before the flag is written.
   static __device__ __forceinline__ void publish(const KArgs& a, int w) {
     if (a.delay_seed) {
       uint32_t h = a.delay_seed ^ (0x9e3779b9u * (uint32_t)(w + 1));
@@ -584,10 +660,9 @@ struct Kernel {
       const int n = (int)(h % 48u);
       for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
     }
-    __threadfence();
     __syncthreads();
     if (threadIdx.x == 0 && w != a.drop_wg)
-      __hip_atomic_store(a.locks + w, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.locks + w, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Wait until workgroup v has published; false if the spin limit ran out.
@@ -595,7 +670,7 @@ struct Kernel {
     if (threadIdx.x == 0) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       int ok = 1;
-      while (__hip_atomic_load(a.locks + v, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
+      while (__hip_atomic_load(a.locks + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
         __builtin_amdgcn_s_sleep(2);
         if (__builtin_amdgcn_s_memrealtime() - t0 > a.spin_limit) {
           ok = 0;
@@ -608,8 +683,8 @@ struct Kernel {
     __syncthreads();
     // The flag is the same for every lane; saying so keeps the work loop (and
     // every buffer descriptor derived from it) wave-uniform.
+    // (the partials are then read with device-scope loads, issued after this)
     const int ok = __builtin_amdgcn_readfirstlane(*s_flag);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __syncthreads();
     return ok != 0;
   }
@@ -661,7 +736,7 @@ struct Kernel {
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q) {
           const v4f v = read_run(acc.v[i][j], q);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rp, base + run_off(i, j, q), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rp, base + run_off(i, j, q), 0, kDeviceScope);
           __builtin_amdgcn_sched_barrier(0);
         }
   }
@@ -728,7 +803,8 @@ struct Kernel {
         const uint32_t base = slot_off(v);
         v4u p[C::NQ];
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q) p[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, base + run_off(i, j, q), 0, 0);
+        for (int q = 0; q < C::NQ; ++q)
+          p[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, base + run_off(i, j, q), 0, kDeviceScope);
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q) x[q] += __builtin_bit_cast(v4f, p[q]);
       }
@@ -928,7 +1004,8 @@ struct Kernel {
           if constexpr (!last) {
             static_for<NRD>([&](auto rc) {
               constexpr int r = decltype(rc)::value;
-              if constexpr (r * NB / NRD == b) read_op<u + 1, r>(cur * C::STAGE, lp, nxo);
+              // early in the sub-step (front-loaded), so they land well before use
+              if constexpr ((NRD <= NB ? r : r * NB / NRD) == b) read_op<u + 1, r>(cur * C::STAGE, lp, nxo);
             });
           }
           static_for<PER_STAGE>([&](auto pc) {
@@ -947,10 +1024,8 @@ struct Kernel {
             mfma_one<u, HB + b>(now, sc0, acc);
             static_for<NSR + NRD>([&](auto rc) {
               constexpr int r = decltype(rc)::value;
-              if constexpr (r * POST / (NSR + NRD) == b) {
-                if constexpr (r < NSR) read_scale<r>(stage_ptr(smem, nxt), lp, sc1);
-                else read_op<0, r - NSR>(nxt * C::STAGE, lp, nxo);
-              }
+              if constexpr (r * POST / (NSR + NRD) == b)
+                post_read_one<r>(stage_ptr(smem, nxt), nxt * C::STAGE, lp, sc1, nxo);
             });
             __builtin_amdgcn_sched_barrier(0);
           });
