@@ -295,10 +295,8 @@ sk_status run(const sk_gemm_args& g) {
   a.A = (const uint8_t*)g.A;
   a.B = (const uint8_t*)g.B;
   if (g.dtype == SK_MXFP4) {
-    if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, ws->S, (int)g.M, (int)(g.K / 32), (int)ksteps, (int)spr,
-                                  stream) != hipSuccess ||
-        sk::launch_scale_relayout((const uint8_t*)g.B_scale, ws->S + sb_at, (int)g.N, (int)(g.K / 32), (int)ksteps,
-                                  (int)spr, stream) != hipSuccess)
+    if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, ws->S, (int)g.M, (const uint8_t*)g.B_scale, ws->S + sb_at,
+                                  (int)g.N, (int)(g.K / 32), (int)ksteps, (int)spr, stream) != hipSuccess)
       return SK_ERR_HIP;
     a.SA = ws->S;
     a.SB = ws->S + sb_at;

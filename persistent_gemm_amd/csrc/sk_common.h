@@ -163,9 +163,10 @@ struct Variant {
 int num_variants();
 const Variant* variant(int index);
 
-// Copies MXFP4 scales [rows][s_pitch] into the k-step-major layout the GEMM
-// reads: dst[ks][r][0..spr) = src[r][ks*spr ...], padded with 127 (x1).
-hipError_t launch_scale_relayout(const uint8_t* src, uint8_t* dst, int rows, int s_pitch, int ksteps, int spr,
-                                 hipStream_t s);
+// Copies the MXFP4 scales of A and of B ([rows][s_pitch] each) into the
+// k-step-major layout the GEMM reads, in one launch:
+// dst[ks][r][0..spr) = src[r][ks*spr ...], padded with 127 (x1).
+hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, int rows_a, const uint8_t* src_b, uint8_t* dst_b,
+                                 int rows_b, int s_pitch, int ksteps, int spr, hipStream_t s);
 
 }  // namespace sk

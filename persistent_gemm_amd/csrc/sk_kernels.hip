@@ -179,7 +179,7 @@ struct Cfg {
   static_assert(BM % RG == 0 && BN % RG == 0, "row groups tile the operands");
   static_assert(MF % 16 == 0, "MFMA blocks cover whole 16-row swizzle periods");
   static_assert(DT != DT_MXFP4 || SPR == 4 || SPR == 8, "scale bytes per row per k-step");
-  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+  static_assert(STAGES >= 2 && STAGES <= 8, "pipeline depth");
   static_assert((STAGES - 2) * LOADS_PER_STAGE_S <= 63, "vmcnt range");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS");
   static_assert(BN <= NT, "one bias element per thread");
@@ -796,17 +796,33 @@ struct Kernel {
       for (int k = 0; k < 4; ++k) t[k] = C::DT == DT_FP8 ? xq[k] * sigma : xq[k];
       return round_run(t, b4);
     };
+    // The block's partial sums: own accumulators, then the partials of
+    // workgroups w-1, w-2, ..., first in that order.  The loads of CHK
+    // contributors are issued together (partials come from memory at device
+    // scope, so one at a time would pay a round trip each); the adds keep
+    // the fixed order.
+    // (8 runs in flight, 4 for eight-wave tiles, whose register file is half)
+    constexpr int CHK_RUNS = C::NW >= 8 ? 4 : 8;
+    constexpr int CHK = CHK_RUNS / C::NQ > 0 ? CHK_RUNS / C::NQ : 1;
     auto block_sums = [&](const typename Acc<C>::T& blk, int i, int j, v4f x[C::NQ]) {
 #pragma unroll
       for (int q = 0; q < C::NQ; ++q) x[q] = read_run(blk, q);
-      for (int v = w - 1; v >= first; --v) {
-        const uint32_t base = slot_off(v);
-        v4u p[C::NQ];
+      for (int v0 = w - 1; v0 >= first; v0 -= CHK) {
+        v4u p[CHK][C::NQ];
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q)
-          p[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, base + run_off(i, j, q), 0, kDeviceScope);
+        for (int c = 0; c < CHK; ++c)
+          if (v0 - c >= first) {
+            const uint32_t base = slot_off(v0 - c);
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q) x[q] += __builtin_bit_cast(v4f, p[q]);
+            for (int q = 0; q < C::NQ; ++q)
+              p[c][q] = __builtin_amdgcn_raw_buffer_load_b128(rp, base + run_off(i, j, q), 0, kDeviceScope);
+          }
+#pragma unroll
+        for (int c = 0; c < CHK; ++c)
+          if (v0 - c >= first) {
+#pragma unroll
+            for (int q = 0; q < C::NQ; ++q) x[q] += __builtin_bit_cast(v4f, p[c][q]);
+          }
       }
     };
 
@@ -1118,65 +1134,86 @@ hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
 // dst[ks][r][j] = src[r][ks * SPR + j] for r < rows, ks < ksteps, j < SPR,
 // with 127 (a scale of 1) where ks * SPR + j >= s_pitch (a ragged last
 // k-step), so that every k-step's scales of consecutive rows are one
-// contiguous block.  Each workgroup moves a 64-row x 64-k-step tile through
+// contiguous block.  Each workgroup moves a 16-row x 64-k-step tile through
 // LDS: read along rows (the source's contiguous direction; 16-byte loads when
-// rows are 16-byte aligned), written as SPR-byte items along rows.
+// rows are 16-byte aligned), written as 16-byte pieces of a k-step's rows
+// when the tile is whole and aligned, else item by item.
+struct RelayoutOp {
+  const uint8_t* src;
+  uint8_t* dst;
+  int rows, vec16, blocks;   // blocks: row tiles of this operand
+};
+
+// One launch re-lays both operands' scales: the first a.blocks row tiles
+// are A's, the rest B's.
 template <int SPR>
-__global__ __launch_bounds__(256) void sk_scale_relayout(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                                         int rows, int s_pitch, int ksteps, int vec16) {
+__global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutOp b, int s_pitch, int ksteps) {
   typedef typename std::conditional<SPR == 4, uint32_t, v2u>::type Item;
-  constexpr int RB = 64 * SPR;                 // bytes of one row's 64 k-steps
-  __shared__ Item tile[64 * 64];               // [k][r]
-  const int r0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  constexpr int RT = 16, KT = 64;              // rows and k-steps of a tile
+  constexpr int RB = KT * SPR;                 // bytes of one row's k-steps
+  __shared__ __attribute__((aligned(16))) Item tile[KT * RT];   // [k][r]
+  const bool is_a = (int)blockIdx.x < a.blocks;
+  const uint8_t* __restrict__ src = is_a ? a.src : b.src;
+  uint8_t* __restrict__ dst = is_a ? a.dst : b.dst;
+  const int rows = is_a ? a.rows : b.rows, vec16 = is_a ? a.vec16 : b.vec16;
+  const int r0 = (is_a ? (int)blockIdx.x : (int)blockIdx.x - a.blocks) * RT, k0 = blockIdx.y * KT;
   const int tid = threadIdx.x;
   uint8_t* t8 = (uint8_t*)tile;
   if (vec16) {
     // s_pitch % 16 == 0: a 16-byte piece is wholly inside the row or past its end
-    constexpr int PR = RB / 16, NP = 64 * PR / 256;
-    v4u v[NP];
+    constexpr int PR = RB / 16, NP = RT * PR / 256;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int pc = tid + i * 256, r = pc / PR, q = pc % PR;
       const int row = r0 + r, col = k0 * SPR + q * 16;
-      v[i] = v4u{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
-      if (row < rows && col < s_pitch) v[i] = *(const v4u*)(src + (int64_t)row * s_pitch + col);
-    }
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pc = tid + i * 256, r = pc / PR, q = pc % PR;
+      v4u v = v4u{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
+      if (row < rows && col < s_pitch) v = *(const v4u*)(src + (int64_t)row * s_pitch + col);
 #pragma unroll
       for (int e = 0; e < 16 / SPR; ++e) {
         const int k = q * (16 / SPR) + e;
-        if constexpr (SPR == 4) tile[k * 64 + r] = v[i][e];
-        else tile[k * 64 + r] = v2u{v[i][2 * e], v[i][2 * e + 1]};
+        if constexpr (SPR == 4) tile[k * RT + r] = v[e];
+        else tile[k * RT + r] = v2u{v[2 * e], v[2 * e + 1]};
       }
     }
   } else {
-    constexpr int NB = 64 * RB / 256;
+    constexpr int NB = RT * RB / 256;
 #pragma unroll 8
     for (int i = 0; i < NB; ++i) {
       const int b = tid + i * 256, r = b / RB, c = b % RB;
       const int row = r0 + r, col = k0 * SPR + c;
       uint8_t x = 127;
       if (row < rows && col < s_pitch) x = src[(int64_t)row * s_pitch + col];
-      t8[((c / SPR) * 64 + r) * SPR + c % SPR] = x;
+      t8[((c / SPR) * RT + r) * SPR + c % SPR] = x;
     }
   }
   __syncthreads();
+  constexpr int QK = RT * SPR / 16;            // 16-byte pieces per k-step of the tile
+  const bool whole = r0 + RT <= rows && ((int64_t)rows * SPR) % 16 == 0;
+  if (whole) {
 #pragma unroll
-  for (int i = 0; i < 64 * 64 / 256; ++i) {
-    const int p = tid + i * 256, k = p / 64, r = p % 64;
-    const int ks = k0 + k, row = r0 + r;
-    if (ks < ksteps && row < rows) *(Item*)(dst + ((int64_t)ks * rows + row) * SPR) = tile[p];
+    for (int i = 0; i < KT * QK / 256; ++i) {
+      const int p = tid + i * 256, k = p / QK, q = p % QK;
+      const int ks = k0 + k;
+      if (ks < ksteps)
+        *(v4u*)(dst + ((int64_t)ks * rows + r0) * SPR + q * 16) = *(const v4u*)(t8 + (k * RT) * SPR + q * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KT * RT / 256; ++i) {
+      const int p = tid + i * 256, k = p / RT, r = p % RT;
+      const int ks = k0 + k, row = r0 + r;
+      if (ks < ksteps && row < rows) *(Item*)(dst + ((int64_t)ks * rows + row) * SPR) = tile[p];
+    }
   }
 }
 
-hipError_t launch_scale_relayout(const uint8_t* src, uint8_t* dst, int rows, int s_pitch, int ksteps, int spr,
-                                 hipStream_t s) {
-  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((ksteps + 63) / 64));
-  const int vec16 = (s_pitch % 16 == 0 && ((uintptr_t)src & 15) == 0) ? 1 : 0;
-  if (spr == 4) hipLaunchKernelGGL(sk_scale_relayout<4>, grid, dim3(256), 0, s, src, dst, rows, s_pitch, ksteps, vec16);
-  else if (spr == 8) hipLaunchKernelGGL(sk_scale_relayout<8>, grid, dim3(256), 0, s, src, dst, rows, s_pitch, ksteps, vec16);
+hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, int rows_a, const uint8_t* src_b, uint8_t* dst_b,
+                                 int rows_b, int s_pitch, int ksteps, int spr, hipStream_t s) {
+  RelayoutOp a{src_a, dst_a, rows_a, (s_pitch % 16 == 0 && ((uintptr_t)src_a & 15) == 0) ? 1 : 0, (rows_a + 15) / 16};
+  RelayoutOp b{src_b, dst_b, rows_b, (s_pitch % 16 == 0 && ((uintptr_t)src_b & 15) == 0) ? 1 : 0, (rows_b + 15) / 16};
+  const dim3 grid((unsigned)(a.blocks + b.blocks), (unsigned)((ksteps + 63) / 64));
+  if (spr == 4) hipLaunchKernelGGL(sk_scale_relayout<4>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  else if (spr == 8) hipLaunchKernelGGL(sk_scale_relayout<8>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -1195,6 +1232,7 @@ static const Variant kVariants[] = {
     SK_VARIANT(DT_MXFP4, 128, 128, 128, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_MXFP4, 64, 64, 64, 32, 2, 2, 4, 2),
     SK_VARIANT(DT_MXFP4, 16, 256, 64, 16, 1, 4, 4, 1),
+    SK_VARIANT(DT_MXFP4, 16, 256, 64, 16, 1, 4, 8, 1),
     SK_VARIANT(DT_MXFP4, 16, 128, 64, 16, 1, 4, 4, 1),
     // bf16
     SK_VARIANT(DT_BF16, 256, 256, 64, 32, 2, 4, 4, 2),
