@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MXFP4 Stream-K GEMM TFLOP/s and % of dense FP4 MFMA peak, 1 MI355X"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
-PEAK_TFLOPS = {"mxfp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+PEAK_TFLOPS = {"mxfp4": 10100.0, "fp8": 5000.0, "mxfp8": 5000.0, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "mxfp4_addmm_8192"
 
@@ -128,6 +128,8 @@ def algorithmic_bytes(w) -> int:
     M, N, K = w.M, w.N, w.K
     if w.dtype == "mxfp4":
         b = (M + N) * (K // 2) + (M + N) * (K // 32)
+    elif w.dtype == "mxfp8":
+        b = (M + N) * K + (M + N) * (K // 32)
     elif w.dtype == "bf16":
         b = (M + N) * K * 2
     else:
@@ -209,6 +211,11 @@ def main() -> int:
         d = {}
         if w.dtype == "mxfp4":
             for k in ("A", "B", "SA", "SB"):
+                d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
+        elif w.dtype == "mxfp8":
+            for k in ("A", "B"):
+                d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
+            for k in ("SA", "SB"):
                 d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
         elif w.dtype == "bf16":
             for k in ("A", "B"):

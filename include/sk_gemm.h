@@ -25,6 +25,9 @@
  *          consecutive K elements starting at k = 0.  E8M0 0xFF (NaN) is
  *          undefined input.  sigma = 1.
  *   bf16   A uint16[M][K], B uint16[N][K] (bf16 bit patterns).  sigma = 1.
+ *   MXFP8  A uint8[M][K], B uint8[N][K], OCP E4M3FN elements; A_scale
+ *          uint8[M][K/32], B_scale uint8[N][K/32] E8M0 block scales as for
+ *          MXFP4.  sigma = 1.
  *   fp8    A uint8[M][K], B uint8[N][K], OCP E4M3FN.  A_scale / B_scale are
  *          device pointers to one fp32 each (per-tensor), NULL meaning 1.0;
  *          sigma = A_scale * B_scale, applied to the fp32 sum before the bias
@@ -36,13 +39,15 @@
  *
  * Precision: fp32 accumulation.  The one rounding to bf16 is round-to-
  * nearest-even of the fp32 value sigma*acc (+) bias taken exactly (the sum is
- * carried with its rounding error, so bias addition does not double-round).
+ * first rounded to odd in fp32, which keeps enough bits that the rounding to
+ * bf16 after it is the correct rounding of the exact sum: adding the bias
+ * never double-rounds).
  *
  * Ownership and asynchrony: all tensor pointers are device pointers owned by
  * the caller and must stay valid until the stream has passed the launch.
  * Calls enqueue on `stream` (a hipStream_t; NULL is the default stream) and
  * return without waiting.  The library owns its scratch (fp32 partial tiles,
- * lock flags, an error word, and for MXFP4 a k-step-major copy of the two
+ * lock flags, an error word, and for MXFP4 / MXFP8 a k-step-major copy of the two
  * scale arrays that a small kernel writes before the GEMM on the same
  * stream), kept per (device, stream), grown on demand and freed by
  * sk_release_workspace().  Device-side failures (a workgroup that
@@ -53,10 +58,10 @@
  *   SK_ERR_ARG          a required pointer is NULL, M, N or K < 1, a size is
  *                       beyond the supported range (M < 2^31, N <= 2^22,
  *                       K <= 2^21, tiles * MAC iterations per tile < 2^31;
- *                       MXFP4: M * K / 32 and N * K / 32 below 2^31),
+ *                       MXFP4 / MXFP8: M * K / 32 and N * K / 32 below 2^31),
  *                       C overlaps an input, bf16 given scales, an unknown
  *                       dtype / policy, or sk_addmm without a bias;
- *   SK_ERR_ALIGN        MXFP4 K not a multiple of 32, fp8 K not a multiple of
+ *   SK_ERR_ALIGN        MXFP4 / MXFP8 K not a multiple of 32, fp8 K not a multiple of
  *                       16, bf16 K not a multiple of 8 (a row of A or B must
  *                       be a whole number of 16-byte chunks), or A, B, C not
  *                       16-byte aligned, or bias not 2-byte aligned;
@@ -86,7 +91,7 @@ typedef enum sk_status {
   SK_ERR_TIMEOUT = 6
 } sk_status;
 
-typedef enum sk_dtype { SK_MXFP4 = 0, SK_BF16 = 1, SK_FP8_E4M3 = 2 } sk_dtype;
+typedef enum sk_dtype { SK_MXFP4 = 0, SK_BF16 = 1, SK_FP8_E4M3 = 2, SK_MXFP8 = 3 } sk_dtype;
 
 /* How output tiles are divided between the persistent workgroups.
  * HYBRID: whole tiles are dealt out round-robin ("data-parallel tail"), and
@@ -115,6 +120,14 @@ sk_status sk_gemm_bf16(const void* A, const void* B, const void* bias, void* C, 
 sk_status sk_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* A_scale, const float* B_scale,
                       const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
 
+/* MXFP8: A, B E4M3FN elements; A_scale, B_scale E8M0 per 32 K (required).  bias may be NULL.
+ * The same block-scaled contraction as MXFP4 with 8-bit elements: the quantized
+ * mode in which the bias is turned into fp32 before it is added ("Fix StreamK
+ * Kernel Bias #67", Technical Details), with the OCP MX v1.0 block scales of the
+ * MXFP4 path ("Stream-k mxfp4 kernel", description). */
+sk_status sk_gemm_mxfp8(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
+                        const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
+
 /* addmm(bias, A, B) = the dtype's GEMM with a bias that is required (alpha = beta = 1).
  * A_scale / B_scale as for that dtype (NULL for bf16). */
 sk_status sk_addmm(sk_dtype dtype, const void* bias, const void* A, const void* B, const void* A_scale,
@@ -127,7 +140,7 @@ typedef struct sk_gemm_args {
   int32_t policy;           /* sk_policy */
   const void* A;
   const void* B;
-  const void* A_scale;      /* MXFP4: uint8 [M][K/32]; fp8: device float* or NULL; bf16: NULL */
+  const void* A_scale;      /* MXFP4, MXFP8: uint8 [M][K/32]; fp8: device float* or NULL; bf16: NULL */
   const void* B_scale;
   const void* bias;         /* bf16[N] or NULL */
   void* C;                  /* bf16[M][N] */

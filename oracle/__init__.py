@@ -26,6 +26,9 @@ one.  Sources:
   M rows, and is added once, after the partial tiles of a split tile have been
   aggregated; in the quantized mode it is turned into fp32 before the add:
   "Fix StreamK Kernel Bias #67", Motivation and Technical Details.
+* MXFP8 (E4M3 elements with the same E8M0 block scales) is the block-scaled
+  form of the quantized mode of "Fix StreamK Kernel Bias #67", Technical
+  Details; it is the MXFP4 contraction with 8-bit elements.
 * Element encodings are not on those pages.  E2M1 (FP4) and E8M0 (the shared
   block scale, one per 32 consecutive K elements) follow the OCP Microscaling
   Formats (MX) v1.0 specification; E4M3FN follows the OCP 8-bit Floating Point
@@ -53,6 +56,7 @@ __all__ = [
     "decode_bf16",
     "unpack_fp4",
     "mxfp4_operand",
+    "mxfp8_operand",
     "rne_bf16_from_double",
     "bf16_to_double",
     "operands",
@@ -120,15 +124,30 @@ def unpack_fp4(packed: np.ndarray, K: int) -> np.ndarray:
     return codes
 
 
+def _apply_block_scales(vals: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
+    """value(r, k) = element(r, k) * 2**(scale[r][k // 32] - 127): one E8M0 scale per 32 consecutive K."""
+    if K % 32:
+        raise ValueError("MX formats need K to be a multiple of the 32-element scale block")
+    sc = decode_e8m0(np.asarray(scales, dtype=np.uint8))
+    if sc.shape != (vals.shape[0], K // 32):
+        raise ValueError("MX scales must be [rows][K/32]")
+    return vals * np.repeat(sc, 32, axis=1)
+
+
 def mxfp4_operand(packed: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
     """Decode an MXFP4 operand: value(r, k) = E2M1(code(r, k)) * 2**(scale[r][k // 32] - 127)."""
     if K % 32:
         raise ValueError("MXFP4 needs K to be a multiple of the 32-element scale block")
-    vals = decode_e2m1(unpack_fp4(packed, K))
-    sc = decode_e8m0(np.asarray(scales, dtype=np.uint8))
-    if sc.shape != (vals.shape[0], K // 32):
-        raise ValueError("MXFP4 scales must be [rows][K/32]")
-    return vals * np.repeat(sc, 32, axis=1)
+    return _apply_block_scales(decode_e2m1(unpack_fp4(packed, K)), scales, K)
+
+
+def mxfp8_operand(elems: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
+    """Decode an MXFP8 operand (OCP MX v1.0, E4M3 elements):
+    value(r, k) = E4M3FN(byte(r, k)) * 2**(scale[r][k // 32] - 127)."""
+    elems = np.asarray(elems, dtype=np.uint8)
+    if elems.shape[1] != K:
+        raise ValueError("MXFP8 rows must hold K bytes")
+    return _apply_block_scales(decode_e4m3fn(elems), scales, K)
 
 
 def rne_bf16_from_double(d: np.ndarray) -> np.ndarray:
@@ -164,11 +183,16 @@ def operands(dtype: str, A, B, SA=None, SB=None, K: int | None = None):
     dtype "bf16":  A, B are uint16[rows][K] bf16 bit patterns; sigma = 1.
     dtype "fp8":   A, B are uint8[rows][K] E4M3FN; SA, SB are the per-tensor fp32
                    scale factors (Python floats), sigma = SA * SB.
+    dtype "mxfp8": A, B are uint8[rows][K] E4M3FN, SA, SB uint8[rows][K/32] E8M0; sigma = 1.
     """
     if dtype == "mxfp4":
         if K is None:
             K = 2 * np.asarray(A).shape[1]
         return mxfp4_operand(A, SA, K), mxfp4_operand(B, SB, K), 1.0
+    if dtype == "mxfp8":
+        if K is None:
+            K = np.asarray(A).shape[1]
+        return mxfp8_operand(A, SA, K), mxfp8_operand(B, SB, K), 1.0
     if dtype == "bf16":
         return decode_bf16(A), decode_bf16(B), 1.0
     if dtype == "fp8":
@@ -208,12 +232,9 @@ def gemm_elements(dtype: str, A, B, rows, cols, SA=None, SB=None, bias=None, K: 
     cols = np.asarray(cols, dtype=np.int64)
     ur, ri = np.unique(rows, return_inverse=True)
     uc, ci = np.unique(cols, return_inverse=True)
-    if dtype == "mxfp4":
-        if K is None:
-            K = 2 * np.asarray(A).shape[1]
-        a = mxfp4_operand(np.asarray(A)[ur], np.asarray(SA)[ur], K)
-        b = mxfp4_operand(np.asarray(B)[uc], np.asarray(SB)[uc], K)
-        sigma = 1.0
+    if dtype in ("mxfp4", "mxfp8"):
+        a, b, sigma = operands(dtype, np.asarray(A)[ur], np.asarray(B)[uc], np.asarray(SA)[ur],
+                               np.asarray(SB)[uc], K)
     else:
         a, b, sigma = operands(dtype, np.asarray(A)[ur], np.asarray(B)[uc], SA, SB, K)
     full_n = np.asarray(B).shape[0]

@@ -8,7 +8,7 @@ library's HIP kernels; there is no fallback.  PyTorch supplies device memory
 and streams only.
 
 Entry points mirror ``include/sk_gemm.h``:
-``gemm_mxfp4``, ``gemm_bf16``, ``gemm_fp8``, ``addmm`` and ``gemm_ex`` (policy,
+``gemm_mxfp4``, ``gemm_mxfp8``, ``gemm_bf16``, ``gemm_fp8``, ``addmm`` and ``gemm_ex`` (policy,
 tile and test hooks), plus ``plan``, ``plan_wg_range``, ``check``,
 ``release_workspace``, ``poison_workspace`` and ``variants``.
 """
@@ -20,18 +20,18 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "SkError", "MXFP4", "BF16", "FP8", "HYBRID", "PURE_SK", "PURE_DP", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
-    "library_path", "load", "gemm_mxfp4", "gemm_bf16", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
+    "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
+    "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
 ]
 
-MXFP4, BF16, FP8 = 0, 1, 2
+MXFP4, BF16, FP8, MXFP8 = 0, 1, 2, 3
 HYBRID, PURE_SK, PURE_DP = 0, 1, 2
 DEBUG_DELAY, DEBUG_DROP_SIGNAL = 1, 2
 
 _STATUS = {0: "SK_OK", 1: "SK_ERR_ARG", 2: "SK_ERR_ALIGN", 3: "SK_ERR_UNSUPPORTED", 4: "SK_ERR_HIP",
            5: "SK_ERR_NOMEM", 6: "SK_ERR_TIMEOUT"}
-_DTYPES = {"mxfp4": MXFP4, "bf16": BF16, "fp8": FP8}
+_DTYPES = {"mxfp4": MXFP4, "bf16": BF16, "fp8": FP8, "mxfp8": MXFP8}
 
 
 class SkError(RuntimeError):
@@ -122,6 +122,7 @@ def load():
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.sk_gemm_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.sk_gemm_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_addmm.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
@@ -139,7 +140,7 @@ def load():
     lib.sk_variant_info.argtypes = [ctypes.c_int32] + [ctypes.POINTER(ctypes.c_int32)] * 6
     lib.sk_status_string.argtypes = [ctypes.c_int]
     lib.sk_status_string.restype = ctypes.c_char_p
-    for name in ("sk_gemm_mxfp4", "sk_gemm_bf16", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
+    for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
                  "sk_plan_wg_range", "sk_plan_wg_work", "sk_check", "sk_debug_poison_workspace", "sk_variant_info"):
         getattr(lib, name).restype = ctypes.c_int
     lib.sk_num_variants.restype = ctypes.c_int32
@@ -204,6 +205,13 @@ def _marshal(dtype, A, B, A_scale, B_scale, bias, C):
         _need(B, "B", (torch.uint8,), (N, kh), dev)
         _need(A_scale, "A_scale", (torch.uint8,), (M, K // 32), dev)
         _need(B_scale, "B_scale", (torch.uint8,), (N, K // 32), dev)
+    elif dtype == MXFP8:
+        M, K = A.shape
+        N = B.shape[0]
+        _need(A, "A", (torch.float8_e4m3fn, torch.uint8), (M, K), dev)
+        _need(B, "B", (torch.float8_e4m3fn, torch.uint8), (N, K), dev)
+        _need(A_scale, "A_scale", (torch.uint8,), (M, K // 32), dev)
+        _need(B_scale, "B_scale", (torch.uint8,), (N, K // 32), dev)
     elif dtype == BF16:
         M, K = A.shape
         N = B.shape[0]
@@ -238,6 +246,14 @@ def gemm_mxfp4(A, B, A_scale, B_scale, bias=None, C=None, grid_cap=0, stream=Non
     M, N, K, C = _marshal(MXFP4, A, B, A_scale, B_scale, bias, C)
     _ok(load().sk_gemm_mxfp4(_ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale), _ptr(bias), _ptr(C), M, N, K,
                              int(grid_cap), _stream(A, stream)), "sk_gemm_mxfp4")
+    return C
+
+
+def gemm_mxfp8(A, B, A_scale, B_scale, bias=None, C=None, grid_cap=0, stream=None):
+    """C = A . B^T (+ bias) for MXFP8 operands (E4M3 elements, E8M0 scales per 32 K); returns C."""
+    M, N, K, C = _marshal(MXFP8, A, B, A_scale, B_scale, bias, C)
+    _ok(load().sk_gemm_mxfp8(_ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale), _ptr(bias), _ptr(C), M, N, K,
+                             int(grid_cap), _stream(A, stream)), "sk_gemm_mxfp8")
     return C
 
 

@@ -55,7 +55,10 @@ std::map<int, DeviceInfo> g_dev;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool dtype_ok(int d) { return d == SK_MXFP4 || d == SK_BF16 || d == SK_FP8_E4M3; }
+bool dtype_ok(int d) { return d == SK_MXFP4 || d == SK_BF16 || d == SK_FP8_E4M3 || d == SK_MXFP8; }
+
+// Block-scaled (MX) input types: one E8M0 scale byte per 32 K elements.
+bool is_mx(int d) { return d == SK_MXFP4 || d == SK_MXFP8; }
 
 // Bytes of one row of A or B for K elements.
 int64_t row_bytes(int dtype, int64_t K) {
@@ -179,9 +182,9 @@ sk_status validate(const sk_gemm_args& g) {
   if (g.policy < SK_POLICY_HYBRID || g.policy > SK_POLICY_PURE_DP) return SK_ERR_ARG;
   if (!g.A || !g.B || !g.C) return SK_ERR_ARG;
   if (g.M < 1 || g.N < 1 || g.K < 1 || g.M >= kMaxM || g.N > kMaxN || g.K > kMaxK) return SK_ERR_ARG;
-  if (g.dtype == SK_MXFP4 && (!g.A_scale || !g.B_scale)) return SK_ERR_ARG;
+  if (is_mx(g.dtype) && (!g.A_scale || !g.B_scale)) return SK_ERR_ARG;
   if (g.dtype == SK_BF16 && (g.A_scale || g.B_scale)) return SK_ERR_ARG;
-  if (g.dtype == SK_MXFP4 && g.K % 32) return SK_ERR_ALIGN;
+  if (is_mx(g.dtype) && g.K % 32) return SK_ERR_ALIGN;
   if (g.dtype == SK_FP8_E4M3 && g.K % 16) return SK_ERR_ALIGN;
   if (g.dtype == SK_BF16 && g.K % 8) return SK_ERR_ALIGN;
   if (((uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)g.C) & 15) return SK_ERR_ALIGN;
@@ -189,11 +192,11 @@ sk_status validate(const sk_gemm_args& g) {
   if (g.dtype == SK_FP8_E4M3 && (((uintptr_t)g.A_scale | (uintptr_t)g.B_scale) & 3)) return SK_ERR_ALIGN;
   const int64_t rb = row_bytes(g.dtype, g.K);
   const int64_t c_bytes = g.M * g.N * 2;
-  const int64_t sbytes = g.dtype == SK_MXFP4 ? g.K / 32 : (g.dtype == SK_FP8_E4M3 ? 4 : 0);
+  const int64_t sbytes = is_mx(g.dtype) ? g.K / 32 : (g.dtype == SK_FP8_E4M3 ? 4 : 0);
   if (overlaps(g.C, c_bytes, g.A, g.M * rb) || overlaps(g.C, c_bytes, g.B, g.N * rb) ||
       overlaps(g.C, c_bytes, g.bias, g.N * 2) ||
-      overlaps(g.C, c_bytes, g.A_scale, g.dtype == SK_MXFP4 ? g.M * sbytes : sbytes) ||
-      overlaps(g.C, c_bytes, g.B_scale, g.dtype == SK_MXFP4 ? g.N * sbytes : sbytes))
+      overlaps(g.C, c_bytes, g.A_scale, is_mx(g.dtype) ? g.M * sbytes : sbytes) ||
+      overlaps(g.C, c_bytes, g.B_scale, is_mx(g.dtype) ? g.N * sbytes : sbytes))
     return SK_ERR_ARG;
   return SK_OK;
 }
@@ -271,20 +274,24 @@ sk_status run(const sk_gemm_args& g) {
   if (st != SK_OK) return st;
   hipStream_t stream = (hipStream_t)g.stream;
   const Variant* v = sk::variant(p.variant);
-  // MXFP4 scales are read from a k-step-major copy: one k-step's scales of a
+  // MX scales are read from a k-step-major copy: one k-step's scales of a
   // tile are then one contiguous block (row-major scales would put each row's
-  // 4 or 8 bytes in a different cache line).  Every offset into the copy must
-  // fit in 32 bits.
-  const int64_t spr = v->kb / 16, ksteps = p.iters_per_tile;
-  int64_t sa_bytes = 0, sb_bytes = 0;
-  if (g.dtype == SK_MXFP4) {
-    sa_bytes = ksteps * g.M * spr;
-    sb_bytes = ksteps * g.N * spr;
+  // 2 to 8 bytes in a different cache line).  Every offset into the copy must
+  // fit in 32 bits.  A k-step holds kb bytes of a row: 2 * kb FP4 or kb FP8
+  // elements, so kb / 16 or kb / 32 scale bytes.
+  const int64_t spr = g.dtype == SK_MXFP4 ? v->kb / 16 : v->kb / 32, ksteps = p.iters_per_tile;
+  int64_t sa_bytes = 0, sb_bytes = 0, rows_a = 0, rows_b = 0;
+  if (is_mx(g.dtype)) {
+    rows_a = sk::relayout_rows((int)g.M, (int)spr);
+    rows_b = sk::relayout_rows((int)g.N, (int)spr);
+    sa_bytes = ksteps * rows_a * spr;
+    sb_bytes = ksteps * rows_b * spr;
     if (sa_bytes >= ((int64_t)1 << 31) || sb_bytes >= ((int64_t)1 << 31)) return SK_ERR_ARG;
   }
   const int64_t sb_at = (sa_bytes + 255) / 256 * 256;
   Workspace* ws = nullptr;
-  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, (size_t)(sb_at + sb_bytes), &ws);
+  // (16 bytes of slack: a tile's last scale dword may reach 2 bytes past B's copy)
+  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, is_mx(g.dtype) ? (size_t)(sb_at + sb_bytes + 16) : 0, &ws);
   if (st != SK_OK) return st;
   uint32_t epoch = 0;
   st = next_epoch(ws, &epoch);
@@ -294,14 +301,14 @@ sk_status run(const sk_gemm_args& g) {
   std::memset(&a, 0, sizeof(a));
   a.A = (const uint8_t*)g.A;
   a.B = (const uint8_t*)g.B;
-  if (g.dtype == SK_MXFP4) {
+  if (is_mx(g.dtype)) {
     if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, ws->S, (int)g.M, (const uint8_t*)g.B_scale, ws->S + sb_at,
                                   (int)g.N, (int)(g.K / 32), (int)ksteps, (int)spr, stream) != hipSuccess)
       return SK_ERR_HIP;
     a.SA = ws->S;
     a.SB = ws->S + sb_at;
-    a.sa_kstride = (uint32_t)(g.M * spr);
-    a.sb_kstride = (uint32_t)(g.N * spr);
+    a.sa_kstride = (uint32_t)(rows_a * spr);
+    a.sb_kstride = (uint32_t)(rows_b * spr);
   } else if (g.dtype == SK_FP8_E4M3) {
     a.fsa = (const float*)g.A_scale;
     a.fsb = (const float*)g.B_scale;
@@ -369,6 +376,11 @@ sk_status sk_gemm_bf16(const void* A, const void* B, const void* bias, void* C, 
 sk_status sk_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* A_scale, const float* B_scale,
                       const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream) {
   return run(base_args(SK_FP8_E4M3, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
+}
+
+sk_status sk_gemm_mxfp8(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
+                        const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream) {
+  return run(base_args(SK_MXFP8, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
 }
 
 sk_status sk_addmm(sk_dtype dtype, const void* bias, const void* A, const void* B, const void* A_scale,

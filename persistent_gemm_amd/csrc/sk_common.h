@@ -6,7 +6,7 @@
 
 namespace sk {
 
-enum : int { DT_MXFP4 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum : int { DT_MXFP4 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP8 = 3 };
 
 // Lock flags per scratch area; the grid never exceeds this many workgroups.
 constexpr int kMaxGrid = 1024;
@@ -38,7 +38,7 @@ struct KArgs {
   uint64_t spin_limit;      // ticks of the 100 MHz realtime counter
   int32_t M, N, K;
   int32_t row_bytes;        // bytes of K data per row of A and of B (their pitch)
-  uint32_t sa_kstride;      // bytes per k-step block of SA (M * SPR) and of SB (N * SPR)
+  uint32_t sa_kstride;      // bytes per k-step block of SA and of SB (padded rows * SPR)
   uint32_t sb_kstride;
   int32_t tiles;            // T
   int32_t sk_tiles;         // tiles [0, sk_tiles) are split by MAC iteration
@@ -163,9 +163,12 @@ struct Variant {
 int num_variants();
 const Variant* variant(int index);
 
-// Copies the MXFP4 scales of A and of B ([rows][s_pitch] each) into the
+// Copies the MX scales of A and of B ([rows][s_pitch] each) into the
 // k-step-major layout the GEMM reads, in one launch:
-// dst[ks][r][0..spr) = src[r][ks*spr ...], padded with 127 (x1).
+// dst[ks][r][0..spr) = src[r][ks*spr ...], padded with 127 (x1), where a
+// k-step's block holds relayout_rows(rows, spr) rows (a whole number of
+// 16-byte pieces).  spr is 2, 4 or 8; dst must be 16-byte aligned.
+int relayout_rows(int rows, int spr);
 hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, int rows_a, const uint8_t* src_b, uint8_t* dst_b,
                                  int rows_b, int s_pitch, int ksteps, int spr, hipStream_t s);
 

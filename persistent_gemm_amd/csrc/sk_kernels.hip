@@ -129,10 +129,13 @@ struct Cfg {
   static constexpr int FM = WTM / MF, FN = WTN / MF;   // MFMA blocks per wave
   static constexpr int NG = 64 / MF;                   // K groups across the lanes
   static constexpr int LB = KB / NG;                   // bytes per lane per row per k-step
-  static constexpr int U = DT == DT_FP8 ? 32 : 16;     // bytes per lane per MFMA
+  // MX: block-scaled operands (E8M0 per 32 K); F8: E4M3 elements
+  static constexpr bool MX = DT == DT_MXFP4 || DT == DT_MXFP8;
+  static constexpr bool F8 = DT == DT_FP8 || DT == DT_MXFP8;
+  static constexpr int U = F8 ? 32 : 16;               // bytes per lane per MFMA
   static constexpr int NU = LB / U;                    // MFMAs per block per k-step
   static constexpr int NCH = U / 16;                   // 16-byte chunks per lane per MFMA
-  static constexpr int SPR = DT == DT_MXFP4 ? KB / 16 : 0;  // scale bytes per row per k-step
+  static constexpr int SPR = DT == DT_MXFP4 ? KB / 16 : (DT == DT_MXFP8 ? KB / 32 : 0);  // scale bytes per row per k-step
   static constexpr int BK = DT == DT_MXFP4 ? 2 * KB : (DT == DT_BF16 ? KB / 2 : KB);
   static constexpr int ACC = MF == 32 ? 16 : 4;        // fp32 accumulators per block per lane
 
@@ -147,8 +150,8 @@ struct Cfg {
   static constexpr int A_GROUPS = BM / RG, B_GROUPS = BN / RG;
   // Scale bytes of a k-step, [row][SPR], filled by dword loads of 64 lanes
   // (256 bytes per instruction), so each area is a whole number of 256 B.
-  static constexpr int SA_INST = DT == DT_MXFP4 ? cdiv(BM * SPR, 256) : 0;
-  static constexpr int SB_INST = DT == DT_MXFP4 ? cdiv(BN * SPR, 256) : 0;
+  static constexpr int SA_INST = MX ? cdiv(BM * SPR, 256) : 0;
+  static constexpr int SB_INST = MX ? cdiv(BN * SPR, 256) : 0;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * KB;
   static constexpr int SA_OFF = (BM + BN) * KB;
@@ -178,7 +181,7 @@ struct Cfg {
   static_assert(KB == 64 || KB == 128, "k-step bytes per row");
   static_assert(BM % RG == 0 && BN % RG == 0, "row groups tile the operands");
   static_assert(MF % 16 == 0, "MFMA blocks cover whole 16-row swizzle periods");
-  static_assert(DT != DT_MXFP4 || SPR == 4 || SPR == 8, "scale bytes per row per k-step");
+  static_assert(!MX || SPR == 2 || SPR == 4 || SPR == 8, "scale bytes per row per k-step");
   static_assert(STAGES >= 2 && STAGES <= 8, "pipeline depth");
   static_assert((STAGES - 2) * LOADS_PER_STAGE_S <= 63, "vmcnt range");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS");
@@ -217,14 +220,14 @@ __device__ __forceinline__ void mfma(typename Acc<C>::T& acc, const v4u* a, cons
     v8i va, vb;
     va[0] = a[0][0]; va[1] = a[0][1]; va[2] = a[0][2]; va[3] = a[0][3];
     vb[0] = b[0][0]; vb[1] = b[0][1]; vb[2] = b[0][2]; vb[3] = b[0][3];
-    if constexpr (C::DT == DT_FP8) {
+    if constexpr (C::F8) {
       va[4] = a[1][0]; va[5] = a[1][1]; va[6] = a[1][2]; va[7] = a[1][3];
       vb[4] = b[1][0]; vb[5] = b[1][1]; vb[6] = b[1][2]; vb[7] = b[1][3];
     } else {
       va[4] = va[5] = va[6] = va[7] = 0;
       vb[4] = vb[5] = vb[6] = vb[7] = 0;
     }
-    constexpr int fmt = C::DT == DT_FP8 ? 0 : 4;   // 0 = E4M3, 4 = E2M1
+    constexpr int fmt = C::F8 ? 0 : 4;   // 0 = E4M3, 4 = E2M1
     if constexpr (C::MF == 32)
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc, fmt, fmt, OP, sb, OP, sa);
     else
@@ -368,11 +371,15 @@ struct Kernel {
     const int rows_b = min(C::BN, a.N - n0);
     t.ra = rsrc_words(a.A + (int64_t)m0 * a.row_bytes, (uint32_t)(rows_a * a.row_bytes));
     t.rb = rsrc_words(a.B + (int64_t)n0 * a.row_bytes, (uint32_t)(rows_b * a.row_bytes));
-    if constexpr (C::DT == DT_MXFP4) {
+    if constexpr (C::MX) {
       // k-step-major scales: k-step ks of row r at SA + ks * sa_kstride + r * SPR
-      // (the k-step's block is reached by moving the base, see rsrc_plus)
-      t.rsa = rsrc_words(a.SA + (int64_t)m0 * C::SPR, (uint32_t)(rows_a * C::SPR));
-      t.rsb = rsrc_words(a.SB + (int64_t)n0 * C::SPR, (uint32_t)(rows_b * C::SPR));
+      // (the k-step's block is reached by moving the base, see rsrc_plus).
+      // The range is rounded up to whole dwords, so the dword holding the last
+      // row's scales is never cut by the range check when SPR = 2; the bytes
+      // past it are scales of rows outside the matrix, whose products are zero
+      // and whose output rows or columns are never stored.
+      t.rsa = rsrc_words(a.SA + (int64_t)m0 * C::SPR, (uint32_t)((rows_a * C::SPR + 3) & ~3));
+      t.rsb = rsrc_words(a.SB + (int64_t)n0 * C::SPR, (uint32_t)((rows_b * C::SPR + 3) & ~3));
     } else {
       t.rsa = t.ra;
       t.rsb = t.rb;
@@ -396,7 +403,7 @@ struct Kernel {
       o.cb[i] = (uint32_t)((p ^ swz(row)) * 16);
       o.b[i] = (uint32_t)row * (uint32_t)a.row_bytes + o.cb[i];
     }
-    if constexpr (C::DT == DT_MXFP4) {
+    if constexpr (C::MX) {
       // the k-step's scale bytes of the tile's rows are contiguous ([row][SPR])
 #pragma unroll
       for (int i = 0; i < C::SA_PT; ++i) {
@@ -427,7 +434,24 @@ struct Kernel {
     // Block rows start at multiples of 16, so the lane's permutation is swz(lr).
     const int x = swz(lr);
 #pragma unroll
-    for (int k = 0; k < C::NU * C::NCH; ++k) p.slot[k] = ((g * (C::LB / 16) + k) ^ x) * 16;
+    for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+      for (int h = 0; h < C::NCH; ++h) {
+        // 16-byte chunk of the k-step row that (lane group g, sub-step u,
+        // operand half h) reads.  With E4M3 elements the scaled MFMA takes
+        // register half h of lane group g as K elements [h*16*NG + 16g, +16)
+        // of its K range, and the scale of its 32-element block b from lane
+        // group b; so for block-scaled E4M3 each hardware block is filled
+        // with the k-step's block b*NU + u, whose scale byte lane group b
+        // holds at op_sel u.  Otherwise lane group g's operands are
+        // contiguous (one 32-element block per lane group for E2M1).
+        int c;
+        if constexpr (C::MX && C::F8)
+          c = 2 * ((h * (C::NG / 2) + g / 2) * C::NU + u) + g % 2;
+        else
+          c = g * (C::LB / 16) + u * C::NCH + h;
+        p.slot[u * C::NCH + h] = (c ^ x) * 16;
+      }
     p.a = smem + C::A_OFF + (wm * C::WTM + lr) * C::KB;
     p.b = smem + C::B_OFF + (wn * C::WTN + lr) * C::KB;
     p.sa = C::SA_OFF + (wm * C::WTM + lr) * C::SPR + g * C::NU;
@@ -442,7 +466,7 @@ struct Kernel {
   }
 
   static __device__ __forceinline__ void read_scales(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
-    if constexpr (C::DT == DT_MXFP4) {
+    if constexpr (C::MX) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) sc.a[i] = scale_word(st + p.sa + i * C::MF * C::SPR);
 #pragma unroll
@@ -506,7 +530,7 @@ struct Kernel {
   }
   template <int R>
   static __device__ __forceinline__ void read_scale(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
-    if constexpr (C::DT == DT_MXFP4) {
+    if constexpr (C::MX) {
       if constexpr (R < C::FM) sc.a[R] = scale_word(st + p.sa + R * C::MF * C::SPR);
       else sc.b[R - C::FM] = scale_word(st + p.sb + (R - C::FM) * C::MF * C::SPR);
     } else {
@@ -585,7 +609,7 @@ struct Kernel {
   static __device__ __forceinline__ void mfma_one(const Ops& o, const Scales& sc, Acc<C>& acc) {
     constexpr BlockIJ bij = block_of(B);
     constexpr int i = bij.i, j = bij.j;
-    mfma<C, (C::DT == DT_MXFP4 ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
+    mfma<C, (C::MX ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
   }
 
   // One direct-to-LDS load of a k-step, by its index P among the k-step's
@@ -629,7 +653,7 @@ struct Kernel {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) mfma<C, (C::DT == DT_MXFP4 ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
+      for (int j = 0; j < C::FN; ++j) mfma<C, (C::MX ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
   }
 
   // Program-order anchor for the accumulators: MFMAs count as side-effect-free,
@@ -978,7 +1002,7 @@ struct Kernel {
       d.t = ti;
       d.valid = have_i;
       d.kbyte = have_i ? (uint32_t)ki * C::KB : 0u;
-      if constexpr (C::DT == DT_MXFP4) {
+      if constexpr (C::MX) {
         d.rsa = rsrc_plus(ti.rsa, have_i ? (uint32_t)ki * sa_kstride : 0u);
         d.rsb = rsrc_plus(ti.rsb, have_i ? (uint32_t)ki * sb_kstride : 0u);
       }
@@ -1129,33 +1153,48 @@ hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- MXFP4 scale re-layout
+// ---------------------------------------------------------------- MX scale re-layout
 
 // dst[ks][r][j] = src[r][ks * SPR + j] for r < rows, ks < ksteps, j < SPR,
 // with 127 (a scale of 1) where ks * SPR + j >= s_pitch (a ragged last
 // k-step), so that every k-step's scales of consecutive rows are one
-// contiguous block.  Each workgroup moves a 16-row x 64-k-step tile through
-// LDS: read along rows (the source's contiguous direction; 16-byte loads when
-// rows are 16-byte aligned), written as 16-byte pieces of a k-step's rows
-// when the tile is whole and aligned, else item by item.
+// contiguous block.  A k-step's block holds dst_rows >= rows rows, a count
+// that makes it a whole number of 16-byte pieces (rows past `rows` are left
+// unwritten), so every block starts 16-byte aligned.  Each workgroup moves a 16-row x KT-k-step tile through
+// LDS (KT * SPR = 256 or 512 bytes of a row): read along rows (the source's
+// contiguous direction; 16-byte loads when rows are 16-byte aligned),
+// written as 16-byte pieces of a k-step's rows when the tile is whole and
+// aligned, else item by item.
 struct RelayoutOp {
   const uint8_t* src;
   uint8_t* dst;
-  int rows, vec16, blocks;   // blocks: row tiles of this operand
+  int rows, dst_rows, vec16, blocks;   // blocks: row tiles of this operand
+};
+
+template <int SPR>
+struct RelayoutShape {
+  static constexpr int RT = 16;                         // rows of a tile
+  static constexpr int KT = SPR == 2 ? 128 : 64;        // k-steps of a tile
 };
 
 // One launch re-lays both operands' scales: the first a.blocks row tiles
 // are A's, the rest B's.
 template <int SPR>
 __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutOp b, int s_pitch, int ksteps) {
-  typedef typename std::conditional<SPR == 4, uint32_t, v2u>::type Item;
-  constexpr int RT = 16, KT = 64;              // rows and k-steps of a tile
+  typedef typename std::conditional<SPR == 2, uint16_t,
+                                    typename std::conditional<SPR == 4, uint32_t, v2u>::type>::type Item;
+  struct Piece {
+    Item x[16 / SPR];
+  };
+  constexpr int RT = RelayoutShape<SPR>::RT, KT = RelayoutShape<SPR>::KT;
   constexpr int RB = KT * SPR;                 // bytes of one row's k-steps
+  static_assert(sizeof(Piece) == 16 && RT * RB % 4096 == 0, "relayout tile");
   __shared__ __attribute__((aligned(16))) Item tile[KT * RT];   // [k][r]
   const bool is_a = (int)blockIdx.x < a.blocks;
   const uint8_t* __restrict__ src = is_a ? a.src : b.src;
   uint8_t* __restrict__ dst = is_a ? a.dst : b.dst;
   const int rows = is_a ? a.rows : b.rows, vec16 = is_a ? a.vec16 : b.vec16;
+  const int dst_rows = is_a ? a.dst_rows : b.dst_rows;
   const int r0 = (is_a ? (int)blockIdx.x : (int)blockIdx.x - a.blocks) * RT, k0 = blockIdx.y * KT;
   const int tid = threadIdx.x;
   uint8_t* t8 = (uint8_t*)tile;
@@ -1168,12 +1207,9 @@ __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutO
       const int row = r0 + r, col = k0 * SPR + q * 16;
       v4u v = v4u{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
       if (row < rows && col < s_pitch) v = *(const v4u*)(src + (int64_t)row * s_pitch + col);
+      const Piece pv = __builtin_bit_cast(Piece, v);
 #pragma unroll
-      for (int e = 0; e < 16 / SPR; ++e) {
-        const int k = q * (16 / SPR) + e;
-        if constexpr (SPR == 4) tile[k * RT + r] = v[e];
-        else tile[k * RT + r] = v2u{v[2 * e], v[2 * e + 1]};
-      }
+      for (int e = 0; e < 16 / SPR; ++e) tile[(q * (16 / SPR) + e) * RT + r] = pv.x[e];
     }
   } else {
     constexpr int NB = RT * RB / 256;
@@ -1188,33 +1224,57 @@ __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutO
   }
   __syncthreads();
   constexpr int QK = RT * SPR / 16;            // 16-byte pieces per k-step of the tile
-  const bool whole = r0 + RT <= rows && ((int64_t)rows * SPR) % 16 == 0;
+  const bool whole = r0 + RT <= rows;
   if (whole) {
 #pragma unroll
     for (int i = 0; i < KT * QK / 256; ++i) {
       const int p = tid + i * 256, k = p / QK, q = p % QK;
       const int ks = k0 + k;
       if (ks < ksteps)
-        *(v4u*)(dst + ((int64_t)ks * rows + r0) * SPR + q * 16) = *(const v4u*)(t8 + (k * RT) * SPR + q * 16);
+        *(v4u*)(dst + ((int64_t)ks * dst_rows + r0) * SPR + q * 16) = *(const v4u*)(t8 + (k * RT) * SPR + q * 16);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < KT * RT / 256; ++i) {
       const int p = tid + i * 256, k = p / RT, r = p % RT;
       const int ks = k0 + k, row = r0 + r;
-      if (ks < ksteps && row < rows) *(Item*)(dst + ((int64_t)ks * rows + row) * SPR) = tile[p];
+      if (ks < ksteps && row < rows) *(Item*)(dst + ((int64_t)ks * dst_rows + row) * SPR) = tile[p];
     }
   }
 }
 
+template <int SPR>
+static void relayout_grid(const RelayoutOp& a, const RelayoutOp& b, int ksteps, dim3* grid) {
+  constexpr int KT = RelayoutShape<SPR>::KT;
+  *grid = dim3((unsigned)(a.blocks + b.blocks), (unsigned)((ksteps + KT - 1) / KT));
+}
+
+int relayout_rows(int rows, int spr) {
+  const int pad = 16 / spr;
+  return (rows + pad - 1) / pad * pad;
+}
+
 hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, int rows_a, const uint8_t* src_b, uint8_t* dst_b,
                                  int rows_b, int s_pitch, int ksteps, int spr, hipStream_t s) {
-  RelayoutOp a{src_a, dst_a, rows_a, (s_pitch % 16 == 0 && ((uintptr_t)src_a & 15) == 0) ? 1 : 0, (rows_a + 15) / 16};
-  RelayoutOp b{src_b, dst_b, rows_b, (s_pitch % 16 == 0 && ((uintptr_t)src_b & 15) == 0) ? 1 : 0, (rows_b + 15) / 16};
-  const dim3 grid((unsigned)(a.blocks + b.blocks), (unsigned)((ksteps + 63) / 64));
-  if (spr == 4) hipLaunchKernelGGL(sk_scale_relayout<4>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
-  else if (spr == 8) hipLaunchKernelGGL(sk_scale_relayout<8>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
-  else return hipErrorInvalidValue;
+  if (spr != 2 && spr != 4 && spr != 8) return hipErrorInvalidValue;
+  if (((uintptr_t)dst_a | (uintptr_t)dst_b) & 15) return hipErrorInvalidValue;
+  RelayoutOp a{src_a, dst_a, rows_a, relayout_rows(rows_a, spr),
+               (s_pitch % 16 == 0 && ((uintptr_t)src_a & 15) == 0) ? 1 : 0, (rows_a + 15) / 16};
+  RelayoutOp b{src_b, dst_b, rows_b, relayout_rows(rows_b, spr),
+               (s_pitch % 16 == 0 && ((uintptr_t)src_b & 15) == 0) ? 1 : 0, (rows_b + 15) / 16};
+  dim3 grid;
+  if (spr == 2) {
+    relayout_grid<2>(a, b, ksteps, &grid);
+    hipLaunchKernelGGL(sk_scale_relayout<2>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  } else if (spr == 4) {
+    relayout_grid<4>(a, b, ksteps, &grid);
+    hipLaunchKernelGGL(sk_scale_relayout<4>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  } else if (spr == 8) {
+    relayout_grid<8>(a, b, ksteps, &grid);
+    hipLaunchKernelGGL(sk_scale_relayout<8>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1246,6 +1306,12 @@ static const Variant kVariants[] = {
     SK_VARIANT(DT_FP8, 128, 128, 128, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_FP8, 64, 64, 64, 32, 2, 2, 4, 2),
     SK_VARIANT(DT_FP8, 16, 256, 128, 16, 1, 4, 3, 1),
+    // MXFP8 (E4M3 elements, E8M0 scale per 32 K)
+    SK_VARIANT(DT_MXFP8, 256, 256, 64, 32, 2, 4, 4, 2),
+    SK_VARIANT(DT_MXFP8, 256, 256, 64, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_MXFP8, 128, 128, 128, 32, 2, 2, 4, 1),
+    SK_VARIANT(DT_MXFP8, 64, 64, 64, 32, 2, 2, 4, 2),
+    SK_VARIANT(DT_MXFP8, 16, 256, 128, 16, 1, 4, 3, 1),
 };
 
 int num_variants() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }

@@ -13,6 +13,8 @@ Distributions (the workloads the Stream-K pages exercise, made synthetic):
 * bf16: N(0, 1) in fp32, rounded to bf16 by torch.
 * fp8: N(0, 1) in fp32, clipped to +-448 and rounded to OCP E4M3FN by torch;
   per-tensor fp32 scales (1.0 unless asked otherwise).
+* MXFP8: E4M3FN elements drawn as for fp8, with E8M0 block scales drawn as
+  for MXFP4 (one per 32 K-elements, uniform on {125, ..., 129}).
 * bias: N(0, 1) in fp32 rounded to bf16, one value per output column.
 """
 
@@ -29,7 +31,7 @@ __all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs"]
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str            # "mxfp4" | "bf16" | "fp8"
+    dtype: str            # "mxfp4" | "bf16" | "fp8" | "mxfp8"
     M: int
     N: int
     K: int
@@ -44,7 +46,7 @@ class Workload:
         return 2 * self.M * self.N * self.K
 
 
-# The five synthetic workloads; the seed of each is fixed so that tests,
+# The synthetic workloads; the seed of each is fixed so that tests,
 # the bench and the oracle all see the same bytes.
 WORKLOADS = {
     "mxfp4_addmm_256x256x512_g5": Workload(
@@ -54,6 +56,8 @@ WORKLOADS = {
     "mxfp4_addmm_8192": Workload("mxfp4_addmm_8192", "mxfp4", 8192, 8192, 8192, True, 1003),
     "fp8_gemm_4096_capsweep": Workload(
         "fp8_gemm_4096_capsweep", "fp8", 4096, 4096, 4096, False, 1004, caps=(1, 32, 64, 128, 256)),
+    # MXFP8 (E4M3 elements, E8M0 block scales) at the large square shape
+    "mxfp8_addmm_8192": Workload("mxfp8_addmm_8192", "mxfp8", 8192, 8192, 8192, True, 1005),
 }
 
 
@@ -68,6 +72,7 @@ def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
     mxfp4: A uint8[M][K/2], B uint8[N][K/2], SA uint8[M][K/32], SB uint8[N][K/32].
     bf16:  A uint16[M][K], B uint16[N][K] (bit patterns); SA = SB = None.
     fp8:   A uint8[M][K], B uint8[N][K] (E4M3FN bytes); SA, SB python floats.
+    mxfp8: A uint8[M][K], B uint8[N][K] (E4M3FN bytes), SA uint8[M][K/32], SB uint8[N][K/32].
     bias:  uint16[N] bf16 bit patterns, or None.
     """
     g = torch.Generator().manual_seed(seed)
@@ -79,6 +84,10 @@ def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
 
     def e8m0(rows):
         return torch.randint(scale_lo, scale_hi + 1, (rows, K // 32), generator=g, dtype=torch.uint8).numpy()
+
+    def e4m3(rows):
+        x = torch.randn(rows, K, generator=g).clamp(-448.0, 448.0)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
     if dtype == "mxfp4":
         if K % 32:
@@ -92,10 +101,14 @@ def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
         out["SA"] = None
         out["B"] = _bf16_bits(torch.randn(N, K, generator=g))
         out["SB"] = None
+    elif dtype == "mxfp8":
+        if K % 32:
+            raise ValueError("MXFP8 needs K % 32 == 0")
+        out["A"] = e4m3(M)
+        out["SA"] = e8m0(M)
+        out["B"] = e4m3(N)
+        out["SB"] = e8m0(N)
     elif dtype == "fp8":
-        def e4m3(rows):
-            x = torch.randn(rows, K, generator=g).clamp(-448.0, 448.0)
-            return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         out["A"] = e4m3(M)
         out["SA"] = float(np.float32(fp8_scales[0]))
         out["B"] = e4m3(N)
@@ -107,11 +120,13 @@ def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
 
 
 def integer_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int, lo: int = -8, hi: int = 8) -> dict:
-    """Small-integer operands (values in [lo, hi]) in the bf16 or fp8 encoding.
+    """Small-integer operands (values in [lo, hi]) in the bf16, fp8 or MXFP8 encoding.
 
     Every product and every partial sum of such inputs is an integer far below
-    2**24, so any fp32 summation order is exact.  The bias, if drawn, is an
-    integer in [-64, 64].
+    2**24, so any fp32 summation order is exact.  MXFP8 adds block scales
+    uniform on {126, 127, 128} (factors 1/2, 1, 2): products are then integers
+    times 2**-2 .. 2**2, and sums stay exact while K * 64 * 4 < 2**22.  The
+    bias, if drawn, is an integer in [-64, 64].
     """
     g = torch.Generator().manual_seed(seed)
     out = {"dtype": dtype, "M": M, "N": N, "K": K}
@@ -124,7 +139,14 @@ def integer_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
         out["A"] = a.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         out["B"] = b.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         out["SA"] = out["SB"] = 1.0
+    elif dtype == "mxfp8":
+        if K % 32:
+            raise ValueError("MXFP8 needs K % 32 == 0")
+        out["A"] = a.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out["B"] = b.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out["SA"] = torch.randint(126, 129, (M, K // 32), generator=g, dtype=torch.uint8).numpy()
+        out["SB"] = torch.randint(126, 129, (N, K // 32), generator=g, dtype=torch.uint8).numpy()
     else:
-        raise ValueError("integer_inputs covers bf16 and fp8")
+        raise ValueError("integer_inputs covers bf16, fp8 and mxfp8")
     out["bias"] = _bf16_bits(torch.randint(-64, 65, (N,), generator=g).float()) if bias else None
     return out

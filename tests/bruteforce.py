@@ -96,6 +96,8 @@ def gemm(dtype: str, A, B, SA, SB, bias, M: int, N: int, K: int):
             byte = int(A[m][k // 2])
             code = (byte >> 4) if (k & 1) else (byte & 0xF)
             return e2m1(code) * e8m0(int(SA[m][k // 32]))
+        if dtype == "mxfp8":
+            return e4m3fn(int(A[m][k])) * e8m0(int(SA[m][k // 32]))
         if dtype == "bf16":
             return bf16(int(A[m][k]))
         return e4m3fn(int(A[m][k]))
@@ -105,6 +107,8 @@ def gemm(dtype: str, A, B, SA, SB, bias, M: int, N: int, K: int):
             byte = int(B[n][k // 2])
             code = (byte >> 4) if (k & 1) else (byte & 0xF)
             return e2m1(code) * e8m0(int(SB[n][k // 32]))
+        if dtype == "mxfp8":
+            return e4m3fn(int(B[n][k])) * e8m0(int(SB[n][k // 32]))
         if dtype == "bf16":
             return bf16(int(B[n][k]))
         return e4m3fn(int(B[n][k]))

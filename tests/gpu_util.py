@@ -24,6 +24,11 @@ def device_inputs(x: dict) -> dict:
     if dt == "mxfp4":
         for k in ("A", "B", "SA", "SB"):
             d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).cuda()
+    elif dt == "mxfp8":
+        for k in ("A", "B"):
+            d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).view(torch.float8_e4m3fn).cuda()
+        for k in ("SA", "SB"):
+            d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).cuda()
     elif dt == "bf16":
         for k in ("A", "B"):
             d[k] = torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16)).view(torch.bfloat16).cuda()

@@ -33,7 +33,7 @@ def test_variants_table():
     v = pg.variants()
     shapes = {(x["dtype"], x["tile_m"], x["tile_n"]) for x in v}
     for need in [(pg.MXFP4, 256, 256), (pg.MXFP4, 64, 64), (pg.MXFP4, 16, 256), (pg.BF16, 256, 256),
-                 (pg.BF16, 128, 192), (pg.FP8, 256, 256)]:
+                 (pg.BF16, 128, 192), (pg.FP8, 256, 256), (pg.MXFP8, 256, 256), (pg.MXFP8, 16, 256)]:
         assert need in shapes
     for x in v:
         assert x["threads"] in (256, 512) and 0 < x["lds_bytes"] <= 160 * 1024
@@ -62,6 +62,10 @@ def _args(**kw):
     (dict(dtype=pg.BF16), 1),                         # bf16 takes no scales
     (dict(dtype=pg.FP8, K=24), 2),
     (dict(dtype=pg.FP8, A_scale=0x30002), 2),
+    (dict(dtype=pg.MXFP8, A_scale=None), 1),          # MXFP8 needs its block scales
+    (dict(dtype=pg.MXFP8, B_scale=None), 1),
+    (dict(dtype=pg.MXFP8, K=80), 2),                  # K must be whole 32-element scale blocks
+    (dict(dtype=pg.MXFP8, C=0x30000 + 16), 1),        # C overlaps A's scales ([M][K/32] bytes)
 ])
 def test_argument_checks(kw, status):
     a = _args(**kw)

@@ -1,4 +1,4 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration the
+"""GPU parity at the workloads' full sizes, in the launch configuration the
 bench times (default tile and policy), plus the other tiles worth checking."""
 
 from __future__ import annotations
@@ -84,3 +84,21 @@ def test_fp8_4096_cap_sweep_within_bound():
     # every cap divides the 256 tiles: the same whole-tile partition, the same bits
     for cap in w.caps:
         assert np.array_equal(results[cap], results[256])
+
+
+def test_mxfp8_addmm_8192_sampled_within_bound():
+    w, x = _wl("mxfp8_addmm_8192")
+    d = device_inputs(x)
+    say("8192^3 mxfp8 addmm, default plan")
+    got = run(d)
+    rng = np.random.default_rng(1)
+    # a 64 x 64 block across a tile corner, the last row and column, and random samples
+    rows = np.concatenate([np.repeat(np.arange(224, 288), 64), np.full(64, 8191), np.arange(8128, 8192),
+                           rng.integers(0, 8192, 20000)])
+    cols = np.concatenate([np.tile(np.arange(224, 288), 64), np.arange(8128, 8192), np.full(64, 8191),
+                           rng.integers(0, 8192, 20000)])
+    Cs, Ds, Ss = oracle.gemm_elements("mxfp8", x["A"], x["B"], rows, cols, x["SA"], x["SB"], x["bias"], K=w.K)
+    ok = oracle.accept(got[rows, cols], Cs, Ds, Ss)
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} sampled elements outside the bound"
+    say("8192^3 mxfp8 addmm, repeat")
+    assert np.array_equal(run(d), got)

@@ -2,9 +2,10 @@
 
 MXFP4 inputs make every fp32 partial sum exact (products are multiples of
 2**-6 below 576, sums stay far below 2**18), so MXFP4 results must match the
-oracle bit for bit at every grid size, policy and tile.  bf16 / fp8 inputs
-with small integer values are exact too; random bf16 / fp8 inputs are held
-to |err| <= 2**-7 * sum|a*b| + one bf16 ulp, and must repeat bit for bit.
+oracle bit for bit at every grid size, policy and tile.  bf16 / fp8 / MXFP8
+inputs with small integer values are exact too; random bf16 / fp8 / MXFP8
+inputs are held to |err| <= 2**-7 * sum|a*b| + one bf16 ulp, and must repeat
+bit for bit.
 """
 
 from __future__ import annotations
@@ -81,8 +82,9 @@ def test_mxfp4_ragged(M, N, K):
         assert_bitexact(run(d, bias=False, tile=tile, policy=pg.PURE_SK, grid_cap=5), Cn, f"no bias {tile}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("M,N,K", [(1, 8, 16), (100, 72, 96), (300, 200, 512), (64, 384, 1040)])
+@pytest.mark.parametrize("dtype,M,N,K", [
+    (dt, M, N, K) for dt in ("bf16", "fp8") for M, N, K in [(1, 8, 16), (100, 72, 96), (300, 200, 512), (64, 384, 1040)]
+] + [("mxfp8", M, N, K) for M, N, K in [(1, 8, 32), (100, 72, 96), (300, 200, 512), (64, 384, 1056)]])
 def test_integer_inputs_exact(dtype, M, N, K):
     x = integer_inputs(dtype, M, N, K, bias=True, seed=M + N + K)
     d = device_inputs(x)
@@ -94,7 +96,7 @@ def test_integer_inputs_exact(dtype, M, N, K):
             assert_bitexact(run(d, grid_cap=g, tile=tile, policy=policy), C, f"{dtype} {tile} {policy} {g}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
 def test_random_within_bound_and_repeatable(dtype):
     M, N, K = 513, 388, 1056
     kw = {"fp8_scales": (0.5, 3.0)} if dtype == "fp8" else {}
@@ -113,7 +115,7 @@ def test_random_within_bound_and_repeatable(dtype):
 
 # ---------------------------------------------------------------- every compiled kernel
 
-_DTYPES = {0: "mxfp4", 1: "bf16", 2: "fp8"}
+_DTYPES = {0: "mxfp4", 1: "bf16", 2: "fp8", 3: "mxfp8"}
 
 
 def _num_variants():
@@ -127,14 +129,14 @@ def _num_variants():
 def test_every_variant_exact(index):
     """Each compiled kernel, chosen by index, on exact inputs spanning several
     tiles with ragged M, N and K tails, under all three policies.  N is once a
-    multiple of 4 (8-byte output runs) and once not (element stores); for
-    MXFP4 one K keeps the scales on the direct-to-LDS path, the other (K/32
-    not a multiple of 8) sends them through registers."""
+    multiple of 8 (whole 16-byte output pieces) and once not (element
+    stores); K is once whole k-steps and once a ragged last k-step (for the
+    MX types, one whose scale block is only partly inside K)."""
     v = pg.variants()[index]
     dtype, bm, bn = _DTYPES[v["dtype"]], v["tile_m"], v["tile_n"]
     M = 2 * bm + 7
-    ragged_k = {"mxfp4": 448, "bf16": 200, "fp8": 208}[dtype]   # K % 32, % 8, % 16 are what the ABI requires
-    for N, K in [(2 * bn + 12, 512 if dtype == "mxfp4" else 256), (bn + 13, ragged_k)]:
+    ragged_k = {"mxfp4": 448, "bf16": 200, "fp8": 208, "mxfp8": 224}[dtype]   # the ABI needs K % 32, % 8, % 16
+    for N, K in [(2 * bn + 16, 512 if dtype == "mxfp4" else 256), (bn + 13, ragged_k)]:
         if dtype == "mxfp4":
             x = make_inputs(dtype, M, N, K, bias=True, seed=3000 + index)
         else:

@@ -5,7 +5,7 @@
 * bf16 rounding against torch's fp32->bf16 conversion, and against hand-built
   doubles where rounding through fp32 first would give the wrong answer;
 * whole GEMMs against an exact-rational brute force (tests/bruteforce.py),
-  hand-worked sums, identity operands, the bias-broadcast property, integer
+  hand-worked sums (MXFP4 and MXFP8, tests/golden/), identity operands, the bias-broadcast property, integer
   matrix products and algebraic invariants.
 
 ``test_planted_mistakes_are_caught`` plants plausible mistakes in the oracle
@@ -171,6 +171,12 @@ def pin_bruteforce_fp8():
             _bruteforce_case("fp8", M, N, K, bias, 300 + seed)
 
 
+def pin_bruteforce_mxfp8():
+    for seed, (M, N, K) in enumerate([(1, 1, 32), (2, 3, 64), (3, 2, 96)]):
+        for bias in (False, True):
+            _bruteforce_case("mxfp8", M, N, K, bias, 400 + seed)
+
+
 def _one_by_one(a_codes, b_codes, sa=127, sb=127, bias=None):
     """MXFP4 with M = N = 1, K = 32 from explicit codes."""
     A = _pack(np.array([a_codes], dtype=np.uint8))
@@ -221,6 +227,42 @@ def pin_handworked_mxfp4():
     B = _pack(np.array([[0] * 32 + [one] * 32], np.uint8))
     C, D = oracle.gemm("mxfp4", A, B, np.array([[120, 128]], np.uint8), np.array([[127, 127]], np.uint8), None, K=64)
     assert D[0, 0] == 64.0 and C[0, 0] == 0x4280
+
+
+def _hex_runs(spec):
+    """'58*1,38*2' -> [0x58, 0x38, 0x38] (E4M3FN bytes for k = 0, 1, ...)."""
+    out = []
+    for part in spec.split(","):
+        byte, count = part.split("*")
+        out += [int(byte, 16)] * int(count)
+    return out
+
+
+def golden_handworked_mxfp8():
+    """Cases of tests/golden/mxfp8_1x1x64_handworked.txt (worked by hand from the formats)."""
+    cases = []
+    with open(os.path.join(GOLDEN, "mxfp8_1x1x64_handworked.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, a, b, sa, sb, bias, total, bits = line.split()
+            cases.append((name, _hex_runs(a), _hex_runs(b), [int(v) for v in sa.split(",")],
+                          [int(v) for v in sb.split(",")], None if bias == "none" else float(bias),
+                          float(total), int(bits, 16)))
+    return cases
+
+
+def pin_handworked_mxfp8():
+    cases = golden_handworked_mxfp8()
+    assert len(cases) == 8
+    for name, a, b, sa, sb, bias, total, bits in cases:
+        assert len(a) == 64 and len(b) == 64, name
+        bb = None if bias is None else _f32_to_bf16_torch(np.array([bias], np.float32))
+        C, D = oracle.gemm("mxfp8", np.array([a], np.uint8), np.array([b], np.uint8), np.array([sa], np.uint8),
+                           np.array([sb], np.uint8), bb, K=64)
+        got = (int(C[0, 0]), float(D[0, 0]))
+        assert got == (bits, total), f"{name}: oracle gives {got}, worked by hand {(bits, total)}"
 
 
 def pin_identity():
@@ -330,6 +372,33 @@ def pin_invariants_mxfp4():
     assert np.array_equal(D6 - D, Dfirst)
 
 
+def pin_invariants_mxfp8():
+    K = 128
+    x = make_inputs("mxfp8", 5, 7, K, bias=True, seed=15)
+    C, D = oracle.gemm("mxfp8", x["A"], x["B"], x["SA"], x["SB"], None, K=K)
+    # one more in every B scale byte doubles the result exactly
+    _, D2 = oracle.gemm("mxfp8", x["A"], x["B"], x["SA"], x["SB"] + 1, None, K=K)
+    assert np.array_equal(D2, 2 * D)
+    # unit block scales reduce MXFP8 to fp8 with per-tensor scales of 1
+    ones_a = np.full_like(x["SA"], 127)
+    ones_b = np.full_like(x["SB"], 127)
+    C3, D3 = oracle.gemm("mxfp8", x["A"], x["B"], ones_a, ones_b, x["bias"], K=K)
+    C4, D4 = oracle.gemm("fp8", x["A"], x["B"], 1.0, 1.0, x["bias"], K=K)
+    assert np.array_equal(C3, C4) and np.array_equal(D3, D4)
+    # a block's scale multiplies exactly that block's 32 K elements
+    SB5 = x["SB"].copy()
+    SB5[:, 2] += 2
+    _, D5 = oracle.gemm("mxfp8", x["A"], x["B"], x["SA"], SB5, None, K=K)
+    Bblk = x["B"].copy()
+    Bblk[:, :64] = 0
+    Bblk[:, 96:] = 0
+    _, Dblk = oracle.gemm("mxfp8", x["A"], Bblk, x["SA"], x["SB"], None, K=K)
+    assert np.array_equal(D5 - D, 3 * Dblk)
+    # swapping the operands transposes the result
+    C6, _ = oracle.gemm("mxfp8", x["B"], x["A"], x["SB"], x["SA"], None, K=K)
+    assert np.array_equal(C6, C.T)
+
+
 def pin_accept():
     x = make_inputs("bf16", 16, 24, 256, bias=True, seed=14)
     C, D = oracle.gemm("bf16", x["A"], x["B"], None, None, x["bias"])
@@ -354,8 +423,8 @@ PINS = [
     pin_e4m3fn_vs_torch, pin_e8m0_vs_torch, pin_bf16_decode_vs_torch, pin_e2m1_bitfields,
     pin_rne_vs_torch_on_floats, pin_rne_from_double_not_via_float, pin_rne_overflow_subnormal_nan,
     pin_rne_vs_rational, pin_bruteforce_mxfp4, pin_bruteforce_bf16, pin_bruteforce_fp8,
-    pin_handworked_mxfp4, pin_identity, pin_bias_broadcast, pin_integer_matmul,
-    pin_invariants_mxfp4, pin_accept,
+    pin_bruteforce_mxfp8, pin_handworked_mxfp4, pin_handworked_mxfp8, pin_identity, pin_bias_broadcast,
+    pin_integer_matmul, pin_invariants_mxfp4, pin_invariants_mxfp8, pin_accept,
 ]
 
 
@@ -448,10 +517,23 @@ def _mut_bf16_decode(mp):
     mp.setattr(oracle, "decode_bf16", lambda u: real(np.asarray(u, np.uint16) ^ np.uint16(1)))
 
 
+def _mut_mxfp8_no_scales(mp):
+    mp.setattr(oracle, "mxfp8_operand", lambda elems, scales, K: oracle.decode_e4m3fn(elems))
+
+
+def _mut_mxfp8_scale_per_16(mp):
+    # each E8M0 byte applied to 16 elements (and the row's second half given the first half's scales)
+    def op(elems, scales, K):
+        sc = oracle.decode_e8m0(np.asarray(scales, np.uint8))
+        rep = np.repeat(sc, 16, axis=1)
+        return oracle.decode_e4m3fn(elems) * np.concatenate([rep, rep], axis=1)[:, :K]
+    mp.setattr(oracle, "mxfp8_operand", op)
+
+
 MUTATIONS = [
     _mut_e2m1_entry, _mut_nibble_order, _mut_scale_block, _mut_drop_bias, _mut_double_bias,
     _mut_round_via_float, _mut_round_truncate, _mut_e4m3_bias, _mut_fp8_sigma, _mut_transpose_b,
-    _mut_bf16_decode,
+    _mut_bf16_decode, _mut_mxfp8_no_scales, _mut_mxfp8_scale_per_16,
 ]
 
 
