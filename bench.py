@@ -17,6 +17,8 @@ infrastructure, never the product path) on the same workload, whole, repeated
 for at least ten seconds.
 
     python bench.py --copy-calibration MIB          # plain device copy (counter reference)
+    python bench.py --co-schedule C [--workload W]  # the GEMM on C CUs beside a memory-bound kernel
+                                                    # on the other CUs (its own JSON line)
     python bench.py --traffic-summary F W CF CW --copy-calibration MIB
                                                     # rocprofv3 --pmc CSVs -> profiles/traffic_<workload>.json
 """
@@ -158,6 +160,102 @@ def cpu_baseline(w, x, budget_s: float = 10.0) -> dict:
                       f"decode, one matrix product with {threads} BLAS threads, bf16 rounding)"}
 
 
+def co_schedule(args, w, d, tile, policy) -> int:
+    """The capped GEMM co-scheduled with other work on one device.
+
+    The GEMM runs on a stream held to CUs [0, C) (its grid is then C
+    workgroups) while a memory-bound elementwise loop (out = in + 1 over
+    1 GiB of fp32) runs on a stream held to the other CUs.  Each is timed
+    alone and both together; the same pair is then run on two unmasked
+    streams with the GEMM's grid capped at C workgroups, which caps the count
+    but lets its workgroups land on any CU.  Prints one JSON line."""
+    import torch
+
+    import persistent_gemm_amd as pg
+
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    g = args.co_schedule
+    if not 0 < g < n:
+        print(f"--co-schedule needs 0 < C < {n}", file=sys.stderr)
+        return 2
+    src = torch.ones(256 << 20, device="cuda")
+    dst = torch.empty_like(src)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def gemm(stream, cap):
+        with torch.cuda.stream(stream):
+            pg.gemm_ex(w.dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap, policy=policy,
+                       tile=tile, variant=args.variant)
+
+    def other(stream):
+        with torch.cuda.stream(stream):
+            torch.add(src, 1.0, out=dst)
+
+    def alone(fn, stream, k):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    def together(sg, cap, so, ng, no):
+        eg = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        eo = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eg[0].record(sg)
+        eo[0].record(so)
+        # interleaved enqueues, so that both streams have work from the start
+        for i in range(max(ng, no)):
+            if i < ng:
+                gemm(sg, cap)
+            if i < no:
+                other(so)
+        eg[1].record(sg)
+        eo[1].record(so)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        return eg[0].elapsed_time(eg[1]) / ng, eo[0].elapsed_time(eo[1]) / no, wall
+
+    def summary(tg, to, k, no, tgt, tot, wall):
+        return {"gemm_ms_alone": round(tg, 5), "other_ms_alone": round(to, 5), "gemm_calls": k, "other_calls": no,
+                "gemm_ms_together": round(tgt, 5), "other_ms_together": round(tot, 5),
+                "wall_ms_together": round(wall, 3), "speedup_vs_serial": round((k * tg + no * to) / wall, 3)}
+
+    k = max(args.steps, 5)
+    sg = pg.cu_masked_stream(range(g))
+    so = pg.cu_masked_stream(range(g, n))
+    try:
+        tg = alone(lambda: gemm(sg, 0), sg, k)
+        to = alone(lambda: other(so), so, k)
+        no = max(1, round(k * tg / to))
+        part = summary(tg, to, k, no, *together(sg, 0, so, k, no))
+        pg.check(sg)
+    finally:
+        pg.destroy_stream(sg)
+        pg.destroy_stream(so)
+    ug, uo = torch.cuda.Stream(), torch.cuda.Stream()
+    tg2 = alone(lambda: gemm(ug, g), ug, k)
+    to2 = alone(lambda: other(uo), uo, k)
+    capped = summary(tg2, to2, k, no, *together(ug, g, uo, k, no))
+    pg.check(ug)
+    moved = 2 * src.numel() * 4
+    print(json.dumps({
+        "metric": "co-scheduled Stream-K GEMM beside a memory-bound kernel, 1 MI355X",
+        "workload": args.workload, "dtype": w.dtype, "device_cus": n, "gemm_cus": g, "other_cus": n - g,
+        "other_kernel": f"out = in + 1 over fp32 buffers ({moved / 2**30:.1f} GiB moved per call)",
+        "gemm_tflops_alone_on_partition": round(w.flops / (tg / 1e3) / 1e12, 3),
+        "other_gbs_alone_on_partition": round(moved / (to / 1e3) / 1e9, 1),
+        "cu_partition": part, "grid_cap_only": capped}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +268,8 @@ def main() -> int:
     ap.add_argument("--variant", type=int, default=None, help="compiled kernel index (default: automatic)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate", type=int, default=0, help="rotate over this many input copies (defeats the MALL)")
+    ap.add_argument("--co-schedule", type=int, default=0, metavar="C",
+                    help="run the GEMM on C CUs beside a memory-bound kernel on the other CUs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB instead (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=4, default=None,
@@ -228,6 +328,9 @@ def main() -> int:
             d["SB"] = torch.tensor([x["SB"]], dtype=torch.float32, device=dev)
         d["bias"] = None if x["bias"] is None else torch.from_numpy(x["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
         return d
+
+    if args.co_schedule:
+        return co_schedule(args, w, to_dev(x), tile, policy)
 
     copies = [to_dev(x)]
     for i in range(1, max(1, args.rotate)):

@@ -216,6 +216,30 @@ void sk_release_workspace(void);
  * NaN partials and stale lock values, so a following call must not depend on their contents. */
 sk_status sk_debug_poison_workspace(void* stream, int64_t scratch_bytes);
 
+/* CU-partitioned streams.  A persistent GEMM held to a chosen set of compute
+ * units exists so that other work can run on the remaining units of the same
+ * device at the same time (the intra-device parallelism named in
+ * "SM-constraint-GEMM by triton persistent kernel", description).
+ *
+ * sk_stream_create_cu_masked creates a HIP stream (default priority) whose
+ * kernels run only on the compute units set in cu_mask: bit (i % 32) of word
+ * i / 32 is CU i; `words` is the number of 32-bit words (1..64), and bits at
+ * or above the device's CU count are ignored.  The calls of this library on
+ * such a stream size their persistent grid to those units: grid_cap <= 0
+ * means all of them and a larger cap is clamped to their number.  Returns
+ * SK_ERR_ARG for a NULL pointer, a bad word count or a mask with no CU of the
+ * device, SK_ERR_HIP if the runtime refuses the stream.  The caller owns the
+ * stream and releases it (and the library's scratch kept for it) with
+ * sk_stream_destroy, which first waits for the stream.
+ *
+ * sk_stream_cu_count reports the compute units kernels on `stream` may use
+ * (every CU for the null stream or an unmasked stream).  For streams not
+ * made here the count is read from the runtime the first time the library
+ * sees the stream and kept for it. */
+sk_status sk_stream_create_cu_masked(const uint32_t* cu_mask, int32_t words, void** stream);
+sk_status sk_stream_destroy(void* stream);
+sk_status sk_stream_cu_count(void* stream, int32_t* count);
+
 /* Number of compiled kernels, and the shape of kernel `index` (host-only). */
 int32_t sk_num_variants(void);
 sk_status sk_variant_info(int32_t index, int32_t* dtype, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k,

@@ -10,7 +10,8 @@ and streams only.
 Entry points mirror ``include/sk_gemm.h``:
 ``gemm_mxfp4``, ``gemm_mxfp8``, ``gemm_bf16``, ``gemm_fp8``, ``addmm`` and ``gemm_ex`` (policy,
 tile and test hooks), plus ``plan``, ``plan_wg_range``, ``check``,
-``release_workspace``, ``poison_workspace`` and ``variants``.
+``release_workspace``, ``poison_workspace``, ``variants`` and the CU-masked
+streams ``cu_masked_stream`` / ``destroy_stream`` / ``stream_cu_count``.
 """
 
 from __future__ import annotations
@@ -23,6 +24,7 @@ __all__ = [
     "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
     "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
+    "cu_masked_stream", "destroy_stream", "stream_cu_count",
 ]
 
 MXFP4, BF16, FP8, MXFP8 = 0, 1, 2, 3
@@ -138,10 +140,15 @@ def load():
     lib.sk_debug_poison_workspace.argtypes = [vp, i64]
     lib.sk_num_variants.argtypes = []
     lib.sk_variant_info.argtypes = [ctypes.c_int32] + [ctypes.POINTER(ctypes.c_int32)] * 6
+    lib.sk_stream_create_cu_masked.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
+                                               ctypes.POINTER(ctypes.c_void_p)]
+    lib.sk_stream_destroy.argtypes = [vp]
+    lib.sk_stream_cu_count.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sk_status_string.argtypes = [ctypes.c_int]
     lib.sk_status_string.restype = ctypes.c_char_p
     for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
-                 "sk_plan_wg_range", "sk_plan_wg_work", "sk_check", "sk_debug_poison_workspace", "sk_variant_info"):
+                 "sk_plan_wg_range", "sk_plan_wg_work", "sk_check", "sk_debug_poison_workspace", "sk_variant_info",
+                 "sk_stream_create_cu_masked", "sk_stream_destroy", "sk_stream_cu_count"):
         getattr(lib, name).restype = ctypes.c_int
     lib.sk_num_variants.restype = ctypes.c_int32
     _LIB = lib
@@ -365,3 +372,40 @@ def variants():
         _ok(lib.sk_variant_info(i, *[ctypes.byref(x) for x in v]), "sk_variant_info")
         out.append(dict(zip(("dtype", "tile_m", "tile_n", "tile_k", "threads", "lds_bytes"), [x.value for x in v])))
     return out
+
+
+# ---------------------------------------------------------------- CU-partitioned streams
+
+def cu_masked_stream(cus, device=None):
+    """A stream whose kernels run only on the compute units listed in `cus`
+    (indices 0 .. CU count - 1), as a torch ExternalStream; the library's
+    calls on it size their grid to those units.  Release with destroy_stream."""
+    torch = _torch()
+    cus = sorted(set(int(c) for c in cus))
+    if not cus or cus[0] < 0:
+        raise ValueError("cus must list compute unit indices >= 0")
+    words = cus[-1] // 32 + 1
+    mask = (ctypes.c_uint32 * words)()
+    for c in cus:
+        mask[c // 32] |= 1 << (c % 32)
+    h = ctypes.c_void_p()
+    _ok(load().sk_stream_create_cu_masked(mask, words, ctypes.byref(h)), "sk_stream_create_cu_masked")
+    return torch.cuda.ExternalStream(h.value, device=device)
+
+
+def destroy_stream(stream):
+    """Waits for a stream made by cu_masked_stream, frees the library's scratch for it and destroys it."""
+    _ok(load().sk_stream_destroy(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)),
+        "sk_stream_destroy")
+
+
+def stream_cu_count(stream=None) -> int:
+    """Compute units kernels on `stream` may use (torch's current stream if None)."""
+    if stream is None:
+        torch = _torch()
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    n = ctypes.c_int32()
+    _ok(load().sk_stream_cu_count(stream, ctypes.byref(n)), "sk_stream_cu_count")
+    return n.value

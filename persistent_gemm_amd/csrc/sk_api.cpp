@@ -52,6 +52,8 @@ struct Workspace {
 std::mutex g_mu;
 std::map<std::pair<int, uintptr_t>, Workspace*> g_ws;
 std::map<int, DeviceInfo> g_dev;
+// Compute units a stream's kernels may use, read once per (device, stream).
+std::map<std::pair<int, uintptr_t>, int> g_stream_cus;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -86,6 +88,39 @@ sk_status device_info(int* dev_out, DeviceInfo* info) {
   *dev_out = dev;
   *info = it->second;
   return SK_OK;
+}
+
+// Number of set bits among the first `cus` bits of a CU mask.
+int mask_count(const uint32_t* mask, int words, int cus) {
+  int n = 0;
+  for (int i = 0; i < words; ++i) {
+    uint32_t w = mask[i];
+    if (32 * i + 32 > cus) w &= (32 * i >= cus) ? 0u : ((1u << (cus - 32 * i)) - 1u);
+    n += __builtin_popcount(w);
+  }
+  return n;
+}
+
+// Compute units that kernels launched on `stream` may use: the size of its
+// CU mask (every CU for the null stream or when the mask cannot be read).
+int stream_cus(int dev, hipStream_t stream, int device_cus) {
+  if (!stream) return device_cus;
+  const auto key = std::make_pair(dev, (uintptr_t)stream);
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_stream_cus.find(key);
+    if (it != g_stream_cus.end()) return it->second;
+  }
+  const int words = (device_cus + 31) / 32;
+  std::vector<uint32_t> mask((size_t)words, 0u);
+  int n = device_cus;
+  if (hipExtStreamGetCUMask(stream, (uint32_t)words, mask.data()) == hipSuccess) {
+    const int m = mask_count(mask.data(), words, device_cus);
+    if (m > 0) n = m;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_stream_cus[key] = n;
+  return n;
 }
 
 // Kernel shape: an explicit (tile_m, tile_n), else a choice by problem shape.
@@ -270,7 +305,10 @@ sk_status run(const sk_gemm_args& g) {
   if (st != SK_OK) return st;
   if (!info.gfx950) return SK_ERR_UNSUPPORTED;
   sk_plan_info p;
-  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, info.cus, &p);
+  // The grid is sized to the compute units the stream may use, so on a
+  // CU-masked stream the cap is a partition of the device, not a count.
+  const int cus = stream_cus(dev, (hipStream_t)g.stream, info.cus);
+  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, cus, &p);
   if (st != SK_OK) return st;
   hipStream_t stream = (hipStream_t)g.stream;
   const Variant* v = sk::variant(p.variant);
@@ -507,6 +545,57 @@ sk_status sk_variant_info(int32_t index, int32_t* dtype, int32_t* tile_m, int32_
   if (tile_k) *tile_k = v->bk;
   if (threads) *threads = v->threads;
   if (lds_bytes) *lds_bytes = v->lds;
+  return SK_OK;
+}
+
+sk_status sk_stream_create_cu_masked(const uint32_t* cu_mask, int32_t words, void** stream) {
+  if (!cu_mask || !stream || words < 1 || words > 64) return SK_ERR_ARG;
+  int dev = 0;
+  DeviceInfo info;
+  sk_status st = device_info(&dev, &info);
+  if (st != SK_OK) return st;
+  const int n = mask_count(cu_mask, words, info.cus);
+  if (n < 1) return SK_ERR_ARG;
+  hipStream_t s = nullptr;
+  if (hipExtStreamCreateWithCUMask(&s, (uint32_t)words, cu_mask) != hipSuccess) return SK_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_stream_cus[std::make_pair(dev, (uintptr_t)s)] = n;
+  *stream = (void*)s;
+  return SK_OK;
+}
+
+sk_status sk_stream_destroy(void* stream) {
+  if (!stream) return SK_ERR_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SK_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return SK_ERR_HIP;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    const auto key = std::make_pair(dev, (uintptr_t)s);
+    auto it = g_ws.find(key);
+    if (it != g_ws.end()) {
+      Workspace* ws = it->second;
+      if (ws) {
+        if (ws->P) hipFree(ws->P);
+        if (ws->S) hipFree(ws->S);
+        if (ws->flags) hipFree(ws->flags);
+        delete ws;
+      }
+      g_ws.erase(it);
+    }
+    g_stream_cus.erase(key);
+  }
+  return hipStreamDestroy(s) == hipSuccess ? SK_OK : SK_ERR_HIP;
+}
+
+sk_status sk_stream_cu_count(void* stream, int32_t* count) {
+  if (!count) return SK_ERR_ARG;
+  int dev = 0;
+  DeviceInfo info;
+  sk_status st = device_info(&dev, &info);
+  if (st != SK_OK) return st;
+  *count = stream_cus(dev, (hipStream_t)stream, info.cus);
   return SK_OK;
 }
 

@@ -206,3 +206,15 @@ def test_plan_ragged_and_hybrid_shapes():
             assert p.tiles_m == -(-M // p.tile_m) and p.iters_per_tile == -(-K // p.tile_k)
             if p.tiles * p.iters_per_tile <= 20000:
                 _check_plan(p, cap)
+
+
+def test_stream_entry_points_check_arguments():
+    lib = pg.load()
+    one = (ctypes.c_uint32 * 1)(1)
+    out = ctypes.c_void_p()
+    assert lib.sk_stream_create_cu_masked(None, 1, ctypes.byref(out)) == 1
+    assert lib.sk_stream_create_cu_masked(one, 0, ctypes.byref(out)) == 1
+    assert lib.sk_stream_create_cu_masked(one, 65, ctypes.byref(out)) == 1
+    assert lib.sk_stream_create_cu_masked(one, 1, None) == 1
+    assert lib.sk_stream_destroy(None) == 1
+    assert lib.sk_stream_cu_count(None, None) == 1

@@ -266,3 +266,63 @@ def test_errors_are_status_codes(small):
                            None, d["A"].data_ptr(), 256, 256, 512, 0, s)
     assert st == 1
     pg.check()
+
+
+# ---------------------------------------------------------------- CU-partitioned streams
+
+def _device_cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def test_cu_masked_stream_sizes_the_grid():
+    """On a stream held to 48 CUs the grid is 48 workgroups: 256 tiles of 64x64
+    then leave 16 over, so the plan has a Stream-K head of 64 tiles."""
+    x = make_inputs("mxfp4", 1024, 1024, 2048, bias=True, seed=21)
+    d = device_inputs(x)
+    C, _ = oracle_full(x)
+    out = torch.empty((1024, 1024), dtype=torch.bfloat16, device="cuda")   # allocated on torch's own stream
+    torch.cuda.synchronize()
+    s = pg.cu_masked_stream(range(48))
+    try:
+        assert pg.stream_cu_count(s) == 48
+        p = pg.plan("mxfp4", 1024, 1024, 2048, tile=(64, 64), num_cus=pg.stream_cu_count(s))
+        assert p.grid == 48 and p.sk_tiles == 64
+        with torch.cuda.stream(s):
+            for cap in (0, 100, 20):
+                say(f"mxfp4 1024x1024x2048 tile 64x64 on a 48-CU stream, cap {cap}")
+                assert_bitexact(run(d, tile=(64, 64), grid_cap=cap, C=out), C, f"48-CU stream cap {cap}")
+    finally:
+        pg.destroy_stream(s)
+    assert pg.stream_cu_count(torch.cuda.current_stream()) == _device_cus()
+
+
+def test_co_scheduled_gemm_beside_other_work():
+    """The GEMM on one half of the CUs while a memory-bound elementwise loop
+    runs on the other half: every result still equals the oracle's."""
+    n = _device_cus()
+    x = make_inputs("mxfp4", 2048, 2048, 4096, bias=True, seed=22)
+    d = device_inputs(x)
+    C, _ = oracle_full(x)
+    s1 = pg.cu_masked_stream(range(n // 2))
+    s2 = pg.cu_masked_stream(range(n // 2, n))
+    try:
+        # every tensor is allocated on torch's own stream, before the masked streams are used
+        src = torch.ones(64 << 20, device="cuda")
+        dst = torch.empty_like(src)
+        outs = [torch.empty((2048, 2048), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s2):
+            for _ in range(20):
+                torch.add(src, 1.0, out=dst)
+        with torch.cuda.stream(s1):
+            for i, o in enumerate(outs):
+                say(f"co-scheduled mxfp4 2048x2048x4096 call {i}")
+                pg.gemm_ex("mxfp4", d["A"], d["B"], d["SA"], d["SB"], d["bias"], o)
+            pg.check()
+        s2.synchronize()
+        for o in outs:
+            assert_bitexact(o.view(torch.int16).cpu().numpy().view(np.uint16), C, "co-scheduled")
+        assert float(dst[0]) == 2.0
+    finally:
+        pg.destroy_stream(s1)
+        pg.destroy_stream(s2)
