@@ -54,14 +54,15 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str, tag: str):
-    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+def traffic_for(workload: str, tag: str, variant: int):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    with these kernel sources and the same compiled kernel."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash() or rec.get("variant") != variant:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -102,8 +103,12 @@ def traffic_summary(args) -> int:
                      "copy_kib_per_dispatch": c_kib, "copy_dispatches": len(c), "scale": factor,
                      "bytes_per_launch": g_kib * 1024.0 * factor}
     out["hbm_bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    import persistent_gemm_amd as pg
     from persistent_gemm_amd.inputs import WORKLOADS
-    out["algorithmic_bytes"] = algorithmic_bytes(WORKLOADS[args.workload])
+    w = WORKLOADS[args.workload]
+    out["algorithmic_bytes"] = algorithmic_bytes(w)
+    # the kernel the default launch uses (the counters were taken on it)
+    out["variant"] = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=w.grid_cap, policy=pg.AUTO, num_cus=256).variant
     path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -264,7 +269,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cap", type=int, default=None, help="grid cap (default: the workload's)")
     ap.add_argument("--tile", default=None, help="tile override, e.g. 256x256")
-    ap.add_argument("--policy", default="hybrid", choices=["hybrid", "sk", "dp"])
+    ap.add_argument("--policy", default="auto", choices=["auto", "hybrid", "sk", "dp"],
+                    help="auto: the measured kernel and policy for the shape (what the plain entry points use)")
     ap.add_argument("--variant", type=int, default=None, help="compiled kernel index (default: automatic)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate", type=int, default=0, help="rotate over this many input copies (defeats the MALL)")
@@ -301,7 +307,7 @@ def main() -> int:
         tile = tuple(int(v) for v in args.tile.lower().split("x"))
     elif w.tile:
         tile = tuple(int(v) for v in w.tile.split("x"))
-    policy = {"hybrid": pg.HYBRID, "sk": pg.PURE_SK, "dp": pg.PURE_DP}[args.policy]
+    policy = {"auto": pg.AUTO, "hybrid": pg.HYBRID, "sk": pg.PURE_SK, "dp": pg.PURE_DP}[args.policy]
 
     x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
     dev = torch.device("cuda:0")
@@ -369,9 +375,9 @@ def main() -> int:
     peak = PEAK_TFLOPS[w.dtype]
     eff_peak = peak * (p.grid / 256.0 if args.workload.startswith("fp8_gemm_4096_cap") else 1.0)
     achieved = flops / avg_kern_s / 1e12
-    default_launch = args.cap is None and args.tile is None and policy == pg.HYBRID and args.variant is None
+    default_launch = args.cap is None and args.tile is None and policy == pg.AUTO and args.variant is None
     tag = "" if default_launch else "_nondefault"
-    traffic = traffic_for(args.workload, tag)
+    traffic = traffic_for(args.workload, tag, p.variant)
     out = {
         "metric": METRIC if w.dtype == "mxfp4" else f"{w.dtype} Stream-K GEMM TFLOP/s, 1 MI355X",
         "value": round(value, 3),
@@ -387,7 +393,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
                    "tile": f"{p.tile_m}x{p.tile_n}x{p.tile_k}", "threads": p.threads, "variant": p.variant,
-                   "policy": args.policy, "grid": p.grid,
+                   "policy": {pg.HYBRID: "hybrid", pg.PURE_SK: "sk", pg.PURE_DP: "dp"}[p.policy],
+                   "policy_requested": args.policy, "grid": p.grid,
                    "sk_tiles": p.sk_tiles, "tiles": p.tiles, "parallelism": "stream-k, 1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": eff_peak, "unit": "TFLOP/s",
                      "frac": round(achieved / eff_peak, 4), "traffic": traffic,

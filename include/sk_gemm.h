@@ -102,7 +102,18 @@ typedef enum sk_dtype { SK_MXFP4 = 0, SK_BF16 = 1, SK_FP8_E4M3 = 2, SK_MXFP8 = 3
  * PURE_DP: whole tiles round-robin, no iteration splitting (the "Persistent"
  *   path that the Stream-K switch turns off in "Fix StreamK Kernel Bias #67",
  *   Improve StreamK Testing). */
-typedef enum sk_policy { SK_POLICY_HYBRID = 0, SK_POLICY_PURE_SK = 1, SK_POLICY_PURE_DP = 2 } sk_policy;
+/* AUTO: the kernel and policy measured fastest at the nearest swept shape
+ *   (the best-config search of "SM-constraint-GEMM by triton persistent
+ *   kernel", description, checklist; the table is compiled into the library), else
+ *   HYBRID with the kernel chosen by problem shape.  A fixed tile or kernel
+ *   keeps its choice and runs HYBRID.  The sk_gemm_* and sk_addmm entry
+ *   points use AUTO. */
+typedef enum sk_policy {
+  SK_POLICY_HYBRID = 0,
+  SK_POLICY_PURE_SK = 1,
+  SK_POLICY_PURE_DP = 2,
+  SK_POLICY_AUTO = 3
+} sk_policy;
 
 /* sk_gemm_args.debug_flags bits (tests only). */
 #define SK_DEBUG_DELAY 1u       /* each workgroup sleeps a seeded pseudo-random time before publishing its partial */

@@ -21,14 +21,14 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
+    "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
     "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
     "cu_masked_stream", "destroy_stream", "stream_cu_count",
 ]
 
 MXFP4, BF16, FP8, MXFP8 = 0, 1, 2, 3
-HYBRID, PURE_SK, PURE_DP = 0, 1, 2
+HYBRID, PURE_SK, PURE_DP, AUTO = 0, 1, 2, 3
 DEBUG_DELAY, DEBUG_DROP_SIGNAL = 1, 2
 
 _STATUS = {0: "SK_OK", 1: "SK_ERR_ARG", 2: "SK_ERR_ALIGN", 3: "SK_ERR_UNSUPPORTED", 4: "SK_ERR_HIP",

@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <map>
@@ -123,6 +124,39 @@ int stream_cus(int dev, hipStream_t stream, int device_cus) {
   return n;
 }
 
+// Measured choices for SK_POLICY_AUTO: the fastest (kernel, policy) at each
+// swept shape (written by persistent_gemm_amd/tune.py).  An entry is used
+// only while the kernel at its index still has the tile and thread count it
+// was measured with.
+struct TuneEntry {
+  int dtype;
+  int64_t M, N, K;
+  int variant, policy;
+  int bm, bn, threads;
+};
+#include "sk_tuning_table.inc"
+
+// The tuned (variant, policy) of the measured shape nearest to (M, N, K)
+// in log scale; false if the table has no usable entry for the dtype.
+bool tuned_choice(int dtype, int64_t M, int64_t N, int64_t K, int* variant, int* policy) {
+  double best = 1e300;
+  bool found = false;
+  for (const TuneEntry& e : kTuneTable) {
+    if (e.dtype != dtype) continue;
+    const Variant* v = sk::variant(e.variant);
+    if (!v || v->dtype != dtype || v->bm != e.bm || v->bn != e.bn || v->threads != e.threads) continue;
+    const double d = std::fabs(std::log2((double)M / (double)e.M)) + std::fabs(std::log2((double)N / (double)e.N)) +
+                     std::fabs(std::log2((double)K / (double)e.K));
+    if (d < best) {
+      best = d;
+      *variant = e.variant;
+      *policy = e.policy;
+      found = true;
+    }
+  }
+  return found;
+}
+
 // Kernel shape: an explicit (tile_m, tile_n), else a choice by problem shape.
 int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n, int forced) {
   const int nv = sk::num_variants();
@@ -156,10 +190,16 @@ int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n, int fo
 sk_status make_plan(int dtype, int policy, int64_t M, int64_t N, int64_t K, int grid_cap, int tile_m, int tile_n,
                     int forced, int num_cus, sk_plan_info* p) {
   if (!dtype_ok(dtype)) return SK_ERR_ARG;
-  if (policy < SK_POLICY_HYBRID || policy > SK_POLICY_PURE_DP) return SK_ERR_ARG;
+  if (policy < SK_POLICY_HYBRID || policy > SK_POLICY_AUTO) return SK_ERR_ARG;
   if (M < 1 || N < 1 || K < 1 || M >= kMaxM || N > kMaxN || K > kMaxK) return SK_ERR_ARG;
   if (num_cus < 1) return SK_ERR_ARG;
   if (forced < 0) return SK_ERR_ARG;
+  if (policy == SK_POLICY_AUTO) {
+    // measured (kernel, policy) unless the caller fixed the kernel; else HYBRID
+    int tv = -1, tp = SK_POLICY_HYBRID;
+    if (forced == 0 && tile_m <= 0 && tile_n <= 0 && tuned_choice(dtype, M, N, K, &tv, &tp)) forced = tv + 1;
+    policy = tp;
+  }
   const int vi = pick_variant(dtype, M, N, tile_m, tile_n, forced);
   if (vi < 0) return SK_ERR_UNSUPPORTED;
   const Variant* v = sk::variant(vi);
@@ -214,7 +254,7 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 sk_status validate(const sk_gemm_args& g) {
   if (!dtype_ok(g.dtype)) return SK_ERR_ARG;
-  if (g.policy < SK_POLICY_HYBRID || g.policy > SK_POLICY_PURE_DP) return SK_ERR_ARG;
+  if (g.policy < SK_POLICY_HYBRID || g.policy > SK_POLICY_AUTO) return SK_ERR_ARG;
   if (!g.A || !g.B || !g.C) return SK_ERR_ARG;
   if (g.M < 1 || g.N < 1 || g.K < 1 || g.M >= kMaxM || g.N > kMaxN || g.K > kMaxK) return SK_ERR_ARG;
   if (is_mx(g.dtype) && (!g.A_scale || !g.B_scale)) return SK_ERR_ARG;
@@ -381,7 +421,7 @@ sk_gemm_args base_args(int dtype, const void* A, const void* B, const void* sa, 
   sk_gemm_args g;
   std::memset(&g, 0, sizeof(g));
   g.dtype = dtype;
-  g.policy = SK_POLICY_HYBRID;
+  g.policy = SK_POLICY_AUTO;
   g.A = A;
   g.B = B;
   g.A_scale = sa;

@@ -218,3 +218,24 @@ def test_stream_entry_points_check_arguments():
     assert lib.sk_stream_create_cu_masked(one, 1, None) == 1
     assert lib.sk_stream_destroy(None) == 1
     assert lib.sk_stream_cu_count(None, None) == 1
+
+
+def test_auto_policy_takes_the_measured_choice():
+    """AUTO plans take (kernel, policy) from the compiled table of measured
+    choices at the nearest swept shape; a fixed tile or kernel runs HYBRID."""
+    import re
+    table = open(os.path.join(ROOT, "persistent_gemm_amd", "csrc", "sk_tuning_table.inc")).read()
+    rows = [tuple(int(v) for v in m.groups()) for m in re.finditer(
+        r"\{(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\}", table)]
+    vs = pg.variants()
+    assert rows, "the table holds measured entries"
+    for dtype, M, N, K, vi, pol, bm, bn, threads in rows:
+        v = vs[vi]
+        assert (v["dtype"], v["tile_m"], v["tile_n"], v["threads"]) == (dtype, bm, bn, threads)
+        p = pg.plan(dtype, M, N, K, policy=pg.AUTO, num_cus=256)
+        assert (p.variant, p.policy) == (vi, pol), (dtype, M, N, K)
+        # a shape a little off the grid takes the same entry
+        q = pg.plan(dtype, M + 8, N - 8, K + 32, policy=pg.AUTO, num_cus=256)
+        assert (q.variant, q.policy) == (vi, pol), (dtype, M, N, K)
+    p = pg.plan(pg.MXFP4, 8192, 8192, 8192, policy=pg.AUTO, tile=(128, 128), num_cus=256)
+    assert (p.tile_m, p.tile_n, p.policy) == (128, 128, pg.HYBRID)

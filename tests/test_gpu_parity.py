@@ -248,6 +248,13 @@ def test_entry_points_agree(small):
               pg.addmm("fp8", dz["bias"], dz["A"], dz["B"], dz["SA"], dz["SB"])):
         pg.check()
         assert_bitexact(c.view(torch.int16).cpu().numpy().view(np.uint16), Cz, "fp8 entry point")
+    u = integer_inputs("mxfp8", 130, 70, 160, bias=True, seed=5)
+    du = device_inputs(u)
+    Cu, _ = oracle_full(u)
+    for c in (pg.gemm_mxfp8(du["A"], du["B"], du["SA"], du["SB"], du["bias"]),
+              pg.addmm("mxfp8", du["bias"], du["A"], du["B"], du["SA"], du["SB"])):
+        pg.check()
+        assert_bitexact(c.view(torch.int16).cpu().numpy().view(np.uint16), Cu, "mxfp8 entry point")
 
 
 def test_errors_are_status_codes(small):
