@@ -675,9 +675,13 @@ struct Kernel {
   // and the flags are device-scope atomics.
   static constexpr int kDeviceScope = 16;   // buffer cache policy: sc1
 
-  // Publish this workgroup's partial: every thread's device-scope stores have
-  // completed (the barrier waits for them) before the flag is written.
+  // Publish this workgroup's partial: every wave waits until its own
+  // device-scope stores of the partial have completed, then the barrier, then
+  // one thread writes the flag.  The wait has to be explicit: the barrier's
+  // workgroup-scope fence does not wait for global stores, so without it the
+  // flag could become visible while some of the partial is still in flight.
   static __device__ __forceinline__ void publish(const KArgs& a, int w) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (a.delay_seed) {
       uint32_t h = a.delay_seed ^ (0x9e3779b9u * (uint32_t)(w + 1));
       h ^= h >> 15; h *= 0x2c1b3c6du; h ^= h >> 12;
