@@ -133,6 +133,9 @@ def copy_calibration(args) -> int:
 def algorithmic_bytes(w) -> int:
     """Each operand, scale, bias and output element once."""
     M, N, K = w.M, w.N, w.K
+    if w.op == "backward":
+        # reads dC, A, B; writes dA, dB, dbias
+        return 2 * (M * N + M * K + N * K) + 2 * (M * K + N * K) + 2 * N
     if w.dtype == "mxfp4":
         b = (M + N) * (K // 2) + (M + N) * (K // 32)
     elif w.dtype == "mxfp8":
@@ -147,6 +150,12 @@ def algorithmic_bytes(w) -> int:
 def cpu_baseline(w, x, budget_s: float = 10.0) -> dict:
     """The oracle on the whole workload, repeated until budget_s of CPU time has passed."""
     import oracle
+    if w.op == "backward":
+        run_once = lambda: oracle.bf16_backward(x["dC"], x["A"], x["B"])
+        what = "decode, two matrix products and a column sum"
+    else:
+        run_once = lambda: oracle.gemm(w.dtype, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=w.K)
+        what = "decode, one matrix product"
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
@@ -154,15 +163,15 @@ def cpu_baseline(w, x, budget_s: float = 10.0) -> dict:
         threads = len(os.sched_getaffinity(0))
     runs, t0 = 0, time.perf_counter()
     while True:
-        oracle.gemm(w.dtype, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=w.K)
+        run_once()
         runs += 1
         t = time.perf_counter() - t0
         if t >= budget_s:
             break
-    flops = 2.0 * w.M * w.N * w.K * runs
+    flops = float(w.flops) * runs
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"the whole {w.M}x{w.N}x{w.K} problem, {runs} oracle run(s) in {t:.1f} s (fp64 numpy: "
-                      f"decode, one matrix product with {threads} BLAS threads, bf16 rounding)"}
+                      f"{what} with {threads} BLAS threads, bf16 rounding)"}
 
 
 def co_schedule(args, w, d, tile, policy) -> int:
@@ -309,45 +318,54 @@ def main() -> int:
         tile = tuple(int(v) for v in w.tile.split("x"))
     policy = {"auto": pg.AUTO, "hybrid": pg.HYBRID, "sk": pg.PURE_SK, "dp": pg.PURE_DP}[args.policy]
 
-    x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.op == "backward":
+        from persistent_gemm_amd.inputs import backward_inputs
+        x = backward_inputs(w.M, w.N, w.K, seed=w.seed)
+        d = {k: torch.from_numpy(x[k].view(np.int16)).view(torch.bfloat16).to(dev) for k in ("dC", "A", "B")}
+        p = pg.plan(w.dtype, w.M, w.K, w.N, grid_cap=cap, policy=policy)   # the dA product's plan
 
-    def to_dev(x):
-        d = {}
-        if w.dtype == "mxfp4":
-            for k in ("A", "B", "SA", "SB"):
-                d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
-        elif w.dtype == "mxfp8":
-            for k in ("A", "B"):
-                d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
-            for k in ("SA", "SB"):
-                d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
-        elif w.dtype == "bf16":
-            for k in ("A", "B"):
-                d[k] = torch.from_numpy(x[k].view(np.int16)).view(torch.bfloat16).to(dev)
-            d["SA"] = d["SB"] = None
-        else:
-            for k in ("A", "B"):
-                d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
-            d["SA"] = torch.tensor([x["SA"]], dtype=torch.float32, device=dev)
-            d["SB"] = torch.tensor([x["SB"]], dtype=torch.float32, device=dev)
-        d["bias"] = None if x["bias"] is None else torch.from_numpy(x["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
-        return d
+        def step(i):
+            pg.gemm_bf16_backward(d["dC"], d["A"], d["B"], grid_cap=cap)
+    else:
+        x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
 
-    if args.co_schedule:
-        return co_schedule(args, w, to_dev(x), tile, policy)
+        def to_dev(x):
+            d = {}
+            if w.dtype == "mxfp4":
+                for k in ("A", "B", "SA", "SB"):
+                    d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
+            elif w.dtype == "mxfp8":
+                for k in ("A", "B"):
+                    d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
+                for k in ("SA", "SB"):
+                    d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
+            elif w.dtype == "bf16":
+                for k in ("A", "B"):
+                    d[k] = torch.from_numpy(x[k].view(np.int16)).view(torch.bfloat16).to(dev)
+                d["SA"] = d["SB"] = None
+            else:
+                for k in ("A", "B"):
+                    d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
+                d["SA"] = torch.tensor([x["SA"]], dtype=torch.float32, device=dev)
+                d["SB"] = torch.tensor([x["SB"]], dtype=torch.float32, device=dev)
+            d["bias"] = None if x["bias"] is None else torch.from_numpy(x["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
+            return d
 
-    copies = [to_dev(x)]
-    for i in range(1, max(1, args.rotate)):
-        copies.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in copies[0].items()})
-    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
-    p = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=cap, policy=policy, tile=tile, variant=args.variant)
+        if args.co_schedule:
+            return co_schedule(args, w, to_dev(x), tile, policy)
 
-    def step(i):
-        d = copies[i % len(copies)]
-        pg.gemm_ex(w.dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap, policy=policy, tile=tile,
-                   variant=args.variant)
+        copies = [to_dev(x)]
+        for i in range(1, max(1, args.rotate)):
+            copies.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in copies[0].items()})
+        C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        p = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=cap, policy=policy, tile=tile, variant=args.variant)
+
+        def step(i):
+            d = copies[i % len(copies)]
+            pg.gemm_ex(w.dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap, policy=policy, tile=tile,
+                       variant=args.variant)
 
     for i in range(args.warmup):
         step(i)
@@ -379,7 +397,9 @@ def main() -> int:
     tag = "" if default_launch else "_nondefault"
     traffic = traffic_for(args.workload, tag, p.variant)
     out = {
-        "metric": METRIC if w.dtype == "mxfp4" else f"{w.dtype} Stream-K GEMM TFLOP/s, 1 MI355X",
+        "metric": (METRIC if w.dtype == "mxfp4" else
+                   f"{w.dtype} Stream-K GEMM backward (dA, dB, dbias) TFLOP/s, 1 MI355X" if w.op == "backward" else
+                   f"{w.dtype} Stream-K GEMM TFLOP/s, 1 MI355X"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -391,7 +411,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
+        "config": {"workload": args.workload, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
                    "tile": f"{p.tile_m}x{p.tile_n}x{p.tile_k}", "threads": p.threads, "variant": p.variant,
                    "policy": {pg.HYBRID: "hybrid", pg.PURE_SK: "sk", pg.PURE_DP: "dp"}[p.policy],
                    "policy_requested": args.policy, "grid": p.grid,

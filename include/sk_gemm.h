@@ -144,6 +144,26 @@ sk_status sk_gemm_mxfp8(const uint8_t* A, const uint8_t* B, const uint8_t* A_sca
 sk_status sk_addmm(sk_dtype dtype, const void* bias, const void* A, const void* B, const void* A_scale,
                    const void* B_scale, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
 
+/* bf16 backward of C = A * B^T + bias (A [M][K], B [N][K], bias [N], as
+ * stored by sk_gemm_bf16 / sk_addmm), given dC = dL/dC (bf16 [M][N]):
+ *     dA[m][k]  = RNE_bf16( sum_n dC[m][n] * B[n][k] )      bf16 [M][K]
+ *     dB[n][k]  = RNE_bf16( sum_m dC[m][n] * A[m][k] )      bf16 [N][K]
+ *     dbias[n]  = RNE_bf16( sum_m dC[m][n] )                bf16 [N]
+ * the gradients that the Stream-K matmul and addmm tests take and compare
+ * with torch's for a, b and the bias ("Fix StreamK Kernel Bias #67", review
+ * comments on the two Stream-K tests).  dA and dB run through the same
+ * Stream-K kernels (policy AUTO, grid as for sk_gemm_bf16): the operands are
+ * first transposed into K-contiguous copies in the library's scratch of
+ * (device, stream), B^T for dA and dC^T, A^T for dB.  dbias is summed in fp32
+ * in a fixed order.  Any of dA, dB, dbias may be NULL (not computed; at least
+ * one is required); A may be NULL when dB is, B when dA is.  M, N and K must
+ * be multiples of 8 (SK_ERR_ALIGN), the sizes as for the GEMMs this makes
+ * (N <= 2^21 for dA, M <= 2^21 for dB, K <= 2^22), outputs must not overlap
+ * inputs or each other (SK_ERR_ARG).  Precision as for sk_gemm_bf16: fp32
+ * accumulation, one rounding. */
+sk_status sk_gemm_bf16_backward(const void* dC, const void* A, const void* B, void* dA, void* dB, void* dbias,
+                                int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
+
 /* Full-control entry point: the same kernels with a chosen policy and tile, plus test hooks.
  * Zero-initialise and fill the fields you need. */
 typedef struct sk_gemm_args {

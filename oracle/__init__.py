@@ -29,6 +29,9 @@ one.  Sources:
 * MXFP8 (E4M3 elements with the same E8M0 block scales) is the block-scaled
   form of the quantized mode of "Fix StreamK Kernel Bias #67", Technical
   Details; it is the MXFP4 contraction with 8-bit elements.
+* The bf16 backward of addmm (the gradients of A, B and the bias that the
+  Stream-K matmul / addmm tests take and compare with torch's): "Fix StreamK
+  Kernel Bias #67", review comments on the two Stream-K tests.
 * Element encodings are not on those pages.  E2M1 (FP4) and E8M0 (the shared
   block scale, one per 32 consecutive K elements) follow the OCP Microscaling
   Formats (MX) v1.0 specification; E4M3FN follows the OCP 8-bit Floating Point
@@ -64,6 +67,7 @@ __all__ = [
     "gemm_elements",
     "abs_product_sums",
     "accept",
+    "bf16_backward",
 ]
 
 # OCP MX v1.0, FP4 (E2M1): code bits are sign | exponent(2, bias 1) | mantissa(1).
@@ -281,3 +285,32 @@ def accept(C_test: np.ndarray, C_ref: np.ndarray, D: np.ndarray, S: np.ndarray |
         bound = np.ldexp(np.asarray(S, dtype=np.float64), -7) + _ulp_bf16(np.maximum(np.abs(D), np.abs(t)))
         ok = np.isfinite(err) & (err <= bound)
     return same | ok
+
+
+def bf16_backward(dC, A, B):
+    """Gradients of C = A . B^T + bias for bf16 operands, given dC = dL/dC.
+
+    dC uint16[M][N], A uint16[M][K], B uint16[N][K] (bf16 bit patterns; A or B
+    may be None when its gradient partner is not wanted).  Returns a dict of
+    (bits, exact value, error-bound sum) triples:
+
+        dA[m][k] = sum_n dC[m][n] * B[n][k]     (needs B)
+        dB[n][k] = sum_m dC[m][n] * A[m][k]     (needs A)
+        dbias[n] = sum_m dC[m][n]
+
+    each value in fp64 (two library matrix products and one sum) and rounded
+    once to bf16; the error-bound sums are the same sums of absolute values.
+    """
+    g = decode_bf16(dC)
+    out = {}
+    if B is not None:
+        b = decode_bf16(B)
+        D = g @ b
+        out["dA"] = (rne_bf16_from_double(D), D, np.abs(g) @ np.abs(b))
+    if A is not None:
+        a = decode_bf16(A)
+        D = g.T @ a
+        out["dB"] = (rne_bf16_from_double(D), D, np.abs(g).T @ np.abs(a))
+    D = g.sum(axis=0)
+    out["dbias"] = (rne_bf16_from_double(D), D, np.abs(g).sum(axis=0))
+    return out

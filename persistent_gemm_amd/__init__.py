@@ -22,7 +22,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
-    "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
+    "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_bf16_backward", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
     "cu_masked_stream", "destroy_stream", "stream_cu_count",
 ]
@@ -127,6 +127,7 @@ def load():
     lib.sk_gemm_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.sk_gemm_bf16_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_addmm.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_ex.argtypes = [ctypes.POINTER(_Args)]
     lib.sk_plan.argtypes = [ctypes.POINTER(_PlanQuery), ctypes.POINTER(_PlanInfo)]
@@ -146,7 +147,7 @@ def load():
     lib.sk_stream_cu_count.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sk_status_string.argtypes = [ctypes.c_int]
     lib.sk_status_string.restype = ctypes.c_char_p
-    for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
+    for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_bf16_backward", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
                  "sk_plan_wg_range", "sk_plan_wg_work", "sk_check", "sk_debug_poison_workspace", "sk_variant_info",
                  "sk_stream_create_cu_masked", "sk_stream_destroy", "sk_stream_cu_count"):
         getattr(lib, name).restype = ctypes.c_int
@@ -269,6 +270,31 @@ def gemm_bf16(A, B, bias=None, C=None, grid_cap=0, stream=None):
     _ok(load().sk_gemm_bf16(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K, int(grid_cap), _stream(A, stream)),
         "sk_gemm_bf16")
     return C
+
+
+def gemm_bf16_backward(dC, A=None, B=None, *, need_dA=True, need_dB=True, need_dbias=True, grid_cap=0,
+                       stream=None):
+    """Gradients of C = A . B^T + bias for bf16: returns (dA, dB, dbias), None where not asked for.
+
+    dC is bf16 [M, N]; A [M, K] is needed for dB and B [N, K] for dA."""
+    torch = _torch()
+    M, N = dC.shape
+    dev = dC.device
+    _need(dC, "dC", (torch.bfloat16, torch.int16, torch.uint16), (M, N), dev)
+    ref = A if A is not None else B
+    if ref is None:
+        raise ValueError("A or B is needed")
+    K = ref.shape[1]
+    if need_dB:
+        _need(A, "A", (torch.bfloat16, torch.int16, torch.uint16), (M, K), dev)
+    if need_dA:
+        _need(B, "B", (torch.bfloat16, torch.int16, torch.uint16), (N, K), dev)
+    dA = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if need_dA else None
+    dB = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if need_dB else None
+    db = torch.empty((N,), dtype=torch.bfloat16, device=dev) if need_dbias else None
+    _ok(load().sk_gemm_bf16_backward(_ptr(dC), _ptr(A), _ptr(B), _ptr(dA), _ptr(dB), _ptr(db), M, N, K,
+                                     int(grid_cap), _stream(dC, stream)), "sk_gemm_bf16_backward")
+    return dA, dB, db
 
 
 def gemm_fp8(A, B, A_scale=None, B_scale=None, bias=None, C=None, grid_cap=0, stream=None):

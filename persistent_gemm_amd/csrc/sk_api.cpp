@@ -46,6 +46,8 @@ struct Workspace {
   size_t p_bytes = 0;
   uint8_t* S = nullptr;       // MXFP4 scales of A and B, k-step-major
   size_t s_bytes = 0;
+  uint8_t* T = nullptr;       // bf16 backward: transposed operands, dbias partial sums
+  size_t t_bytes = 0;
   uint32_t* flags = nullptr;  // kMaxGrid locks, then the error word
   uint32_t epoch = 0;         // last epoch used
 };
@@ -325,6 +327,19 @@ sk_status get_workspace(int dev, hipStream_t stream, size_t p_bytes, size_t s_by
   return SK_OK;
 }
 
+// The backward pass's buffer of (device, stream), grown to t_bytes; called
+// with g_mu unlocked.
+sk_status get_aux(int dev, hipStream_t stream, size_t t_bytes, uint8_t** out) {
+  Workspace* ws = nullptr;
+  sk_status st = get_workspace(dev, stream, 0, 0, &ws);
+  if (st != SK_OK) return st;
+  std::lock_guard<std::mutex> lk(g_mu);
+  st = grow(stream, &ws->T, &ws->t_bytes, t_bytes);
+  if (st != SK_OK) return st;
+  *out = ws->T;
+  return SK_OK;
+}
+
 // Next epoch of a workspace; restarts the flags when the counter would wrap.
 sk_status next_epoch(Workspace* ws, uint32_t* epoch) {
   std::lock_guard<std::mutex> lk(g_mu);
@@ -467,6 +482,57 @@ sk_status sk_addmm(sk_dtype dtype, const void* bias, const void* A, const void* 
   return run(base_args((int)dtype, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
 }
 
+sk_status sk_gemm_bf16_backward(const void* dC, const void* A, const void* B, void* dA, void* dB, void* dbias,
+                                int64_t M, int64_t N, int64_t K, int grid_cap, void* stream) {
+  if (!dC || (!dA && !dB && !dbias)) return SK_ERR_ARG;
+  if ((dA && !B) || (dB && !A)) return SK_ERR_ARG;
+  if (M < 1 || N < 1 || K < 1 || K > kMaxN) return SK_ERR_ARG;
+  if ((dA && (N > kMaxK || M >= kMaxM)) || (dB && (M > kMaxK || N >= kMaxM))) return SK_ERR_ARG;
+  if (M % 8 || N % 8 || K % 8) return SK_ERR_ALIGN;
+  if (((uintptr_t)dC | (uintptr_t)A | (uintptr_t)B | (uintptr_t)dA | (uintptr_t)dB) & 15) return SK_ERR_ALIGN;
+  if (dbias && ((uintptr_t)dbias & 1)) return SK_ERR_ALIGN;
+  const int64_t bc = M * N * 2, ba = M * K * 2, bb = N * K * 2;
+  for (const void* out : {(const void*)dA, (const void*)dB, (const void*)dbias}) {
+    const int64_t n = out == dA ? ba : (out == dB ? bb : N * 2);
+    if (out && (overlaps(out, n, dC, bc) || overlaps(out, n, A, ba) || overlaps(out, n, B, bb))) return SK_ERR_ARG;
+  }
+  if ((dA && dB && overlaps(dA, ba, dB, bb)) || (dA && dbias && overlaps(dA, ba, dbias, N * 2)) ||
+      (dB && dbias && overlaps(dB, bb, dbias, N * 2)))
+    return SK_ERR_ARG;
+  int dev = 0;
+  DeviceInfo info;
+  sk_status st = device_info(&dev, &info);
+  if (st != SK_OK) return st;
+  if (!info.gfx950) return SK_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  // transposed operands, each 256-byte aligned: B^T [K][N]; dC^T [N][M]; A^T [K][M]; dbias partials
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t at_bt = 0, at_dct = up(dA ? bb : 0), at_at = at_dct + up(dB ? bc : 0), at_part = at_at + up(dB ? ba : 0);
+  const int64_t total = at_part + (dbias ? sk::colsum_scratch_bytes((int)M, (int)N) : 0);
+  uint8_t* T = nullptr;
+  st = get_aux(dev, s, (size_t)total, &T);
+  if (st != SK_OK) return st;
+  if (dA) {
+    // dA[m][k] = sum_n dC[m][n] B[n][k]: A' = dC (K' = N contiguous), B' = B^T [K][N]
+    if (sk::launch_transpose_bf16((const uint16_t*)B, (uint16_t*)(T + at_bt), (int)N, (int)K, s) != hipSuccess)
+      return SK_ERR_HIP;
+    st = run(base_args(SK_BF16, dC, T + at_bt, nullptr, nullptr, nullptr, dA, M, K, N, grid_cap, stream));
+    if (st != SK_OK) return st;
+  }
+  if (dB) {
+    // dB[n][k] = sum_m dC[m][n] A[m][k]: A' = dC^T [N][M], B' = A^T [K][M] (K' = M)
+    if (sk::launch_transpose_bf16((const uint16_t*)dC, (uint16_t*)(T + at_dct), (int)M, (int)N, s) != hipSuccess ||
+        sk::launch_transpose_bf16((const uint16_t*)A, (uint16_t*)(T + at_at), (int)M, (int)K, s) != hipSuccess)
+      return SK_ERR_HIP;
+    st = run(base_args(SK_BF16, T + at_dct, T + at_at, nullptr, nullptr, nullptr, dB, N, K, M, grid_cap, stream));
+    if (st != SK_OK) return st;
+  }
+  if (dbias && sk::launch_colsum_bf16((const uint16_t*)dC, (float*)(T + at_part), (uint16_t*)dbias, (int)M, (int)N,
+                                      s) != hipSuccess)
+    return SK_ERR_HIP;
+  return SK_OK;
+}
+
 sk_status sk_gemm_ex(const sk_gemm_args* args) {
   if (!args) return SK_ERR_ARG;
   return run(*args);
@@ -548,6 +614,7 @@ void sk_release_workspace(void) {
     hipStreamSynchronize(ws->stream);
     if (ws->P) hipFree(ws->P);
     if (ws->S) hipFree(ws->S);
+    if (ws->T) hipFree(ws->T);
     if (ws->flags) hipFree(ws->flags);
     delete ws;
   }
@@ -619,6 +686,7 @@ sk_status sk_stream_destroy(void* stream) {
       if (ws) {
         if (ws->P) hipFree(ws->P);
         if (ws->S) hipFree(ws->S);
+        if (ws->T) hipFree(ws->T);
         if (ws->flags) hipFree(ws->flags);
         delete ws;
       }

@@ -169,6 +169,14 @@ const Variant* variant(int index);
 // k-step's block holds relayout_rows(rows, spr) rows (a whole number of
 // 16-byte pieces).  spr is 2, 4 or 8; dst must be 16-byte aligned.
 int relayout_rows(int rows, int spr);
+
+// bf16 backward helpers (sk_backward.hip).  dst[c][r] = src[r][c] for a
+// rows x cols bf16 matrix.
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int rows, int cols, hipStream_t s);
+// dbias[n] = bf16(sum over m of dC[m][n]), fp32 sums in a fixed order; `part`
+// holds colsum_scratch_bytes(M, N) bytes of device scratch.
+int64_t colsum_scratch_bytes(int M, int N);
+hipError_t launch_colsum_bf16(const uint16_t* dc, float* part, uint16_t* dbias, int M, int N, hipStream_t s);
 hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, int rows_a, const uint8_t* src_b, uint8_t* dst_b,
                                  int rows_b, int s_pitch, int ksteps, int spr, hipStream_t s);
 

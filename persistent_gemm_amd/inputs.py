@@ -25,7 +25,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs", "backward_inputs"]
 
 
 @dataclass(frozen=True)
@@ -40,10 +40,12 @@ class Workload:
     grid_cap: int = 0     # 0 = every CU
     tile: str | None = None
     caps: tuple = field(default_factory=tuple)
+    op: str = "forward"   # "forward" (C = A B^T + bias) or "backward" (dA, dB, dbias of it)
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        # the backward makes two products of the forward's size
+        return (4 if self.op == "backward" else 2) * self.M * self.N * self.K
 
 
 # The synthetic workloads; the seed of each is fixed so that tests,
@@ -58,6 +60,9 @@ WORKLOADS = {
         "fp8_gemm_4096_capsweep", "fp8", 4096, 4096, 4096, False, 1004, caps=(1, 32, 64, 128, 256)),
     # MXFP8 (E4M3 elements, E8M0 block scales) at the large square shape
     "mxfp8_addmm_8192": Workload("mxfp8_addmm_8192", "mxfp8", 8192, 8192, 8192, True, 1005),
+    # the bf16 addmm's backward (dA, dB, dbias) at the bf16 forward's shape
+    "bf16_addmm_backward_4096": Workload("bf16_addmm_backward_4096", "bf16", 4096, 4096, 4096, True, 1006,
+                                         op="backward"),
 }
 
 
@@ -150,3 +155,20 @@ def integer_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
         raise ValueError("integer_inputs covers bf16, fp8 and mxfp8")
     out["bias"] = _bf16_bits(torch.randint(-64, 65, (N,), generator=g).float()) if bias else None
     return out
+
+
+
+def backward_inputs(M: int, N: int, K: int, *, seed: int, integer: bool = False) -> dict:
+    """dC uint16[M][N], A uint16[M][K], B uint16[N][K] (bf16 bit patterns), drawn in that order:
+    N(0, 1) rounded to bf16, or integers in [-8, 8] with integer=True (every sum then exact)."""
+    g = torch.Generator().manual_seed(seed)
+
+    def draw(r, c):
+        if integer:
+            return _bf16_bits(torch.randint(-8, 9, (r, c), generator=g).float())
+        return _bf16_bits(torch.randn(r, c, generator=g))
+
+    dC = draw(M, N)
+    A = draw(M, K)
+    B = draw(N, K)
+    return {"M": M, "N": N, "K": K, "dC": dC, "A": A, "B": B}

@@ -125,3 +125,14 @@ def gemm(dtype: str, A, B, SA, SB, bias, M: int, N: int, K: int):
                 d += bf16(int(bias[n]))
             out[m][n] = round_bf16(d)
     return out
+
+
+def bf16_backward(dC, A, B, M: int, N: int, K: int):
+    """Bits of dA = dC B, dB = dC^T A and dbias = column sums of dC, all exact then rounded once."""
+    g = [[bf16(int(dC[m][n])) for n in range(N)] for m in range(M)]
+    a = [[bf16(int(A[m][k])) for k in range(K)] for m in range(M)]
+    b = [[bf16(int(B[n][k])) for k in range(K)] for n in range(N)]
+    dA = [[round_bf16(sum((g[m][n] * b[n][k] for n in range(N)), Fraction(0))) for k in range(K)] for m in range(M)]
+    dB = [[round_bf16(sum((g[m][n] * a[m][k] for m in range(M)), Fraction(0))) for k in range(K)] for n in range(N)]
+    db = [round_bf16(sum((g[m][n] for m in range(M)), Fraction(0))) for n in range(N)]
+    return dA, dB, db

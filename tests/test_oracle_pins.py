@@ -22,7 +22,7 @@ import torch
 
 import bruteforce as bf
 import oracle
-from persistent_gemm_amd.inputs import integer_inputs, make_inputs
+from persistent_gemm_amd.inputs import backward_inputs, integer_inputs, make_inputs
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -399,6 +399,51 @@ def pin_invariants_mxfp8():
     assert np.array_equal(C6, C.T)
 
 
+def pin_bruteforce_bf16_backward():
+    for seed, (M, N, K) in enumerate([(1, 1, 1), (2, 3, 4), (3, 3, 3), (4, 2, 5)]):
+        x = backward_inputs(M, N, K, seed=500 + seed)
+        o = oracle.bf16_backward(x["dC"], x["A"], x["B"])
+        dA, dB, db = bf.bf16_backward(x["dC"], x["A"], x["B"], M, N, K)
+        assert np.array_equal(o["dA"][0], np.array(dA, np.uint16)), (M, N, K)
+        assert np.array_equal(o["dB"][0], np.array(dB, np.uint16)), (M, N, K)
+        assert np.array_equal(o["dbias"][0], np.array(db, np.uint16)), (M, N, K)
+
+
+def pin_bf16_backward_vs_autograd():
+    """torch's own autograd of addmm (fp64, on the CPU) gives the same gradients:
+    bit for bit on integer inputs, to fp64 rounding on random ones."""
+    for integer, (M, N, K) in [(True, (6, 5, 7)), (True, (8, 8, 8)), (False, (9, 4, 6))]:
+        x = backward_inputs(M, N, K, seed=600 + M, integer=integer)
+        a = torch.from_numpy(oracle.decode_bf16(x["A"])).requires_grad_()
+        b = torch.from_numpy(oracle.decode_bf16(x["B"])).requires_grad_()
+        bias = torch.zeros(N, dtype=torch.float64, requires_grad=True)
+        g = torch.from_numpy(oracle.decode_bf16(x["dC"]))
+        torch.addmm(bias, a, b.t()).backward(g)
+        o = oracle.bf16_backward(x["dC"], x["A"], x["B"])
+        for name, ref in (("dA", a.grad), ("dB", b.grad), ("dbias", bias.grad)):
+            got = o[name][1]
+            if integer:
+                assert np.array_equal(got, ref.numpy()), name
+            else:
+                assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12), name
+
+
+def pin_bf16_backward_identities():
+    x = backward_inputs(8, 8, 8, seed=700, integer=True)
+    o = oracle.bf16_backward(x["dC"], x["A"], x["B"])
+    g, a, b = (oracle.decode_bf16(x[k]) for k in ("dC", "A", "B"))
+    # adjoint identity: <dC, A B^T> = <dA, A> = <dB, B> (exact on integers)
+    lhs = float((g * (a @ b.T)).sum())
+    assert lhs == float((o["dA"][1] * a).sum()) == float((o["dB"][1] * b).sum())
+    # B = I gives dA = dC; A = I gives dB = dC^T; dbias is the column sum
+    eye = np.eye(8, dtype=np.float32).view(np.uint32) >> 16
+    eye = eye.astype(np.uint16)
+    assert np.array_equal(oracle.bf16_backward(x["dC"], None, eye)["dA"][0], x["dC"])
+    assert np.array_equal(oracle.bf16_backward(x["dC"], eye, None)["dB"][0], x["dC"].T)
+    ones = np.full((8, 1), 0x3F80, np.uint16)                       # bf16 1.0
+    assert np.array_equal(oracle.bf16_backward(x["dC"], ones, None)["dB"][0][:, 0], o["dbias"][0])
+
+
 def pin_accept():
     x = make_inputs("bf16", 16, 24, 256, bias=True, seed=14)
     C, D = oracle.gemm("bf16", x["A"], x["B"], None, None, x["bias"])
@@ -425,6 +470,7 @@ PINS = [
     pin_rne_vs_rational, pin_bruteforce_mxfp4, pin_bruteforce_bf16, pin_bruteforce_fp8,
     pin_bruteforce_mxfp8, pin_handworked_mxfp4, pin_handworked_mxfp8, pin_identity, pin_bias_broadcast,
     pin_integer_matmul, pin_invariants_mxfp4, pin_invariants_mxfp8, pin_accept,
+    pin_bruteforce_bf16_backward, pin_bf16_backward_vs_autograd, pin_bf16_backward_identities,
 ]
 
 
@@ -530,10 +576,38 @@ def _mut_mxfp8_scale_per_16(mp):
     mp.setattr(oracle, "mxfp8_operand", op)
 
 
+def _mut_backward_transposed_b(mp):
+    # dA taken with B transposed (only shape-consistent when N == K)
+    real = oracle.bf16_backward
+
+    def bwd(dC, A, B):
+        out = real(dC, A, B)
+        if B is not None and np.asarray(B).shape[0] == np.asarray(B).shape[1]:
+            g, b = oracle.decode_bf16(dC), oracle.decode_bf16(B)
+            D = g @ b.T
+            out["dA"] = (oracle.rne_bf16_from_double(D), D, out["dA"][2])
+        return out
+    mp.setattr(oracle, "bf16_backward", bwd)
+
+
+def _mut_backward_dbias_rows(mp):
+    real = oracle.bf16_backward
+
+    def bwd(dC, A, B):
+        out = real(dC, A, B)
+        g = oracle.decode_bf16(dC)
+        if g.shape[0] == g.shape[1]:
+            D = g.sum(axis=1)
+            out["dbias"] = (oracle.rne_bf16_from_double(D), D, out["dbias"][2])
+        return out
+    mp.setattr(oracle, "bf16_backward", bwd)
+
+
 MUTATIONS = [
     _mut_e2m1_entry, _mut_nibble_order, _mut_scale_block, _mut_drop_bias, _mut_double_bias,
     _mut_round_via_float, _mut_round_truncate, _mut_e4m3_bias, _mut_fp8_sigma, _mut_transpose_b,
-    _mut_bf16_decode, _mut_mxfp8_no_scales, _mut_mxfp8_scale_per_16,
+    _mut_bf16_decode, _mut_mxfp8_no_scales, _mut_mxfp8_scale_per_16, _mut_backward_transposed_b,
+    _mut_backward_dbias_rows,
 ]
 
 
