@@ -139,6 +139,20 @@ sk_status sk_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* A_scale, 
 sk_status sk_gemm_mxfp8(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
                         const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
 
+/* Block-scaled operands of either element width: a_fmt and b_fmt are SK_MXFP4
+ * or SK_MXFP8 (A and B laid out as for that type, scales E8M0 [rows][K/32],
+ * required; bias may be NULL).  The mixed products are among the other MX
+ * formats of the quantized mode ("Fix StreamK Kernel Bias #67", Technical
+ * Details; MX formats of "Stream-k mxfp4 kernel", description).  Equal formats
+ * are sk_gemm_mxfp4 / sk_gemm_mxfp8.  For mixed formats the E2M1 operand is
+ * first widened to E4M3 bytes in the library's scratch of (device, stream):
+ * every E2M1 value is an E4M3 value, so the result is the same exact
+ * contraction, computed by the MXFP8 kernels.  Errors as for those entry
+ * points; SK_ERR_ARG also for a format that is not MX. */
+sk_status sk_gemm_mx(sk_dtype a_fmt, sk_dtype b_fmt, const uint8_t* A, const uint8_t* B, const uint8_t* A_scale,
+                     const uint8_t* B_scale, const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap,
+                     void* stream);
+
 /* addmm(bias, A, B) = the dtype's GEMM with a bias that is required (alpha = beta = 1).
  * A_scale / B_scale as for that dtype (NULL for bf16). */
 sk_status sk_addmm(sk_dtype dtype, const void* bias, const void* A, const void* B, const void* A_scale,

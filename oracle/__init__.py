@@ -68,6 +68,7 @@ __all__ = [
     "abs_product_sums",
     "accept",
     "bf16_backward",
+    "gemm_mx",
 ]
 
 # OCP MX v1.0, FP4 (E2M1): code bits are sign | exponent(2, bias 1) | mantissa(1).
@@ -314,3 +315,21 @@ def bf16_backward(dC, A, B):
     D = g.sum(axis=0)
     out["dbias"] = (rne_bf16_from_double(D), D, np.abs(g).sum(axis=0))
     return out
+
+
+def gemm_mx(a_fmt: str, b_fmt: str, A, B, SA, SB, bias=None, K: int | None = None):
+    """Block-scaled operands of either element width ("mxfp4" or "mxfp8" each):
+    the same plain contraction as gemm(), each operand decoded by its own format.
+    Returns (C uint16[M][N] bf16 bits, D float64[M][N])."""
+    def decode(fmt, X, S, k):
+        if fmt == "mxfp4":
+            return mxfp4_operand(X, S, k)
+        if fmt == "mxfp8":
+            return mxfp8_operand(X, S, k)
+        raise ValueError(f"not an MX format: {fmt!r}")
+    if K is None:
+        K = 2 * np.asarray(A).shape[1] if a_fmt == "mxfp4" else np.asarray(A).shape[1]
+    a = decode(a_fmt, A, SA, K)
+    b = decode(b_fmt, B, SB, K)
+    D = a @ b.T + _beta(bias, b.shape[0])[None, :]
+    return rne_bf16_from_double(D), D

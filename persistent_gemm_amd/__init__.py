@@ -22,7 +22,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
-    "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_bf16_backward", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
+    "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_bf16_backward", "gemm_mx", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
     "cu_masked_stream", "destroy_stream", "stream_cu_count",
 ]
@@ -128,6 +128,7 @@ def load():
     lib.sk_gemm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_bf16_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.sk_gemm_mx.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_addmm.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_ex.argtypes = [ctypes.POINTER(_Args)]
     lib.sk_plan.argtypes = [ctypes.POINTER(_PlanQuery), ctypes.POINTER(_PlanInfo)]
@@ -147,7 +148,7 @@ def load():
     lib.sk_stream_cu_count.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sk_status_string.argtypes = [ctypes.c_int]
     lib.sk_status_string.restype = ctypes.c_char_p
-    for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_bf16_backward", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
+    for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_bf16_backward", "sk_gemm_mx", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
                  "sk_plan_wg_range", "sk_plan_wg_work", "sk_check", "sk_debug_poison_workspace", "sk_variant_info",
                  "sk_stream_create_cu_masked", "sk_stream_destroy", "sk_stream_cu_count"):
         getattr(lib, name).restype = ctypes.c_int
@@ -269,6 +270,33 @@ def gemm_bf16(A, B, bias=None, C=None, grid_cap=0, stream=None):
     M, N, K, C = _marshal(BF16, A, B, None, None, bias, C)
     _ok(load().sk_gemm_bf16(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K, int(grid_cap), _stream(A, stream)),
         "sk_gemm_bf16")
+    return C
+
+
+def gemm_mx(a_fmt, b_fmt, A, B, A_scale, B_scale, bias=None, C=None, grid_cap=0, stream=None):
+    """C = A . B^T (+ bias) for block-scaled operands of either width: a_fmt, b_fmt in ("mxfp4", "mxfp8").
+
+    A MXFP4 operand is uint8 [rows, K/2] (packed E2M1), a MXFP8 one E4M3 [rows, K]; scales uint8 [rows, K/32]."""
+    torch = _torch()
+    fa, fb = _dt(a_fmt), _dt(b_fmt)
+    if fa not in (MXFP4, MXFP8) or fb not in (MXFP4, MXFP8):
+        raise ValueError("gemm_mx takes mxfp4 or mxfp8 operands")
+    dev = A.device
+    M = A.shape[0]
+    N = B.shape[0]
+    K = 2 * A.shape[1] if fa == MXFP4 else A.shape[1]
+    for t, nm, f, rows in ((A, "A", fa, M), (B, "B", fb, N)):
+        if f == MXFP4:
+            _need(t, nm, (torch.uint8,), (rows, K // 2), dev)
+        else:
+            _need(t, nm, (torch.float8_e4m3fn, torch.uint8), (rows, K), dev)
+    _need(A_scale, "A_scale", (torch.uint8,), (M, K // 32), dev)
+    _need(B_scale, "B_scale", (torch.uint8,), (N, K // 32), dev)
+    if bias is not None:
+        _need(bias, "bias", (torch.bfloat16, torch.int16, torch.uint16), (N,), dev)
+    C = _out(C, M, N, dev)
+    _ok(load().sk_gemm_mx(fa, fb, _ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale), _ptr(bias), _ptr(C), M, N, K,
+                          int(grid_cap), _stream(A, stream)), "sk_gemm_mx")
     return C
 
 

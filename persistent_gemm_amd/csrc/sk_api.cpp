@@ -533,6 +533,36 @@ sk_status sk_gemm_bf16_backward(const void* dC, const void* A, const void* B, vo
   return SK_OK;
 }
 
+sk_status sk_gemm_mx(sk_dtype a_fmt, sk_dtype b_fmt, const uint8_t* A, const uint8_t* B, const uint8_t* A_scale,
+                     const uint8_t* B_scale, const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap,
+                     void* stream) {
+  if (!is_mx(a_fmt) || !is_mx(b_fmt)) return SK_ERR_ARG;
+  if (a_fmt == b_fmt) return run(base_args(a_fmt, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
+  // One operand E2M1, the other E4M3: the E2M1 one is widened to E4M3 bytes
+  // (exact) in scratch and the MXFP8 kernels run.  The scaled MFMA runs at the
+  // E4M3 rate whenever either operand is E4M3, so only the widening pass is
+  // added.
+  if (!A || !B || !C || !A_scale || !B_scale) return SK_ERR_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxM || N > kMaxN || K > kMaxK) return SK_ERR_ARG;
+  if (K % 32) return SK_ERR_ALIGN;
+  if (((uintptr_t)A | (uintptr_t)B) & 15) return SK_ERR_ALIGN;
+  const bool a4 = a_fmt == SK_MXFP4;
+  const int64_t rows4 = a4 ? M : N;
+  const uint8_t* src4 = a4 ? A : B;
+  if (overlaps(C, M * N * 2, src4, rows4 * (K / 2))) return SK_ERR_ARG;
+  int dev = 0;
+  DeviceInfo info;
+  sk_status st = device_info(&dev, &info);
+  if (st != SK_OK) return st;
+  if (!info.gfx950) return SK_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* wide = nullptr;
+  st = get_aux(dev, s, (size_t)(rows4 * K), &wide);
+  if (st != SK_OK) return st;
+  if (sk::launch_widen_e2m1(src4, wide, rows4 * (K / 2), s) != hipSuccess) return SK_ERR_HIP;
+  return run(base_args(SK_MXFP8, a4 ? wide : A, a4 ? B : wide, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
+}
+
 sk_status sk_gemm_ex(const sk_gemm_args* args) {
   if (!args) return SK_ERR_ARG;
   return run(*args);

@@ -170,6 +170,10 @@ const Variant* variant(int index);
 // 16-byte pieces).  spr is 2, 4 or 8; dst must be 16-byte aligned.
 int relayout_rows(int rows, int spr);
 
+// dst[r][k] (E4M3 bytes) = the E2M1 codes of src (packed, even k in the low
+// nibble), for `bytes` source bytes (a multiple of 16; 16-byte aligned).
+hipError_t launch_widen_e2m1(const uint8_t* src, uint8_t* dst, int64_t bytes, hipStream_t s);
+
 // bf16 backward helpers (sk_backward.hip).  dst[c][r] = src[r][c] for a
 // rows x cols bf16 matrix.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int rows, int cols, hipStream_t s);

@@ -1,0 +1,69 @@
+// Widening of a packed MXFP4 operand to MXFP8 elements, so that a product of
+// one MXFP4 and one MXFP8 operand runs on the MXFP8 kernels: every E2M1 value
+// (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) is exactly an E4M3FN value,
+// and the E8M0 block scales stay as they are.  Bound by HBM.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sk_common.h"
+
+namespace sk {
+
+namespace {
+
+// E4M3FN byte of each E2M1 code (sign bit 7; exponent bias 7, three mantissa
+// bits): 0.5 = 2^-1 -> 0x30, 1 -> 0x38, 1.5 -> 0x3C, 2 -> 0x40, 3 -> 0x44,
+// 4 -> 0x48, 6 -> 0x4C; code 8 (-0) -> 0x80.
+__device__ __forceinline__ uint32_t e2m1_to_e4m3(uint32_t code) {
+  const uint32_t mag = code & 7u, sign = (code & 8u) << 4;
+  // magnitudes 1..7: exponent field 6 + (mag >> 1) for mag >= 2 (E2M1 field
+  // e is worth 2^(e-1), E4M3 field f is worth 2^(f-7)), 6 for mag 1 (0.5);
+  // mantissa bit 2 from the E2M1 mantissa bit (mag & 1) when mag >= 2
+  uint32_t e;
+  if (mag == 0u) e = 0u;
+  else if (mag == 1u) e = 0x30u;
+  else e = ((6u + (mag >> 1)) << 3) | ((mag & 1u) << 2);
+  return sign | e;
+}
+
+typedef uint32_t v4w __attribute__((ext_vector_type(4)));
+
+// dst[r][k] = E4M3 byte of the E2M1 code at src[r][k / 2] (even k in the low
+// nibble).  Each thread widens 16 source bytes (32 codes) into 32 bytes.
+__global__ __launch_bounds__(256) void sk_widen_e2m1(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                      int64_t pieces) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  const v4w x = *(const v4w*)(src + i * 16);
+  v4w y[2];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (x[w] >> (8 * b)) & 0xffu;
+      const uint32_t pair = e2m1_to_e4m3(byte & 15u) | (e2m1_to_e4m3(byte >> 4) << 8);
+      if (b < 2) lo |= pair << (16 * b);
+      else hi |= pair << (16 * (b - 2));
+    }
+    y[w / 2][2 * (w % 2)] = lo;
+    y[w / 2][2 * (w % 2) + 1] = hi;
+  }
+  v4w* q = (v4w*)(dst + i * 32);
+  q[0] = y[0];
+  q[1] = y[1];
+}
+
+}  // namespace
+
+hipError_t launch_widen_e2m1(const uint8_t* src, uint8_t* dst, int64_t bytes, hipStream_t s) {
+  if (bytes % 16 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return hipErrorInvalidValue;
+  const int64_t pieces = bytes / 16;
+  if (pieces == 0) return hipSuccess;
+  hipLaunchKernelGGL(sk_widen_e2m1, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, src, dst, pieces);
+  return hipGetLastError();
+}
+
+}  // namespace sk

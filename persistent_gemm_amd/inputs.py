@@ -25,7 +25,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs", "backward_inputs"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs", "backward_inputs", "mixed_inputs"]
 
 
 @dataclass(frozen=True)
@@ -60,6 +60,8 @@ WORKLOADS = {
         "fp8_gemm_4096_capsweep", "fp8", 4096, 4096, 4096, False, 1004, caps=(1, 32, 64, 128, 256)),
     # MXFP8 (E4M3 elements, E8M0 block scales) at the large square shape
     "mxfp8_addmm_8192": Workload("mxfp8_addmm_8192", "mxfp8", 8192, 8192, 8192, True, 1005),
+    # one MXFP4 and one MXFP8 operand (A E2M1, B E4M3), at the large square shape
+    "mxfp4_mxfp8_addmm_8192": Workload("mxfp4_mxfp8_addmm_8192", "mxfp4_mxfp8", 8192, 8192, 8192, True, 1007),
     # the bf16 addmm's backward (dA, dB, dbias) at the bf16 forward's shape
     "bf16_addmm_backward_4096": Workload("bf16_addmm_backward_4096", "bf16", 4096, 4096, 4096, True, 1006,
                                          op="backward"),
@@ -172,3 +174,34 @@ def backward_inputs(M: int, N: int, K: int, *, seed: int, integer: bool = False)
     A = draw(M, K)
     B = draw(N, K)
     return {"M": M, "N": N, "K": K, "dC": dC, "A": A, "B": B}
+
+
+def mixed_inputs(a_fmt: str, b_fmt: str, M: int, N: int, K: int, *, bias: bool, seed: int,
+                 integer_fp8: bool = False) -> dict:
+    """Block-scaled operands of formats a_fmt / b_fmt ("mxfp4" or "mxfp8"), drawn in the order
+    A, SA, B, SB, bias as make_inputs does.  MXFP4 codes are uniform over all 16; MXFP8
+    elements are N(0, 1) in E4M3FN, or integers in [-8, 8] with integer_fp8=True, whose
+    block scales are then uniform on {126, 127, 128} (every sum then stays exact)."""
+    if K % 32:
+        raise ValueError("MX formats need K % 32 == 0")
+    g = torch.Generator().manual_seed(seed)
+    out = {"a_fmt": a_fmt, "b_fmt": b_fmt, "M": M, "N": N, "K": K}
+
+    def operand(fmt, rows):
+        if fmt == "mxfp4":
+            codes = torch.randint(0, 16, (rows, K), generator=g, dtype=torch.uint8)
+            x = (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous().numpy()
+            s = torch.randint(125, 130, (rows, K // 32), generator=g, dtype=torch.uint8).numpy()
+        elif integer_fp8:
+            x = torch.randint(-8, 9, (rows, K), generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            s = torch.randint(126, 129, (rows, K // 32), generator=g, dtype=torch.uint8).numpy()
+        else:
+            x = torch.randn(rows, K, generator=g).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+            x = x.view(torch.uint8).numpy()
+            s = torch.randint(125, 130, (rows, K // 32), generator=g, dtype=torch.uint8).numpy()
+        return x, s
+
+    out["A"], out["SA"] = operand(a_fmt, M)
+    out["B"], out["SB"] = operand(b_fmt, N)
+    out["bias"] = _bf16_bits(torch.randn(N, generator=g)) if bias else None
+    return out

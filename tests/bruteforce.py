@@ -136,3 +136,22 @@ def bf16_backward(dC, A, B, M: int, N: int, K: int):
     dB = [[round_bf16(sum((g[m][n] * a[m][k] for m in range(M)), Fraction(0))) for k in range(K)] for n in range(N)]
     db = [round_bf16(sum((g[m][n] for m in range(M)), Fraction(0))) for n in range(N)]
     return dA, dB, db
+
+
+def gemm_mx(a_fmt: str, b_fmt: str, A, B, SA, SB, bias, M: int, N: int, K: int):
+    """C bits for operands of formats a_fmt / b_fmt ("mxfp4" or "mxfp8"), all exact."""
+    def val(fmt, X, S, r, k):
+        if fmt == "mxfp4":
+            byte = int(X[r][k // 2])
+            code = (byte >> 4) if (k & 1) else (byte & 0xF)
+            return e2m1(code) * e8m0(int(S[r][k // 32]))
+        return e4m3fn(int(X[r][k])) * e8m0(int(S[r][k // 32]))
+
+    out = [[0] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            d = sum((val(a_fmt, A, SA, m, k) * val(b_fmt, B, SB, n, k) for k in range(K)), Fraction(0))
+            if bias is not None:
+                d += bf16(int(bias[n]))
+            out[m][n] = round_bf16(d)
+    return out

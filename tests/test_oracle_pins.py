@@ -22,7 +22,7 @@ import torch
 
 import bruteforce as bf
 import oracle
-from persistent_gemm_amd.inputs import backward_inputs, integer_inputs, make_inputs
+from persistent_gemm_amd.inputs import backward_inputs, integer_inputs, make_inputs, mixed_inputs
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -444,6 +444,34 @@ def pin_bf16_backward_identities():
     assert np.array_equal(oracle.bf16_backward(x["dC"], ones, None)["dB"][0][:, 0], o["dbias"][0])
 
 
+def pin_bruteforce_mixed_mx():
+    for a_fmt, b_fmt in (("mxfp4", "mxfp8"), ("mxfp8", "mxfp4")):
+        for seed, (M, N, K) in enumerate([(1, 1, 32), (2, 3, 64), (3, 2, 32)]):
+            for bias in (False, True):
+                x = mixed_inputs(a_fmt, b_fmt, M, N, K, bias=bias, seed=800 + seed)
+                C, _ = oracle.gemm_mx(a_fmt, b_fmt, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=K)
+                want = bf.gemm_mx(a_fmt, b_fmt, x["A"], x["B"], x["SA"], x["SB"], x["bias"], M, N, K)
+                assert np.array_equal(C, np.array(want, np.uint16)), (a_fmt, b_fmt, M, N, K, bias)
+
+
+def pin_mixed_mx_reduces_to_mxfp4():
+    """B given as torch's own E4M3 encodings of E2M1 values: the mixed product equals
+    the MXFP4 product of the same codes, and equal formats reduce to gemm()."""
+    M, N, K = 5, 6, 96
+    x = make_inputs("mxfp4", M, N, K, bias=True, seed=16)
+    C4, D4 = oracle.gemm("mxfp4", x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=K)
+    bvals = oracle.decode_e2m1(oracle.unpack_fp4(x["B"], K))
+    B8 = torch.from_numpy(bvals).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    Cm, Dm = oracle.gemm_mx("mxfp4", "mxfp8", x["A"], B8, x["SA"], x["SB"], x["bias"], K=K)
+    assert np.array_equal(Cm, C4) and np.array_equal(Dm, D4)
+    avals = oracle.decode_e2m1(oracle.unpack_fp4(x["A"], K))
+    A8 = torch.from_numpy(avals).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    Cr, _ = oracle.gemm_mx("mxfp8", "mxfp4", A8, x["B"], x["SA"], x["SB"], x["bias"], K=K)
+    assert np.array_equal(Cr, C4)
+    Ce, _ = oracle.gemm_mx("mxfp4", "mxfp4", x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=K)
+    assert np.array_equal(Ce, C4)
+
+
 def pin_accept():
     x = make_inputs("bf16", 16, 24, 256, bias=True, seed=14)
     C, D = oracle.gemm("bf16", x["A"], x["B"], None, None, x["bias"])
@@ -471,6 +499,7 @@ PINS = [
     pin_bruteforce_mxfp8, pin_handworked_mxfp4, pin_handworked_mxfp8, pin_identity, pin_bias_broadcast,
     pin_integer_matmul, pin_invariants_mxfp4, pin_invariants_mxfp8, pin_accept,
     pin_bruteforce_bf16_backward, pin_bf16_backward_vs_autograd, pin_bf16_backward_identities,
+    pin_bruteforce_mixed_mx, pin_mixed_mx_reduces_to_mxfp4,
 ]
 
 
@@ -603,11 +632,21 @@ def _mut_backward_dbias_rows(mp):
     mp.setattr(oracle, "bf16_backward", bwd)
 
 
+def _mut_mixed_b_scales_ignored(mp):
+    real = oracle.gemm_mx
+
+    def gm(a_fmt, b_fmt, A, B, SA, SB, bias=None, K=None):
+        if a_fmt != b_fmt:
+            SB = np.full_like(np.asarray(SB), 127)
+        return real(a_fmt, b_fmt, A, B, SA, SB, bias, K)
+    mp.setattr(oracle, "gemm_mx", gm)
+
+
 MUTATIONS = [
     _mut_e2m1_entry, _mut_nibble_order, _mut_scale_block, _mut_drop_bias, _mut_double_bias,
     _mut_round_via_float, _mut_round_truncate, _mut_e4m3_bias, _mut_fp8_sigma, _mut_transpose_b,
     _mut_bf16_decode, _mut_mxfp8_no_scales, _mut_mxfp8_scale_per_16, _mut_backward_transposed_b,
-    _mut_backward_dbias_rows,
+    _mut_backward_dbias_rows, _mut_mixed_b_scales_ignored,
 ]
 
 
