@@ -367,24 +367,25 @@ sk_status run(const sk_gemm_args& g) {
   if (st != SK_OK) return st;
   hipStream_t stream = (hipStream_t)g.stream;
   const Variant* v = sk::variant(p.variant);
-  // MX scales are read from a k-step-major copy: one k-step's scales of a
-  // tile are then one contiguous block (row-major scales would put each row's
-  // 2 to 8 bytes in a different cache line).  Every offset into the copy must
-  // fit in 32 bits.  A k-step holds kb bytes of a row: 2 * kb FP4 or kb FP8
-  // elements, so kb / 16 or kb / 32 scale bytes.
+  // MX scales are read from a k-step-major copy in the kernel's lane order:
+  // one k-step's scales of a tile are one contiguous block (row-major scales
+  // would put each row's 2 to 8 bytes in a different cache line), and each
+  // lane finds the bytes of all its MFMA blocks together.  The copy holds
+  // whole tiles.  Every offset into it must fit in 32 bits.  A k-step holds
+  // kb bytes of a row: 2 * kb FP4 or kb FP8 elements, so kb / 16 or kb / 32
+  // scale bytes.
   const int64_t spr = g.dtype == SK_MXFP4 ? v->kb / 16 : v->kb / 32, ksteps = p.iters_per_tile;
   int64_t sa_bytes = 0, sb_bytes = 0, rows_a = 0, rows_b = 0;
   if (is_mx(g.dtype)) {
-    rows_a = sk::relayout_rows((int)g.M, (int)spr);
-    rows_b = sk::relayout_rows((int)g.N, (int)spr);
+    rows_a = cdiv(g.M, v->bm) * v->bm;
+    rows_b = cdiv(g.N, v->bn) * v->bn;
     sa_bytes = ksteps * rows_a * spr;
     sb_bytes = ksteps * rows_b * spr;
     if (sa_bytes >= ((int64_t)1 << 31) || sb_bytes >= ((int64_t)1 << 31)) return SK_ERR_ARG;
   }
   const int64_t sb_at = (sa_bytes + 255) / 256 * 256;
   Workspace* ws = nullptr;
-  // (16 bytes of slack: a tile's last scale dword may reach 2 bytes past B's copy)
-  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, is_mx(g.dtype) ? (size_t)(sb_at + sb_bytes + 16) : 0, &ws);
+  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, is_mx(g.dtype) ? (size_t)(sb_at + sb_bytes) : 0, &ws);
   if (st != SK_OK) return st;
   uint32_t epoch = 0;
   st = next_epoch(ws, &epoch);
@@ -395,8 +396,10 @@ sk_status run(const sk_gemm_args& g) {
   a.A = (const uint8_t*)g.A;
   a.B = (const uint8_t*)g.B;
   if (is_mx(g.dtype)) {
-    if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, ws->S, (int)g.M, (const uint8_t*)g.B_scale, ws->S + sb_at,
-                                  (int)g.N, (int)(g.K / 32), (int)ksteps, (int)spr, stream) != hipSuccess)
+    const sk::ScaleLayout la{(int)g.M, v->bm, v->mfma, v->ng, v->bm / v->wm / v->mfma, v->nu};
+    const sk::ScaleLayout lb{(int)g.N, v->bn, v->mfma, v->ng, v->bn / v->wn / v->mfma, v->nu};
+    if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, ws->S, la, (const uint8_t*)g.B_scale, ws->S + sb_at, lb,
+                                  (int)(g.K / 32), (int)ksteps, (int)spr, stream) != hipSuccess)
       return SK_ERR_HIP;
     a.SA = ws->S;
     a.SB = ws->S + sb_at;

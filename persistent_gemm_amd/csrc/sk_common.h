@@ -157,18 +157,29 @@ struct Variant {
   int mfma;         // 32 (32x32 MFMA) or 16 (16x16 MFMA)
   int threads;
   int lds;
+  int wm, wn;       // waves along M and N
+  int ng, nu;       // MFMA lane groups, MFMAs per block per k-step
   hipError_t (*launch)(int grid, const KArgs& a, hipStream_t s);
 };
 
 int num_variants();
 const Variant* variant(int index);
 
+// How one operand's MX scales are laid out for the kernel: tiles of
+// tile_rows rows, each k-step's block in the MFMA lane order given by the
+// block rows (mf), lane groups (ng), blocks per wave (nblk) and MFMAs per
+// block per k-step (nu); ng * nu is the scale bytes per row per k-step.
+struct ScaleLayout {
+  int rows, tile_rows, mf, ng, nblk, nu;
+};
+
 // Copies the MX scales of A and of B ([rows][s_pitch] each) into the
-// k-step-major layout the GEMM reads, in one launch:
-// dst[ks][r][0..spr) = src[r][ks*spr ...], padded with 127 (x1), where a
-// k-step's block holds relayout_rows(rows, spr) rows (a whole number of
-// 16-byte pieces).  spr is 2, 4 or 8; dst must be 16-byte aligned.
-int relayout_rows(int rows, int spr);
+// k-step-major, lane-ordered copies the kernel reads, in one launch; each
+// copy holds whole tiles (rows rounded up to tile_rows).  spr is 2, 4 or 8;
+// dst must be 16-byte aligned.
+hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, const ScaleLayout& la, const uint8_t* src_b,
+                                 uint8_t* dst_b, const ScaleLayout& lb, int s_pitch, int ksteps, int spr,
+                                 hipStream_t s);
 
 // dst[r][k] (E4M3 bytes) = the E2M1 codes of src (packed, even k in the low
 // nibble), for `bytes` source bytes (a multiple of 16; 16-byte aligned).

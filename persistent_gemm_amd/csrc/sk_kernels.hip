@@ -138,6 +138,10 @@ struct Cfg {
   static constexpr int SPR = DT == DT_MXFP4 ? KB / 16 : (DT == DT_MXFP8 ? KB / 32 : 0);  // scale bytes per row per k-step
   static constexpr int BK = DT == DT_MXFP4 ? 2 * KB : (DT == DT_BF16 ? KB / 2 : KB);
   static constexpr int ACC = MF == 32 ? 16 : 4;        // fp32 accumulators per block per lane
+  // MX scale bytes a lane reads per k-step: its lane group's NU bytes of each
+  // of its FM (FN) blocks, stored contiguously by the scale pre-pass
+  static constexpr int NSA = MX ? FM * NU : 1, NSB = MX ? FN * NU : 1;
+  static constexpr int SWA = (NSA + 3) / 4, SWB = (NSB + 3) / 4;   // 32-bit words holding them
 
   // LDS image of one operand k-slice: rows of KB bytes, one after another.  The
   // 16-byte chunks of row r are stored permuted: slot p holds chunk p ^ swz(r),
@@ -182,6 +186,7 @@ struct Cfg {
   static_assert(BM % RG == 0 && BN % RG == 0, "row groups tile the operands");
   static_assert(MF % 16 == 0, "MFMA blocks cover whole 16-row swizzle periods");
   static_assert(!MX || SPR == 2 || SPR == 4 || SPR == 8, "scale bytes per row per k-step");
+  static_assert(NSA <= 16 && NSB <= 16 && (NSA & (NSA - 1)) == 0 && (NSB & (NSB - 1)) == 0, "packed scale reads");
   static_assert(STAGES >= 2 && STAGES <= 8, "pipeline depth");
   static_assert((STAGES - 2) * LOADS_PER_STAGE_S <= 63, "vmcnt range");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS");
@@ -207,7 +212,7 @@ struct Acc {
 // One MFMA block of C, computed as the transposed product (B block x A block):
 // lane l then holds C row (l % MF) and, for each accumulator quad, four
 // consecutive columns, which the epilogue stores as one 8-byte run.
-template <class C, int OP>
+template <class C, int OPA, int OPB>
 __device__ __forceinline__ void mfma(typename Acc<C>::T& acc, const v4u* a, const v4u* b, int sa, int sb) {
   if constexpr (C::DT == DT_BF16) {
     v8bf va = __builtin_bit_cast(v8bf, a[0]);
@@ -229,9 +234,9 @@ __device__ __forceinline__ void mfma(typename Acc<C>::T& acc, const v4u* a, cons
     }
     constexpr int fmt = C::F8 ? 0 : 4;   // 0 = E4M3, 4 = E2M1
     if constexpr (C::MF == 32)
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc, fmt, fmt, OP, sb, OP, sa);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc, fmt, fmt, OPB, sb, OPA, sa);
     else
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vb, va, acc, fmt, fmt, OP, sb, OP, sa);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vb, va, acc, fmt, fmt, OPB, sb, OPA, sa);
   }
 }
 
@@ -350,15 +355,17 @@ struct Kernel {
     v4u a[C::FM][C::NCH];
     v4u b[C::FN][C::NCH];
   };
+  // A lane's scale bytes of one k-step: byte i * NU + u is block i's scale in
+  // sub-step u (0x7f, a factor of 1, for the unscaled types).
   struct Scales {
-    int a[C::FM];
-    int b[C::FN];
+    uint32_t a[C::SWA];
+    uint32_t b[C::SWB];
   };
   struct LdsPtrs {
     const lds_u8* a;                 // lane's row in block 0 of its A rows
     const lds_u8* b;
     int slot[C::NU * C::NCH];        // byte offset of the lane's chunk for (sub-step, half)
-    int sa, sb;                      // byte offsets of the lane's block-0 scale words inside a stage
+    int sa, sb;                      // byte offsets of the lane's packed scale bytes inside a stage
   };
 
   static __device__ __forceinline__ lds_u8* stage_ptr(lds_u8* smem, int s) { return smem + s * C::STAGE; }
@@ -372,14 +379,12 @@ struct Kernel {
     t.ra = rsrc_words(a.A + (int64_t)m0 * a.row_bytes, (uint32_t)(rows_a * a.row_bytes));
     t.rb = rsrc_words(a.B + (int64_t)n0 * a.row_bytes, (uint32_t)(rows_b * a.row_bytes));
     if constexpr (C::MX) {
-      // k-step-major scales: k-step ks of row r at SA + ks * sa_kstride + r * SPR
-      // (the k-step's block is reached by moving the base, see rsrc_plus).
-      // The range is rounded up to whole dwords, so the dword holding the last
-      // row's scales is never cut by the range check when SPR = 2; the bytes
-      // past it are scales of rows outside the matrix, whose products are zero
-      // and whose output rows or columns are never stored.
-      t.rsa = rsrc_words(a.SA + (int64_t)m0 * C::SPR, (uint32_t)((rows_a * C::SPR + 3) & ~3));
-      t.rsb = rsrc_words(a.SB + (int64_t)n0 * C::SPR, (uint32_t)((rows_b * C::SPR + 3) & ~3));
+      // k-step-major scales, a tile's k-step block of BM * SPR bytes at
+      // SA + ks * sa_kstride + m0 * SPR in the packed lane order (the k-step's
+      // block is reached by moving the base, see rsrc_plus).  The scale copy
+      // holds whole tiles (rows past M carry 127), so the range is the block.
+      t.rsa = rsrc_words(a.SA + (int64_t)m0 * C::SPR, (uint32_t)(C::BM * C::SPR));
+      t.rsb = rsrc_words(a.SB + (int64_t)n0 * C::SPR, (uint32_t)(C::BN * C::SPR));
     } else {
       t.rsa = t.ra;
       t.rsb = t.rb;
@@ -454,30 +459,48 @@ struct Kernel {
       }
     p.a = smem + C::A_OFF + (wm * C::WTM + lr) * C::KB;
     p.b = smem + C::B_OFF + (wn * C::WTN + lr) * C::KB;
-    p.sa = C::SA_OFF + (wm * C::WTM + lr) * C::SPR + g * C::NU;
-    p.sb = C::SB_OFF + (wn * C::WTN + lr) * C::SPR + g * C::NU;
+    // packed order of a tile's k-step scales: [wave row][lane row][lane group][block][sub-step]
+    p.sa = C::SA_OFF + ((wm * C::MF + lr) * C::NG + g) * C::NSA;
+    p.sb = C::SB_OFF + ((wn * C::MF + lr) * C::NG + g) * C::NSB;
     return p;
   }
 
-  static __device__ __forceinline__ int scale_word(const lds_u8* p) {
-    if constexpr (C::NU == 4) return *(const __attribute__((address_space(3))) int*)p;
-    else if constexpr (C::NU == 2) return (int)*(const __attribute__((address_space(3))) uint16_t*)p;
-    else return (int)*p;
-  }
-
-  static __device__ __forceinline__ void read_scales(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
-    if constexpr (C::MX) {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) sc.a[i] = scale_word(st + p.sa + i * C::MF * C::SPR);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) sc.b[j] = scale_word(st + p.sb + j * C::MF * C::SPR);
+  // The lane's n packed scale bytes (n = 1, 2, 4, 8 or 16) in one LDS read.
+  template <int NB, int NW>
+  static __device__ __forceinline__ void read_packed(const lds_u8* p, uint32_t (&w)[NW]) {
+    typedef const __attribute__((address_space(3))) uint8_t* P8;
+    if constexpr (NB == 1) w[0] = *(P8)p;
+    else if constexpr (NB == 2) w[0] = *(const __attribute__((address_space(3))) uint16_t*)p;
+    else if constexpr (NB == 4) w[0] = *(const __attribute__((address_space(3))) uint32_t*)p;
+    else if constexpr (NB == 8) {
+      const v2u x = *(const __attribute__((address_space(3))) v2u*)p;
+      w[0] = x[0];
+      w[1] = x[1];
     } else {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) sc.a[i] = 0x7f7f7f7f;   // unit E8M0 block scales
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) sc.b[j] = 0x7f7f7f7f;
+      const v4u x = *(const __attribute__((address_space(3))) v4u*)p;
+      w[0] = x[0];
+      w[1] = x[1];
+      w[2] = x[2];
+      w[3] = x[3];
     }
   }
+  static __device__ __forceinline__ void read_scale_a(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
+    if constexpr (C::MX) read_packed<C::NSA>(st + p.sa, sc.a);
+  }
+  static __device__ __forceinline__ void read_scale_b(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
+    if constexpr (C::MX) read_packed<C::NSB>(st + p.sb, sc.b);
+  }
+  static __device__ __forceinline__ void read_scales(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
+    if constexpr (C::MX) {
+      read_scale_a(st, p, sc);
+      read_scale_b(st, p, sc);
+    } else {
+      sc.a[0] = 0x7f7f7f7f;   // unit E8M0 block scales
+      sc.b[0] = 0x7f7f7f7f;
+    }
+  }
+  // Scale word and op_sel byte of block i in sub-step u.
+  static constexpr int sbyte(int i, int u) { return i * C::NU + u; }
 
   // LDS operands of sub-step U (one MFMA K slice) of the stage at byte offset `so`.
   template <int U>
@@ -498,7 +521,7 @@ struct Kernel {
   // interleaved (A0, B0, A1, B1, ...) so that the first MFMAs of a sub-step
   // find their operands first.
   static constexpr int NRD = (C::FM + C::FN) * C::NCH;   // operand reads per sub-step
-  static constexpr int NSR = C::FM + C::FN;              // scale reads per stage
+  static constexpr int NSR = C::MX ? 2 : 0;               // packed scale reads per stage (A's, B's)
   struct ReadDesc {
     bool a;
     int blk, h;
@@ -528,16 +551,6 @@ struct Kernel {
     else
       o.b[d.blk][d.h] = *(const __attribute__((address_space(3))) v4u*)(p.b + off + d.blk * C::MF * C::KB);
   }
-  template <int R>
-  static __device__ __forceinline__ void read_scale(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
-    if constexpr (C::MX) {
-      if constexpr (R < C::FM) sc.a[R] = scale_word(st + p.sa + R * C::MF * C::SPR);
-      else sc.b[R - C::FM] = scale_word(st + p.sb + (R - C::FM) * C::MF * C::SPR);
-    } else {
-      if constexpr (R < C::FM) sc.a[R] = 0x7f7f7f7f;
-      else sc.b[R - C::FM] = 0x7f7f7f7f;
-    }
-  }
   // MFMA order inside a sub-step, in "shells" that follow the read order:
   // once A_t and B_t are in, every block (i, j) with max(i, j) == t can go.
   struct BlockIJ {
@@ -564,7 +577,8 @@ struct Kernel {
     return BlockIJ{0, 0};
   }
   // Reads after the barrier, in the order the next k-step's first MFMAs need
-  // them: for each t, A_t's scales and operand, then B_t's (R < NSR + NRD).
+  // them: A's packed scales, A_0's operand, B's packed scales, B_0's operand,
+  // then A_t's and B_t's operands for t >= 1 (R < NSR + NRD).
   struct PostRead {
     bool scale, a;
     int blk, h;
@@ -573,29 +587,34 @@ struct Kernel {
     const int m = C::FM > C::FN ? C::FM : C::FN;
     for (int t = 0; t < m; ++t) {
       if (t < C::FM) {
-        if (r == 0) return PostRead{true, true, t, 0};
-        --r;
+        if (C::MX && t == 0) {
+          if (r == 0) return PostRead{true, true, 0, 0};
+          --r;
+        }
         for (int h = 0; h < C::NCH; ++h) {
           if (r == 0) return PostRead{false, true, t, h};
           --r;
         }
       }
       if (t < C::FN) {
-        if (r == 0) return PostRead{true, false, t, 0};
-        --r;
+        if (C::MX && t == 0) {
+          if (r == 0) return PostRead{true, false, 0, 0};
+          --r;
+        }
         for (int h = 0; h < C::NCH; ++h) {
           if (r == 0) return PostRead{false, false, t, h};
           --r;
         }
       }
     }
-    return PostRead{true, true, 0, 0};
+    return PostRead{false, true, 0, 0};
   }
   template <int R>
   static __device__ __forceinline__ void post_read_one(const lds_u8* st, int so, const LdsPtrs& p, Scales& sc, Ops& o) {
     constexpr PostRead d = post_read(R);
     if constexpr (d.scale) {
-      read_scale<d.a ? d.blk : C::FM + d.blk>(st, p, sc);
+      if constexpr (d.a) read_scale_a(st, p, sc);
+      else read_scale_b(st, p, sc);
     } else {
       const int off = so + p.slot[d.h];
       if constexpr (d.a)
@@ -609,7 +628,8 @@ struct Kernel {
   static __device__ __forceinline__ void mfma_one(const Ops& o, const Scales& sc, Acc<C>& acc) {
     constexpr BlockIJ bij = block_of(B);
     constexpr int i = bij.i, j = bij.j;
-    mfma<C, (C::MX ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
+    constexpr int ba = C::MX ? sbyte(i, U) : 0, bb = C::MX ? sbyte(j, U) : 0;
+    mfma<C, ba % 4, bb % 4>(acc.v[i][j], o.a[i], o.b[j], (int)sc.a[ba / 4], (int)sc.b[bb / 4]);
   }
 
   // One direct-to-LDS load of a k-step, by its index P among the k-step's
@@ -646,14 +666,6 @@ struct Kernel {
       const int ins = (wave + i * C::NW) % C::SB_INST;
       dma_load4(d.rsb, d.valid ? o.sb[i] : kOob, 0u, d.lds + C::SB_OFF + ins * 256);
     }
-  }
-
-  template <int U>
-  static __device__ __forceinline__ void mfmas(const Ops& o, const Scales& sc, Acc<C>& acc) {
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) mfma<C, (C::MX ? U : 0)>(acc.v[i][j], o.a[i], o.b[j], sc.a[i], sc.b[j]);
   }
 
   // Program-order anchor for the accumulators: MFMAs count as side-effect-free,
@@ -1095,6 +1107,7 @@ struct Kernel {
     Ops o0, o1;
     Scales sc0, sc1;
     read_scales(stage_ptr(smem, 0), lp, sc0);
+    sc1 = sc0;   // (the unscaled types never read scales again)
     read_ops<0>(0, lp, o0);
     for (;;) {
       Acc<C> acc;
@@ -1159,126 +1172,114 @@ hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------- MX scale re-layout
 
-// dst[ks][r][j] = src[r][ks * SPR + j] for r < rows, ks < ksteps, j < SPR,
-// with 127 (a scale of 1) where ks * SPR + j >= s_pitch (a ragged last
-// k-step), so that every k-step's scales of consecutive rows are one
-// contiguous block.  A k-step's block holds dst_rows >= rows rows, a count
-// that makes it a whole number of 16-byte pieces (rows past `rows` are left
-// unwritten), so every block starts 16-byte aligned.  Each workgroup moves a 16-row x KT-k-step tile through
-// LDS (KT * SPR = 256 or 512 bytes of a row): read along rows (the source's
-// contiguous direction; 16-byte loads when rows are 16-byte aligned),
-// written as 16-byte pieces of a k-step's rows when the tile is whole and
-// aligned, else item by item.
+// The scale pre-pass: src[r][c] (E8M0, [rows][s_pitch]) into the copy the
+// kernel reads, k-step major and in the MFMA lane order of a tile:
+//
+//   dst[ks][t][q] for q < TR * SPR, q = (((v * MF + l) * NG + g) * NB + i) * NU + u
+//                = src[t * TR + v * (NB * MF) + i * MF + l][ks * SPR + g * NU + u]
+//
+// t is the tile (TR rows: BM for A, BN for B), v the wave row (of NB * MF rows),
+// l the row inside an MFMA block, g the lane group, i the block and u the
+// sub-step; so a lane's NB * NU bytes for a k-step are contiguous.  127 (a
+// scale of 1) stands for rows past `rows` and bytes past s_pitch (a ragged last
+// k-step).  All the factors are powers of two, given as shifts.  One
+// workgroup moves a tile's rows for 64 / SPR k-steps (64 bytes of each row)
+// through LDS: rows are read 16 bytes at a time when aligned, each k-step's
+// block is written 16 bytes at a time.
 struct RelayoutOp {
   const uint8_t* src;
   uint8_t* dst;
-  int rows, dst_rows, vec16, blocks;   // blocks: row tiles of this operand
+  int rows, dst_rows, vec16, blocks;   // dst_rows: rows rounded up to whole tiles; blocks: tiles
+  int tr, mf_s, ng_s, nb_s, nu_s;      // TR, and log2 of MF, NG, NB, NU
 };
 
-template <int SPR>
-struct RelayoutShape {
-  static constexpr int RT = 16;                         // rows of a tile
-  static constexpr int KT = SPR == 2 ? 128 : 64;        // k-steps of a tile
-};
-
-// One launch re-lays both operands' scales: the first a.blocks row tiles
-// are A's, the rest B's.
 template <int SPR>
 __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutOp b, int s_pitch, int ksteps) {
-  typedef typename std::conditional<SPR == 2, uint16_t,
-                                    typename std::conditional<SPR == 4, uint32_t, v2u>::type>::type Item;
-  struct Piece {
-    Item x[16 / SPR];
-  };
-  constexpr int RT = RelayoutShape<SPR>::RT, KT = RelayoutShape<SPR>::KT;
-  constexpr int RB = KT * SPR;                 // bytes of one row's k-steps
-  static_assert(sizeof(Piece) == 16 && RT * RB % 4096 == 0, "relayout tile");
-  __shared__ __attribute__((aligned(16))) Item tile[KT * RT];   // [k][r]
+  constexpr int KT = 64 / SPR;                 // k-steps per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t t8[256 * 64];   // [tile row][64 bytes]
   const bool is_a = (int)blockIdx.x < a.blocks;
-  const uint8_t* __restrict__ src = is_a ? a.src : b.src;
-  uint8_t* __restrict__ dst = is_a ? a.dst : b.dst;
-  const int rows = is_a ? a.rows : b.rows, vec16 = is_a ? a.vec16 : b.vec16;
-  const int dst_rows = is_a ? a.dst_rows : b.dst_rows;
-  const int r0 = (is_a ? (int)blockIdx.x : (int)blockIdx.x - a.blocks) * RT, k0 = blockIdx.y * KT;
+  const RelayoutOp o = is_a ? a : b;
+  const int tb = is_a ? (int)blockIdx.x : (int)blockIdx.x - a.blocks;
+  const int r0 = tb * o.tr, k0 = blockIdx.y * KT;
   const int tid = threadIdx.x;
-  uint8_t* t8 = (uint8_t*)tile;
-  if (vec16) {
+  const uint8_t* __restrict__ src = o.src;
+  if (o.vec16) {
     // s_pitch % 16 == 0: a 16-byte piece is wholly inside the row or past its end
-    constexpr int PR = RB / 16, NP = RT * PR / 256;
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pc = tid + i * 256, r = pc / PR, q = pc % PR;
-      const int row = r0 + r, col = k0 * SPR + q * 16;
+    for (int pc = tid; pc < o.tr * 4; pc += 256) {
+      const int r = pc >> 2, q = pc & 3, row = r0 + r, col = k0 * SPR + q * 16;
       v4u v = v4u{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
-      if (row < rows && col < s_pitch) v = *(const v4u*)(src + (int64_t)row * s_pitch + col);
-      const Piece pv = __builtin_bit_cast(Piece, v);
-#pragma unroll
-      for (int e = 0; e < 16 / SPR; ++e) tile[(q * (16 / SPR) + e) * RT + r] = pv.x[e];
+      if (row < o.rows && col < s_pitch) v = *(const v4u*)(src + (int64_t)row * s_pitch + col);
+      *(v4u*)(t8 + r * 64 + q * 16) = v;
     }
   } else {
-    constexpr int NB = RT * RB / 256;
-#pragma unroll 8
-    for (int i = 0; i < NB; ++i) {
-      const int b = tid + i * 256, r = b / RB, c = b % RB;
-      const int row = r0 + r, col = k0 * SPR + c;
-      uint8_t x = 127;
-      if (row < rows && col < s_pitch) x = src[(int64_t)row * s_pitch + col];
-      t8[((c / SPR) * RT + r) * SPR + c % SPR] = x;
+    for (int bi = tid; bi < o.tr * 64; bi += 256) {
+      const int r = bi >> 6, c = bi & 63, row = r0 + r, col = k0 * SPR + c;
+      t8[bi] = (row < o.rows && col < s_pitch) ? src[(int64_t)row * s_pitch + col] : (uint8_t)127;
     }
   }
   __syncthreads();
-  constexpr int QK = RT * SPR / 16;            // 16-byte pieces per k-step of the tile
-  const bool whole = r0 + RT <= rows;
-  if (whole) {
+  const int qb = o.tr * SPR / 16;              // 16-byte pieces of one k-step's tile block
+  const int mf_m = (1 << o.mf_s) - 1, ng_m = (1 << o.ng_s) - 1, nb_m = (1 << o.nb_s) - 1, nu_m = (1 << o.nu_s) - 1;
+  for (int pc = tid; pc < KT * qb; pc += 256) {
+    const int k = pc / qb, q0 = (pc - k * qb) * 16, ks = k0 + k;
+    if (ks >= ksteps) continue;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < KT * QK / 256; ++i) {
-      const int p = tid + i * 256, k = p / QK, q = p % QK;
-      const int ks = k0 + k;
-      if (ks < ksteps)
-        *(v4u*)(dst + ((int64_t)ks * dst_rows + r0) * SPR + q * 16) = *(const v4u*)(t8 + (k * RT) * SPR + q * 16);
+    for (int e = 0; e < 16; ++e) {
+      int q = q0 + e;
+      const int u = q & nu_m;
+      q >>= o.nu_s;
+      const int i = q & nb_m;
+      q >>= o.nb_s;
+      const int g = q & ng_m;
+      q >>= o.ng_s;
+      const int l = q & mf_m, v = q >> o.mf_s;
+      const int r = (((v << o.nb_s) + i) << o.mf_s) + l, j = (g << o.nu_s) + u;
+      w[e >> 2] |= (uint32_t)t8[r * 64 + k * SPR + j] << (8 * (e & 3));
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < KT * RT / 256; ++i) {
-      const int p = tid + i * 256, k = p / RT, r = p % RT;
-      const int ks = k0 + k, row = r0 + r;
-      if (ks < ksteps && row < rows) *(Item*)(dst + ((int64_t)ks * dst_rows + row) * SPR) = tile[p];
-    }
+    *(v4u*)(o.dst + ((int64_t)ks * o.dst_rows + r0) * SPR + q0) = v4u{w[0], w[1], w[2], w[3]};
   }
 }
 
-template <int SPR>
-static void relayout_grid(const RelayoutOp& a, const RelayoutOp& b, int ksteps, dim3* grid) {
-  constexpr int KT = RelayoutShape<SPR>::KT;
-  *grid = dim3((unsigned)(a.blocks + b.blocks), (unsigned)((ksteps + KT - 1) / KT));
+namespace {
+int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
 }
+}  // namespace
 
-int relayout_rows(int rows, int spr) {
-  const int pad = 16 / spr;
-  return (rows + pad - 1) / pad * pad;
-}
-
-hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, int rows_a, const uint8_t* src_b, uint8_t* dst_b,
-                                 int rows_b, int s_pitch, int ksteps, int spr, hipStream_t s) {
+hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, const ScaleLayout& la, const uint8_t* src_b,
+                                 uint8_t* dst_b, const ScaleLayout& lb, int s_pitch, int ksteps, int spr,
+                                 hipStream_t s) {
   if (spr != 2 && spr != 4 && spr != 8) return hipErrorInvalidValue;
   if (((uintptr_t)dst_a | (uintptr_t)dst_b) & 15) return hipErrorInvalidValue;
-  RelayoutOp a{src_a, dst_a, rows_a, relayout_rows(rows_a, spr),
-               (s_pitch % 16 == 0 && ((uintptr_t)src_a & 15) == 0) ? 1 : 0, (rows_a + 15) / 16};
-  RelayoutOp b{src_b, dst_b, rows_b, relayout_rows(rows_b, spr),
-               (s_pitch % 16 == 0 && ((uintptr_t)src_b & 15) == 0) ? 1 : 0, (rows_b + 15) / 16};
-  dim3 grid;
-  if (spr == 2) {
-    relayout_grid<2>(a, b, ksteps, &grid);
-    hipLaunchKernelGGL(sk_scale_relayout<2>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
-  } else if (spr == 4) {
-    relayout_grid<4>(a, b, ksteps, &grid);
-    hipLaunchKernelGGL(sk_scale_relayout<4>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
-  } else if (spr == 8) {
-    relayout_grid<8>(a, b, ksteps, &grid);
-    hipLaunchKernelGGL(sk_scale_relayout<8>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
-  } else {
-    return hipErrorInvalidValue;
+  auto op = [&](const uint8_t* src, uint8_t* dst, const ScaleLayout& l) {
+    RelayoutOp o;
+    o.src = src;
+    o.dst = dst;
+    o.rows = l.rows;
+    o.tr = l.tile_rows;
+    o.dst_rows = (l.rows + l.tile_rows - 1) / l.tile_rows * l.tile_rows;
+    o.blocks = o.dst_rows / l.tile_rows;
+    o.vec16 = (s_pitch % 16 == 0 && ((uintptr_t)src & 15) == 0) ? 1 : 0;
+    o.mf_s = log2i(l.mf);
+    o.ng_s = log2i(l.ng);
+    o.nb_s = log2i(l.nblk);
+    o.nu_s = log2i(l.nu);
+    return o;
+  };
+  for (const ScaleLayout* l : {&la, &lb}) {
+    const bool pow2 = !(l->mf & (l->mf - 1)) && !(l->ng & (l->ng - 1)) && !(l->nblk & (l->nblk - 1)) &&
+                      !(l->nu & (l->nu - 1));
+    if (!pow2 || l->ng * l->nu != spr || l->tile_rows % (l->nblk * l->mf) || l->tile_rows > 256 || l->tile_rows < 16)
+      return hipErrorInvalidValue;
   }
+  const RelayoutOp a = op(src_a, dst_a, la), b = op(src_b, dst_b, lb);
+  const dim3 grid((unsigned)(a.blocks + b.blocks), (unsigned)((ksteps + 64 / spr - 1) / (64 / spr)));
+  if (spr == 2) hipLaunchKernelGGL(sk_scale_relayout<2>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  else if (spr == 4) hipLaunchKernelGGL(sk_scale_relayout<4>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  else hipLaunchKernelGGL(sk_scale_relayout<8>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
   return hipGetLastError();
 }
 
@@ -1286,7 +1287,9 @@ hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, int rows_
 #define SK_VARIANT(DT, BM, BN, KB, MF, WM, WN, ST, OCC)                                                   \
   Variant {                                                                                              \
     DT, BM, BN, KB, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::BK, MF, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NT, \
-        SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::LDS_TOTAL, &launch_variant<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC> \
+        SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::LDS_TOTAL, WM, WN,                                       \
+        SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NG, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NU,          \
+        &launch_variant<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC>                                     \
   }
 
 static const Variant kVariants[] = {
