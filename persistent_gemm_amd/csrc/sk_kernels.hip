@@ -1185,7 +1185,8 @@ hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
 // k-step).  All the factors are powers of two, given as shifts.  One
 // workgroup moves a tile's rows for 64 / SPR k-steps (64 bytes of each row)
 // through LDS: rows are read 16 bytes at a time when aligned, each k-step's
-// block is written 16 bytes at a time.
+// block is written 16 bytes at a time.  The LDS rows are 68 bytes apart (17
+// banks), since the lanes of a wave gather bytes from rows a few apart.
 struct RelayoutOp {
   const uint8_t* src;
   uint8_t* dst;
@@ -1196,7 +1197,8 @@ struct RelayoutOp {
 template <int SPR>
 __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutOp b, int s_pitch, int ksteps) {
   constexpr int KT = 64 / SPR;                 // k-steps per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t t8[256 * 64];   // [tile row][64 bytes]
+  constexpr int PITCH = 68;                    // LDS bytes per tile row
+  __shared__ __attribute__((aligned(16))) uint8_t t8[256 * PITCH];   // [tile row][64 bytes + 4]
   const bool is_a = (int)blockIdx.x < a.blocks;
   const RelayoutOp o = is_a ? a : b;
   const int tb = is_a ? (int)blockIdx.x : (int)blockIdx.x - a.blocks;
@@ -1209,12 +1211,16 @@ __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutO
       const int r = pc >> 2, q = pc & 3, row = r0 + r, col = k0 * SPR + q * 16;
       v4u v = v4u{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
       if (row < o.rows && col < s_pitch) v = *(const v4u*)(src + (int64_t)row * s_pitch + col);
-      *(v4u*)(t8 + r * 64 + q * 16) = v;
+      uint32_t* d = (uint32_t*)(t8 + r * PITCH + q * 16);
+      d[0] = v[0];
+      d[1] = v[1];
+      d[2] = v[2];
+      d[3] = v[3];
     }
   } else {
     for (int bi = tid; bi < o.tr * 64; bi += 256) {
       const int r = bi >> 6, c = bi & 63, row = r0 + r, col = k0 * SPR + c;
-      t8[bi] = (row < o.rows && col < s_pitch) ? src[(int64_t)row * s_pitch + col] : (uint8_t)127;
+      t8[r * PITCH + c] = (row < o.rows && col < s_pitch) ? src[(int64_t)row * s_pitch + col] : (uint8_t)127;
     }
   }
   __syncthreads();
@@ -1235,7 +1241,7 @@ __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutO
       q >>= o.ng_s;
       const int l = q & mf_m, v = q >> o.mf_s;
       const int r = (((v << o.nb_s) + i) << o.mf_s) + l, j = (g << o.nu_s) + u;
-      w[e >> 2] |= (uint32_t)t8[r * 64 + k * SPR + j] << (8 * (e & 3));
+      w[e >> 2] |= (uint32_t)t8[r * PITCH + k * SPR + j] << (8 * (e & 3));
     }
     *(v4u*)(o.dst + ((int64_t)ks * o.dst_rows + r0) * SPR + q0) = v4u{w[0], w[1], w[2], w[3]};
   }
