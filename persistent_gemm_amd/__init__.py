@@ -177,10 +177,20 @@ def _stream(t, stream):
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     torch = _torch()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None and t.device.type == "cuda":
+        return raw(t.device.index if t.device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _need(t, name, dtypes, shape, device):
+    """Raises unless t is a contiguous tensor of one of `dtypes`, of `shape`, on `device`."""
+    try:
+        ok = t.device == device and t.dtype in dtypes and t.shape == shape and t.is_contiguous()
+    except AttributeError:
+        raise TypeError(f"{name} must be a tensor") from None
+    if ok:
+        return
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
@@ -190,8 +200,7 @@ def _need(t, name, dtypes, shape, device):
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    raise ValueError(f"{name} must be contiguous")
 
 
 def _out(C, M, N, device):

@@ -333,3 +333,24 @@ def test_co_scheduled_gemm_beside_other_work():
     finally:
         pg.destroy_stream(s1)
         pg.destroy_stream(s2)
+
+
+def test_fixup_many_splits_repeated_calls_exact():
+    """Regression test for the publish ordering (every wave's partial stores
+    complete before the flag is written): back-to-back calls whose tiles are
+    all split between several workgroups, each checked bit for bit."""
+    cases = [("mxfp4", 16, 8192, 4096, (16, 128)), ("mxfp4", 256, 768, 2048, (64, 64)),
+             ("mxfp8", 128, 1024, 2048, (64, 64))]
+    for dtype, M, N, K, tile in cases:
+        x = (make_inputs(dtype, M, N, K, bias=True, seed=M + K) if dtype == "mxfp4"
+             else integer_inputs(dtype, M, N, K, bias=True, seed=M + K))
+        d = device_inputs(x)
+        C, _ = oracle_full(x)
+        outs = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(24)]
+        say(f"repeated split calls {dtype} {M}x{N}x{K} tile {tile}")
+        for i, o in enumerate(outs):
+            pg.gemm_ex(dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], o, policy=pg.PURE_SK,
+                       grid_cap=(256, 200, 97)[i % 3], tile=tile)
+        pg.check()
+        for o in outs:
+            assert_bitexact(o.view(torch.int16).cpu().numpy().view(np.uint16), C, f"{dtype} {M}x{N}x{K} {tile}")
