@@ -288,7 +288,8 @@ def main() -> int:
                     help="auto: the measured kernel and policy for the shape (what the plain entry points use)")
     ap.add_argument("--variant", type=int, default=None, help="compiled kernel index (default: automatic)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--rotate", type=int, default=0, help="rotate over this many input copies (defeats the MALL)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="rotate over this many input copies (defeats the MALL; default: the workload's)")
     ap.add_argument("--co-schedule", type=int, default=0, metavar="C",
                     help="run the GEMM on C CUs beside a memory-bound kernel on the other CUs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -374,7 +375,7 @@ def main() -> int:
             return co_schedule(args, w, to_dev(x), tile, policy)
 
         copies = [to_dev(x)]
-        for i in range(1, max(1, args.rotate)):
+        for i in range(1, max(1, args.rotate or w.rotate)):
             copies.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in copies[0].items()})
         C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
         p = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=cap, policy=policy, tile=tile, variant=args.variant)
@@ -429,6 +430,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
+                   "input_copies": max(1, args.rotate or w.rotate),
                    "tile": f"{p.tile_m}x{p.tile_n}x{p.tile_k}", "threads": p.threads, "variant": p.variant,
                    "policy": {pg.HYBRID: "hybrid", pg.PURE_SK: "sk", pg.PURE_DP: "dp"}[p.policy],
                    "policy_requested": args.policy, "grid": p.grid,
