@@ -95,16 +95,29 @@ __global__ __launch_bounds__(256) void sk_colsum_partial(const uint16_t* __restr
   for (int j = 0; j < 8; ++j) out[j] = s[j];
 }
 
-// Second pass: dbias[n] = bf16 of the sum of the chunk partials, in
-// increasing chunk order (a fixed order, so the bits repeat), rounded once to
-// nearest-even (NaN kept quiet).
+// Second pass: dbias[n] = bf16 of the sum of the chunk partials, rounded once
+// to nearest-even (NaN kept quiet).  A workgroup handles 32 columns with 8
+// threads each: thread t of a column sums the t-th contiguous run of chunks in
+// increasing order, then the column's first thread adds the 8 run sums in
+// increasing t.  The association is fixed, so the bits repeat.
 __global__ __launch_bounds__(256) void sk_colsum_final(const float* __restrict__ part, uint16_t* __restrict__ dbias,
                                                         int chunks, int N) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
+  __shared__ float run_sum[8][32];
+  const int col = threadIdx.x & 31, t = threadIdx.x >> 5;
+  const int n = blockIdx.x * 32 + col;
+  const int per = (chunks + 7) / 8, c0 = t * per, c1 = min(chunks, c0 + per);
   float s = 0.0f;
-  for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * N + n];
-  const uint32_t u = __float_as_uint(s);
+  if (n < N) {
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) s += part[(int64_t)c * N + n];
+  }
+  run_sum[t][col] = s;
+  __syncthreads();
+  if (t != 0 || n >= N) return;
+  float r = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r += run_sum[k][col];
+  const uint32_t u = __float_as_uint(r);
   uint16_t h;
   if ((u & 0x7fffffffu) > 0x7f800000u) h = (uint16_t)((u >> 16) | 0x40u);
   else h = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
@@ -128,7 +141,7 @@ hipError_t launch_colsum_bf16(const uint16_t* dc, float* part, uint16_t* dbias, 
                      s, dc, part, M, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sk_colsum_final, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, part, dbias, chunks, N);
+  hipLaunchKernelGGL(sk_colsum_final, dim3((unsigned)((N + 31) / 32)), dim3(256), 0, s, part, dbias, chunks, N);
   return hipGetLastError();
 }
 

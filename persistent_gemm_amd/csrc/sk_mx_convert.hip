@@ -16,7 +16,7 @@ namespace {
 // E4M3FN byte of each E2M1 code (sign bit 7; exponent bias 7, three mantissa
 // bits): 0.5 = 2^-1 -> 0x30, 1 -> 0x38, 1.5 -> 0x3C, 2 -> 0x40, 3 -> 0x44,
 // 4 -> 0x48, 6 -> 0x4C; code 8 (-0) -> 0x80.
-__device__ __forceinline__ uint32_t e2m1_to_e4m3(uint32_t code) {
+[[maybe_unused]] __device__ __forceinline__ uint32_t e2m1_to_e4m3(uint32_t code) {
   const uint32_t mag = code & 7u, sign = (code & 8u) << 4;
   // magnitudes 1..7: exponent field 6 + (mag >> 1) for mag >= 2 (E2M1 field
   // e is worth 2^(e-1), E4M3 field f is worth 2^(f-7)), 6 for mag 1 (0.5);
@@ -30,6 +30,21 @@ __device__ __forceinline__ uint32_t e2m1_to_e4m3(uint32_t code) {
 
 typedef uint32_t v4w __attribute__((ext_vector_type(4)));
 
+// The E4M3 bytes of the eight E2M1 magnitudes as a byte table for v_perm_b32,
+// whose selector bytes 0..3 pick bytes of its second operand and 4..7 bytes of
+// its first: bytes 0x00 0x30 0x38 0x3C | 0x40 0x44 0x48 0x4C.
+constexpr uint32_t kMagLo = 0x3C383000u, kMagHi = 0x4C484440u;
+
+// Eight E2M1 codes (one source dword, even K in each byte's low nibble) to
+// eight E4M3 bytes in K order, as two dwords.
+__device__ __forceinline__ void widen_word(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  const uint32_t ev = __builtin_amdgcn_perm(kMagHi, kMagLo, x & 0x07070707u) | ((x & 0x08080808u) << 4);
+  const uint32_t od = __builtin_amdgcn_perm(kMagHi, kMagLo, (x >> 4) & 0x07070707u) | (x & 0x80808080u);
+  // interleave: K order is ev.b0 od.b0 ev.b1 od.b1 | ev.b2 od.b2 ev.b3 od.b3
+  lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+  hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+}
+
 // dst[r][k] = E4M3 byte of the E2M1 code at src[r][k / 2] (even k in the low
 // nibble).  Each thread widens 16 source bytes (32 codes) into 32 bytes.
 __global__ __launch_bounds__(256) void sk_widen_e2m1(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
@@ -37,23 +52,13 @@ __global__ __launch_bounds__(256) void sk_widen_e2m1(const uint8_t* __restrict__
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= pieces) return;
   const v4w x = *(const v4w*)(src + i * 16);
-  v4w y[2];
+  uint32_t w[8];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t byte = (x[w] >> (8 * b)) & 0xffu;
-      const uint32_t pair = e2m1_to_e4m3(byte & 15u) | (e2m1_to_e4m3(byte >> 4) << 8);
-      if (b < 2) lo |= pair << (16 * b);
-      else hi |= pair << (16 * (b - 2));
-    }
-    y[w / 2][2 * (w % 2)] = lo;
-    y[w / 2][2 * (w % 2) + 1] = hi;
-  }
+  for (int k = 0; k < 4; ++k) widen_word(x[k], w[2 * k], w[2 * k + 1]);
+  const v4w y0 = v4w{w[0], w[1], w[2], w[3]}, y1 = v4w{w[4], w[5], w[6], w[7]};
   v4w* q = (v4w*)(dst + i * 32);
-  q[0] = y[0];
-  q[1] = y[1];
+  q[0] = y0;
+  q[1] = y1;
 }
 
 }  // namespace
