@@ -45,13 +45,17 @@ PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "mxfp4_addmm_8192"
 
 
+# the sources that decide the forward GEMM kernels and their launch (the
+# backward and the E2M1 widening pass live in files of their own)
+GEMM_SOURCES = ("sk_api.cpp", "sk_common.h", "sk_kernels.hip", "sk_tuning_table.inc")
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "persistent_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in GEMM_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

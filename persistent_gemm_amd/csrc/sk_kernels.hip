@@ -1042,6 +1042,10 @@ struct Kernel {
     constexpr int HB = NB / 2;                            // slots of the last sub-step before the barrier
     constexpr int PRE = (C::NU - 1) * NB + HB;            // slots before the barrier
     constexpr int POST = NB - HB;
+    // The k-step's loads are spread over the slots before the barrier.  With
+    // two stages the loads issued in a k-step are waited for at its own
+    // barrier, so they all go out in the first slots instead.
+    constexpr int DMA_SPAN = S == 2 ? (PRE < PER_STAGE ? PRE : PER_STAGE) : PRE;
     auto kstep_interleaved = [&](int d, Ops& o0, Ops& o1, Scales& sc0, Scales& sc1, Acc<C>& acc) {
       const int cur = d % S, nxt = (d + 1) % S;
       const DmaCtx dc = dma_ctx();
@@ -1066,7 +1070,7 @@ struct Kernel {
           }
           static_for<PER_STAGE>([&](auto pc) {
             constexpr int pp = decltype(pc)::value;
-            if constexpr (pp * PRE / PER_STAGE == slot) dma_piece<pp>(dc, lo, row_bytes);
+            if constexpr (pp * DMA_SPAN / PER_STAGE == slot) dma_piece<pp>(dc, lo, row_bytes);
           });
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -1325,6 +1329,13 @@ static const Variant kVariants[] = {
     SK_VARIANT(DT_MXFP8, 128, 128, 128, 32, 2, 2, 4, 1),
     SK_VARIANT(DT_MXFP8, 64, 64, 64, 32, 2, 2, 4, 2),
     SK_VARIANT(DT_MXFP8, 16, 256, 128, 16, 1, 4, 3, 1),
+    // 256x256 tiles with 128-byte k-steps in two stages (half the barriers per K)
+    SK_VARIANT(DT_MXFP4, 256, 256, 128, 32, 2, 2, 2, 1),
+    SK_VARIANT(DT_MXFP4, 256, 256, 128, 32, 2, 4, 2, 2),
+    SK_VARIANT(DT_BF16, 256, 256, 128, 32, 2, 2, 2, 1),
+    SK_VARIANT(DT_BF16, 256, 256, 128, 32, 2, 4, 2, 2),
+    SK_VARIANT(DT_FP8, 256, 256, 128, 32, 2, 2, 2, 1),
+    SK_VARIANT(DT_FP8, 256, 256, 128, 32, 2, 4, 2, 2),
 };
 
 int num_variants() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
