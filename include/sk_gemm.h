@@ -118,6 +118,9 @@ typedef enum sk_policy {
 /* sk_gemm_args.debug_flags bits (tests only). */
 #define SK_DEBUG_DELAY 1u       /* each workgroup sleeps a seeded pseudo-random time before publishing its partial */
 #define SK_DEBUG_DROP_SIGNAL 2u /* workgroup drop_signal_wg never publishes its partial tile's flag */
+#define SK_DEBUG_RELAYOUT 4u    /* MX: always copy the scales into the kernel's lane order first, even where a
+                                   kernel of at most 128-row tiles could read the caller's [rows][K/32] scales
+                                   directly (K a whole number of k-steps, scale arrays 4-byte aligned) */
 
 /* MXFP4: A, B packed E2M1; A_scale, B_scale E8M0 (required).  bias may be NULL. */
 sk_status sk_gemm_mxfp4(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,

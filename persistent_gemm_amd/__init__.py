@@ -21,7 +21,7 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL",
+    "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL", "DEBUG_RELAYOUT",
     "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_bf16_backward", "gemm_mx", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
     "cu_masked_stream", "destroy_stream", "stream_cu_count",
@@ -29,7 +29,7 @@ __all__ = [
 
 MXFP4, BF16, FP8, MXFP8 = 0, 1, 2, 3
 HYBRID, PURE_SK, PURE_DP, AUTO = 0, 1, 2, 3
-DEBUG_DELAY, DEBUG_DROP_SIGNAL = 1, 2
+DEBUG_DELAY, DEBUG_DROP_SIGNAL, DEBUG_RELAYOUT = 1, 2, 4
 
 _STATUS = {0: "SK_OK", 1: "SK_ERR_ARG", 2: "SK_ERR_ALIGN", 3: "SK_ERR_UNSUPPORTED", 4: "SK_ERR_HIP",
            5: "SK_ERR_NOMEM", 6: "SK_ERR_TIMEOUT"}

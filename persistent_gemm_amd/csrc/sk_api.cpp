@@ -375,8 +375,14 @@ sk_status run(const sk_gemm_args& g) {
   // kb bytes of a row: 2 * kb FP4 or kb FP8 elements, so kb / 16 or kb / 32
   // scale bytes.
   const int64_t spr = g.dtype == SK_MXFP4 ? v->kb / 16 : v->kb / 32, ksteps = p.iters_per_tile;
+  // Kernels of at most 128-row tiles instead gather the scales straight from the caller's
+  // arrays, saving the re-layout launch: when K is whole k-steps (so no
+  // k-step reads past a row's last scale byte) and the scale arrays are
+  // 4-byte aligned (dword loads).
+  const bool direct = is_mx(g.dtype) && v->launch_direct != nullptr && !(g.debug_flags & SK_DEBUG_RELAYOUT) &&
+                      (g.K / 32) % spr == 0 && !(((uintptr_t)g.A_scale | (uintptr_t)g.B_scale) & 3);
   int64_t sa_bytes = 0, sb_bytes = 0, rows_a = 0, rows_b = 0;
-  if (is_mx(g.dtype)) {
+  if (is_mx(g.dtype) && !direct) {
     rows_a = cdiv(g.M, v->bm) * v->bm;
     rows_b = cdiv(g.N, v->bn) * v->bn;
     sa_bytes = ksteps * rows_a * spr;
@@ -385,7 +391,8 @@ sk_status run(const sk_gemm_args& g) {
   }
   const int64_t sb_at = (sa_bytes + 255) / 256 * 256;
   Workspace* ws = nullptr;
-  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, is_mx(g.dtype) ? (size_t)(sb_at + sb_bytes) : 0, &ws);
+  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, is_mx(g.dtype) && !direct ? (size_t)(sb_at + sb_bytes) : 0,
+                     &ws);
   if (st != SK_OK) return st;
   uint32_t epoch = 0;
   st = next_epoch(ws, &epoch);
@@ -395,7 +402,13 @@ sk_status run(const sk_gemm_args& g) {
   std::memset(&a, 0, sizeof(a));
   a.A = (const uint8_t*)g.A;
   a.B = (const uint8_t*)g.B;
-  if (is_mx(g.dtype)) {
+  if (direct) {
+    a.SA = (const uint8_t*)g.A_scale;
+    a.SB = (const uint8_t*)g.B_scale;
+    a.sa_kstride = (uint32_t)spr;
+    a.sb_kstride = (uint32_t)spr;
+    a.s_pitch = (int32_t)(g.K / 32);
+  } else if (is_mx(g.dtype)) {
     const sk::ScaleLayout la{(int)g.M, v->bm, v->mfma, v->ng, v->bm / v->wm / v->mfma, v->nu};
     const sk::ScaleLayout lb{(int)g.N, v->bn, v->mfma, v->ng, v->bn / v->wn / v->mfma, v->nu};
     if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, ws->S, la, (const uint8_t*)g.B_scale, ws->S + sb_at, lb,
@@ -430,7 +443,7 @@ sk_status run(const sk_gemm_args& g) {
   a.spin_limit = g.spin_limit_ticks ? g.spin_limit_ticks : kDefaultSpin;
   a.drop_wg = (g.debug_flags & SK_DEBUG_DROP_SIGNAL) ? g.drop_signal_wg : -1;
   a.delay_seed = (g.debug_flags & SK_DEBUG_DELAY) ? (g.delay_seed ? g.delay_seed : 1u) : 0u;
-  if (v->launch(p.grid, a, stream) != hipSuccess) return SK_ERR_HIP;
+  if ((direct ? v->launch_direct : v->launch)(p.grid, a, stream) != hipSuccess) return SK_ERR_HIP;
   return SK_OK;
 }
 

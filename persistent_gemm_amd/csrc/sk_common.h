@@ -26,8 +26,8 @@ constexpr int64_t kMaxIters = ((int64_t)1 << 31) - 1;
 struct KArgs {
   const uint8_t* A;
   const uint8_t* B;
-  const uint8_t* SA;        // MXFP4 block scales of A, k-step-major: [k-step][M][SPR]
-  const uint8_t* SB;        // MXFP4 block scales of B, k-step-major: [k-step][N][SPR]
+  const uint8_t* SA;        // MX block scales of A, k-step-major: [k-step][M][SPR] (direct kernels: [M][s_pitch])
+  const uint8_t* SB;        // MX block scales of B, k-step-major: [k-step][N][SPR] (direct kernels: [N][s_pitch])
   const float* fsa;         // fp8 per-tensor scale of A (NULL = 1)
   const float* fsb;         // fp8 per-tensor scale of B (NULL = 1)
   const uint16_t* bias;     // bf16[N] or NULL
@@ -49,6 +49,7 @@ struct KArgs {
   uint32_t epoch;           // this launch's flag value
   int32_t drop_wg;          // test hook: this workgroup never publishes (-1: none)
   uint32_t delay_seed;      // test hook: nonzero = seeded sleeps before publishing
+  int32_t s_pitch;          // row pitch (bytes) of SA and SB when they are the caller's [rows][K/32] scales
 };
 
 // Stream-K partition of S = q*G + r MAC iterations: workgroup w owns
@@ -160,6 +161,9 @@ struct Variant {
   int wm, wn;       // waves along M and N
   int ng, nu;       // MFMA lane groups, MFMAs per block per k-step
   hipError_t (*launch)(int grid, const KArgs& a, hipStream_t s);
+  // The same kernel reading MX scales straight from the caller's row-major
+  // [rows][K/32] arrays (no re-layout pass), or nullptr where not compiled.
+  hipError_t (*launch_direct)(int grid, const KArgs& a, hipStream_t s);
 };
 
 int num_variants();

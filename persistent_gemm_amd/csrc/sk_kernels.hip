@@ -329,9 +329,15 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 
 // ---------------------------------------------------------------- the kernel body
 
-template <class C>
+// DIRECT: MX scales are gathered straight from the caller's [rows][K/32]
+// arrays (a k-step's SPR bytes of each row land in LDS as [row][SPR]), with no
+// re-layout pass before the launch; a lane then reads its blocks' scale bytes
+// one block at a time.  Needs SPR >= 4 (a dword of a row never spans two rows)
+// and K a multiple of the k-step (no k-step reads past a row's last scale).
+template <class C, bool DIRECT = false>
 struct Kernel {
   static constexpr int NT = C::NT;
+  static_assert(!DIRECT || (C::MX && C::SPR >= 4), "direct scale reads need MX scales, at least 4 bytes per row");
 
   struct TileCtx {
     v4u ra, rb, rsa, rsb;   // A, B and (MXFP4) their scales, from the tile's first row
@@ -378,7 +384,13 @@ struct Kernel {
     const int rows_b = min(C::BN, a.N - n0);
     t.ra = rsrc_words(a.A + (int64_t)m0 * a.row_bytes, (uint32_t)(rows_a * a.row_bytes));
     t.rb = rsrc_words(a.B + (int64_t)n0 * a.row_bytes, (uint32_t)(rows_b * a.row_bytes));
-    if constexpr (C::MX) {
+    if constexpr (DIRECT) {
+      // the caller's scales: the tile's rows, [row][s_pitch]; a k-step moves
+      // the base by SPR bytes (see rsrc_plus), and since K is a whole number
+      // of k-steps every byte read lies inside the tile's rows
+      t.rsa = rsrc_words(a.SA + (int64_t)m0 * a.s_pitch, (uint32_t)(rows_a * a.s_pitch));
+      t.rsb = rsrc_words(a.SB + (int64_t)n0 * a.s_pitch, (uint32_t)(rows_b * a.s_pitch));
+    } else if constexpr (C::MX) {
       // k-step-major scales, a tile's k-step block of BM * SPR bytes at
       // SA + ks * sa_kstride + m0 * SPR in the packed lane order (the k-step's
       // block is reached by moving the base, see rsrc_plus).  The scale copy
@@ -410,15 +422,21 @@ struct Kernel {
     }
     if constexpr (C::MX) {
       // the k-step's scale bytes of the tile's rows are contiguous ([row][SPR])
+      // (DIRECT: byte `byte` of the [row][SPR] block is byte byte % SPR of
+      // the k-step's scales in row byte / SPR of the caller's array)
 #pragma unroll
       for (int i = 0; i < C::SA_PT; ++i) {
         const int byte = ((wave + i * C::NW) % C::SA_INST) * 256 + lane * 4;
-        o.sa[i] = byte < C::BM * C::SPR ? (uint32_t)byte : kOob;
+        const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch + (uint32_t)(byte % C::SPR)
+                                    : (uint32_t)byte;
+        o.sa[i] = byte < C::BM * C::SPR ? src : kOob;
       }
 #pragma unroll
       for (int i = 0; i < C::SB_PT; ++i) {
         const int byte = ((wave + i * C::NW) % C::SB_INST) * 256 + lane * 4;
-        o.sb[i] = byte < C::BN * C::SPR ? (uint32_t)byte : kOob;
+        const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch + (uint32_t)(byte % C::SPR)
+                                    : (uint32_t)byte;
+        o.sb[i] = byte < C::BN * C::SPR ? src : kOob;
       }
     }
     return o;
@@ -459,9 +477,15 @@ struct Kernel {
       }
     p.a = smem + C::A_OFF + (wm * C::WTM + lr) * C::KB;
     p.b = smem + C::B_OFF + (wn * C::WTN + lr) * C::KB;
-    // packed order of a tile's k-step scales: [wave row][lane row][lane group][block][sub-step]
-    p.sa = C::SA_OFF + ((wm * C::MF + lr) * C::NG + g) * C::NSA;
-    p.sb = C::SB_OFF + ((wn * C::MF + lr) * C::NG + g) * C::NSB;
+    if constexpr (DIRECT) {
+      // [row][SPR]: the lane's row in block 0, its lane group's NU bytes
+      p.sa = C::SA_OFF + (wm * C::WTM + lr) * C::SPR + g * C::NU;
+      p.sb = C::SB_OFF + (wn * C::WTN + lr) * C::SPR + g * C::NU;
+    } else {
+      // packed order of a tile's k-step scales: [wave row][lane row][lane group][block][sub-step]
+      p.sa = C::SA_OFF + ((wm * C::MF + lr) * C::NG + g) * C::NSA;
+      p.sb = C::SB_OFF + ((wn * C::MF + lr) * C::NG + g) * C::NSB;
+    }
     return p;
   }
 
@@ -484,11 +508,29 @@ struct Kernel {
       w[3] = x[3];
     }
   }
+  // DIRECT: the NU bytes of each of NB blocks (MF rows apart in the [row][SPR]
+  // image), placed where the packed read would put them (block i at byte i * NU).
+  template <int NB, int NW>
+  static __device__ __forceinline__ void read_blocks(const lds_u8* p, uint32_t (&w)[NW]) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = 0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const lds_u8* q = p + i * C::MF * C::SPR;
+      uint32_t x;
+      if constexpr (C::NU == 1) x = *q;
+      else if constexpr (C::NU == 2) x = *(const __attribute__((address_space(3))) uint16_t*)q;
+      else x = *(const __attribute__((address_space(3))) uint32_t*)q;
+      w[(i * C::NU) / 4] |= x << (8 * ((i * C::NU) % 4));
+    }
+  }
   static __device__ __forceinline__ void read_scale_a(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
-    if constexpr (C::MX) read_packed<C::NSA>(st + p.sa, sc.a);
+    if constexpr (DIRECT) read_blocks<C::FM>(st + p.sa, sc.a);
+    else if constexpr (C::MX) read_packed<C::NSA>(st + p.sa, sc.a);
   }
   static __device__ __forceinline__ void read_scale_b(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
-    if constexpr (C::MX) read_packed<C::NSB>(st + p.sb, sc.b);
+    if constexpr (DIRECT) read_blocks<C::FN>(st + p.sb, sc.b);
+    else if constexpr (C::MX) read_packed<C::NSB>(st + p.sb, sc.b);
   }
   static __device__ __forceinline__ void read_scales(const lds_u8* st, const LdsPtrs& p, Scales& sc) {
     if constexpr (C::MX) {
@@ -1161,17 +1203,31 @@ struct Kernel {
   }
 };
 
-template <class C, int OCC>
+template <class C, int OCC, bool DIRECT>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void sk_gemm_kernel(KArgs a) {
   (void)a;   // read through kargs()
-  Kernel<C>::run();
+  Kernel<C, DIRECT>::run();
 }
 
-template <class C, int OCC>
+template <class C, int OCC, bool DIRECT>
 hipError_t launch_variant(int grid, const KArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((sk_gemm_kernel<C, OCC>), dim3(grid), dim3(C::NT), 0, s, a);
+  hipLaunchKernelGGL((sk_gemm_kernel<C, OCC, DIRECT>), dim3(grid), dim3(C::NT), 0, s, a);
   return hipGetLastError();
+}
+
+typedef hipError_t (*Launcher)(int, const KArgs&, hipStream_t);
+
+// The direct-scale twin is compiled for the MX kernels with at most 128 rows
+// per tile, which serve the small and skinny problems: there the separate
+// re-layout launch is a large part of a call (16x8192x8192 MXFP4: 19.1 ->
+// 15.3 us; 128x8192x8192: 27.8 -> 24.1 us).  The 256x256 kernels keep the
+// re-laid copy: gathering 256 rows' scale bytes per k-step costs them more
+// than the pass (8192^3: 258 -> 284 us).
+template <class C, int OCC>
+constexpr Launcher direct_launcher() {
+  if constexpr (C::MX && C::SPR >= 4 && C::BM <= 128) return &launch_variant<C, OCC, true>;
+  else return nullptr;
 }
 
 // ---------------------------------------------------------------- MX scale re-layout
@@ -1299,7 +1355,8 @@ hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, const Sca
     DT, BM, BN, KB, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::BK, MF, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NT, \
         SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::LDS_TOTAL, WM, WN,                                       \
         SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NG, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NU,          \
-        &launch_variant<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC>                                     \
+        &launch_variant<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC, false>,                             \
+        direct_launcher<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC>()                                   \
   }
 
 static const Variant kVariants[] = {

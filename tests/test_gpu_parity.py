@@ -149,6 +149,41 @@ def test_every_variant_exact(index):
             assert_bitexact(got, C, f"variant {index} {M}x{N}x{K} policy {policy} grid {g}")
 
 
+@pytest.mark.parametrize("dtype", ["mxfp4", "mxfp8"])
+def test_direct_scale_reads(dtype):
+    """MX kernels of up to 128-row tiles read the scales straight from the caller's
+    [rows][K/32] arrays when K is a whole number of k-steps and the arrays are
+    4-byte aligned, and otherwise (or under DEBUG_RELAYOUT) re-lay them first.
+    Every such kernel, all three policies, both paths, against the oracle;
+    then scale arrays starting 4 bytes (still direct) and 1 byte (re-laid)
+    into their allocation."""
+    for index, v in enumerate(pg.variants()):
+        if _DTYPES[v["dtype"]] != dtype or v["tile_m"] > 128:
+            continue
+        M, N, K = 2 * v["tile_m"] + 3, 2 * v["tile_n"] + 8, 1024
+        if dtype == "mxfp4":
+            x = make_inputs(dtype, M, N, K, bias=True, seed=3500 + index)
+        else:
+            x = integer_inputs(dtype, M, N, K, bias=True, seed=3500 + index)
+        d = device_inputs(x)
+        C, _ = oracle_full(x)
+        for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 7), (pg.PURE_DP, 3)]:
+            for flags in (0, pg.DEBUG_RELAYOUT):
+                say(f"variant {index} ({dtype} {v['tile_m']}x{v['tile_n']}) {M}x{N}x{K} policy {policy} flags {flags}")
+                got = run(d, grid_cap=g, policy=policy, variant=index, debug_flags=flags)
+                assert_bitexact(got, C, f"variant {index} policy {policy} flags {flags}")
+        for shift in (4, 1):
+            e = dict(d)
+            for k in ("SA", "SB"):
+                t = d[k]
+                buf = torch.zeros(t.numel() + 16, dtype=torch.uint8, device=t.device)
+                buf[shift:shift + t.numel()] = t.reshape(-1)
+                e[k] = buf[shift:shift + t.numel()].view(t.shape)
+            say(f"variant {index} scale arrays at offset {shift}")
+            got = run(e, grid_cap=0, policy=pg.HYBRID, variant=index)
+            assert_bitexact(got, C, f"variant {index} scales at offset {shift}")
+
+
 # ---------------------------------------------------------------- fixup protocol
 
 def test_bias_added_exactly_once_on_split_tiles():
