@@ -139,23 +139,60 @@ struct TuneEntry {
 #include "sk_tuning_table.inc"
 
 // The tuned (variant, policy) of the measured shape nearest to (M, N, K)
-// in log scale; false if the table has no usable entry for the dtype.
+// in log scale; false if the table has no usable entry for the dtype.  The
+// entries' logarithms are taken once, and each host thread remembers its last
+// answer, so a repeated call costs one comparison (the scan alone took about
+// 8 us per call, as long as a small kernel).
 bool tuned_choice(int dtype, int64_t M, int64_t N, int64_t K, int* variant, int* policy) {
+  constexpr int kEntries = (int)(sizeof(kTuneTable) / sizeof(kTuneTable[0]));
+  struct Logs {
+    double m[kEntries], n[kEntries], k[kEntries];
+    bool usable[kEntries];
+  };
+  static const Logs logs = [] {
+    Logs l;
+    for (int i = 0; i < kEntries; ++i) {
+      const TuneEntry& e = kTuneTable[i];
+      const Variant* v = sk::variant(e.variant);
+      l.usable[i] = v && v->dtype == e.dtype && v->bm == e.bm && v->bn == e.bn && v->threads == e.threads;
+      l.m[i] = std::log2((double)e.M);
+      l.n[i] = std::log2((double)e.N);
+      l.k[i] = std::log2((double)e.K);
+    }
+    return l;
+  }();
+  struct Last {
+    int dtype = -1;
+    int64_t M = 0, N = 0, K = 0;
+    bool found = false;
+    int variant = 0, policy = 0;
+  };
+  thread_local Last last;
+  if (last.dtype == dtype && last.M == M && last.N == N && last.K == K) {
+    *variant = last.variant;
+    *policy = last.policy;
+    return last.found;
+  }
+  const double lm = std::log2((double)M), ln = std::log2((double)N), lk = std::log2((double)K);
   double best = 1e300;
   bool found = false;
-  for (const TuneEntry& e : kTuneTable) {
-    if (e.dtype != dtype) continue;
-    const Variant* v = sk::variant(e.variant);
-    if (!v || v->dtype != dtype || v->bm != e.bm || v->bn != e.bn || v->threads != e.threads) continue;
-    const double d = std::fabs(std::log2((double)M / (double)e.M)) + std::fabs(std::log2((double)N / (double)e.N)) +
-                     std::fabs(std::log2((double)K / (double)e.K));
+  for (int i = 0; i < kEntries; ++i) {
+    if (kTuneTable[i].dtype != dtype || !logs.usable[i]) continue;
+    const double d = std::fabs(lm - logs.m[i]) + std::fabs(ln - logs.n[i]) + std::fabs(lk - logs.k[i]);
     if (d < best) {
       best = d;
-      *variant = e.variant;
-      *policy = e.policy;
+      *variant = kTuneTable[i].variant;
+      *policy = kTuneTable[i].policy;
       found = true;
     }
   }
+  last.dtype = dtype;
+  last.M = M;
+  last.N = N;
+  last.K = K;
+  last.found = found;
+  last.variant = found ? *variant : 0;
+  last.policy = found ? *policy : 0;
   return found;
 }
 
