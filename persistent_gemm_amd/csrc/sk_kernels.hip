@@ -1393,9 +1393,6 @@ static const Variant kVariants[] = {
     SK_VARIANT(DT_BF16, 256, 256, 128, 32, 2, 4, 2, 2),
     SK_VARIANT(DT_FP8, 256, 256, 128, 32, 2, 2, 2, 1),
     SK_VARIANT(DT_FP8, 256, 256, 128, 32, 2, 4, 2, 2),
-    // skinny MXFP4 with deep rings (more bytes in flight per CU)
-    SK_VARIANT(DT_MXFP4, 16, 128, 128, 16, 1, 4, 8, 1),
-    SK_VARIANT(DT_MXFP4, 16, 128, 64, 16, 1, 4, 8, 1),
 };
 
 int num_variants() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
