@@ -184,6 +184,44 @@ def test_direct_scale_reads(dtype):
             assert_bitexact(got, C, f"variant {index} scales at offset {shift}")
 
 
+def _midpoint_inputs(M, N, K):
+    """MXFP4 operands whose exact products sum to +-257 (seven 6*6, one 2*2, one
+    1*1) or, where A's scale is 2^3, to +-2056: both lie exactly on a bf16
+    rounding boundary.  The bias of column n is one of +-2^-20, +-2^-16
+    (which the fp32 sum swallows or ties on, leaving it on the boundary), 0,
+    -0, 1 and 2^-32, so the correct bf16 depends on the bias's sign even
+    where the fp32 sum does not show it."""
+    row = np.zeros(K, np.uint8)
+    row[:7], row[7], row[8] = 7, 4, 2
+    a = np.tile(row, (M, 1))
+    a[1::2] |= 8                                   # odd rows negative
+    b = np.tile(row, (N, 1))
+    pack = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    sa = np.full((M, K // 32), 127, np.uint8)
+    sa[2::4] = 130
+    sb = np.full((N, K // 32), 127, np.uint8)
+    pattern = np.array([0x3580, 0xB580, 0x3780, 0xB780, 0x0000, 0x8000, 0x3F80, 0x2F80], np.uint16)
+    bias = pattern[np.arange(N) % len(pattern)]
+    return {"dtype": "mxfp4", "M": M, "N": N, "K": K, "A": pack(a), "B": pack(b), "SA": sa, "SB": sb,
+            "bias": bias}
+
+
+def test_bias_add_on_bf16_rounding_boundaries():
+    """The epilogue rounds acc + bias once: sums whose fp32 value sits exactly on
+    a bf16 rounding boundary must still round by the exact sum's side of it,
+    on whole and on split tiles, in the 256x256, 64x64 and 16-row kernels."""
+    x = _midpoint_inputs(69, 131, 256)
+    C, _ = oracle_full(x)
+    # the pins of this test: 257 + 2^-20 rounds up to 258, 257 - 2^-20 down to 256, 257 to 256 (even)
+    assert C[0, 0] == 0x4381 and C[0, 1] == 0x4380 and C[0, 4] == 0x4380
+    d = device_inputs(x)
+    for kw in [dict(policy=pg.AUTO), dict(tile=(256, 256), policy=pg.HYBRID),
+               dict(tile=(64, 64), policy=pg.PURE_SK, grid_cap=7), dict(tile=(64, 64), policy=pg.PURE_DP),
+               dict(tile=(16, 128), policy=pg.PURE_SK, grid_cap=11)]:
+        say(f"midpoint sums {kw}")
+        assert_bitexact(run(d, **kw), C, f"midpoint sums {kw}")
+
+
 # ---------------------------------------------------------------- fixup protocol
 
 def test_bias_added_exactly_once_on_split_tiles():
