@@ -239,3 +239,25 @@ def test_auto_policy_takes_the_measured_choice():
         assert (q.variant, q.policy) == (vi, pol), (dtype, M, N, K)
     p = pg.plan(pg.MXFP4, 8192, 8192, 8192, policy=pg.AUTO, tile=(128, 128), num_cus=256)
     assert (p.tile_m, p.tile_n, p.policy) == (128, 128, pg.HYBRID)
+
+
+def test_auto_choice_cache_keeps_answers_apart():
+    """The AUTO lookup remembers its last answer per host thread: interleaved
+    shapes and dtypes, and several threads at once, must still each get the
+    entry their own shape selects (the answers of a first, serial pass)."""
+    from concurrent.futures import ThreadPoolExecutor
+    queries = [(d, M, N, K) for d in (pg.MXFP4, pg.BF16, pg.FP8, pg.MXFP8)
+               for (M, N, K) in ((16, 8192, 8192), (8192, 8192, 8192), (1024, 4096, 1024), (16, 1024, 1024))]
+
+    def answer(q):
+        p = pg.plan(q[0], q[1], q[2], q[3], policy=pg.AUTO, num_cus=256)
+        return p.variant, p.policy, p.grid
+
+    want = {q: answer(q) for q in queries}
+    for q in reversed(queries):            # interleaved, each differing from the one before
+        assert answer(q) == want[q], q
+    for q in queries:                      # the same query twice in a row
+        assert answer(q) == answer(q) == want[q], q
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        got = list(ex.map(answer, queries * 8))
+    assert got == [want[q] for q in queries * 8]
