@@ -280,6 +280,16 @@ def co_schedule(args, w, d, tile, policy) -> int:
     return 0
 
 
+def hold_device(torch, cycles: int) -> None:
+    """Queue a spin kernel of about `cycles` GPU clocks on the current stream, so
+    the host can enqueue the timed calls before the device reaches them (the
+    events around those calls then time the device, not the host).  Without
+    torch's spin kernel the calls are simply timed as enqueued."""
+    spin = getattr(torch.cuda, "_sleep", None)
+    if spin is not None:
+        spin(int(cycles))
+
+
 def vendor(args, w, copies, C, ours) -> int:
     """The vendor library on the same device inputs: torch.addmm (bf16) and
     torch._scaled_mm (fp8 per-tensor, MXFP4 / MXFP8 with E8M0 blocks of 32),
@@ -319,7 +329,7 @@ def vendor(args, w, copies, C, ours) -> int:
         for i in range(args.warmup):
             fn(i)
         torch.cuda.synchronize()
-        torch.cuda._sleep(20_000_000)   # the queue stays ahead of the host: events time the device
+        hold_device(torch, 20_000_000)   # the queue stays ahead of the host: events time the device
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(args.steps):
@@ -491,7 +501,7 @@ def main() -> int:
     # events see the launches back to back (the per-call events above also
     # count the time a call waits for the host when the call is short).
     torch.cuda.synchronize()
-    torch.cuda._sleep(200_000 * args.steps)
+    hold_device(torch, 200_000 * args.steps)
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     d0.record(stream)
     for i in range(args.steps):
