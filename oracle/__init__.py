@@ -69,6 +69,7 @@ __all__ = [
     "accept",
     "bf16_backward",
     "gemm_mx",
+    "abs_product_sums_mx",
 ]
 
 # OCP MX v1.0, FP4 (E2M1): code bits are sign | exponent(2, bias 1) | mantissa(1).
@@ -317,19 +318,32 @@ def bf16_backward(dC, A, B):
     return out
 
 
+def _mx_decode(fmt: str, X, S, K: int) -> np.ndarray:
+    if fmt == "mxfp4":
+        return mxfp4_operand(X, S, K)
+    if fmt == "mxfp8":
+        return mxfp8_operand(X, S, K)
+    raise ValueError(f"not an MX format: {fmt!r}")
+
+
+def _mx_k(a_fmt: str, A, K):
+    if K is not None:
+        return K
+    return 2 * np.asarray(A).shape[1] if a_fmt == "mxfp4" else np.asarray(A).shape[1]
+
+
 def gemm_mx(a_fmt: str, b_fmt: str, A, B, SA, SB, bias=None, K: int | None = None):
     """Block-scaled operands of either element width ("mxfp4" or "mxfp8" each):
     the same plain contraction as gemm(), each operand decoded by its own format.
     Returns (C uint16[M][N] bf16 bits, D float64[M][N])."""
-    def decode(fmt, X, S, k):
-        if fmt == "mxfp4":
-            return mxfp4_operand(X, S, k)
-        if fmt == "mxfp8":
-            return mxfp8_operand(X, S, k)
-        raise ValueError(f"not an MX format: {fmt!r}")
-    if K is None:
-        K = 2 * np.asarray(A).shape[1] if a_fmt == "mxfp4" else np.asarray(A).shape[1]
-    a = decode(a_fmt, A, SA, K)
-    b = decode(b_fmt, B, SB, K)
+    K = _mx_k(a_fmt, A, K)
+    a = _mx_decode(a_fmt, A, SA, K)
+    b = _mx_decode(b_fmt, B, SB, K)
     D = a @ b.T + _beta(bias, b.shape[0])[None, :]
     return rne_bf16_from_double(D), D
+
+
+def abs_product_sums_mx(a_fmt: str, b_fmt: str, A, B, SA, SB, K: int | None = None) -> np.ndarray:
+    """S[m][n] = sum_k |a(m,k) * b(n,k)| for operands of formats a_fmt / b_fmt (sigma = 1)."""
+    K = _mx_k(a_fmt, A, K)
+    return np.abs(_mx_decode(a_fmt, A, SA, K)) @ np.abs(_mx_decode(b_fmt, B, SB, K)).T

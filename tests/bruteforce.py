@@ -155,3 +155,70 @@ def gemm_mx(a_fmt: str, b_fmt: str, A, B, SA, SB, bias, M: int, N: int, K: int):
                 d += bf16(int(bias[n]))
             out[m][n] = round_bf16(d)
     return out
+
+
+# ---------------------------------------------------------------- the tolerance arithmetic
+
+def _operand_value(dtype: str, X, S, r: int, k: int) -> Fraction:
+    """Element (r, k) of an operand of `dtype`, decoded from its bit fields."""
+    if dtype == "mxfp4":
+        byte = int(X[r][k // 2])
+        code = (byte >> 4) if (k & 1) else (byte & 0xF)
+        return e2m1(code) * e8m0(int(S[r][k // 32]))
+    if dtype == "mxfp8":
+        return e4m3fn(int(X[r][k])) * e8m0(int(S[r][k // 32]))
+    if dtype == "bf16":
+        return bf16(int(X[r][k]))
+    return e4m3fn(int(X[r][k]))
+
+
+def abs_sums(dtype: str, A, B, SA, SB, M: int, N: int, K: int):
+    """Exact S[m][n] = |sigma| * sum_k |a(m,k) * b(n,k)| (sigma = SA * SB for fp8, else 1),
+    and the exact D[m][n] = sigma * sum_k a(m,k) * b(n,k) (no bias), as Fractions."""
+    sigma = Fraction(float(SA)) * Fraction(float(SB)) if dtype == "fp8" else Fraction(1)
+    S = [[Fraction(0)] * N for _ in range(M)]
+    D = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        a = [_operand_value(dtype, A, SA, m, k) for k in range(K)]
+        for n in range(N):
+            b = [_operand_value(dtype, B, SB, n, k) for k in range(K)]
+            S[m][n] = abs(sigma) * sum((abs(x * y) for x, y in zip(a, b)), Fraction(0))
+            D[m][n] = sigma * sum((x * y for x, y in zip(a, b)), Fraction(0))
+    return S, D
+
+
+def mixed_abs_sums(a_fmt: str, b_fmt: str, A, B, SA, SB, M: int, N: int, K: int):
+    """Exact sum_k |a(m,k) * b(n,k)| for block-scaled operands of formats a_fmt / b_fmt."""
+    return [[sum((abs(_operand_value(a_fmt, A, SA, m, k) * _operand_value(b_fmt, B, SB, n, k)) for k in range(K)),
+                 Fraction(0)) for n in range(N)] for m in range(M)]
+
+
+def backward_abs_sums(dC, A, B, M: int, N: int, K: int):
+    """Exact error-bound sums of the bf16 backward: sum_n |dC[m][n] B[n][k]|,
+    sum_m |dC[m][n] A[m][k]| and sum_m |dC[m][n]|."""
+    g = [[bf16(int(dC[m][n])) for n in range(N)] for m in range(M)]
+    a = [[bf16(int(A[m][k])) for k in range(K)] for m in range(M)]
+    b = [[bf16(int(B[n][k])) for k in range(K)] for n in range(N)]
+    sA = [[sum((abs(g[m][n] * b[n][k]) for n in range(N)), Fraction(0)) for k in range(K)] for m in range(M)]
+    sB = [[sum((abs(g[m][n] * a[m][k]) for m in range(M)), Fraction(0)) for k in range(K)] for n in range(N)]
+    sb = [sum((abs(g[m][n]) for m in range(M)), Fraction(0)) for n in range(N)]
+    return sA, sB, sb
+
+
+def ulp_bf16(x: Fraction) -> Fraction:
+    """Spacing of the bf16 grid at |x|, from the format: 8 significant bits, so
+    2**(e - 7) for 2**e <= |x| < 2**(e+1) with e >= -126; the subnormal spacing
+    2**-133 below 2**-126 (and at 0)."""
+    a = abs(Fraction(x))
+    if a < Fraction(2) ** -126:
+        return Fraction(2) ** -133
+    return Fraction(2) ** (_floor_log2(a) - 7)
+
+
+def accept(c_bits: int, ref_bits: int, D: Fraction, S: Fraction) -> bool:
+    """The parity bar, exactly: bits equal (either zero matches either zero), or
+    |c - D| <= 2**-7 * S + ulp_bf16(max(|D|, |c|))."""
+    if c_bits == ref_bits or ((c_bits | ref_bits) & 0x7FFF) == 0:
+        return True
+    c = bf16(c_bits)
+    return abs(c - D) <= S / 128 + ulp_bf16(max(abs(D), abs(c)))

@@ -492,6 +492,114 @@ def pin_accept():
     assert oracle.accept(np.array([0x8000], np.uint16), z, np.zeros(1), None).all()
 
 
+# ---------------------------------------------------------------- the tolerance arithmetic
+#
+# The parity bar for inexact results is |C - D| <= 2**-7 * S + ulp_bf16(max(|D|, |C|)) with
+# S = |sigma| * sum_k |a b|.  Every bounded GPU result rests on S, the ulp and accept(); each is
+# pinned here to an exact-rational computation written from the definitions (tests/bruteforce.py).
+
+def _exact_float(x) -> float:
+    """A Fraction that must be exactly representable in fp64, as that float."""
+    f = float(x)
+    assert bf.Fraction(f) == x, f"{x} is not exact in fp64"
+    return f
+
+
+def pin_abs_sums_vs_rational():
+    """abs_product_sums and the S and D of gemm_elements equal the exact sums (every product
+    and partial sum of these tiny cases is exact in fp64, so any summation order gives them)."""
+    cases = [("mxfp4", 3, 4, 96), ("bf16", 4, 3, 40), ("fp8", 3, 5, 48), ("mxfp8", 2, 4, 64)]
+    for i, (dtype, M, N, K) in enumerate(cases):
+        kw = {"fp8_scales": (0.5, 3.0)} if dtype == "fp8" else {}     # sigma = 1.5
+        x = make_inputs(dtype, M, N, K, bias=True, seed=900 + i, **kw)
+        S, D = bf.abs_sums(dtype, x["A"], x["B"], x["SA"], x["SB"], M, N, K)
+        Sx = np.array([[_exact_float(v) for v in row] for row in S])
+        Dx = np.array([[_exact_float(v) for v in row] for row in D])
+        got = oracle.abs_product_sums(dtype, x["A"], x["B"], x["SA"], x["SB"], K=K)
+        assert np.array_equal(got, Sx), dtype
+        rows = np.repeat(np.arange(M), N)
+        cols = np.tile(np.arange(N), M)
+        _, De, Se = oracle.gemm_elements(dtype, x["A"], x["B"], rows, cols, x["SA"], x["SB"], None, K=K)
+        assert np.array_equal(Se.reshape(M, N), Sx), dtype
+        assert np.array_equal(De.reshape(M, N), Dx), dtype
+        # with the bias, D moves by exactly bias[n] and S does not move
+        _, Db, Sb = oracle.gemm_elements(dtype, x["A"], x["B"], rows, cols, x["SA"], x["SB"], x["bias"], K=K)
+        assert np.array_equal(Sb.reshape(M, N), Sx), dtype
+        assert np.array_equal(Db.reshape(M, N) - Dx, np.broadcast_to(oracle.decode_bf16(x["bias"]), (M, N)))
+
+
+def pin_mixed_abs_sums_vs_rational():
+    for a_fmt, b_fmt in (("mxfp4", "mxfp8"), ("mxfp8", "mxfp4")):
+        M, N, K = 3, 2, 64
+        x = mixed_inputs(a_fmt, b_fmt, M, N, K, bias=False, seed=910)
+        want = bf.mixed_abs_sums(a_fmt, b_fmt, x["A"], x["B"], x["SA"], x["SB"], M, N, K)
+        got = oracle.abs_product_sums_mx(a_fmt, b_fmt, x["A"], x["B"], x["SA"], x["SB"], K=K)
+        assert np.array_equal(got, np.array([[_exact_float(v) for v in r] for r in want])), (a_fmt, b_fmt)
+
+
+def pin_backward_abs_sums_vs_rational():
+    for seed, (M, N, K) in enumerate([(2, 3, 4), (4, 2, 5)]):
+        x = backward_inputs(M, N, K, seed=920 + seed)
+        o = oracle.bf16_backward(x["dC"], x["A"], x["B"])
+        sA, sB, sb = bf.backward_abs_sums(x["dC"], x["A"], x["B"], M, N, K)
+        assert np.array_equal(o["dA"][2], np.array([[_exact_float(v) for v in r] for r in sA]))
+        assert np.array_equal(o["dB"][2], np.array([[_exact_float(v) for v in r] for r in sB]))
+        assert np.array_equal(o["dbias"][2], np.array([_exact_float(v) for v in sb]))
+
+
+def pin_ulp_bf16():
+    """The bf16 spacing: hand-picked values, the gap to the next bf16 read off the bit
+    patterns of every positive finite bf16 (below the largest), and the exact-rational
+    definition on random doubles (including values between bf16 grid points)."""
+    hand = {1.0: 2.0 ** -7, 1.99: 2.0 ** -7, 2.0: 2.0 ** -6, -1.5: 2.0 ** -7, 3 * 2.0 ** 100: 2.0 ** 94,
+            2.0 ** -126: 2.0 ** -133, 2.0 ** -130: 2.0 ** -133, 0.0: 2.0 ** -133, 255.9: 1.0, 256.0: 2.0}
+    x = np.array(list(hand.keys()))
+    assert np.array_equal(oracle._ulp_bf16(x), np.array(list(hand.values())))
+    bits = np.arange(1, 0x7F7F, dtype=np.uint16)              # +denormals .. below the largest finite
+    v = oracle.decode_bf16(bits)
+    gap = oracle.decode_bf16(bits + np.uint16(1)) - v
+    assert np.array_equal(oracle._ulp_bf16(v), gap)
+    rng = np.random.default_rng(17)
+    r = rng.standard_normal(2000) * np.ldexp(1.0, rng.integers(-140, 120, 2000))
+    want = np.array([float(bf.ulp_bf16(bf.Fraction(float(t)))) for t in r])
+    assert np.array_equal(oracle._ulp_bf16(r), want)
+
+
+def pin_accept_exact():
+    """accept() against the exact-rational bar on results placed at, just inside and just
+    outside the bound (values chosen so every fp64 step of accept() is exact)."""
+    # by hand: D = 100, S = 128 -> 2**-7 S = 1; the bf16 spacing at 100 is 0.5, so the bound is 1.5
+    D = np.array([100.0] * 6)
+    S = np.array([128.0] * 6)
+    c = np.array([101.5, 102.0, 98.5, 98.0, 100.5, 100.0])
+    want = np.array([True, False, True, False, True, True])
+    cb = oracle.rne_bf16_from_double(c)
+    ref = oracle.rne_bf16_from_double(D)
+    assert np.array_equal(oracle.accept(cb, ref, D, S), want)
+    # random: D with 20-bit mantissas, S with 12, results at the bf16 points around D +- the bound
+    rng = np.random.default_rng(19)
+    cases = []
+    for _ in range(400):
+        d = float(rng.integers(-2**20, 2**20)) * 2.0 ** int(rng.integers(-30, -10))
+        sv = float(rng.integers(0, 2**12)) * 2.0 ** int(rng.integers(-16, -4))
+        bound = sv / 128 + float(bf.ulp_bf16(bf.Fraction(abs(d))))
+        for t in (-1.0, 1.0):
+            target = d + t * bound
+            below = int(oracle.rne_bf16_from_double(np.array([target]))[0])
+            for bits in {below, below + 1, below - 1} - {-1}:
+                if (bits & 0x7FFF) < 0x7F80:
+                    cases.append((bits, d, sv))
+    cb = np.array([c[0] for c in cases], np.uint16)
+    Dv = np.array([c[1] for c in cases])
+    Sv = np.array([c[2] for c in cases])
+    ref = oracle.rne_bf16_from_double(Dv)
+    got = oracle.accept(cb, ref, Dv, Sv)
+    want = np.array([bf.accept(int(b), int(r), bf.Fraction(d), bf.Fraction(sv))
+                     for b, r, d, sv in zip(cb, ref, Dv, Sv)])
+    assert got.sum() > 100 and (~got).sum() > 100          # both sides of the bar are exercised
+    assert np.array_equal(got, want)
+
+
 PINS = [
     pin_e4m3fn_vs_torch, pin_e8m0_vs_torch, pin_bf16_decode_vs_torch, pin_e2m1_bitfields,
     pin_rne_vs_torch_on_floats, pin_rne_from_double_not_via_float, pin_rne_overflow_subnormal_nan,
@@ -500,6 +608,8 @@ PINS = [
     pin_integer_matmul, pin_invariants_mxfp4, pin_invariants_mxfp8, pin_accept,
     pin_bruteforce_bf16_backward, pin_bf16_backward_vs_autograd, pin_bf16_backward_identities,
     pin_bruteforce_mixed_mx, pin_mixed_mx_reduces_to_mxfp4,
+    pin_abs_sums_vs_rational, pin_mixed_abs_sums_vs_rational, pin_backward_abs_sums_vs_rational,
+    pin_ulp_bf16, pin_accept_exact,
 ]
 
 
@@ -642,11 +752,75 @@ def _mut_mixed_b_scales_ignored(mp):
     mp.setattr(oracle, "gemm_mx", gm)
 
 
+def _mut_abs_sums_one_sided(mp):
+    # |a| @ b^T: the absolute value taken on one operand only
+    def S(dtype, A, B, SA=None, SB=None, K=None):
+        a, b, sigma = oracle.operands(dtype, A, B, SA, SB, K)
+        return abs(sigma) * (np.abs(a) @ b.T)
+    mp.setattr(oracle, "abs_product_sums", S)
+
+
+def _mut_abs_sums_outer(mp):
+    # (sum_k |a|)(sum_k |b|): an outer product of row sums instead of sum_k |a b|
+    def S(dtype, A, B, SA=None, SB=None, K=None):
+        a, b, sigma = oracle.operands(dtype, A, B, SA, SB, K)
+        return abs(sigma) * np.outer(np.abs(a).sum(axis=1), np.abs(b).sum(axis=1))
+    mp.setattr(oracle, "abs_product_sums", S)
+
+
+def _mut_abs_sums_no_sigma(mp):
+    def S(dtype, A, B, SA=None, SB=None, K=None):
+        a, b, sigma = oracle.operands(dtype, A, B, SA, SB, K)
+        return np.abs(a) @ np.abs(b).T
+    mp.setattr(oracle, "abs_product_sums", S)
+
+
+def _mut_elements_S_one_sided(mp):
+    real = oracle.gemm_elements
+
+    def ge(dtype, A, B, rows, cols, SA=None, SB=None, bias=None, K=None):
+        C, D, S = real(dtype, A, B, rows, cols, SA, SB, bias, K)
+        a, b, sigma = oracle.operands(dtype, A, B, SA, SB, K)
+        S = abs(sigma) * np.einsum("ik,ik->i", np.abs(a[np.asarray(rows)]), b[np.asarray(cols)])
+        return C, D, S
+    mp.setattr(oracle, "gemm_elements", ge)
+
+
+def _mut_backward_S_one_sided(mp):
+    real = oracle.bf16_backward
+
+    def bwd(dC, A, B):
+        out = real(dC, A, B)
+        if B is not None:
+            g, b = oracle.decode_bf16(dC), oracle.decode_bf16(B)
+            out["dA"] = (out["dA"][0], out["dA"][1], np.abs(g) @ b)
+        return out
+    mp.setattr(oracle, "bf16_backward", bwd)
+
+
+def _mut_mixed_S_one_sided(mp):
+    def S(a_fmt, b_fmt, A, B, SA, SB, K=None):
+        K = oracle._mx_k(a_fmt, A, K)
+        return np.abs(oracle._mx_decode(a_fmt, A, SA, K)) @ oracle._mx_decode(b_fmt, B, SB, K).T
+    mp.setattr(oracle, "abs_product_sums_mx", S)
+
+
+def _mut_ulp_half(mp):
+    real = oracle._ulp_bf16
+    mp.setattr(oracle, "_ulp_bf16", lambda x: real(x) / 2)
+
+
+def _mut_bound_without_ulp(mp):
+    mp.setattr(oracle, "_ulp_bf16", lambda x: np.zeros(np.shape(x)))
+
+
 MUTATIONS = [
     _mut_e2m1_entry, _mut_nibble_order, _mut_scale_block, _mut_drop_bias, _mut_double_bias,
     _mut_round_via_float, _mut_round_truncate, _mut_e4m3_bias, _mut_fp8_sigma, _mut_transpose_b,
     _mut_bf16_decode, _mut_mxfp8_no_scales, _mut_mxfp8_scale_per_16, _mut_backward_transposed_b,
     _mut_backward_dbias_rows, _mut_mixed_b_scales_ignored,
+    _mut_abs_sums_one_sided, _mut_abs_sums_outer, _mut_abs_sums_no_sigma, _mut_elements_S_one_sided,
+    _mut_backward_S_one_sided, _mut_mixed_S_one_sided, _mut_ulp_half, _mut_bound_without_ulp,
 ]
 
 
