@@ -1,5 +1,9 @@
-"""GPU parity at the workloads' full sizes, in the launch configuration the
-bench times (default tile and policy), plus the other tiles worth checking."""
+"""GPU parity at the workloads' full sizes.
+
+Each workload is first run through the plain entry point (policy AUTO: the
+tuned kernel and policy, which is exactly the launch bench.py times) and the
+whole output is compared with the oracle; then other tiles and policies of
+interest are checked against the oracle or against that first result."""
 
 from __future__ import annotations
 
@@ -22,35 +26,60 @@ def _wl(name):
     return w, make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
 
 
+# The kernels the tuned table picks for the timed workloads (variant indices as in
+# sk_variant_info); the tests assert them so that a retuned table cannot leave
+# the timed kernel unchecked.
+BENCHED = {"mxfp4_addmm_8192": 23, "bf16_addmm_4096": 25, "mxfp4_gemm_16x8192x8192": 6}
+
+
+def _auto_plan(w):
+    p = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=w.grid_cap, policy=pg.AUTO)
+    assert p.variant == BENCHED[w.name], f"{w.name}: AUTO now picks kernel {p.variant}; update BENCHED"
+    return p
+
+
+def _plain(w, d, bias=True):
+    """The plain entry point (AUTO), as bench.py calls it; C as uint16 bits."""
+    b = d["bias"] if bias else None
+    if w.dtype == "mxfp4":
+        out = pg.gemm_mxfp4(d["A"], d["B"], d["SA"], d["SB"], b, grid_cap=w.grid_cap)
+    else:
+        out = pg.gemm_bf16(d["A"], d["B"], b, grid_cap=w.grid_cap)
+    pg.check()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
 def test_skinny_mxfp4_16x8192x8192_bitexact():
     w, x = _wl("mxfp4_gemm_16x8192x8192")
     d = device_inputs(x)
     C, _ = oracle_full(x)
+    p = _auto_plan(w)
+    say(f"skinny 16x8192x8192, plain entry point (kernel {p.variant}, grid {p.grid}, sk_tiles {p.sk_tiles})")
+    assert_bitexact(_plain(w, d), C, "AUTO")
     for tile, policy, g in [(None, pg.HYBRID, 0), ((16, 128), pg.HYBRID, 0), ((16, 256), pg.PURE_SK, 100),
                             ((16, 256), pg.PURE_DP, 0), ((64, 64), pg.HYBRID, 0)]:
         say(f"skinny 16x8192x8192 tile {tile} policy {policy} grid {g}")
         assert_bitexact(run(d, tile=tile, policy=policy, grid_cap=g), C, f"{tile} {policy} {g}")
 
 
-def test_large_mxfp4_addmm_8192_sampled_bitexact():
+def test_large_mxfp4_addmm_8192_bitexact():
+    """The whole 8192^3 output of the timed launch, bit for bit (the oracle takes seconds)."""
     w, x = _wl("mxfp4_addmm_8192")
     d = device_inputs(x)
-    say("8192^3 mxfp4 addmm, default plan")
-    got = run(d)
-    rng = np.random.default_rng(0)
-    # a 128 x 128 block spanning a tile corner, the last rows/cols, and random samples
-    rows = np.concatenate([np.repeat(np.arange(192, 320), 128), np.repeat(np.arange(8064, 8192), 2),
-                           rng.integers(0, 8192, 30000)])
-    cols = np.concatenate([np.tile(np.arange(192, 320), 128), np.tile([0, 8191], 128),
-                           rng.integers(0, 8192, 30000)])
-    Cs, _, _ = oracle.gemm_elements("mxfp4", x["A"], x["B"], rows, cols, x["SA"], x["SB"], x["bias"], K=w.K)
-    sub = got[rows, cols]
-    ok = oracle.accept(sub, Cs, None, None)
-    assert ok.all(), f"{(~ok).sum()} of {ok.size} sampled elements differ"
-    for tile, policy, g in [((128, 128), pg.HYBRID, 0), ((256, 256), pg.PURE_SK, 0), ((256, 256), pg.HYBRID, 200)]:
+    p = _auto_plan(w)
+    say(f"8192^3 mxfp4 addmm, plain entry point (kernel {p.variant}, grid {p.grid}, policy {p.policy})")
+    got = _plain(w, d)
+    say("8192^3 oracle")
+    C, _ = oracle_full(x)
+    assert_bitexact(got, C, "8192^3 AUTO")
+    say("8192^3 repeat")
+    assert np.array_equal(_plain(w, d), got)
+    # other kernels and partitions: every fp32 partial sum is exact, so the same bits
+    for tile, policy, g in [(None, pg.HYBRID, 0), ((128, 128), pg.HYBRID, 0), ((256, 256), pg.PURE_SK, 0),
+                            ((256, 256), pg.HYBRID, 200)]:
         say(f"8192^3 tile {tile} policy {policy} grid {g}")
         again = run(d, tile=tile, policy=policy, grid_cap=g)
-        assert np.array_equal(again, got), f"{tile} {policy} {g} differs from the default plan"
+        assert np.array_equal(again, got), f"{tile} {policy} {g} differs from the oracle"
 
 
 @pytest.fixture(scope="module")
@@ -59,6 +88,15 @@ def bf16_4096():
     C, D = oracle_full(x)
     S = oracle.abs_product_sums("bf16", x["A"], x["B"])
     return w, x, device_inputs(x), C, D, S
+
+
+def test_bf16_addmm_4096_timed_launch_within_bound(bf16_4096):
+    w, x, d, C, D, S = bf16_4096
+    p = _auto_plan(w)
+    say(f"bf16 4096^3 addmm, plain entry point (kernel {p.variant}, grid {p.grid})")
+    first = _plain(w, d)
+    assert_within_bound(first, C, D, S, "AUTO")
+    assert np.array_equal(_plain(w, d), first)
 
 
 @pytest.mark.parametrize("tile", [None, (128, 192), (128, 128)])

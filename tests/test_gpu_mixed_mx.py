@@ -57,9 +57,7 @@ def test_mixed_random_within_bound_and_repeatable(a_fmt, b_fmt):
     M, N, K = 513, 388, 1056
     x = mixed_inputs(a_fmt, b_fmt, M, N, K, bias=True, seed=31)
     C, D = oracle.gemm_mx(a_fmt, b_fmt, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=K)
-    fa = oracle.mxfp4_operand if a_fmt == "mxfp4" else oracle.mxfp8_operand
-    fb = oracle.mxfp4_operand if b_fmt == "mxfp4" else oracle.mxfp8_operand
-    S = np.abs(fa(x["A"], x["SA"], K)) @ np.abs(fb(x["B"], x["SB"], K)).T
+    S = oracle.abs_product_sums_mx(a_fmt, b_fmt, x["A"], x["B"], x["SA"], x["SB"], K=K)
     d = _dev(x)
     say(f"mixed {a_fmt} x {b_fmt} random {M}x{N}x{K}")
     first = _run(x, d)
