@@ -45,13 +45,20 @@
  *
  * Ownership and asynchrony: all tensor pointers are device pointers owned by
  * the caller and must stay valid until the stream has passed the launch.
- * Calls enqueue on `stream` (a hipStream_t; NULL is the default stream) and
- * return without waiting.  The library owns its scratch (fp32 partial tiles,
- * lock flags, an error word, and for MXFP4 / MXFP8 a k-step-major copy of the two
- * scale arrays that a small kernel writes before the GEMM on the same
- * stream), kept per (device, stream), grown on demand and freed by
- * sk_release_workspace().  Device-side failures (a workgroup that
+ * Calls enqueue on `stream` (a hipStream_t passed as void*; NULL is the
+ * default stream) and return without waiting.  The library owns its scratch
+ * (fp32 partial tiles, lock flags, an error word, and for MXFP4 / MXFP8 a
+ * k-step-major copy of the two scale arrays that a small kernel writes before
+ * the GEMM on the same stream), kept per (device, stream), grown on demand and
+ * freed by sk_release_workspace().  Device-side failures (a workgroup that
  * waited past its spin limit) are reported by sk_check().
+ *
+ * HIP graphs: a stream that is being captured is refused (SK_ERR_UNSUPPORTED,
+ * nothing enqueued).  The lock flags of the fixup are compared with a
+ * per-launch epoch that is a kernel argument, so a captured launch would
+ * replay with a fixed epoch and an owner could take the flags of the previous
+ * replay for this one's; the scratch may also have to grow, which needs a
+ * synchronisation that capture forbids.
  *
  * Errors: every call returns an sk_status and never aborts.  Arguments are
  * checked before anything is launched:
@@ -65,8 +72,9 @@
  *                       16, bf16 K not a multiple of 8 (a row of A or B must
  *                       be a whole number of 16-byte chunks), or A, B, C not
  *                       16-byte aligned, or bias not 2-byte aligned;
- *   SK_ERR_UNSUPPORTED  the current device is not gfx950, or a tile override
- *                       names no compiled kernel for that dtype;
+ *   SK_ERR_UNSUPPORTED  the current device is not gfx950, a tile override
+ *                       names no compiled kernel for that dtype, or the stream
+ *                       is being captured into a HIP graph;
  *   SK_ERR_HIP          a HIP runtime call failed;
  *   SK_ERR_NOMEM        scratch could not be allocated;
  *   SK_ERR_TIMEOUT      (sk_check only) a workgroup gave up waiting for a
@@ -122,15 +130,28 @@ typedef enum sk_policy {
                                    kernel of at most 128-row tiles could read the caller's [rows][K/32] scales
                                    directly (K a whole number of k-steps, scale arrays 4-byte aligned) */
 
-/* MXFP4: A, B packed E2M1; A_scale, B_scale E8M0 (required).  bias may be NULL. */
+/* MXFP4: A, B packed E2M1; A_scale, B_scale E8M0 (required).  bias may be NULL.
+ * The FP4 GEMM with Stream-K load balancing over the K-loop ("Stream-k mxfp4
+ * kernel", author's description and pull request overview: the FP4 Stream-K
+ * kernel behind the matmul_fp4 dispatch, with per-workgroup partial tiles and
+ * lock flags).  Policy AUTO; grid_cap as for every entry point (<= 0: all the
+ * stream's compute units).  stream is a hipStream_t passed as void*. */
 sk_status sk_gemm_mxfp4(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
                         const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
 
-/* bf16 x bf16 -> bf16.  bias may be NULL. */
+/* bf16 x bf16 -> bf16.  bias may be NULL.  The Stream-K matmul that the bias
+ * page's correctness tests run on both the Persistent and the Stream-K path and
+ * compare with torch.mm / torch.addmm ("Fix StreamK Kernel Bias #67", pull
+ * request overview and the review comments on the two tests).  Policy AUTO. */
 sk_status sk_gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
                        int grid_cap, void* stream);
 
-/* fp8 (E4M3FN) with per-tensor fp32 scales (device pointers to one float each, NULL = 1.0).  bias may be NULL. */
+/* fp8 (E4M3FN) with per-tensor fp32 scales (device pointers to one float each, NULL = 1.0).  bias may be NULL.
+ * The quantized mode of the Stream-K kernel, in which the bias is converted to
+ * fp32 before it is added to the scaled sum ("Fix StreamK Kernel Bias #67",
+ * Technical Details); the persistent grid may be capped to a number of compute
+ * units ("SM-constraint-GEMM by triton persistent kernel", description).
+ * Policy AUTO. */
 sk_status sk_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* A_scale, const float* B_scale,
                       const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
 
@@ -157,7 +178,11 @@ sk_status sk_gemm_mx(sk_dtype a_fmt, sk_dtype b_fmt, const uint8_t* A, const uin
                      void* stream);
 
 /* addmm(bias, A, B) = the dtype's GEMM with a bias that is required (alpha = beta = 1).
- * A_scale / B_scale as for that dtype (NULL for bf16). */
+ * A_scale / B_scale as for that dtype (NULL for bf16).  The bias runs along N, is
+ * broadcast over the M rows and is added once, after the partial tiles of a split
+ * tile have been aggregated ("Fix StreamK Kernel Bias #67", Motivation and
+ * Technical Details; the tests compare with torch.addmm, hence alpha = beta = 1).
+ * Policy AUTO; SK_ERR_ARG when bias is NULL. */
 sk_status sk_addmm(sk_dtype dtype, const void* bias, const void* A, const void* B, const void* A_scale,
                    const void* B_scale, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
 
@@ -182,7 +207,10 @@ sk_status sk_gemm_bf16_backward(const void* dC, const void* A, const void* B, vo
                                 int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
 
 /* Full-control entry point: the same kernels with a chosen policy and tile, plus test hooks.
- * Zero-initialise and fill the fields you need. */
+ * Zero-initialise and fill the fields you need.  The policies are the Stream-K
+ * partition of the MAC-iteration space ("Stream-k mxfp4 kernel", description)
+ * and the Persistent path the bias page's tests switch between ("Fix StreamK
+ * Kernel Bias #67", pull request overview); errors as for sk_gemm_mxfp4. */
 typedef struct sk_gemm_args {
   int32_t dtype;            /* sk_dtype */
   int32_t policy;           /* sk_policy */
@@ -206,7 +234,12 @@ typedef struct sk_gemm_args {
 
 sk_status sk_gemm_ex(const sk_gemm_args* args);
 
-/* The partition a call would use (host-only; no device work).  num_cus = 0 asks the current device. */
+/* The partition a call would use (host-only; no device work).  num_cus = 0 asks the current device.
+ * Grid G = min(cap, compute units, work), with a cap above the unit count clamped
+ * to it ("SM-constraint-GEMM by triton persistent kernel", Nsys Results: 133
+ * requested on a 132-unit device ran 132); the Stream-K ranges split the MAC
+ * iterations ("Stream-k mxfp4 kernel", description).  SK_ERR_ARG on a bad query,
+ * SK_ERR_UNSUPPORTED when no compiled kernel has the requested tile. */
 typedef struct sk_plan_query {
   int32_t dtype, policy;
   int64_t M, N, K;
@@ -235,7 +268,9 @@ typedef struct sk_plan_info {
 
 sk_status sk_plan(const sk_plan_query* q, sk_plan_info* out);
 
-/* Stream-K iteration range [begin, end) of workgroup wg under plan p (host-only). */
+/* Stream-K iteration range [begin, end) of workgroup wg under plan p (host-only): the
+ * contiguous range of MAC iterations each persistent workgroup owns ("Stream-k mxfp4
+ * kernel", description).  SK_ERR_ARG for a NULL pointer or wg outside [0, grid). */
 sk_status sk_plan_wg_range(const sk_plan_info* p, int32_t wg, int64_t* begin, int64_t* end);
 
 /* One unit of a workgroup's work: MAC iterations [k0, k1) of output tile `tile`.
@@ -249,15 +284,25 @@ typedef struct sk_work_item {
 } sk_work_item;
 
 /* The ordered work list the kernel runs for workgroup wg under plan p (host-only; the
- * kernel walks the same list).  Writes at most max_items items; *count gets the total. */
+ * kernel walks the same list).  Writes at most max_items items; *count gets the total.
+ * Contributors publish a partial tile and its lock flag, the finishing workgroup
+ * aggregates them and then adds the bias ("Stream-k mxfp4 kernel", the per-workgroup
+ * locks and P buffers of the Copilot comment; "Fix StreamK Kernel Bias #67",
+ * Motivation).  SK_ERR_ARG for a NULL pointer or wg outside [0, grid). */
 sk_status sk_plan_wg_work(const sk_plan_info* p, int32_t wg, sk_work_item* items, int32_t max_items,
                           int32_t* count);
 
-/* Waits for `stream`, then reports (and clears) a device-side timeout recorded in this
- * device/stream's scratch since the last check. */
+/* Waits for `stream` (a hipStream_t), then reports (and clears) a device-side timeout
+ * recorded in this device/stream's scratch since the last check: SK_ERR_TIMEOUT when an
+ * owner gave up waiting for a contributor's lock flag (the per-workgroup locks of
+ * "Stream-k mxfp4 kernel", Copilot comment), SK_ERR_UNSUPPORTED on a capturing stream,
+ * SK_ERR_HIP when the runtime fails. */
 sk_status sk_check(void* stream);
 
-/* Waits for every stream that has scratch, then frees all scratch of every device. */
+/* Waits for every stream that has scratch, then frees all scratch of every device.
+ * The scratch is kept per (device, stream) rather than as one global buffer on the
+ * default device ("Stream-k mxfp4 kernel", Copilot comment on the global Stream-K
+ * scratch buffers). */
 void sk_release_workspace(void);
 
 /* Test hook: fill the current device/stream's scratch (grown to at least scratch_bytes) with

@@ -388,8 +388,30 @@ sk_status next_epoch(Workspace* ws, uint32_t* epoch) {
   return SK_OK;
 }
 
+// A stream being captured into a HIP graph is refused before anything is
+// enqueued: the fixup compares lock flags with an epoch passed as a kernel
+// argument, so a replayed launch would reuse one epoch and an owner could
+// accept the flags (and read the partials) of the previous replay; growing
+// the scratch would also need a synchronisation that capture forbids.
+sk_status refuse_capture(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SK_ERR_HIP;
+  return cs == hipStreamCaptureStatusNone ? SK_OK : SK_ERR_UNSUPPORTED;
+}
+
+// The scratch one launch uses: partial tiles, re-laid scales, the flag words
+// (locks, then the error word) and this launch's epoch.
+struct Scratch {
+  float* P = nullptr;
+  uint8_t* S = nullptr;
+  uint32_t* flags = nullptr;
+  uint32_t epoch = 0;
+};
+
 sk_status run(const sk_gemm_args& g) {
   sk_status st = validate(g);
+  if (st != SK_OK) return st;
+  st = refuse_capture((hipStream_t)g.stream);
   if (st != SK_OK) return st;
   int dev = 0;
   DeviceInfo info;
@@ -427,13 +449,18 @@ sk_status run(const sk_gemm_args& g) {
     if (sa_bytes >= ((int64_t)1 << 31) || sb_bytes >= ((int64_t)1 << 31)) return SK_ERR_ARG;
   }
   const int64_t sb_at = (sa_bytes + 255) / 256 * 256;
-  Workspace* ws = nullptr;
-  st = get_workspace(dev, stream, (size_t)p.scratch_bytes, is_mx(g.dtype) && !direct ? (size_t)(sb_at + sb_bytes) : 0,
-                     &ws);
-  if (st != SK_OK) return st;
-  uint32_t epoch = 0;
-  st = next_epoch(ws, &epoch);
-  if (st != SK_OK) return st;
+  const size_t s_need = is_mx(g.dtype) && !direct ? (size_t)(sb_at + sb_bytes) : 0;
+  Scratch sc;
+  {
+    Workspace* ws = nullptr;
+    st = get_workspace(dev, stream, (size_t)p.scratch_bytes, s_need, &ws);
+    if (st != SK_OK) return st;
+    st = next_epoch(ws, &sc.epoch);
+    if (st != SK_OK) return st;
+    sc.P = ws->P;
+    sc.S = ws->S;
+    sc.flags = ws->flags;
+  }
 
   KArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -448,11 +475,11 @@ sk_status run(const sk_gemm_args& g) {
   } else if (is_mx(g.dtype)) {
     const sk::ScaleLayout la{(int)g.M, v->bm, v->mfma, v->ng, v->bm / v->wm / v->mfma, v->nu};
     const sk::ScaleLayout lb{(int)g.N, v->bn, v->mfma, v->ng, v->bn / v->wn / v->mfma, v->nu};
-    if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, ws->S, la, (const uint8_t*)g.B_scale, ws->S + sb_at, lb,
+    if (sk::launch_scale_relayout((const uint8_t*)g.A_scale, sc.S, la, (const uint8_t*)g.B_scale, sc.S + sb_at, lb,
                                   (int)(g.K / 32), (int)ksteps, (int)spr, stream) != hipSuccess)
       return SK_ERR_HIP;
-    a.SA = ws->S;
-    a.SB = ws->S + sb_at;
+    a.SA = sc.S;
+    a.SB = sc.S + sb_at;
     a.sa_kstride = (uint32_t)(rows_a * spr);
     a.sb_kstride = (uint32_t)(rows_b * spr);
   } else if (g.dtype == SK_FP8_E4M3) {
@@ -461,9 +488,9 @@ sk_status run(const sk_gemm_args& g) {
   }
   a.bias = (const uint16_t*)g.bias;
   a.C = (uint16_t*)g.C;
-  a.P = ws->P;
-  a.locks = ws->flags;
-  a.err = ws->flags + sk::kErrIndex;
+  a.P = sc.P;
+  a.locks = sc.flags;
+  a.err = sc.flags + sk::kErrIndex;
   a.M = (int32_t)g.M;
   a.N = (int32_t)g.N;
   a.K = (int32_t)g.K;
@@ -476,7 +503,7 @@ sk_status run(const sk_gemm_args& g) {
   a.tiles_n = p.tiles_n;
   a.iters = p.iters_per_tile;
   a.G = p.grid;
-  a.epoch = epoch;
+  a.epoch = sc.epoch;
   a.spin_limit = g.spin_limit_ticks ? g.spin_limit_ticks : kDefaultSpin;
   a.drop_wg = (g.debug_flags & SK_DEBUG_DROP_SIGNAL) ? g.drop_signal_wg : -1;
   a.delay_seed = (g.debug_flags & SK_DEBUG_DELAY) ? (g.delay_seed ? g.delay_seed : 1u) : 0u;
@@ -554,7 +581,9 @@ sk_status sk_gemm_bf16_backward(const void* dC, const void* A, const void* B, vo
     return SK_ERR_ARG;
   int dev = 0;
   DeviceInfo info;
-  sk_status st = device_info(&dev, &info);
+  sk_status st = refuse_capture((hipStream_t)stream);
+  if (st != SK_OK) return st;
+  st = device_info(&dev, &info);
   if (st != SK_OK) return st;
   if (!info.gfx950) return SK_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
@@ -605,7 +634,9 @@ sk_status sk_gemm_mx(sk_dtype a_fmt, sk_dtype b_fmt, const uint8_t* A, const uin
   if (overlaps(C, M * N * 2, src4, rows4 * (K / 2))) return SK_ERR_ARG;
   int dev = 0;
   DeviceInfo info;
-  sk_status st = device_info(&dev, &info);
+  sk_status st = refuse_capture((hipStream_t)stream);
+  if (st != SK_OK) return st;
+  st = device_info(&dev, &info);
   if (st != SK_OK) return st;
   if (!info.gfx950) return SK_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
@@ -669,6 +700,8 @@ sk_status sk_plan_wg_work(const sk_plan_info* p, int32_t wg, sk_work_item* items
 sk_status sk_check(void* stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SK_ERR_HIP;
+  const sk_status cap = refuse_capture((hipStream_t)stream);
+  if (cap != SK_OK) return cap;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SK_ERR_HIP;
   Workspace* ws = nullptr;
   {
@@ -708,7 +741,9 @@ void sk_release_workspace(void) {
 sk_status sk_debug_poison_workspace(void* stream, int64_t scratch_bytes) {
   int dev = 0;
   DeviceInfo info;
-  sk_status st = device_info(&dev, &info);
+  sk_status st = refuse_capture((hipStream_t)stream);
+  if (st != SK_OK) return st;
+  st = device_info(&dev, &info);
   if (st != SK_OK) return st;
   Workspace* ws = nullptr;
   st = get_workspace(dev, (hipStream_t)stream, scratch_bytes > 0 ? (size_t)scratch_bytes : 0, 0, &ws);

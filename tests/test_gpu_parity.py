@@ -348,6 +348,40 @@ def test_errors_are_status_codes(small):
     pg.check()
 
 
+def test_graph_capture_is_refused(small):
+    """A stream that is being captured into a HIP graph is refused with
+    SK_ERR_UNSUPPORTED before anything is enqueued (the fixup's epoch is a kernel
+    argument, so a replay would reuse it); after the capture the same call runs
+    normally."""
+    x, d, C = small
+    lib = pg.load()
+    out = torch.full((256, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    side = torch.zeros(16, device="cuda")
+    p = lambda t: t.data_ptr()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    got = []
+    say("capture: sk_gemm_mxfp4, sk_gemm_mx and sk_check on a capturing stream")
+    with torch.cuda.graph(graph):
+        s = torch.cuda.current_stream().cuda_stream
+        got.append(lib.sk_gemm_mxfp4(p(d["A"]), p(d["B"]), p(d["SA"]), p(d["SB"]), p(d["bias"]), p(out),
+                                     256, 256, 512, 5, s))
+        got.append(lib.sk_gemm_mx(0, 0, p(d["A"]), p(d["B"]), p(d["SA"]), p(d["SB"]), p(d["bias"]), p(out),
+                                  256, 256, 512, 5, s))
+        got.append(lib.sk_check(s))
+        side.add_(1.0)
+    assert got == [3, 3, 3], got
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(side[0]) == i + 1.0
+        assert bool((out == 7.0).all()), "a refused call wrote C"
+    say("after capture: the same call, eager")
+    pg.gemm_mxfp4(d["A"], d["B"], d["SA"], d["SB"], d["bias"], out, grid_cap=5)
+    pg.check()
+    assert_bitexact(out.view(torch.int16).cpu().numpy().view(np.uint16), C, "after capture")
+
+
 # ---------------------------------------------------------------- CU-partitioned streams
 
 def _device_cus():
