@@ -12,9 +12,15 @@ MFMA peak are quoted.  Prints one JSON line.
 The ``roofline`` object uses kernel durations measured here with HIP events on
 the launch stream; ``traffic`` comes from the rocprofv3 counter summary kept
 under profiles/ and is reported only while the kernel sources are the ones
-that summary was taken with.  ``cpu_baseline`` times the CPU oracle (test
-infrastructure, never the product path) on the same workload, whole, repeated
-for at least ten seconds.
+that summary was taken with (it counts L2-to-fabric bytes, MALL hits
+included: an upper bound on HBM bytes).  ``cpu_baseline`` times the CPU oracle
+(test infrastructure, never the product path) on the same workload, whole,
+repeated for at least ten seconds.  The default run also times the other
+synthetic configurations at their default launches (``other_configs``: the
+256x256x512 MXFP4 addmm on 5 workgroups, the bf16 addmm at 4096^3, the
+16x8192x8192 MXFP4 GEMM over rotating input copies and the fp8 4096^3 GEMM at
+grid caps 1, 32, 64, 128 and 256), each with its roofline and a shorter oracle
+baseline; ``--no-others`` skips them.
 
     python bench.py --copy-calibration MIB          # plain device copy (counter reference)
     python bench.py --co-schedule C [--workload W]  # the GEMM on C CUs beside a memory-bound kernel
@@ -166,11 +172,12 @@ def cpu_baseline(w, x, budget_s: float = 10.0) -> dict:
     else:
         run_once = lambda: oracle.gemm(w.dtype, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=w.K)
         what = "decode, one matrix product"
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity set
-        threads = len(os.sched_getaffinity(0))
+    except Exception:  # threadpoolctl missing: assume BLAS uses the affinity set
+        threads = cores
     runs, t0 = 0, time.perf_counter()
     while True:
         run_once()
@@ -179,9 +186,10 @@ def cpu_baseline(w, x, budget_s: float = 10.0) -> dict:
         if t >= budget_s:
             break
     flops = float(w.flops) * runs
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "blas_threads": int(threads),
+            "kind": "oracle",
             "sample": f"the whole {w.M}x{w.N}x{w.K} problem, {runs} oracle run(s) in {t:.1f} s (fp64 numpy: "
-                      f"{what} with {threads} BLAS threads, bf16 rounding)"}
+                      f"{what} with {threads} BLAS threads on {cores} cores of the affinity set, bf16 rounding)"}
 
 
 def co_schedule(args, w, d, tile, policy) -> int:
@@ -360,6 +368,149 @@ def pg_call(w, c, bias, C):
     return pg.gemm_ex(w.dtype, c["A"], c["B"], c["SA"], c["SB"], bias, C, policy=pg.AUTO)
 
 
+def device_inputs(torch, w, x, dev) -> dict:
+    """Host arrays of one forward workload -> device tensors for the binding."""
+    d = {}
+    if w.dtype == "mxfp4":
+        for k in ("A", "B", "SA", "SB"):
+            d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
+    elif w.dtype == "mxfp8":
+        for k in ("A", "B"):
+            d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
+        for k in ("SA", "SB"):
+            d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
+    elif w.dtype == "bf16":
+        for k in ("A", "B"):
+            d[k] = torch.from_numpy(x[k].view(np.int16)).view(torch.bfloat16).to(dev)
+        d["SA"] = d["SB"] = None
+    else:
+        for k in ("A", "B"):
+            d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
+        d["SA"] = torch.tensor([x["SA"]], dtype=torch.float32, device=dev)
+        d["SB"] = torch.tensor([x["SB"]], dtype=torch.float32, device=dev)
+    d["bias"] = None if x["bias"] is None else torch.from_numpy(x["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
+    return d
+
+
+def time_steps(torch, pg, step, steps: int, warmup: int) -> dict:
+    """Wall time per step over `steps` timed steps (after `warmup`), HIP events around
+    each call, and the device time per call: the same steps again between two
+    events on the launch stream, with a spin kernel queued first so that the host
+    stays ahead and the calls run back to back."""
+    for i in range(warmup):
+        step(i)
+    pg.check()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pg.check()
+    call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    torch.cuda.synchronize()
+    hold_device(torch, 200_000 * steps)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for i in range(steps):
+        step(i)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    pg.check()
+    return {"ms_per_step": wall / steps * 1e3, "call_ms": call_ms, "dev_ms": d0.elapsed_time(d1) / steps}
+
+
+def roofline_of(w, p, dev_ms: float, call_ms, traffic, cap_scaled: bool) -> dict:
+    """The roofline object of one workload: MFMA-bound (FLOP/s against the dtype's dense
+    peak, scaled by grid/256 for a capped grid) or, for the 16-row MXFP4 shape,
+    HBM-bound (algorithmic bytes/s against 8 TB/s)."""
+    s = dev_ms / 1e3
+    ab = algorithmic_bytes(w)
+    peak = PEAK_TFLOPS[w.dtype] * (p.grid / 256.0 if cap_scaled else 1.0)
+    achieved = float(w.flops) / s / 1e12
+    r = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+         "frac": round(achieved / peak, 4), "traffic": traffic,
+         "traffic_what": ("HBM bytes per launch, upper bound: the L2-to-fabric FETCH_SIZE + WRITE_SIZE counters of "
+                          "the kernel (MALL hits included), each scaled by what it reads for a plain copy"),
+         "kernel_ms": {"mean": round(dev_ms, 5),
+                       "how": "device time per call, back-to-back calls between two HIP events"},
+         "call_ms": {"mean": round(float(np.mean(call_ms)), 5), "min": round(float(np.min(call_ms)), 5),
+                     "median": round(float(np.median(call_ms)), 5), "max": round(float(np.max(call_ms)), 5),
+                     "how": "HIP events around each call of the timed loop"},
+         "algorithmic_bytes": ab, "hbm_gbs_at_algorithmic_bytes": round(ab / s / 1e9, 1)}
+    if w.dtype == "mxfp4" and w.M <= 16:
+        r.update({"bound": "hbm", "achieved": round(ab / s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                  "frac": round(ab / s / 1e9 / PEAK_HBM_GBS, 4)})
+    return r
+
+
+def plan_config(pg, p) -> dict:
+    return {"tile": f"{p.tile_m}x{p.tile_n}x{p.tile_k}", "threads": p.threads, "variant": p.variant,
+            "policy": {pg.HYBRID: "hybrid", pg.PURE_SK: "sk", pg.PURE_DP: "dp"}[p.policy], "grid": p.grid,
+            "sk_tiles": p.sk_tiles, "tiles": p.tiles}
+
+
+# The other synthetic configurations, each timed at its default launch beside the
+# headline (the MXFP4 addmm at 8192^3): the 256x256x512 MXFP4 addmm on a grid of
+# 5 (latency-bound), the bf16 addmm at 4096^3, the skinny 16x8192x8192 MXFP4
+# GEMM (HBM-bound, timed over rotating input copies) and the fp8 4096^3 GEMM at
+# each grid cap of its sweep.
+OTHER_CONFIGS = ("mxfp4_addmm_256x256x512_g5", "bf16_addmm_4096", "mxfp4_gemm_16x8192x8192",
+                 "fp8_gemm_4096_capsweep")
+
+
+def other_configs(torch, pg, dev, steps: int, warmup: int, cpu: bool) -> list:
+    from persistent_gemm_amd.inputs import WORKLOADS, make_inputs
+    out = []
+    for name in OTHER_CONFIGS:
+        w = WORKLOADS[name]
+        x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
+        copies = [device_inputs(torch, w, x, dev)]
+        for _ in range(1, max(1, w.rotate)):
+            copies.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in copies[0].items()})
+        C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        tile = tuple(int(v) for v in w.tile.split("x")) if w.tile else None
+        caps = w.caps or (w.grid_cap,)
+        rec = {"workload": name, "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
+               "input_copies": len(copies)}
+        runs = []
+        for cap in caps:
+            p = pg.plan(w.dtype, w.M, w.N, w.K, grid_cap=cap, policy=pg.AUTO, tile=tile)
+
+            def step(i, cap=cap):
+                c = copies[i % len(copies)]
+                pg.gemm_ex(w.dtype, c["A"], c["B"], c["SA"], c["SB"], c["bias"], C, grid_cap=cap, policy=pg.AUTO,
+                           tile=tile)
+
+            # a capped call takes up to 256/cap times longer (about 10 ms at cap 1): fewer repetitions there
+            n = max(3, min(steps, steps * p.grid // 256)) if w.caps else steps
+            t = time_steps(torch, pg, step, n, min(warmup, n))
+            r = {"grid_cap": cap, "steps": n, "ms_per_step": round(t["ms_per_step"], 5),
+                 "value": round(float(w.flops) / (t["ms_per_step"] / 1e3) / 1e12, 3), "unit": "TFLOP/s",
+                 "config": plan_config(pg, p),
+                 "roofline": roofline_of(w, p, t["dev_ms"], t["call_ms"], None, bool(w.caps))}
+            if name == "mxfp4_addmm_256x256x512_g5":
+                # 67 MFLOP on 5 workgroups: the call is bound by launch and fixup latency, not by a roofline
+                r["roofline"].update({"bound": "latency"})
+            runs.append(r)
+        if len(runs) == 1:
+            rec.update(runs[0])
+        else:
+            rec["cap_sweep"] = runs
+        if cpu:
+            rec["cpu_baseline"] = cpu_baseline(w, x, budget_s=3.0)
+        out.append(rec)
+        del copies, C
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -371,7 +522,9 @@ def main() -> int:
     ap.add_argument("--policy", default="auto", choices=["auto", "hybrid", "sk", "dp"],
                     help="auto: the measured kernel and policy for the shape (what the plain entry points use)")
     ap.add_argument("--variant", type=int, default=None, help="compiled kernel index (default: automatic)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other configurations (only the named workload is timed)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="rotate over this many input copies (defeats the MALL; default: the workload's)")
     ap.add_argument("--co-schedule", type=int, default=0, metavar="C",
@@ -435,33 +588,10 @@ def main() -> int:
             pg.gemm_mx("mxfp4", "mxfp8", d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap)
     else:
         x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
-
-        def to_dev(x):
-            d = {}
-            if w.dtype == "mxfp4":
-                for k in ("A", "B", "SA", "SB"):
-                    d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
-            elif w.dtype == "mxfp8":
-                for k in ("A", "B"):
-                    d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
-                for k in ("SA", "SB"):
-                    d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
-            elif w.dtype == "bf16":
-                for k in ("A", "B"):
-                    d[k] = torch.from_numpy(x[k].view(np.int16)).view(torch.bfloat16).to(dev)
-                d["SA"] = d["SB"] = None
-            else:
-                for k in ("A", "B"):
-                    d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
-                d["SA"] = torch.tensor([x["SA"]], dtype=torch.float32, device=dev)
-                d["SB"] = torch.tensor([x["SB"]], dtype=torch.float32, device=dev)
-            d["bias"] = None if x["bias"] is None else torch.from_numpy(x["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
-            return d
-
         if args.co_schedule:
-            return co_schedule(args, w, to_dev(x), tile, policy)
+            return co_schedule(args, w, device_inputs(torch, w, x, dev), tile, policy)
 
-        copies = [to_dev(x)]
+        copies = [device_inputs(torch, w, x, dev)]
         for i in range(1, max(1, args.rotate or w.rotate)):
             copies.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in copies[0].items()})
         C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
@@ -475,47 +605,9 @@ def main() -> int:
         if args.vendor:
             return vendor(args, w, copies, C, step)
 
-    for i in range(args.warmup):
-        step(i)
-    pg.check()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pg.check()
-
-    call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_per_step = wall / args.steps * 1e3
-
-    # Device time per call: the same steps again between two events, with a
-    # spin kernel queued first so the host stays ahead of the device and the
-    # events see the launches back to back (the per-call events above also
-    # count the time a call waits for the host when the call is short).
-    torch.cuda.synchronize()
-    hold_device(torch, 200_000 * args.steps)
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    pg.check()
-    dev_ms = d0.elapsed_time(d1) / args.steps
-    avg_kern_s = dev_ms / 1e3
-    flops = float(w.flops)
-    value = flops / (ms_per_step / 1e3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
-    eff_peak = peak * (p.grid / 256.0 if args.workload.startswith("fp8_gemm_4096_cap") else 1.0)
-    achieved = flops / avg_kern_s / 1e12
+    t = time_steps(torch, pg, step, args.steps, args.warmup)
+    ms_per_step = t["ms_per_step"]
+    value = float(w.flops) / (ms_per_step / 1e3) / 1e12
     default_launch = args.cap is None and args.tile is None and policy == pg.AUTO and args.variant is None
     tag = "" if default_launch else "_nondefault"
     traffic = traffic_for(args.workload, tag, p.variant)
@@ -535,29 +627,19 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
-                   "input_copies": max(1, args.rotate or w.rotate),
-                   "tile": f"{p.tile_m}x{p.tile_n}x{p.tile_k}", "threads": p.threads, "variant": p.variant,
-                   "policy": {pg.HYBRID: "hybrid", pg.PURE_SK: "sk", pg.PURE_DP: "dp"}[p.policy],
-                   "policy_requested": args.policy, "grid": p.grid,
-                   "sk_tiles": p.sk_tiles, "tiles": p.tiles, "parallelism": "stream-k, 1 GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": eff_peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / eff_peak, 4), "traffic": traffic,
-                     "kernel_ms": {"mean": round(dev_ms, 5),
-                                   "how": "device time per call, back-to-back calls between two HIP events"},
-                     "call_ms": {"mean": round(float(np.mean(call_ms)), 5), "min": round(float(np.min(call_ms)), 5),
-                                 "median": round(float(np.median(call_ms)), 5),
-                                 "max": round(float(np.max(call_ms)), 5),
-                                 "how": "HIP events around each call of the timed loop"},
-                     "algorithmic_bytes": algorithmic_bytes(w),
-                     "hbm_gbs_at_algorithmic_bytes": round(algorithmic_bytes(w) / avg_kern_s / 1e9, 1)},
+                   "input_copies": max(1, args.rotate or w.rotate), **plan_config(pg, p),
+                   "policy_requested": args.policy, "parallelism": "stream-k, 1 GPU"},
+        "roofline": roofline_of(w, p, t["dev_ms"], t["call_ms"], traffic,
+                                args.workload.startswith("fp8_gemm_4096_cap")),
     }
-    if w.dtype == "mxfp4" and w.M <= 16:
-        ab = algorithmic_bytes(w)
-        out["roofline"].update({"bound": "hbm", "achieved": round(ab / avg_kern_s / 1e9, 1),
-                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(ab / avg_kern_s / 1e9 / PEAK_HBM_GBS, 4)})
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x)
+    if args.workload == DEFAULT_WORKLOAD and default_launch and not args.no_others:
+        del step
+        if w.op == "forward" and w.dtype != "mxfp4_mxfp8":
+            del copies, C
+        torch.cuda.empty_cache()
+        out["other_configs"] = other_configs(torch, pg, dev, args.steps, args.warmup, not args.no_cpu)
     print(json.dumps(out), flush=True)
     return 0
 
