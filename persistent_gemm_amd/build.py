@@ -20,16 +20,20 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    objs = []
+    """Compile every source (in parallel) and link the shared library; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+    objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd.insert(1, "-x")
             cmd.insert(2, "hip")
-        _run(cmd, verbose)
+        cmds.append(cmd)
         objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

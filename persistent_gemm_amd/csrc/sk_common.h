@@ -196,7 +196,5 @@ hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int rows, i
 // holds colsum_scratch_bytes(M, N) bytes of device scratch.
 int64_t colsum_scratch_bytes(int M, int N);
 hipError_t launch_colsum_bf16(const uint16_t* dc, float* part, uint16_t* dbias, int M, int N, hipStream_t s);
-hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, int rows_a, const uint8_t* src_b, uint8_t* dst_b,
-                                 int rows_b, int s_pitch, int ksteps, int spr, hipStream_t s);
 
 }  // namespace sk

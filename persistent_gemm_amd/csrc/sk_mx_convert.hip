@@ -13,21 +13,6 @@ namespace sk {
 
 namespace {
 
-// E4M3FN byte of each E2M1 code (sign bit 7; exponent bias 7, three mantissa
-// bits): 0.5 = 2^-1 -> 0x30, 1 -> 0x38, 1.5 -> 0x3C, 2 -> 0x40, 3 -> 0x44,
-// 4 -> 0x48, 6 -> 0x4C; code 8 (-0) -> 0x80.
-[[maybe_unused]] __device__ __forceinline__ uint32_t e2m1_to_e4m3(uint32_t code) {
-  const uint32_t mag = code & 7u, sign = (code & 8u) << 4;
-  // magnitudes 1..7: exponent field 6 + (mag >> 1) for mag >= 2 (E2M1 field
-  // e is worth 2^(e-1), E4M3 field f is worth 2^(f-7)), 6 for mag 1 (0.5);
-  // mantissa bit 2 from the E2M1 mantissa bit (mag & 1) when mag >= 2
-  uint32_t e;
-  if (mag == 0u) e = 0u;
-  else if (mag == 1u) e = 0x30u;
-  else e = ((6u + (mag >> 1)) << 3) | ((mag & 1u) << 2);
-  return sign | e;
-}
-
 typedef uint32_t v4w __attribute__((ext_vector_type(4)));
 
 // The E4M3 bytes of the eight E2M1 magnitudes as a byte table for v_perm_b32,
