@@ -78,7 +78,9 @@
  *   SK_ERR_HIP          a HIP runtime call failed;
  *   SK_ERR_NOMEM        scratch could not be allocated;
  *   SK_ERR_TIMEOUT      (sk_check only) a workgroup gave up waiting for a
- *                       partial tile; the affected output tiles are unwritten.
+ *                       partial tile; the affected output tiles are unwritten;
+ *   SK_ERR_SCRATCH      (sk_gemm_mxfp4_noalloc only) the call needs more
+ *                       scratch than its fixed buffer holds.
  */
 #ifndef SK_GEMM_H
 #define SK_GEMM_H
@@ -96,7 +98,8 @@ typedef enum sk_status {
   SK_ERR_UNSUPPORTED = 3,
   SK_ERR_HIP = 4,
   SK_ERR_NOMEM = 5,
-  SK_ERR_TIMEOUT = 6
+  SK_ERR_TIMEOUT = 6,
+  SK_ERR_SCRATCH = 7
 } sk_status;
 
 typedef enum sk_dtype { SK_MXFP4 = 0, SK_BF16 = 1, SK_FP8_E4M3 = 2, SK_MXFP8 = 3 } sk_dtype;
@@ -138,6 +141,31 @@ typedef enum sk_policy {
  * stream's compute units).  stream is a hipStream_t passed as void*. */
 sk_status sk_gemm_mxfp4(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
                         const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
+
+/* sk_gemm_mxfp4 for callers that cannot allocate device memory (code in a serving
+ * loop that must not call hipMalloc, harnesses that forbid allocation): the same
+ * arguments, kernels and result, with every piece of scratch -- lock flags and the
+ * error word, fp32 partial tiles, the re-laid MX scales -- taken from one fixed
+ * device array of the library (a static __device__ buffer of 8 KiB of flags plus
+ * 32 MiB, of which each device the library runs on keeps its own copy until the
+ * process ends).  Nothing is allocated, freed or grown, by this library or by any
+ * library it calls, after the first call on a device, which looks up the array's
+ * address and clears its flag words.
+ *   Limits: partial tiles plus re-laid scales must fit in 32 MiB.  When the tuned
+ *   plan's partial tiles do not fit, the same kernel runs data-parallel over whole
+ *   tiles instead (MXFP4 sums are exact in fp32 in any order, so C is bit-for-bit
+ *   the same); when the re-laid scales alone do not fit ((M + N) * K / 32 bytes,
+ *   rounded up to whole tiles, about 32 MiB) the call returns SK_ERR_SCRATCH and
+ *   enqueues nothing.
+ *   Sharing: every call on a device uses that device's one array, which keeps the
+ *   last call's contents; calls whose execution overlaps on one device (two
+ *   streams, or two host threads without ordering) race on it and may give wrong
+ *   results -- order them on one stream.  A device-side timeout is reported by
+ *   sk_check on any stream of the device.  Errors otherwise as for sk_gemm_mxfp4;
+ *   a capturing stream is refused the same way. */
+sk_status sk_gemm_mxfp4_noalloc(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
+                                const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap,
+                                void* stream);
 
 /* bf16 x bf16 -> bf16.  bias may be NULL.  The Stream-K matmul that the bias
  * page's correctness tests run on both the Persistent and the Stream-K path and

@@ -22,7 +22,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL", "DEBUG_RELAYOUT",
-    "library_path", "load", "gemm_mxfp4", "gemm_mxfp8", "gemm_bf16", "gemm_bf16_backward", "gemm_mx", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
+    "library_path", "load", "gemm_mxfp4", "gemm_mxfp4_noalloc", "gemm_mxfp8", "gemm_bf16", "gemm_bf16_backward", "gemm_mx", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
     "cu_masked_stream", "destroy_stream", "stream_cu_count",
 ]
@@ -32,7 +32,7 @@ HYBRID, PURE_SK, PURE_DP, AUTO = 0, 1, 2, 3
 DEBUG_DELAY, DEBUG_DROP_SIGNAL, DEBUG_RELAYOUT = 1, 2, 4
 
 _STATUS = {0: "SK_OK", 1: "SK_ERR_ARG", 2: "SK_ERR_ALIGN", 3: "SK_ERR_UNSUPPORTED", 4: "SK_ERR_HIP",
-           5: "SK_ERR_NOMEM", 6: "SK_ERR_TIMEOUT"}
+           5: "SK_ERR_NOMEM", 6: "SK_ERR_TIMEOUT", 7: "SK_ERR_SCRATCH"}
 _DTYPES = {"mxfp4": MXFP4, "bf16": BF16, "fp8": FP8, "mxfp8": MXFP8}
 
 
@@ -124,6 +124,7 @@ def load():
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.sk_gemm_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.sk_gemm_mxfp4_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.sk_gemm_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
@@ -148,7 +149,7 @@ def load():
     lib.sk_stream_cu_count.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
     lib.sk_status_string.argtypes = [ctypes.c_int]
     lib.sk_status_string.restype = ctypes.c_char_p
-    for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_bf16_backward", "sk_gemm_mx", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
+    for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp4_noalloc", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_bf16_backward", "sk_gemm_mx", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
                  "sk_plan_wg_range", "sk_plan_wg_work", "sk_check", "sk_debug_poison_workspace", "sk_variant_info",
                  "sk_stream_create_cu_masked", "sk_stream_destroy", "sk_stream_cu_count"):
         getattr(lib, name).restype = ctypes.c_int
@@ -264,6 +265,15 @@ def gemm_mxfp4(A, B, A_scale, B_scale, bias=None, C=None, grid_cap=0, stream=Non
     M, N, K, C = _marshal(MXFP4, A, B, A_scale, B_scale, bias, C)
     _ok(load().sk_gemm_mxfp4(_ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale), _ptr(bias), _ptr(C), M, N, K,
                              int(grid_cap), _stream(A, stream)), "sk_gemm_mxfp4")
+    return C
+
+
+def gemm_mxfp4_noalloc(A, B, A_scale, B_scale, bias=None, C=None, grid_cap=0, stream=None):
+    """gemm_mxfp4 with the library's fixed device scratch (no device allocation by the
+    library; pass C to avoid the binding's own torch.empty).  Returns C."""
+    M, N, K, C = _marshal(MXFP4, A, B, A_scale, B_scale, bias, C)
+    _ok(load().sk_gemm_mxfp4_noalloc(_ptr(A), _ptr(B), _ptr(A_scale), _ptr(B_scale), _ptr(bias), _ptr(C), M, N, K,
+                                     int(grid_cap), _stream(A, stream)), "sk_gemm_mxfp4_noalloc")
     return C
 
 

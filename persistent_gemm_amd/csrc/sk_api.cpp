@@ -388,6 +388,46 @@ sk_status next_epoch(Workspace* ws, uint32_t* epoch) {
   return SK_OK;
 }
 
+// ---------------------------------------------------------------- fixed scratch (no allocation)
+//
+// sk_gemm_mxfp4_noalloc runs the same kernels with their scratch (lock flags
+// and the error word, fp32 partial tiles, the re-laid MX scales) taken from
+// this file-scope device array instead of the per-(device, stream)
+// workspace, for callers that cannot allocate device memory.  Each device the
+// library runs on holds its own copy until the process ends.  Host code never
+// uses the array's name as an address: its device address is read once per
+// device (static_scratch) and only that pointer is passed on.
+constexpr size_t kStaticFlagBytes = 8192;               // the flag words, rounded up
+constexpr size_t kStaticDataBytes = (size_t)32 << 20;   // partial tiles and re-laid scales
+static_assert(sk::kFlagWords * sizeof(uint32_t) <= kStaticFlagBytes, "flag words fit");
+static __device__ __align__(256) uint8_t scratch[kStaticFlagBytes + kStaticDataBytes];
+
+constexpr int kMaxDevices = 64;
+struct StaticScratch {
+  uint8_t* ptr = nullptr;   // device address of `scratch` on this device
+  uint32_t epoch = 0;       // last epoch used on it
+};
+StaticScratch g_static[kMaxDevices];   // guarded by g_mu
+
+// The device address of this device's copy of `scratch`, set up on the first
+// call: the address comes from the runtime (the array's name is only a
+// host-side stand-in), and the flag words are cleared once, on `stream`,
+// before any kernel reads them.  Called with g_mu unlocked.
+sk_status static_scratch(int dev, hipStream_t stream, uint8_t** out) {
+  if (dev < 0 || dev >= kMaxDevices) return SK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_mu);
+  StaticScratch& st = g_static[dev];
+  if (!st.ptr) {
+    uint8_t* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SK_ERR_HIP;
+    if (hipMemsetAsync(ptr, 0, kStaticFlagBytes, stream) != hipSuccess) return SK_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return SK_ERR_HIP;
+    st.ptr = ptr;
+  }
+  *out = st.ptr;
+  return SK_OK;
+}
+
 // A stream being captured into a HIP graph is refused before anything is
 // enqueued: the fixup compares lock flags with an epoch passed as a kernel
 // argument, so a replayed launch would reuse one epoch and an owner could
@@ -408,7 +448,10 @@ struct Scratch {
   uint32_t epoch = 0;
 };
 
-sk_status run(const sk_gemm_args& g) {
+// fixed: take the scratch from this device's `scratch` array (nothing is
+// allocated); a plan whose partial tiles do not fit there runs data-parallel
+// instead, and one whose re-laid scales do not fit is refused (SK_ERR_SCRATCH).
+sk_status run(const sk_gemm_args& g, bool fixed = false) {
   sk_status st = validate(g);
   if (st != SK_OK) return st;
   st = refuse_capture((hipStream_t)g.stream);
@@ -424,6 +467,12 @@ sk_status run(const sk_gemm_args& g) {
   const int cus = stream_cus(dev, (hipStream_t)g.stream, info.cus);
   st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, cus, &p);
   if (st != SK_OK) return st;
+  if (fixed && (uint64_t)p.scratch_bytes > kStaticDataBytes) {
+    // The same kernel over whole tiles needs no partial tiles.  Only MXFP4 takes
+    // this path, whose fp32 sums are exact in any order: the bits are the same.
+    st = make_plan(g.dtype, SK_POLICY_PURE_DP, g.M, g.N, g.K, g.grid_cap, 0, 0, p.variant + 1, cus, &p);
+    if (st != SK_OK) return st;
+  }
   hipStream_t stream = (hipStream_t)g.stream;
   const Variant* v = sk::variant(p.variant);
   // MX scales are read from a k-step-major copy in the kernel's lane order:
@@ -451,7 +500,23 @@ sk_status run(const sk_gemm_args& g) {
   const int64_t sb_at = (sa_bytes + 255) / 256 * 256;
   const size_t s_need = is_mx(g.dtype) && !direct ? (size_t)(sb_at + sb_bytes) : 0;
   Scratch sc;
-  {
+  if (fixed) {
+    const size_t p_at = ((size_t)p.scratch_bytes + 255) / 256 * 256;
+    if (p_at + s_need > kStaticDataBytes) return SK_ERR_SCRATCH;
+    uint8_t* base = nullptr;
+    st = static_scratch(dev, stream, &base);
+    if (st != SK_OK) return st;
+    sc.flags = (uint32_t*)base;
+    sc.P = (float*)(base + kStaticFlagBytes);
+    sc.S = base + kStaticFlagBytes + p_at;
+    std::lock_guard<std::mutex> lk(g_mu);
+    StaticScratch& ss = g_static[dev];
+    if (ss.epoch == 0xFFFFFFFFu) {
+      if (hipMemsetAsync(sc.flags, 0, sk::kMaxGrid * sizeof(uint32_t), stream) != hipSuccess) return SK_ERR_HIP;
+      ss.epoch = 0;
+    }
+    sc.epoch = ++ss.epoch;
+  } else {
     Workspace* ws = nullptr;
     st = get_workspace(dev, stream, (size_t)p.scratch_bytes, s_need, &ws);
     if (st != SK_OK) return st;
@@ -539,6 +604,12 @@ extern "C" {
 sk_status sk_gemm_mxfp4(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
                         const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream) {
   return run(base_args(SK_MXFP4, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
+}
+
+sk_status sk_gemm_mxfp4_noalloc(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
+                                const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap,
+                                void* stream) {
+  return run(base_args(SK_MXFP4, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream), true);
 }
 
 sk_status sk_gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
@@ -703,20 +774,26 @@ sk_status sk_check(void* stream) {
   const sk_status cap = refuse_capture((hipStream_t)stream);
   if (cap != SK_OK) return cap;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SK_ERR_HIP;
-  Workspace* ws = nullptr;
+  // the error words this stream's launches may have set: its workspace's,
+  // and the fixed scratch's of this device (sk_gemm_mxfp4_noalloc)
+  uint32_t* words[2] = {nullptr, nullptr};
   {
     std::lock_guard<std::mutex> lk(g_mu);
     auto it = g_ws.find(std::make_pair(dev, (uintptr_t)stream));
-    if (it == g_ws.end()) return SK_OK;
-    ws = it->second;
+    if (it != g_ws.end() && it->second) words[0] = it->second->flags + sk::kErrIndex;
+    if (dev >= 0 && dev < kMaxDevices && g_static[dev].ptr) words[1] = (uint32_t*)g_static[dev].ptr + sk::kErrIndex;
   }
-  uint32_t err = 0;
-  if (hipMemcpy(&err, ws->flags + sk::kErrIndex, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return SK_ERR_HIP;
-  if (err) {
-    if (hipMemset(ws->flags + sk::kErrIndex, 0, sizeof(uint32_t)) != hipSuccess) return SK_ERR_HIP;
-    return SK_ERR_TIMEOUT;
+  bool timed_out = false;
+  for (uint32_t* wp : words) {
+    if (!wp) continue;
+    uint32_t err = 0;
+    if (hipMemcpy(&err, wp, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return SK_ERR_HIP;
+    if (err) {
+      if (hipMemset(wp, 0, sizeof(uint32_t)) != hipSuccess) return SK_ERR_HIP;
+      timed_out = true;
+    }
   }
-  return SK_OK;
+  return timed_out ? SK_ERR_TIMEOUT : SK_OK;
 }
 
 void sk_release_workspace(void) {
@@ -834,6 +911,7 @@ const char* sk_status_string(sk_status s) {
     case SK_ERR_HIP: return "HIP runtime error";
     case SK_ERR_NOMEM: return "out of device memory";
     case SK_ERR_TIMEOUT: return "a workgroup timed out waiting for a partial tile";
+    case SK_ERR_SCRATCH: return "the call needs more device scratch than the fixed no-allocation buffer holds";
   }
   return "unknown status";
 }

@@ -79,8 +79,9 @@ def test_addmm_requires_bias():
 
 def test_status_strings():
     lib = pg.load()
-    for s in range(7):
+    for s in range(8):
         assert lib.sk_status_string(s)
+    assert b"scratch" in lib.sk_status_string(7)
     assert lib.sk_check  # exported
 
 
