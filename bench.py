@@ -511,6 +511,30 @@ def other_configs(torch, pg, dev, steps: int, warmup: int, cpu: bool) -> list:
     return out
 
 
+def trace_calls(args, torch, pg, w, copies, C, cap, policy, tile, p) -> int:
+    """The launch's phase trace on `args.trace` calls (after the warm-ups), one JSON line each."""
+    buf = torch.zeros(32 * p.grid, dtype=torch.int64, device=C.device)
+    for i in range(args.warmup):
+        d = copies[i % len(copies)]
+        pg.gemm_ex(w.dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap, policy=policy, tile=tile,
+                   variant=args.variant)
+    pg.check()
+    for i in range(args.trace):
+        d = copies[(args.warmup + i) % len(copies)]
+        buf.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pg.gemm_ex(w.dtype, d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap, policy=policy, tile=tile,
+                   variant=args.variant, trace=buf)
+        e1.record()
+        pg.check()
+        summ = pg.phase_summary(buf.cpu().numpy(), p.grid)
+        print(json.dumps({"workload": args.workload, "call": i, "event_us": round(e0.elapsed_time(e1) * 1e3, 2),
+                          "config": plan_config(pg, p), "input_copies": len(copies), "phases": summ}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -534,6 +558,10 @@ def main() -> int:
     ap.add_argument("--vendor", action="store_true",
                     help="time the vendor library (hipBLASLt through torch.addmm / torch._scaled_mm) on the "
                          "same inputs instead (context only; its own JSON line)")
+    ap.add_argument("--trace", type=int, default=0, metavar="CALLS",
+                    help="instead of timing, run CALLS calls of the launch with the library's phase trace and "
+                         "print each call's phase summary (per-workgroup 100 MHz stamps: ramp, streaming, "
+                         "fixup waits, epilogues) as one JSON line")
     ap.add_argument("--traffic-summary", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV output (no GPU)")
@@ -604,6 +632,8 @@ def main() -> int:
 
         if args.vendor:
             return vendor(args, w, copies, C, step)
+        if args.trace:
+            return trace_calls(args, torch, pg, w, copies, C, cap, policy, tile, p)
 
     t = time_steps(torch, pg, step, args.steps, args.warmup)
     ms_per_step = t["ms_per_step"]

@@ -258,6 +258,17 @@ typedef struct sk_gemm_args {
   int32_t variant;          /* 0: automatic; k > 0: compiled kernel k-1 (see sk_variant_info), which must
                                match dtype (SK_ERR_UNSUPPORTED otherwise); overrides tile_m, tile_n */
   uint64_t spin_limit_ticks;/* owner wait limit in ticks of the 100 MHz device clock; 0 = 2e8 (2 s) */
+  uint64_t* trace;          /* NULL, or a device buffer of 32 uint64 per workgroup of the launch (sk_plan's
+                               grid): a phase trace.  Wave 0 of workgroup w writes 100 MHz timestamps
+                               (s_memrealtime) to trace[32 w + i]: i = 0 entry; 29 after the first
+                               argument reads; 28 first stages' loads issued; 27 stage 0 landed; for its
+                               work items j < 6, i = 1 + 4 j first k-step, 2 + 4 j k-steps done, 3 + 4 j
+                               partial published / owner's waits done, 4 + 4 j item finished; 30 the item
+                               count; 31 exit.  Words of items not reached are left as they were.  The
+                               timing of traced calls is the same code's (the stores are wave 0's only);
+                               the stamps let the phases of a persistent launch -- ramp, streaming,
+                               fixup waits, epilogues -- be read per workgroup ("SM-constraint-GEMM by
+                               triton persistent kernel", SM usage by nsys profile). */
 } sk_gemm_args;
 
 sk_status sk_gemm_ex(const sk_gemm_args* args);

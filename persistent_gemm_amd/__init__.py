@@ -24,7 +24,7 @@ __all__ = [
     "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL", "DEBUG_RELAYOUT",
     "library_path", "load", "gemm_mxfp4", "gemm_mxfp4_noalloc", "gemm_mxfp8", "gemm_bf16", "gemm_bf16_backward", "gemm_mx", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
-    "cu_masked_stream", "destroy_stream", "stream_cu_count",
+    "cu_masked_stream", "destroy_stream", "stream_cu_count", "phase_summary",
 ]
 
 MXFP4, BF16, FP8, MXFP8 = 0, 1, 2, 3
@@ -55,6 +55,7 @@ class _Args(ctypes.Structure):
         ("debug_flags", ctypes.c_uint32), ("delay_seed", ctypes.c_uint32),
         ("drop_signal_wg", ctypes.c_int32), ("variant", ctypes.c_int32),
         ("spin_limit_ticks", ctypes.c_uint64),
+        ("trace", ctypes.c_void_p),
     ]
 
 
@@ -362,8 +363,11 @@ def addmm(dtype, bias, A, B, A_scale=None, B_scale=None, C=None, grid_cap=0, str
 
 def gemm_ex(dtype, A, B, A_scale=None, B_scale=None, bias=None, C=None, *, grid_cap=0, policy=HYBRID,
             tile=None, stream=None, debug_flags=0, delay_seed=0, drop_signal_wg=-1, spin_limit_ticks=0,
-            variant=None):
-    """The same kernels with an explicit policy / tile and the test hooks of sk_gemm_ex."""
+            variant=None, trace=None):
+    """The same kernels with an explicit policy / tile and the test hooks of sk_gemm_ex.
+
+    trace: None, or a device int64 tensor of at least 32 * grid elements that receives the
+    launch's phase trace (see sk_gemm_args.trace; phase_summary turns it into durations)."""
     d = _dt(dtype)
     M, N, K, C = _marshal(d, A, B, A_scale, B_scale, bias, C)
     a = _Args()
@@ -377,8 +381,38 @@ def gemm_ex(dtype, A, B, A_scale=None, B_scale=None, bias=None, C=None, *, grid_
     a.debug_flags, a.delay_seed = int(debug_flags), int(delay_seed)
     a.drop_signal_wg, a.spin_limit_ticks = int(drop_signal_wg), int(spin_limit_ticks)
     a.variant = 0 if variant is None else int(variant) + 1
+    if trace is not None:
+        p = plan(d, M, N, K, grid_cap=grid_cap, policy=policy, tile=tile, variant=variant,
+                 num_cus=stream_cu_count(a.stream))
+        if trace.device != A.device or trace.dtype.itemsize != 8 or trace.numel() < 32 * p.grid or \
+                not trace.is_contiguous():
+            raise ValueError(f"trace must be a contiguous 8-byte tensor of at least {32 * p.grid} elements on "
+                             f"{A.device}")
+        a.trace = trace.data_ptr()
     _ok(load().sk_gemm_ex(ctypes.byref(a)), "sk_gemm_ex")
     return C
+
+
+def phase_summary(words, grid: int) -> dict:
+    """Phase durations (microseconds) from a launch's trace words (host int array of 32 * grid):
+    min / median / max over the workgroups of each phase, relative to the earliest entry."""
+    import numpy as np
+    t = np.asarray(words, dtype=np.int64).reshape(-1, 32)[:grid]
+    t0 = t[:, 0].min()
+    us = lambda v: (np.asarray(v, dtype=np.float64)) / 100.0
+    f = lambda a: [round(float(np.min(a)), 2), round(float(np.median(a)), 2), round(float(np.max(a)), 2)]
+    out = {"workgroups": int(grid), "span_us": round(float(us(t[:, 31].max() - t0)), 2),
+           "entry_us": f(us(t[:, 0] - t0)), "exit_us": f(us(t[:, 31] - t0)),
+           "prologue_args_us": f(us(t[:, 29] - t[:, 0])), "prologue_issue_us": f(us(t[:, 28] - t[:, 29])),
+           "prologue_land_us": f(us(t[:, 27] - t[:, 28])), "items": []}
+    n = t[:, 30]
+    for j in range(min(int(n.max()), 6)):
+        has = n > j
+        st, ke, fx, en = (t[has, 1 + 4 * j + i] for i in range(4))
+        out["items"].append({"item": j, "workgroups": int(has.sum()), "start_us": f(us(st - t0)),
+                             "ksteps_us": f(us(ke - st)), "publish_or_wait_us": f(us(fx - ke)),
+                             "epilogue_us": f(us(en - fx)), "end_us": f(us(en - t0))})
+    return out
 
 
 def plan(dtype, M, N, K, *, grid_cap=0, policy=HYBRID, tile=None, num_cus=0, variant=None) -> Plan:

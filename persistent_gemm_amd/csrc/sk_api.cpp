@@ -570,6 +570,7 @@ sk_status run(const sk_gemm_args& g, bool fixed = false) {
   a.G = p.grid;
   a.epoch = sc.epoch;
   a.spin_limit = g.spin_limit_ticks ? g.spin_limit_ticks : kDefaultSpin;
+  a.trace = g.trace;
   a.drop_wg = (g.debug_flags & SK_DEBUG_DROP_SIGNAL) ? g.drop_signal_wg : -1;
   a.delay_seed = (g.debug_flags & SK_DEBUG_DELAY) ? (g.delay_seed ? g.delay_seed : 1u) : 0u;
   if ((direct ? v->launch_direct : v->launch)(p.grid, a, stream) != hipSuccess) return SK_ERR_HIP;

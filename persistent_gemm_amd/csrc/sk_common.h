@@ -50,7 +50,12 @@ struct KArgs {
   int32_t drop_wg;          // test hook: this workgroup never publishes (-1: none)
   uint32_t delay_seed;      // test hook: nonzero = seeded sleeps before publishing
   int32_t s_pitch;          // row pitch (bytes) of SA and SB when they are the caller's [rows][K/32] scales
+  uint64_t* trace;          // NULL, or kTraceWords 100 MHz timestamps per workgroup (see sk_gemm_args.trace)
 };
+
+// Phase trace of a launch (sk_gemm_args.trace): kTraceWords words per workgroup.
+constexpr int kTraceWords = 32;
+constexpr int kTraceItems = 6;   // items recorded per workgroup (words 1 .. 4 * kTraceItems)
 
 // Stream-K partition of S = q*G + r MAC iterations: workgroup w owns
 // [begin(w), begin(w+1)), the first r workgroups getting one extra iteration.

@@ -1014,9 +1014,20 @@ struct Kernel {
     constexpr int PER_STAGE = C::LOADS_PER_STAGE_S;
     const int w = blockIdx.x;
     const int tid = threadIdx.x;
+    // Phase trace (only when the caller passed a buffer): wave 0 of each
+    // workgroup stores s_memrealtime stamps at the phase boundaries, at most
+    // kTraceItems work items, and nothing else changes.
+    uint64_t* const tr = kargs().trace;
+    const bool rec = tr != nullptr && tid == 0;
+    int item = 0;
+    if (rec) tr[w * kTraceWords] = __builtin_amdgcn_s_memrealtime();
+    auto stamp = [&](int slot) {
+      if (rec && item < kTraceItems) tr[w * kTraceWords + 1 + 4 * item + slot] = __builtin_amdgcn_s_memrealtime();
+    };
     const LoadOffs lo = load_offsets(kargs());
     const LdsPtrs lp = lds_ptrs(smem);
     const int row_bytes = kargs().row_bytes;
+    if (rec) tr[w * kTraceWords + 29] = __builtin_amdgcn_s_memrealtime();
     const uint32_t sa_kstride = kargs().sa_kstride, sb_kstride = kargs().sb_kstride;
 
     // Two cursors over the same work list: one issues loads, one computes.
@@ -1145,9 +1156,11 @@ struct Kernel {
       advance_issue();
     });
     uint32_t bias_h = load_bias(ic.tile);
+    if (rec) tr[w * kTraceWords + 28] = __builtin_amdgcn_s_memrealtime();
     // stage 0 landed: everything but the loads of the stages after it (and the bias load)
     wait_vmcnt_n<(S - 2) * PER_STAGE>();
     lds_barrier();
+    if (rec) tr[w * kTraceWords + 27] = __builtin_amdgcn_s_memrealtime();
     // Operands of the next k-step: each k-step reads the next one's scales
     // and first operands (also across items), so they are read here once.
     Ops o0, o1;
@@ -1159,15 +1172,18 @@ struct Kernel {
       Acc<C> acc;
       acc.zero();
       int n = ic.k1 - ic.k0;   // at least one k-step per item
+      stamp(0);
       do {
         kstep_interleaved(done, o0, o1, sc0, sc1, acc);
         ++done;
       } while (--n > 0);
 
       // ---- the item is complete
+      stamp(1);
       if (ic.mode == WORK_CONTRIB) {
         store_partial(kargs(), w, acc);
         publish(kargs(), w);
+        stamp(2);
       } else {
         bool ok = true;
         int first = w;   // lowest contributing workgroup (w: none)
@@ -1180,6 +1196,7 @@ struct Kernel {
               break;
             }
         }
+        stamp(2);
         if (ok) {
           lds_barrier();   // every wave is done with the previous tile's bias
           if (tid < C::BN) *(__attribute__((address_space(3))) uint16_t*)(smem + C::BIAS_OFF + tid * 2) = (uint16_t)bias_h;
@@ -1189,10 +1206,16 @@ struct Kernel {
           lds_barrier();   // ... which must wait until every wave is done staging output there
         }
       }
+      stamp(3);
+      ++item;
       if (!advance(w, cc, ic)) break;
       bias_h = load_bias(ic.tile);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (rec) {
+      tr[w * kTraceWords + 30] = (uint64_t)item;
+      tr[w * kTraceWords + 31] = __builtin_amdgcn_s_memrealtime();
+    }
   }
 
   static __device__ __forceinline__ void run() {
@@ -1393,6 +1416,12 @@ static const Variant kVariants[] = {
     SK_VARIANT(DT_BF16, 256, 256, 128, 32, 2, 4, 2, 2),
     SK_VARIANT(DT_FP8, 256, 256, 128, 32, 2, 2, 2, 1),
     SK_VARIANT(DT_FP8, 256, 256, 128, 32, 2, 4, 2, 2),
+    // 16-row MXFP4 tiles with 128-byte k-steps: every row read of a k-step is a
+    // whole 128-byte line, so each line in flight carries twice the bytes
+    SK_VARIANT(DT_MXFP4, 16, 128, 128, 16, 1, 4, 4, 1),
+    SK_VARIANT(DT_MXFP4, 16, 128, 128, 16, 1, 4, 8, 1),
+    SK_VARIANT(DT_MXFP4, 16, 64, 128, 16, 1, 2, 8, 1),
+    SK_VARIANT(DT_MXFP4, 16, 32, 128, 16, 1, 1, 8, 1),
 };
 
 int num_variants() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }

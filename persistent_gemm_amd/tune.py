@@ -134,8 +134,29 @@ def sweep(dtype: str, reps: int):
     return rows
 
 
-def write(results: dict, table: str, summary: str) -> None:
+def _kept(table: str, summary: str, swept) -> tuple:
+    """Entries (table lines) and summary rows of the dtypes not swept now, from the current files."""
+    names = {v: k for k, v in DTYPE_CODE.items()}
+    lines, rows = [], []
+    if os.path.exists(table):
+        for line in open(table):
+            t = line.strip()
+            if t.startswith("{") and "//" in t:
+                code = int(t[1:].split(",")[0])
+                if code in names and names[code] not in swept:
+                    lines.append("    " + t)
+    if os.path.exists(summary):
+        for line in open(summary):
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if line.startswith("| ") and cells and cells[0] in DTYPE_CODE and cells[0] not in swept:
+                rows.append(line.rstrip("\n"))
+    return lines, rows
+
+
+def write(results: dict, table: str, summary: str, keep_others: bool = True) -> None:
     vs = pg.variants()
+    # entries of the other dtypes come from the table in the tree (the outputs may be elsewhere)
+    kept_lines, kept_rows = _kept(TABLE, SUMMARY, set(results)) if keep_others else ([], [])
     stamp = datetime.date.today().isoformat()
     lines = ["// Measured (kernel, policy) choices for SK_POLICY_AUTO.  Written by",
              f"// persistent_gemm_amd/tune.py ({stamp}, one MI355X): the fastest kernel and policy",
@@ -147,6 +168,7 @@ def write(results: dict, table: str, summary: str) -> None:
             v = vs[vi]
             lines.append(f"    {{{DTYPE_CODE[dtype]}, {M}, {N}, {K}, {vi}, {POLICIES[pname]}, "
                          f"{v['tile_m']}, {v['tile_n']}, {v['threads']}}},  // {dtype}")
+    lines += kept_lines
     lines.append("    {-1, 1, 1, 1, 0, 0, 0, 0, 0},  // end marker (never matches a dtype)")
     lines.append("};")
     with open(table, "w") as f:
@@ -154,6 +176,7 @@ def write(results: dict, table: str, summary: str) -> None:
     md = ["# Tuning table: untuned vs measured-best kernel and policy per shape", "",
           f"Command (repository root, one MI355X, {stamp}):", "",
           "```", "python -m persistent_gemm_amd.tune --dtypes " + ",".join(results), "```", "",
+          "Rows of dtypes not named in the command are kept from the previous sweep.", "",
           "Untuned: HYBRID with the kernel chosen by problem shape.  Best: the fastest kernel and policy",
           "(HYBRID, PURE_SK, PURE_DP) over every compiled kernel of the dtype.  Median of timed calls",
           "(HIP events on the launch stream), whole device.", "",
@@ -164,6 +187,7 @@ def write(results: dict, table: str, summary: str) -> None:
             v = vs[vi]
             md.append(f"| {dtype} | {M} | {N} | {K} | {bv} | {bt:.4f} | {vi} ({v['tile_m']}x{v['tile_n']}, "
                       f"{v['threads']} threads) | {pname} | {t:.4f} | {bt / t:.2f} |")
+    md += kept_rows
     with open(summary, "w") as f:
         f.write("\n".join(md) + "\n")
 
@@ -174,10 +198,12 @@ def main() -> int:
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--table-out", default=TABLE)
     ap.add_argument("--summary-out", default=SUMMARY)
+    ap.add_argument("--replace-all", action="store_true",
+                    help="drop the entries of dtypes not swept (default: keep them)")
     args = ap.parse_args()
     torch.cuda.set_device(0)
     results = {d: sweep(d, args.reps) for d in args.dtypes.split(",")}
-    write(results, args.table_out, args.summary_out)
+    write(results, args.table_out, args.summary_out, keep_others=not args.replace_all)
     print(f"wrote {args.table_out} and {args.summary_out}; rebuild the library to use the table", flush=True)
     return 0
 

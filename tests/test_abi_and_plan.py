@@ -36,7 +36,7 @@ def test_variants_table():
                  (pg.BF16, 128, 192), (pg.FP8, 256, 256), (pg.MXFP8, 256, 256), (pg.MXFP8, 16, 256)]:
         assert need in shapes
     for x in v:
-        assert x["threads"] in (256, 512) and 0 < x["lds_bytes"] <= 160 * 1024
+        assert x["threads"] in (64, 128, 256, 512) and 0 < x["lds_bytes"] <= 160 * 1024
 
 
 # ---------------------------------------------------------------- argument checks (host only)

@@ -382,6 +382,29 @@ def test_graph_capture_is_refused(small):
     assert_bitexact(out.view(torch.int16).cpu().numpy().view(np.uint16), C, "after capture")
 
 
+def test_phase_trace_is_ordered_and_changes_nothing(small):
+    """A traced call gives the same bits; every workgroup's stamps are in phase order and its
+    recorded item count is the length of its work list from the host planner."""
+    x, d, C = small
+    for policy, g in [(pg.PURE_SK, 5), (pg.HYBRID, 7), (pg.PURE_DP, 3)]:
+        p = pg.plan("mxfp4", 256, 256, 512, grid_cap=g, tile=(64, 64), policy=policy)
+        buf = torch.zeros(32 * p.grid, dtype=torch.int64, device="cuda")
+        say(f"traced call policy {policy} grid {g}")
+        got = run(d, grid_cap=g, tile=(64, 64), policy=policy, trace=buf)
+        assert_bitexact(got, C, f"traced policy {policy}")
+        t = buf.cpu().numpy().reshape(p.grid, 32)
+        for w in range(p.grid):
+            items = pg.plan_wg_work(p, w)
+            assert t[w, 30] == len(items), (w, t[w, 30], len(items))
+            seq = [t[w, 0], t[w, 29], t[w, 28], t[w, 27]]
+            for j in range(min(len(items), 6)):
+                seq += [t[w, 1 + 4 * j + i] for i in range(4)]
+            seq.append(t[w, 31])
+            assert all(a <= b for a, b in zip(seq, seq[1:])), (w, seq)
+        s = pg.phase_summary(buf.cpu().numpy(), p.grid)
+        assert s["span_us"] > 0 and len(s["items"]) == int(t[:, 30].max())
+
+
 # ---------------------------------------------------------------- CU-partitioned streams
 
 def _device_cus():
