@@ -28,19 +28,23 @@ one.  Sources:
   "Fix StreamK Kernel Bias #67", Motivation and Technical Details.
 * MXFP8 (E4M3 elements with the same E8M0 block scales) is the block-scaled
   form of the quantized mode of "Fix StreamK Kernel Bias #67", Technical
-  Details; it is the MXFP4 contraction with 8-bit elements.
+  Details; it is the MXFP4 contraction with 8-bit elements.  MXFP6 (E2M3 or
+  E3M2 elements, the same scales) is the same contraction with 6-bit elements,
+  and the mixed forms decode each operand by its own format.
 * The bf16 backward of addmm (the gradients of A, B and the bias that the
   Stream-K matmul / addmm tests take and compare with torch's): "Fix StreamK
   Kernel Bias #67", review comments on the two Stream-K tests.
-* Element encodings are not on those pages.  E2M1 (FP4) and E8M0 (the shared
-  block scale, one per 32 consecutive K elements) follow the OCP Microscaling
-  Formats (MX) v1.0 specification; E4M3FN follows the OCP 8-bit Floating Point
+* Element encodings are not on those pages.  E2M1 (FP4), E2M3 and E3M2 (FP6)
+  and E8M0 (the shared block scale, one per 32 consecutive K elements) follow
+  the OCP Microscaling Formats (MX) v1.0 specification; E4M3FN follows the OCP 8-bit Floating Point
   (OFP8) specification; bf16 is the top half of an IEEE binary32.
 
 Readings where the pages are silent: the bf16 output is rounded once, to
 nearest-even, straight from the fp64 value (never through fp32, which would
 double-round); for fp8 the per-tensor scale is applied before the bias is
-added; the two FP4 codes of a byte hold the even K index in the low nibble.
+added; the two FP4 codes of a byte hold the even K index in the low nibble;
+FP6 codes are packed four to three bytes as a little-endian bit stream (code
+k at bits 6k .. 6k+5 of the row's stream).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 something other than itself (torch's own format conversions, closed forms,
@@ -70,6 +74,10 @@ __all__ = [
     "bf16_backward",
     "gemm_mx",
     "abs_product_sums_mx",
+    "decode_e2m3",
+    "decode_e3m2",
+    "unpack_fp6",
+    "mxfp6_operand",
 ]
 
 # OCP MX v1.0, FP4 (E2M1): code bits are sign | exponent(2, bias 1) | mantissa(1).
@@ -87,6 +95,31 @@ def decode_e2m1(codes: np.ndarray) -> np.ndarray:
     if codes.size and int(codes.max()) > 15:
         raise ValueError("E2M1 codes are 4-bit")
     return E2M1_VALUES[codes]
+
+
+def _decode_fp6(codes: np.ndarray, ebits: int, mbits: int) -> np.ndarray:
+    """6-bit sign | exponent(ebits) | mantissa(mbits) codes -> fp64 (OCP MX v1.0 FP6: no
+    infinities or NaNs; bias 2**(ebits-1) - 1; exponent 0 is subnormal)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    if codes.size and int(codes.max()) > 63:
+        raise ValueError("FP6 codes are 6-bit")
+    c = codes.astype(np.int64)
+    bias = (1 << (ebits - 1)) - 1
+    sign = np.where(c & 0x20, -1.0, 1.0)
+    e = (c >> mbits) & ((1 << ebits) - 1)
+    m = (c & ((1 << mbits) - 1)).astype(np.float64) / (1 << mbits)
+    mag = np.where(e == 0, np.ldexp(m, 1 - bias), np.ldexp(1.0 + m, (e - bias).astype(np.int32)))
+    return sign * mag
+
+
+def decode_e2m3(codes: np.ndarray) -> np.ndarray:
+    """FP6 E2M3 codes (0..63) -> fp64: sign bit 5, exponent bits 4:3 (bias 1), mantissa bits 2:0."""
+    return _decode_fp6(codes, 2, 3)
+
+
+def decode_e3m2(codes: np.ndarray) -> np.ndarray:
+    """FP6 E3M2 codes (0..63) -> fp64: sign bit 5, exponent bits 4:2 (bias 3), mantissa bits 1:0."""
+    return _decode_fp6(codes, 3, 2)
 
 
 def decode_e8m0(e: np.ndarray) -> np.ndarray:
@@ -130,6 +163,20 @@ def unpack_fp4(packed: np.ndarray, K: int) -> np.ndarray:
     return codes
 
 
+def unpack_fp6(packed: np.ndarray, K: int) -> np.ndarray:
+    """uint8[rows][3K/4] -> codes uint8[rows][K]: each 3 bytes b0 b1 b2 hold four codes as the
+    24-bit little-endian word w = b0 | b1 << 8 | b2 << 16, code 4j+i = (w >> 6i) & 63."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    if K % 4 or packed.shape[1] != 3 * K // 4:
+        raise ValueError("packed FP6 rows must hold 3K/4 bytes")
+    b = packed.reshape(packed.shape[0], K // 4, 3).astype(np.uint32)
+    w = b[:, :, 0] | (b[:, :, 1] << 8) | (b[:, :, 2] << 16)
+    codes = np.empty((packed.shape[0], K // 4, 4), dtype=np.uint8)
+    for i in range(4):
+        codes[:, :, i] = (w >> (6 * i)) & 63
+    return codes.reshape(packed.shape[0], K)
+
+
 def _apply_block_scales(vals: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
     """value(r, k) = element(r, k) * 2**(scale[r][k // 32] - 127): one E8M0 scale per 32 consecutive K."""
     if K % 32:
@@ -154,6 +201,13 @@ def mxfp8_operand(elems: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
     if elems.shape[1] != K:
         raise ValueError("MXFP8 rows must hold K bytes")
     return _apply_block_scales(decode_e4m3fn(elems), scales, K)
+
+
+def mxfp6_operand(packed: np.ndarray, scales: np.ndarray, K: int, fmt: str = "e2m3") -> np.ndarray:
+    """Decode an MXFP6 operand: value(r, k) = FP6(code(r, k)) * 2**(scale[r][k // 32] - 127),
+    with FP6 = E2M3 (fmt "e2m3") or E3M2 (fmt "e3m2")."""
+    dec = {"e2m3": decode_e2m3, "e3m2": decode_e3m2}[fmt]
+    return _apply_block_scales(dec(unpack_fp6(packed, K)), scales, K)
 
 
 def rne_bf16_from_double(d: np.ndarray) -> np.ndarray:
@@ -190,6 +244,8 @@ def operands(dtype: str, A, B, SA=None, SB=None, K: int | None = None):
     dtype "fp8":   A, B are uint8[rows][K] E4M3FN; SA, SB are the per-tensor fp32
                    scale factors (Python floats), sigma = SA * SB.
     dtype "mxfp8": A, B are uint8[rows][K] E4M3FN, SA, SB uint8[rows][K/32] E8M0; sigma = 1.
+    dtype "mxfp6_e2m3" / "mxfp6_e3m2": A, B are uint8[rows][3K/4] packed FP6, SA, SB uint8[rows][K/32]
+    E8M0; sigma = 1.
     """
     if dtype == "mxfp4":
         if K is None:
@@ -199,6 +255,11 @@ def operands(dtype: str, A, B, SA=None, SB=None, K: int | None = None):
         if K is None:
             K = np.asarray(A).shape[1]
         return mxfp8_operand(A, SA, K), mxfp8_operand(B, SB, K), 1.0
+    if dtype in ("mxfp6_e2m3", "mxfp6_e3m2"):
+        if K is None:
+            K = 4 * np.asarray(A).shape[1] // 3
+        f = dtype[-4:]
+        return mxfp6_operand(A, SA, K, f), mxfp6_operand(B, SB, K, f), 1.0
     if dtype == "bf16":
         return decode_bf16(A), decode_bf16(B), 1.0
     if dtype == "fp8":
@@ -238,7 +299,7 @@ def gemm_elements(dtype: str, A, B, rows, cols, SA=None, SB=None, bias=None, K: 
     cols = np.asarray(cols, dtype=np.int64)
     ur, ri = np.unique(rows, return_inverse=True)
     uc, ci = np.unique(cols, return_inverse=True)
-    if dtype in ("mxfp4", "mxfp8"):
+    if dtype in ("mxfp4", "mxfp8", "mxfp6_e2m3", "mxfp6_e3m2"):
         a, b, sigma = operands(dtype, np.asarray(A)[ur], np.asarray(B)[uc], np.asarray(SA)[ur],
                                np.asarray(SB)[uc], K)
     else:
@@ -323,17 +384,25 @@ def _mx_decode(fmt: str, X, S, K: int) -> np.ndarray:
         return mxfp4_operand(X, S, K)
     if fmt == "mxfp8":
         return mxfp8_operand(X, S, K)
+    if fmt in ("mxfp6_e2m3", "mxfp6_e3m2"):
+        return mxfp6_operand(X, S, K, fmt[-4:])
     raise ValueError(f"not an MX format: {fmt!r}")
 
 
 def _mx_k(a_fmt: str, A, K):
     if K is not None:
         return K
-    return 2 * np.asarray(A).shape[1] if a_fmt == "mxfp4" else np.asarray(A).shape[1]
+    cols = np.asarray(A).shape[1]
+    if a_fmt == "mxfp4":
+        return 2 * cols
+    if a_fmt.startswith("mxfp6"):
+        return 4 * cols // 3
+    return cols
 
 
 def gemm_mx(a_fmt: str, b_fmt: str, A, B, SA, SB, bias=None, K: int | None = None):
-    """Block-scaled operands of either element width ("mxfp4" or "mxfp8" each):
+    """Block-scaled operands of any MX element format ("mxfp4", "mxfp6_e2m3", "mxfp6_e3m2" or
+    "mxfp8" each):
     the same plain contraction as gemm(), each operand decoded by its own format.
     Returns (C uint16[M][N] bf16 bits, D float64[M][N])."""
     K = _mx_k(a_fmt, A, K)

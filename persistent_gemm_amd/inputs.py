@@ -15,6 +15,9 @@ Distributions (the workloads the Stream-K pages exercise, made synthetic):
   per-tensor fp32 scales (1.0 unless asked otherwise).
 * MXFP8: E4M3FN elements drawn as for fp8, with E8M0 block scales drawn as
   for MXFP4 (one per 32 K-elements, uniform on {125, ..., 129}).
+* MXFP6 (E2M3 or E3M2): every 6-bit code equally likely, packed four to
+  three bytes (a little-endian bit stream: code k at bits 6k .. 6k+5), with
+  E8M0 block scales drawn as for MXFP4.
 * bias: N(0, 1) in fp32 rounded to bf16, one value per output column.
 """
 
@@ -25,13 +28,13 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs", "backward_inputs", "mixed_inputs"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs", "backward_inputs", "mixed_inputs", "pack_fp6"]
 
 
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str            # "mxfp4" | "bf16" | "fp8" | "mxfp8"
+    dtype: str            # "mxfp4" | "bf16" | "fp8" | "mxfp8" | "mxfp6_e2m3" | "mxfp6_e3m2" | "mxfp4_mxfp8"
     M: int
     N: int
     K: int
@@ -64,6 +67,9 @@ WORKLOADS = {
     "mxfp8_addmm_8192": Workload("mxfp8_addmm_8192", "mxfp8", 8192, 8192, 8192, True, 1005),
     # one MXFP4 and one MXFP8 operand (A E2M1, B E4M3), at the large square shape
     "mxfp4_mxfp8_addmm_8192": Workload("mxfp4_mxfp8_addmm_8192", "mxfp4_mxfp8", 8192, 8192, 8192, True, 1007),
+    # MXFP6 (E2M3 and E3M2 elements, E8M0 block scales) at the large square shape
+    "mxfp6_e2m3_addmm_8192": Workload("mxfp6_e2m3_addmm_8192", "mxfp6_e2m3", 8192, 8192, 8192, True, 1008),
+    "mxfp6_e3m2_addmm_8192": Workload("mxfp6_e3m2_addmm_8192", "mxfp6_e3m2", 8192, 8192, 8192, True, 1009),
     # the bf16 addmm's backward (dA, dB, dbias) at the bf16 forward's shape
     "bf16_addmm_backward_4096": Workload("bf16_addmm_backward_4096", "bf16", 4096, 4096, 4096, True, 1006,
                                          op="backward"),
@@ -74,6 +80,17 @@ def _bf16_bits(x: torch.Tensor) -> np.ndarray:
     return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """uint8 codes[rows][K] (0..63, K % 4 == 0) -> uint8[rows][3K/4]: four codes per three bytes,
+    the 24-bit little-endian word of bytes 3j..3j+2 holding code 4j+i at bits 6i .. 6i+5."""
+    c = np.asarray(codes, dtype=np.uint32).reshape(codes.shape[0], -1, 4)
+    w = c[:, :, 0] | (c[:, :, 1] << 6) | (c[:, :, 2] << 12) | (c[:, :, 3] << 18)
+    out = np.empty((codes.shape[0], c.shape[1], 3), dtype=np.uint8)
+    for i in range(3):
+        out[:, :, i] = (w >> (8 * i)) & 0xFF
+    return out.reshape(codes.shape[0], -1)
+
+
 def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
                 scale_lo: int = 125, scale_hi: int = 129, fp8_scales=(1.0, 1.0)) -> dict:
     """Draw one problem.  Returns a dict with keys A, B, SA, SB, bias (None if absent).
@@ -82,6 +99,7 @@ def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
     bf16:  A uint16[M][K], B uint16[N][K] (bit patterns); SA = SB = None.
     fp8:   A uint8[M][K], B uint8[N][K] (E4M3FN bytes); SA, SB python floats.
     mxfp8: A uint8[M][K], B uint8[N][K] (E4M3FN bytes), SA uint8[M][K/32], SB uint8[N][K/32].
+    mxfp6_e2m3, mxfp6_e3m2: A uint8[M][3K/4], B uint8[N][3K/4] (packed FP6), SA, SB as for MXFP4.
     bias:  uint16[N] bf16 bit patterns, or None.
     """
     g = torch.Generator().manual_seed(seed)
@@ -97,6 +115,9 @@ def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
     def e4m3(rows):
         x = torch.randn(rows, K, generator=g).clamp(-448.0, 448.0)
         return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    def fp6(rows):
+        return pack_fp6(torch.randint(0, 64, (rows, K), generator=g, dtype=torch.uint8).numpy())
 
     if dtype == "mxfp4":
         if K % 32:
@@ -116,6 +137,13 @@ def make_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
         out["A"] = e4m3(M)
         out["SA"] = e8m0(M)
         out["B"] = e4m3(N)
+        out["SB"] = e8m0(N)
+    elif dtype in ("mxfp6_e2m3", "mxfp6_e3m2"):
+        if K % 32:
+            raise ValueError("MXFP6 needs K % 32 == 0")
+        out["A"] = fp6(M)
+        out["SA"] = e8m0(M)
+        out["B"] = fp6(N)
         out["SB"] = e8m0(N)
     elif dtype == "fp8":
         out["A"] = e4m3(M)

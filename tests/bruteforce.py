@@ -23,6 +23,31 @@ def e2m1(code: int) -> Fraction:
     return s * mag
 
 
+def fp6(code: int, ebits: int) -> Fraction:
+    """FP6 from its fields: sign bit 5, then `ebits` exponent bits (bias 2**(ebits-1) - 1) and
+    5 - ebits mantissa bits; exponent 0 is subnormal (OCP MX v1.0: E2M3 has ebits 2, E3M2 3)."""
+    mbits = 5 - ebits
+    s = -1 if code & 0b100000 else 1
+    e = (code >> mbits) & ((1 << ebits) - 1)
+    m = code & ((1 << mbits) - 1)
+    bias = (1 << (ebits - 1)) - 1
+    if e == 0:
+        mag = Fraction(m, 1 << mbits) * Fraction(2) ** (1 - bias)
+    else:
+        mag = Fraction(2) ** (e - bias) * (1 + Fraction(m, 1 << mbits))
+    return s * mag
+
+
+def fp6_code(packed_row, k: int) -> int:
+    """Code k of a row of packed FP6 bytes, read bit by bit: bit b of the row's stream is bit
+    b % 8 of byte b // 8, and code k is bits 6k .. 6k+5 (lowest first)."""
+    v = 0
+    for i in range(6):
+        b = 6 * k + i
+        v |= ((int(packed_row[b // 8]) >> (b % 8)) & 1) << i
+    return v
+
+
 def e8m0(byte: int) -> Fraction:
     if byte == 255:
         raise ValueError("NaN scale")
@@ -91,6 +116,9 @@ def round_bf16(x: Fraction) -> int:
 
 def gemm(dtype: str, A, B, SA, SB, bias, M: int, N: int, K: int):
     """C[m][n] bits for D = sigma * sum_k a*b + bias[n], all exact."""
+    if dtype.startswith("mxfp6"):
+        return gemm_mx(dtype, dtype, A, B, SA, SB, bias, M, N, K)
+
     def a_val(m, k):
         if dtype == "mxfp4":
             byte = int(A[m][k // 2])
@@ -139,13 +167,10 @@ def bf16_backward(dC, A, B, M: int, N: int, K: int):
 
 
 def gemm_mx(a_fmt: str, b_fmt: str, A, B, SA, SB, bias, M: int, N: int, K: int):
-    """C bits for operands of formats a_fmt / b_fmt ("mxfp4" or "mxfp8"), all exact."""
+    """C bits for operands of MX formats a_fmt / b_fmt ("mxfp4", "mxfp6_e2m3", "mxfp6_e3m2",
+    "mxfp8"), all exact."""
     def val(fmt, X, S, r, k):
-        if fmt == "mxfp4":
-            byte = int(X[r][k // 2])
-            code = (byte >> 4) if (k & 1) else (byte & 0xF)
-            return e2m1(code) * e8m0(int(S[r][k // 32]))
-        return e4m3fn(int(X[r][k])) * e8m0(int(S[r][k // 32]))
+        return _operand_value(fmt, X, S, r, k)
 
     out = [[0] * N for _ in range(M)]
     for m in range(M):
@@ -161,6 +186,8 @@ def gemm_mx(a_fmt: str, b_fmt: str, A, B, SA, SB, bias, M: int, N: int, K: int):
 
 def _operand_value(dtype: str, X, S, r: int, k: int) -> Fraction:
     """Element (r, k) of an operand of `dtype`, decoded from its bit fields."""
+    if dtype in ("mxfp6_e2m3", "mxfp6_e3m2"):
+        return fp6(fp6_code(X[r], k), 2 if dtype.endswith("e2m3") else 3) * e8m0(int(S[r][k // 32]))
     if dtype == "mxfp4":
         byte = int(X[r][k // 2])
         code = (byte >> 4) if (k & 1) else (byte & 0xF)

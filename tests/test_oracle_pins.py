@@ -22,7 +22,7 @@ import torch
 
 import bruteforce as bf
 import oracle
-from persistent_gemm_amd.inputs import backward_inputs, integer_inputs, make_inputs, mixed_inputs
+from persistent_gemm_amd.inputs import backward_inputs, integer_inputs, make_inputs, mixed_inputs, pack_fp6
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -492,6 +492,98 @@ def pin_accept():
     assert oracle.accept(np.array([0x8000], np.uint16), z, np.zeros(1), None).all()
 
 
+# ---------------------------------------------------------------- MXFP6
+
+def pin_fp6_bitfields():
+    """E2M3 and E3M2 on all 64 codes against the field-by-field definition (and the sign of zero)."""
+    codes = np.arange(64, dtype=np.uint8)
+    for dec, eb in ((oracle.decode_e2m3, 2), (oracle.decode_e3m2, 3)):
+        got = dec(codes)
+        want = np.array([float(bf.fp6(c, eb)) for c in range(64)])
+        assert np.array_equal(got, want)
+        assert np.array_equal(np.signbit(got), codes >= 32)
+    # the format's extremes: largest finite and smallest subnormal
+    assert oracle.decode_e2m3(np.array([0x1F, 0x01]))[0] == 7.5 and oracle.decode_e2m3(np.array([0x01]))[0] == 0.125
+    assert oracle.decode_e3m2(np.array([0x1F]))[0] == 28.0 and oracle.decode_e3m2(np.array([0x01]))[0] == 0.0625
+
+
+def pin_fp6_bit_order():
+    """Four codes in three bytes, the lowest bits first: worked by hand, then bit by bit."""
+    # bytes c1 20 08 -> word 0x0820C1 -> codes 0x01, 0x03, 0x02, 0x02
+    assert np.array_equal(oracle.unpack_fp6(np.array([[0xC1, 0x20, 0x08]], np.uint8), 4), [[1, 3, 2, 2]])
+    rng = np.random.default_rng(23)
+    codes = rng.integers(0, 64, (3, 96)).astype(np.uint8)
+    packed = pack_fp6(codes)
+    got = oracle.unpack_fp6(packed, 96)
+    assert np.array_equal(got, [[bf.fp6_code(packed[r], k) for k in range(96)] for r in range(3)])
+    assert np.array_equal(got, codes)
+
+
+def golden_handworked_mxfp6():
+    cases = []
+    with open(os.path.join(GOLDEN, "mxfp6_1x1x64_handworked.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, fmt, a, b, sa, sb, bias, total, bits = line.split()
+            cases.append((name, fmt, _hex_runs(a), _hex_runs(b), [int(v) for v in sa.split(",")],
+                          [int(v) for v in sb.split(",")], None if bias == "none" else float(bias),
+                          float(total), int(bits, 16)))
+    return cases
+
+
+def pin_handworked_mxfp6():
+    cases = golden_handworked_mxfp6()
+    assert len(cases) == 11
+    for name, fmt, a, b, sa, sb, bias, total, bits in cases:
+        assert len(a) == 64 and len(b) == 64, name
+        bb = None if bias is None else _f32_to_bf16_torch(np.array([bias], np.float32))
+        C, D = oracle.gemm("mxfp6_" + fmt, pack_fp6(np.array([a], np.uint8)), pack_fp6(np.array([b], np.uint8)),
+                           np.array([sa], np.uint8), np.array([sb], np.uint8), bb, K=64)
+        got = (int(C[0, 0]), float(D[0, 0]))
+        assert got == (bits, total), f"{name}: oracle gives {got}, worked by hand {(bits, total)}"
+
+
+def pin_bruteforce_mxfp6():
+    for dtype in ("mxfp6_e2m3", "mxfp6_e3m2"):
+        for seed, (M, N, K) in enumerate([(1, 1, 32), (2, 3, 64), (3, 2, 96)]):
+            for bias in (False, True):
+                _bruteforce_case(dtype, M, N, K, bias, 950 + seed)
+
+
+def pin_mxfp6_reduces_to_mxfp8():
+    """Every E2M3 and E3M2 value is an E4M3FN value: with B's elements re-encoded as torch's own
+    E4M3FN bytes of the same values, the MXFP6 result equals the MXFP8 oracle's, bit for bit."""
+    for dtype, dec in (("mxfp6_e2m3", oracle.decode_e2m3), ("mxfp6_e3m2", oracle.decode_e3m2)):
+        M, N, K = 4, 5, 96
+        x = make_inputs(dtype, M, N, K, bias=True, seed=960)
+        C6, D6 = oracle.gemm(dtype, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=K)
+        e4 = lambda X: torch.from_numpy(dec(oracle.unpack_fp6(X, K))).float().to(torch.float8_e4m3fn).view(
+            torch.uint8).numpy()
+        C8, D8 = oracle.gemm("mxfp8", e4(x["A"]), e4(x["B"]), x["SA"], x["SB"], x["bias"], K=K)
+        assert np.array_equal(C6, C8) and np.array_equal(D6, D8), dtype
+        Cm, _ = oracle.gemm_mx(dtype, "mxfp8", x["A"], e4(x["B"]), x["SA"], x["SB"], x["bias"], K=K)
+        assert np.array_equal(Cm, C6), dtype
+
+
+def pin_invariants_mxfp6():
+    for dtype in ("mxfp6_e2m3", "mxfp6_e3m2"):
+        K = 128
+        x = make_inputs(dtype, 5, 6, K, bias=False, seed=970)
+        C, D = oracle.gemm(dtype, x["A"], x["B"], x["SA"], x["SB"], None, K=K)
+        _, D2 = oracle.gemm(dtype, x["A"], x["B"], x["SA"] + 1, x["SB"], None, K=K)
+        assert np.array_equal(D2, 2 * D)
+        # permuting whole 32-wide blocks (24 bytes each) with their scales changes nothing
+        perm = np.array([3, 1, 0, 2])
+        Ab = x["A"].reshape(5, 4, 24)[:, perm].reshape(5, 96)
+        Bb = x["B"].reshape(6, 4, 24)[:, perm].reshape(6, 96)
+        _, D3 = oracle.gemm(dtype, Ab, Bb, x["SA"][:, perm], x["SB"][:, perm], None, K=K)
+        assert np.array_equal(D3, D)
+        C4, _ = oracle.gemm(dtype, x["B"], x["A"], x["SB"], x["SA"], None, K=K)
+        assert np.array_equal(C4, C.T)
+
+
 # ---------------------------------------------------------------- the tolerance arithmetic
 #
 # The parity bar for inexact results is |C - D| <= 2**-7 * S + ulp_bf16(max(|D|, |C|)) with
@@ -610,6 +702,8 @@ PINS = [
     pin_bruteforce_mixed_mx, pin_mixed_mx_reduces_to_mxfp4,
     pin_abs_sums_vs_rational, pin_mixed_abs_sums_vs_rational, pin_backward_abs_sums_vs_rational,
     pin_ulp_bf16, pin_accept_exact,
+    pin_fp6_bitfields, pin_fp6_bit_order, pin_handworked_mxfp6, pin_bruteforce_mxfp6, pin_mxfp6_reduces_to_mxfp8,
+    pin_invariants_mxfp6,
 ]
 
 
@@ -814,6 +908,36 @@ def _mut_bound_without_ulp(mp):
     mp.setattr(oracle, "_ulp_bf16", lambda x: np.zeros(np.shape(x)))
 
 
+def _mut_fp6_formats_swapped(mp):
+    # E2M3 codes decoded as E3M2 (and the other way round)
+    a, b = oracle.decode_e2m3, oracle.decode_e3m2
+    mp.setattr(oracle, "decode_e2m3", b)
+    mp.setattr(oracle, "decode_e3m2", a)
+
+
+def _mut_fp6_big_endian(mp):
+    # the three bytes of a group read as a big-endian word
+    def unpack(packed, K):
+        p = np.asarray(packed, dtype=np.uint8).reshape(np.asarray(packed).shape[0], -1, 3)[:, :, ::-1]
+        return _real_unpack_fp6(np.ascontiguousarray(p).reshape(p.shape[0], -1), K)
+    mp.setattr(oracle, "unpack_fp6", unpack)
+
+
+def _mut_fp6_subnormal_scale(mp):
+    # subnormals without the 2^(1 - bias) factor
+    def dec(codes, ebits, mbits):
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        bias = (1 << (ebits - 1)) - 1
+        sign = np.where(c & 0x20, -1.0, 1.0)
+        e = (c >> mbits) & ((1 << ebits) - 1)
+        m = (c & ((1 << mbits) - 1)).astype(np.float64) / (1 << mbits)
+        return sign * np.where(e == 0, m, np.ldexp(1.0 + m, (e - bias).astype(np.int32)))
+    mp.setattr(oracle, "_decode_fp6", dec)
+
+
+_real_unpack_fp6 = oracle.unpack_fp6
+
+
 MUTATIONS = [
     _mut_e2m1_entry, _mut_nibble_order, _mut_scale_block, _mut_drop_bias, _mut_double_bias,
     _mut_round_via_float, _mut_round_truncate, _mut_e4m3_bias, _mut_fp8_sigma, _mut_transpose_b,
@@ -821,6 +945,7 @@ MUTATIONS = [
     _mut_backward_dbias_rows, _mut_mixed_b_scales_ignored,
     _mut_abs_sums_one_sided, _mut_abs_sums_outer, _mut_abs_sums_no_sigma, _mut_elements_S_one_sided,
     _mut_backward_S_one_sided, _mut_mixed_S_one_sided, _mut_ulp_half, _mut_bound_without_ulp,
+    _mut_fp6_formats_swapped, _mut_fp6_big_endian, _mut_fp6_subnormal_scale,
 ]
 
 
