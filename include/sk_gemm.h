@@ -28,6 +28,13 @@
  *   MXFP8  A uint8[M][K], B uint8[N][K], OCP E4M3FN elements; A_scale
  *          uint8[M][K/32], B_scale uint8[N][K/32] E8M0 block scales as for
  *          MXFP4.  sigma = 1.
+ *   MXFP6  A uint8[M][3K/4], B uint8[N][3K/4]: OCP E2M3 (SK_MXFP6_E2M3) or
+ *          E3M2 (SK_MXFP6_E3M2) 6-bit codes packed as one little-endian bit
+ *          stream per row (code k is bits 6k .. 6k+5 of the row, bit b of the
+ *          stream being bit b % 8 of byte b / 8), so each block of 32
+ *          elements is 24 bytes.  Scales as for MXFP4.  sigma = 1.
+ *   mixed  SK_MXFP4_MXFP8: A as for MXFP4, B as for MXFP8; SK_MXFP8_MXFP4:
+ *          A as for MXFP8, B as for MXFP4.  Scales as for MXFP4.  sigma = 1.
  *   fp8    A uint8[M][K], B uint8[N][K], OCP E4M3FN.  A_scale / B_scale are
  *          device pointers to one fp32 each (per-tensor), NULL meaning 1.0;
  *          sigma = A_scale * B_scale, applied to the fp32 sum before the bias
@@ -47,7 +54,7 @@
  * the caller and must stay valid until the stream has passed the launch.
  * Calls enqueue on `stream` (a hipStream_t passed as void*; NULL is the
  * default stream) and return without waiting.  The library owns its scratch
- * (fp32 partial tiles, lock flags, an error word, and for MXFP4 / MXFP8 a
+ * (fp32 partial tiles, lock flags, an error word, and for the MX types a
  * k-step-major copy of the two scale arrays that a small kernel writes before
  * the GEMM on the same stream), kept per (device, stream), grown on demand and
  * freed by sk_release_workspace().  Device-side failures (a workgroup that
@@ -65,13 +72,14 @@
  *   SK_ERR_ARG          a required pointer is NULL, M, N or K < 1, a size is
  *                       beyond the supported range (M < 2^31, N <= 2^22,
  *                       K <= 2^21, tiles * MAC iterations per tile < 2^31;
- *                       MXFP4 / MXFP8: M * K / 32 and N * K / 32 below 2^31),
+ *                       MX types: M * K / 32 and N * K / 32 below 2^31),
  *                       C overlaps an input, bf16 given scales, an unknown
  *                       dtype / policy, or sk_addmm without a bias;
- *   SK_ERR_ALIGN        MXFP4 / MXFP8 K not a multiple of 32, fp8 K not a multiple of
- *                       16, bf16 K not a multiple of 8 (a row of A or B must
- *                       be a whole number of 16-byte chunks), or A, B, C not
- *                       16-byte aligned, or bias not 2-byte aligned;
+ *   SK_ERR_ALIGN        an MX type with K not a multiple of 32 (whole
+ *                       scale blocks), fp8 K not a multiple of 16, bf16 K
+ *                       not a multiple of 8 (a row of A or B must be a whole
+ *                       number of 16-byte chunks), or A, B, C not 16-byte
+ *                       aligned, or bias not 2-byte aligned;
  *   SK_ERR_UNSUPPORTED  the current device is not gfx950, a tile override
  *                       names no compiled kernel for that dtype, or the stream
  *                       is being captured into a HIP graph;
@@ -102,7 +110,10 @@ typedef enum sk_status {
   SK_ERR_SCRATCH = 7
 } sk_status;
 
-typedef enum sk_dtype { SK_MXFP4 = 0, SK_BF16 = 1, SK_FP8_E4M3 = 2, SK_MXFP8 = 3 } sk_dtype;
+typedef enum sk_dtype {
+  SK_MXFP4 = 0, SK_BF16 = 1, SK_FP8_E4M3 = 2, SK_MXFP8 = 3, SK_MXFP6_E2M3 = 4, SK_MXFP6_E3M2 = 5,
+  SK_MXFP4_MXFP8 = 6, SK_MXFP8_MXFP4 = 7
+} sk_dtype;
 
 /* How output tiles are divided between the persistent workgroups.
  * HYBRID: whole tiles are dealt out round-robin ("data-parallel tail"), and
@@ -191,16 +202,18 @@ sk_status sk_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* A_scale, 
 sk_status sk_gemm_mxfp8(const uint8_t* A, const uint8_t* B, const uint8_t* A_scale, const uint8_t* B_scale,
                         const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap, void* stream);
 
-/* Block-scaled operands of either element width: a_fmt and b_fmt are SK_MXFP4
- * or SK_MXFP8 (A and B laid out as for that type, scales E8M0 [rows][K/32],
- * required; bias may be NULL).  The mixed products are among the other MX
- * formats of the quantized mode ("Fix StreamK Kernel Bias #67", Technical
- * Details; MX formats of "Stream-k mxfp4 kernel", description).  Equal formats
- * are sk_gemm_mxfp4 / sk_gemm_mxfp8.  For mixed formats the E2M1 operand is
- * first widened to E4M3 bytes in the library's scratch of (device, stream):
- * every E2M1 value is an E4M3 value, so the result is the same exact
- * contraction, computed by the MXFP8 kernels.  Errors as for those entry
- * points; SK_ERR_ARG also for a format that is not MX. */
+/* Block-scaled operands of any OCP MX element type: a_fmt and b_fmt are
+ * SK_MXFP4, SK_MXFP6_E2M3, SK_MXFP6_E3M2 or SK_MXFP8 (A and B laid out as for
+ * that type, scales E8M0 [rows][K/32], required; bias may be NULL).  MXFP6
+ * and the mixed MXFP4 x MXFP8 products are the other MX formats of the
+ * quantized mode ("Fix StreamK Kernel Bias #67", Technical Details; MX formats
+ * of "Stream-k mxfp4 kernel", description).  Equal formats run that type's
+ * kernels (as sk_gemm_mxfp4 / sk_gemm_mxfp8 do); an MXFP4 operand with an
+ * MXFP8 one runs the SK_MXFP4_MXFP8 / SK_MXFP8_MXFP4 kernels, in which the
+ * scaled MFMA takes each operand in its own format.  Policy AUTO.  Errors as
+ * for sk_gemm_mxfp4; SK_ERR_ARG also for a format that is not MX, and
+ * SK_ERR_UNSUPPORTED for an MXFP6 operand with an operand of another format
+ * (not compiled). */
 sk_status sk_gemm_mx(sk_dtype a_fmt, sk_dtype b_fmt, const uint8_t* A, const uint8_t* B, const uint8_t* A_scale,
                      const uint8_t* B_scale, const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap,
                      void* stream);

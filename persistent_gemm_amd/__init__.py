@@ -21,19 +21,24 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL", "DEBUG_RELAYOUT",
+    "SkError", "MXFP4", "BF16", "FP8", "MXFP8", "MXFP6_E2M3", "MXFP6_E3M2", "MXFP4_MXFP8", "MXFP8_MXFP4", "HYBRID", "PURE_SK", "PURE_DP", "AUTO", "DEBUG_DELAY", "DEBUG_DROP_SIGNAL", "DEBUG_RELAYOUT",
     "library_path", "load", "gemm_mxfp4", "gemm_mxfp4_noalloc", "gemm_mxfp8", "gemm_bf16", "gemm_bf16_backward", "gemm_mx", "gemm_fp8", "addmm", "gemm_ex", "plan", "plan_wg_range",
     "plan_wg_work", "check", "release_workspace", "poison_workspace", "variants", "Plan",
     "cu_masked_stream", "destroy_stream", "stream_cu_count", "phase_summary",
 ]
 
 MXFP4, BF16, FP8, MXFP8 = 0, 1, 2, 3
+MXFP6_E2M3, MXFP6_E3M2, MXFP4_MXFP8, MXFP8_MXFP4 = 4, 5, 6, 7
 HYBRID, PURE_SK, PURE_DP, AUTO = 0, 1, 2, 3
 DEBUG_DELAY, DEBUG_DROP_SIGNAL, DEBUG_RELAYOUT = 1, 2, 4
 
 _STATUS = {0: "SK_OK", 1: "SK_ERR_ARG", 2: "SK_ERR_ALIGN", 3: "SK_ERR_UNSUPPORTED", 4: "SK_ERR_HIP",
            5: "SK_ERR_NOMEM", 6: "SK_ERR_TIMEOUT", 7: "SK_ERR_SCRATCH"}
-_DTYPES = {"mxfp4": MXFP4, "bf16": BF16, "fp8": FP8, "mxfp8": MXFP8}
+_DTYPES = {"mxfp4": MXFP4, "bf16": BF16, "fp8": FP8, "mxfp8": MXFP8, "mxfp6_e2m3": MXFP6_E2M3,
+           "mxfp6_e3m2": MXFP6_E3M2, "mxfp4_mxfp8": MXFP4_MXFP8, "mxfp8_mxfp4": MXFP8_MXFP4}
+# element format of A and of B for each block-scaled dtype
+_MX_FORMATS = {MXFP4: (MXFP4, MXFP4), MXFP8: (MXFP8, MXFP8), MXFP6_E2M3: (MXFP6_E2M3, MXFP6_E2M3),
+               MXFP6_E3M2: (MXFP6_E3M2, MXFP6_E3M2), MXFP4_MXFP8: (MXFP4, MXFP8), MXFP8_MXFP4: (MXFP8, MXFP4)}
 
 
 class SkError(RuntimeError):
@@ -213,23 +218,37 @@ def _out(C, M, N, device):
     return C
 
 
+def _mx_k(fmt, cols):
+    """K of a row of `cols` bytes of MX element format fmt (E2M1 4 bits, FP6 6, E4M3 8)."""
+    if fmt == MXFP4:
+        return 2 * cols
+    if fmt in (MXFP6_E2M3, MXFP6_E3M2):
+        if cols % 3:
+            raise ValueError("an MXFP6 row holds 3K/4 bytes")
+        return 4 * cols // 3
+    return cols
+
+
+def _mx_operand(t, nm, fmt, rows, K, dev):
+    torch = _torch()
+    if fmt == MXFP4:
+        _need(t, nm, (torch.uint8,), (rows, K // 2), dev)
+    elif fmt in (MXFP6_E2M3, MXFP6_E3M2):
+        _need(t, nm, (torch.uint8,), (rows, 3 * K // 4), dev)
+    else:
+        _need(t, nm, (torch.float8_e4m3fn, torch.uint8), (rows, K), dev)
+
+
 def _marshal(dtype, A, B, A_scale, B_scale, bias, C):
     """Checks tensors for one dtype; returns (M, N, K, C)."""
     torch = _torch()
     dev = A.device
-    if dtype == MXFP4:
-        M, kh = A.shape
-        N = B.shape[0]
-        K = 2 * kh
-        _need(A, "A", (torch.uint8,), (M, kh), dev)
-        _need(B, "B", (torch.uint8,), (N, kh), dev)
-        _need(A_scale, "A_scale", (torch.uint8,), (M, K // 32), dev)
-        _need(B_scale, "B_scale", (torch.uint8,), (N, K // 32), dev)
-    elif dtype == MXFP8:
-        M, K = A.shape
-        N = B.shape[0]
-        _need(A, "A", (torch.float8_e4m3fn, torch.uint8), (M, K), dev)
-        _need(B, "B", (torch.float8_e4m3fn, torch.uint8), (N, K), dev)
+    if dtype in _MX_FORMATS:
+        fa, fb = _MX_FORMATS[dtype]
+        M, N = A.shape[0], B.shape[0]
+        K = _mx_k(fa, A.shape[1])
+        _mx_operand(A, "A", fa, M, K, dev)
+        _mx_operand(B, "B", fb, N, K, dev)
         _need(A_scale, "A_scale", (torch.uint8,), (M, K // 32), dev)
         _need(B_scale, "B_scale", (torch.uint8,), (N, K // 32), dev)
     elif dtype == BF16:
@@ -294,22 +313,22 @@ def gemm_bf16(A, B, bias=None, C=None, grid_cap=0, stream=None):
 
 
 def gemm_mx(a_fmt, b_fmt, A, B, A_scale, B_scale, bias=None, C=None, grid_cap=0, stream=None):
-    """C = A . B^T (+ bias) for block-scaled operands of either width: a_fmt, b_fmt in ("mxfp4", "mxfp8").
+    """C = A . B^T (+ bias) for block-scaled operands: a_fmt, b_fmt in ("mxfp4", "mxfp6_e2m3",
+    "mxfp6_e3m2", "mxfp8").
 
-    A MXFP4 operand is uint8 [rows, K/2] (packed E2M1), a MXFP8 one E4M3 [rows, K]; scales uint8 [rows, K/32]."""
+    An MXFP4 operand is uint8 [rows, K/2] (packed E2M1), an MXFP6 one uint8 [rows, 3K/4] (packed
+    6-bit codes), an MXFP8 one E4M3 [rows, K]; scales uint8 [rows, K/32]."""
     torch = _torch()
     fa, fb = _dt(a_fmt), _dt(b_fmt)
-    if fa not in (MXFP4, MXFP8) or fb not in (MXFP4, MXFP8):
-        raise ValueError("gemm_mx takes mxfp4 or mxfp8 operands")
+    fmts = (MXFP4, MXFP8, MXFP6_E2M3, MXFP6_E3M2)
+    if fa not in fmts or fb not in fmts:
+        raise ValueError("gemm_mx takes mxfp4, mxfp6_e2m3, mxfp6_e3m2 or mxfp8 operands")
     dev = A.device
     M = A.shape[0]
     N = B.shape[0]
-    K = 2 * A.shape[1] if fa == MXFP4 else A.shape[1]
-    for t, nm, f, rows in ((A, "A", fa, M), (B, "B", fb, N)):
-        if f == MXFP4:
-            _need(t, nm, (torch.uint8,), (rows, K // 2), dev)
-        else:
-            _need(t, nm, (torch.float8_e4m3fn, torch.uint8), (rows, K), dev)
+    K = _mx_k(fa, A.shape[1])
+    _mx_operand(A, "A", fa, M, K, dev)
+    _mx_operand(B, "B", fb, N, K, dev)
     _need(A_scale, "A_scale", (torch.uint8,), (M, K // 32), dev)
     _need(B_scale, "B_scale", (torch.uint8,), (N, K // 32), dev)
     if bias is not None:

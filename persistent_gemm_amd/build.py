@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libskgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sk_kernels.hip", "sk_backward.hip", "sk_mx_convert.hip", "sk_api.cpp"]
+SOURCES = ["sk_kernels.hip", "sk_kernels_mx.hip", "sk_backward.hip", "sk_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # keep hipcc from emitting packed-fp32 arithmetic on its own
@@ -31,7 +31,7 @@ def build(verbose: bool = False) -> str:
             cmd.insert(2, "hip")
         cmds.append(cmd)
         objs.append(obj)
-    with ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(cmds), 5)) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
     tmp = LIB + ".tmp"

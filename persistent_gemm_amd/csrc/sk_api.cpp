@@ -60,16 +60,21 @@ std::map<std::pair<int, uintptr_t>, int> g_stream_cus;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool dtype_ok(int d) { return d == SK_MXFP4 || d == SK_BF16 || d == SK_FP8_E4M3 || d == SK_MXFP8; }
+bool dtype_ok(int d) { return d >= SK_MXFP4 && d <= SK_MXFP8_MXFP4; }
 
 // Block-scaled (MX) input types: one E8M0 scale byte per 32 K elements.
-bool is_mx(int d) { return d == SK_MXFP4 || d == SK_MXFP8; }
+bool is_mx(int d) { return dtype_ok(d) && d != SK_BF16 && d != SK_FP8_E4M3; }
 
-// Bytes of one row of A or B for K elements.
-int64_t row_bytes(int dtype, int64_t K) {
+// Bytes of one row of A (b: of B) for K elements: E2M1 4 bits, E2M3 / E3M2 6,
+// E4M3 8, bf16 16 per element.
+int64_t row_bytes(int dtype, int64_t K, bool b = false) {
   switch (dtype) {
     case SK_MXFP4: return K / 2;
     case SK_BF16: return 2 * K;
+    case SK_MXFP6_E2M3:
+    case SK_MXFP6_E3M2: return 3 * K / 4;
+    case SK_MXFP4_MXFP8: return b ? K : K / 2;
+    case SK_MXFP8_MXFP4: return b ? K / 2 : K;
     default: return K;
   }
 }
@@ -304,10 +309,10 @@ sk_status validate(const sk_gemm_args& g) {
   if (((uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)g.C) & 15) return SK_ERR_ALIGN;
   if (g.bias && ((uintptr_t)g.bias & 1)) return SK_ERR_ALIGN;
   if (g.dtype == SK_FP8_E4M3 && (((uintptr_t)g.A_scale | (uintptr_t)g.B_scale) & 3)) return SK_ERR_ALIGN;
-  const int64_t rb = row_bytes(g.dtype, g.K);
+  const int64_t rb = row_bytes(g.dtype, g.K), rbb = row_bytes(g.dtype, g.K, true);
   const int64_t c_bytes = g.M * g.N * 2;
   const int64_t sbytes = is_mx(g.dtype) ? g.K / 32 : (g.dtype == SK_FP8_E4M3 ? 4 : 0);
-  if (overlaps(g.C, c_bytes, g.A, g.M * rb) || overlaps(g.C, c_bytes, g.B, g.N * rb) ||
+  if (overlaps(g.C, c_bytes, g.A, g.M * rb) || overlaps(g.C, c_bytes, g.B, g.N * rbb) ||
       overlaps(g.C, c_bytes, g.bias, g.N * 2) ||
       overlaps(g.C, c_bytes, g.A_scale, is_mx(g.dtype) ? g.M * sbytes : sbytes) ||
       overlaps(g.C, c_bytes, g.B_scale, is_mx(g.dtype) ? g.N * sbytes : sbytes))
@@ -480,7 +485,8 @@ sk_status run(const sk_gemm_args& g, bool fixed = false) {
   // would put each row's 2 to 8 bytes in a different cache line), and each
   // lane finds the bytes of all its MFMA blocks together.  The copy holds
   // whole tiles.  Every offset into it must fit in 32 bits.  A k-step holds
-  // kb bytes of a row: 2 * kb FP4 or kb FP8 elements, so kb / 16 or kb / 32
+  // kb bytes of a row's LDS image: 2 * kb E2M1 elements for MXFP4, kb elements
+  // for the other MX types (one byte per element there), so kb / 16 or kb / 32
   // scale bytes.
   const int64_t spr = g.dtype == SK_MXFP4 ? v->kb / 16 : v->kb / 32, ksteps = p.iters_per_tile;
   // Kernels of at most 128-row tiles instead gather the scales straight from the caller's
@@ -560,6 +566,7 @@ sk_status run(const sk_gemm_args& g, bool fixed = false) {
   a.N = (int32_t)g.N;
   a.K = (int32_t)g.K;
   a.row_bytes = (int32_t)row_bytes(g.dtype, g.K);
+  a.row_bytes_b = (int32_t)row_bytes(g.dtype, g.K, true);
   a.tiles = (int32_t)p.tiles;
   a.sk_tiles = (int32_t)p.sk_tiles;
   a.q = (int32_t)p.iters_per_wg;
@@ -690,33 +697,17 @@ sk_status sk_gemm_bf16_backward(const void* dC, const void* A, const void* B, vo
 sk_status sk_gemm_mx(sk_dtype a_fmt, sk_dtype b_fmt, const uint8_t* A, const uint8_t* B, const uint8_t* A_scale,
                      const uint8_t* B_scale, const void* bias, void* C, int64_t M, int64_t N, int64_t K, int grid_cap,
                      void* stream) {
-  if (!is_mx(a_fmt) || !is_mx(b_fmt)) return SK_ERR_ARG;
-  if (a_fmt == b_fmt) return run(base_args(a_fmt, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
-  // One operand E2M1, the other E4M3: the E2M1 one is widened to E4M3 bytes
-  // (exact) in scratch and the MXFP8 kernels run.  The scaled MFMA runs at the
-  // E4M3 rate whenever either operand is E4M3, so only the widening pass is
-  // added.
-  if (!A || !B || !C || !A_scale || !B_scale) return SK_ERR_ARG;
-  if (M < 1 || N < 1 || K < 1 || M >= kMaxM || N > kMaxN || K > kMaxK) return SK_ERR_ARG;
-  if (K % 32) return SK_ERR_ALIGN;
-  if (((uintptr_t)A | (uintptr_t)B) & 15) return SK_ERR_ALIGN;
-  const bool a4 = a_fmt == SK_MXFP4;
-  const int64_t rows4 = a4 ? M : N;
-  const uint8_t* src4 = a4 ? A : B;
-  if (overlaps(C, M * N * 2, src4, rows4 * (K / 2))) return SK_ERR_ARG;
-  int dev = 0;
-  DeviceInfo info;
-  sk_status st = refuse_capture((hipStream_t)stream);
-  if (st != SK_OK) return st;
-  st = device_info(&dev, &info);
-  if (st != SK_OK) return st;
-  if (!info.gfx950) return SK_ERR_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t* wide = nullptr;
-  st = get_aux(dev, s, (size_t)(rows4 * K), &wide);
-  if (st != SK_OK) return st;
-  if (sk::launch_widen_e2m1(src4, wide, rows4 * (K / 2), s) != hipSuccess) return SK_ERR_HIP;
-  return run(base_args(SK_MXFP8, a4 ? wide : A, a4 ? B : wide, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
+  // the same format for both operands: that type's kernels; one MXFP4 and one
+  // MXFP8 operand: the mixed kernels, in which the scaled MFMA takes each in its
+  // own format; other pairs are not compiled
+  auto element_format = [](int d) { return is_mx(d) && d != SK_MXFP4_MXFP8 && d != SK_MXFP8_MXFP4; };
+  if (!element_format(a_fmt) || !element_format(b_fmt)) return SK_ERR_ARG;
+  int dtype = -1;
+  if (a_fmt == b_fmt) dtype = a_fmt;
+  else if (a_fmt == SK_MXFP4 && b_fmt == SK_MXFP8) dtype = SK_MXFP4_MXFP8;
+  else if (a_fmt == SK_MXFP8 && b_fmt == SK_MXFP4) dtype = SK_MXFP8_MXFP4;
+  if (dtype < 0) return SK_ERR_UNSUPPORTED;
+  return run(base_args(dtype, A, B, A_scale, B_scale, bias, C, M, N, K, grid_cap, stream));
 }
 
 sk_status sk_gemm_ex(const sk_gemm_args* args) {

@@ -6,7 +6,13 @@
 
 namespace sk {
 
-enum : int { DT_MXFP4 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP8 = 3 };
+// Input types.  DT_MXFP4_MXFP8 / DT_MXFP8_MXFP4: A in one MX format and B in
+// the other (E2M1 x E4M3 or E4M3 x E2M1, each with its own E8M0 scales).
+enum : int {
+  DT_MXFP4 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP8 = 3, DT_MXFP6_E2M3 = 4, DT_MXFP6_E3M2 = 5,
+  DT_MXFP4_MXFP8 = 6, DT_MXFP8_MXFP4 = 7
+};
+constexpr int kNumDtypes = 8;
 
 // Lock flags per scratch area; the grid never exceeds this many workgroups.
 constexpr int kMaxGrid = 1024;
@@ -37,7 +43,8 @@ struct KArgs {
   uint32_t* err;            // set to 1 when a wait gives up
   uint64_t spin_limit;      // ticks of the 100 MHz realtime counter
   int32_t M, N, K;
-  int32_t row_bytes;        // bytes of K data per row of A and of B (their pitch)
+  int32_t row_bytes;        // bytes of K data per row of A (its pitch)
+  int32_t row_bytes_b;      // the same for B (differs from A's when the formats differ)
   uint32_t sa_kstride;      // bytes per k-step block of SA and of SB (padded rows * SPR)
   uint32_t sb_kstride;
   int32_t tiles;            // T
@@ -189,10 +196,6 @@ struct ScaleLayout {
 hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, const ScaleLayout& la, const uint8_t* src_b,
                                  uint8_t* dst_b, const ScaleLayout& lb, int s_pitch, int ksteps, int spr,
                                  hipStream_t s);
-
-// dst[r][k] (E4M3 bytes) = the E2M1 codes of src (packed, even k in the low
-// nibble), for `bytes` source bytes (a multiple of 16; 16-byte aligned).
-hipError_t launch_widen_e2m1(const uint8_t* src, uint8_t* dst, int64_t bytes, hipStream_t s);
 
 // bf16 backward helpers (sk_backward.hip).  dst[c][r] = src[r][c] for a
 // rows x cols bf16 matrix.

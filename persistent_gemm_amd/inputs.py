@@ -28,7 +28,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs", "backward_inputs", "mixed_inputs", "pack_fp6"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "integer_inputs", "exact_inputs", "backward_inputs", "mixed_inputs",
+           "pack_fp6"]
 
 
 @dataclass(frozen=True)
@@ -189,6 +190,58 @@ def integer_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int,
     return out
 
 
+def exact_inputs(dtype: str, M: int, N: int, K: int, *, bias: bool, seed: int) -> dict:
+    """Inputs of `dtype` on which every fp32 partial sum, taken in any order, is exact, so that
+    every correct kernel gives the oracle's bits.  Each element is a multiple of a grid step
+    q, so each product is a multiple of q_a * q_b; partial sums are then exact while
+    sum_k |a*b| stays below 2**24 * q_a * q_b, returned as "exact_below" (the tests check it
+    on the oracle's sums).
+
+    * mxfp4: make_inputs (E2M1 steps of 2**-1, scales 2**-2 .. 2**2: q = 2**-3);
+    * bf16, fp8, mxfp8: integer_inputs (mxfp8 scales 2**-1 .. 2: q = 2**-1);
+    * mxfp6_e2m3: every code (steps of 2**-3), scales on {126, 127, 128}: q = 2**-4;
+    * mxfp6_e3m2: codes whose exponent field is 3 .. 6 (magnitudes 1 .. 14, steps of 2**-2
+      and up), scales on {126, 127, 128}: q = 2**-3;
+    * mxfp4_mxfp8, mxfp8_mxfp4: mixed_inputs with integer E4M3 elements (q = 2**-3 for the
+      E2M1 operand, 2**-1 for the E4M3 one).
+    """
+    if dtype == "mxfp4":
+        out = make_inputs(dtype, M, N, K, bias=bias, seed=seed)
+        out["exact_below"] = 2.0 ** 18
+    elif dtype in ("bf16", "fp8"):
+        out = integer_inputs(dtype, M, N, K, bias=bias, seed=seed)
+        out["exact_below"] = 2.0 ** 24
+    elif dtype == "mxfp8":
+        out = integer_inputs(dtype, M, N, K, bias=bias, seed=seed)
+        out["exact_below"] = 2.0 ** 22
+    elif dtype in ("mxfp4_mxfp8", "mxfp8_mxfp4"):
+        a_fmt, b_fmt = dtype.split("_")
+        out = mixed_inputs(a_fmt, b_fmt, M, N, K, bias=bias, seed=seed, integer_fp8=True)
+        out["exact_below"] = 2.0 ** 20
+    elif dtype in ("mxfp6_e2m3", "mxfp6_e3m2"):
+        if K % 32:
+            raise ValueError("MXFP6 needs K % 32 == 0")
+        g = torch.Generator().manual_seed(seed)
+        out = {"dtype": dtype, "M": M, "N": N, "K": K}
+
+        def codes(rows):
+            if dtype == "mxfp6_e2m3":
+                return torch.randint(0, 64, (rows, K), generator=g, dtype=torch.uint8)
+            sign = torch.randint(0, 2, (rows, K), generator=g, dtype=torch.uint8)
+            expo = torch.randint(3, 7, (rows, K), generator=g, dtype=torch.uint8)
+            mant = torch.randint(0, 4, (rows, K), generator=g, dtype=torch.uint8)
+            return (sign << 5) | (expo << 2) | mant
+
+        out["A"] = pack_fp6(codes(M).numpy())
+        out["SA"] = torch.randint(126, 129, (M, K // 32), generator=g, dtype=torch.uint8).numpy()
+        out["B"] = pack_fp6(codes(N).numpy())
+        out["SB"] = torch.randint(126, 129, (N, K // 32), generator=g, dtype=torch.uint8).numpy()
+        out["bias"] = _bf16_bits(torch.randint(-64, 65, (N,), generator=g).float()) if bias else None
+        out["exact_below"] = 2.0 ** 16 if dtype == "mxfp6_e2m3" else 2.0 ** 18
+    else:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return out
+
 
 def backward_inputs(M: int, N: int, K: int, *, seed: int, integer: bool = False) -> dict:
     """dC uint16[M][N], A uint16[M][K], B uint16[N][K] (bf16 bit patterns), drawn in that order:
@@ -215,7 +268,8 @@ def mixed_inputs(a_fmt: str, b_fmt: str, M: int, N: int, K: int, *, bias: bool, 
     if K % 32:
         raise ValueError("MX formats need K % 32 == 0")
     g = torch.Generator().manual_seed(seed)
-    out = {"a_fmt": a_fmt, "b_fmt": b_fmt, "M": M, "N": N, "K": K}
+    out = {"a_fmt": a_fmt, "b_fmt": b_fmt, "M": M, "N": N, "K": K,
+           "dtype": a_fmt if a_fmt == b_fmt else f"{a_fmt}_{b_fmt}"}
 
     def operand(fmt, rows):
         if fmt == "mxfp4":

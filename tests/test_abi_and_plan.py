@@ -55,7 +55,7 @@ def _args(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(A=None), 1), (dict(B=None), 1), (dict(C=None), 1), (dict(A_scale=None), 1),
     (dict(M=0), 1), (dict(N=-3), 1), (dict(K=0), 1), (dict(K=(1 << 21) + 32), 1), (dict(M=1 << 31), 1),
-    (dict(dtype=7), 1), (dict(policy=9), 1),
+    (dict(dtype=8), 1), (dict(policy=9), 1),
     (dict(K=48), 2), (dict(A=0x10008), 2), (dict(C=0x50002), 2), (dict(bias=0x60001), 2),
     (dict(C=0x10000 + 64), 1),                        # C overlaps A
     (dict(dtype=pg.BF16, K=12, A_scale=None, B_scale=None), 2),
@@ -66,10 +66,30 @@ def _args(**kw):
     (dict(dtype=pg.MXFP8, B_scale=None), 1),
     (dict(dtype=pg.MXFP8, K=80), 2),                  # K must be whole 32-element scale blocks
     (dict(dtype=pg.MXFP8, C=0x30000 + 16), 1),        # C overlaps A's scales ([M][K/32] bytes)
+    (dict(dtype=pg.MXFP6_E2M3, K=48), 2),
+    (dict(dtype=pg.MXFP6_E3M2, A_scale=None), 1),
+    (dict(dtype=pg.MXFP6_E2M3, C=0x20000 + 4096 + 16), 1),   # B spans 64 rows * 96 bytes
+    (dict(dtype=pg.MXFP4_MXFP8, C=0x20000 + 6144 + 16), 1),  # B is MXFP8: 64 rows * 128 bytes
+    (dict(dtype=pg.MXFP8_MXFP4, C=0x10000 + 4096 + 16), 1),  # A is MXFP8
+    (dict(dtype=pg.MXFP8_MXFP4, K=80), 2),
 ])
 def test_argument_checks(kw, status):
     a = _args(**kw)
     assert pg.load().sk_gemm_ex(ctypes.byref(a)) == status
+
+
+def test_gemm_mx_format_pairs():
+    """Formats that are not MX are rejected; an MXFP6 operand with one of another format has
+    no compiled kernel.  Both are decided before anything touches a device."""
+    lib = pg.load()
+    call = lambda fa, fb: lib.sk_gemm_mx(fa, fb, 0x10000, 0x20000, 0x30000, 0x40000, None, 0x50000, 64, 64, 128,
+                                         0, None)
+    assert call(pg.BF16, pg.MXFP4) == 1
+    assert call(pg.MXFP4, pg.FP8) == 1
+    assert call(pg.MXFP4_MXFP8, pg.MXFP4_MXFP8) == 1
+    assert call(pg.MXFP6_E2M3, pg.MXFP4) == 3
+    assert call(pg.MXFP6_E2M3, pg.MXFP6_E3M2) == 3
+    assert call(pg.MXFP8, pg.MXFP6_E3M2) == 3
 
 
 def test_addmm_requires_bias():

@@ -2,7 +2,8 @@
 MXFP4, one MXFP8) through sk_gemm_mx against the CPU oracle: bit for bit when
 the MXFP8 operand holds small integers (every sum exact), within |err| <=
 2**-7 * sum|a*b| + one bf16 ulp on random E4M3 inputs, with bit-identical
-repeats; equal formats give the same bits as their own entry points."""
+repeats; equal formats (MXFP4, MXFP6, MXFP8) give the same bits as the
+dtype's own kernels."""
 
 from __future__ import annotations
 
@@ -63,6 +64,22 @@ def test_mixed_random_within_bound_and_repeatable(a_fmt, b_fmt):
     first = _run(x, d)
     assert_within_bound(first, C, D, S, f"{a_fmt} x {b_fmt}")
     assert np.array_equal(_run(x, d), first)
+
+
+def test_equal_mxfp6_formats_match_gemm_ex():
+    from persistent_gemm_amd.inputs import exact_inputs
+    from gpu_util import assert_exact_inputs, device_inputs, oracle_full, run
+    for fmt in ("mxfp6_e2m3", "mxfp6_e3m2"):
+        x = exact_inputs(fmt, 130, 72, 160, bias=True, seed=33)
+        assert_exact_inputs(x)
+        d = device_inputs(x)
+        say(f"gemm_mx {fmt} x {fmt}")
+        got = pg.gemm_mx(fmt, fmt, d["A"], d["B"], d["SA"], d["SB"], d["bias"])
+        pg.check()
+        got = got.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, run(d))
+        C, _ = oracle_full(x)
+        assert_bitexact(got, C, f"{fmt} x {fmt}")
 
 
 def test_equal_formats_match_their_entry_points():

@@ -3,9 +3,10 @@
 MXFP4 inputs make every fp32 partial sum exact (products are multiples of
 2**-6 below 576, sums stay far below 2**18), so MXFP4 results must match the
 oracle bit for bit at every grid size, policy and tile.  bf16 / fp8 / MXFP8
-inputs with small integer values are exact too; random bf16 / fp8 / MXFP8
-inputs are held to |err| <= 2**-7 * sum|a*b| + one bf16 ulp, and must repeat
-bit for bit.
+inputs with small integer values are exact too, and so are the MXFP6 and
+mixed MXFP4 x MXFP8 inputs of inputs.exact_inputs (elements on a coarse grid,
+checked against their sums); random bf16 / fp8 / MXFP8 / MXFP6 inputs are
+held to |err| <= 2**-7 * sum|a*b| + one bf16 ulp, and must repeat bit for bit.
 """
 
 from __future__ import annotations
@@ -16,12 +17,13 @@ import torch
 
 import oracle
 import persistent_gemm_amd as pg
-from persistent_gemm_amd.inputs import WORKLOADS, integer_inputs, make_inputs
+from persistent_gemm_amd.inputs import WORKLOADS, exact_inputs, integer_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from gpu_util import assert_bitexact, assert_within_bound, device_inputs, oracle_full, run, say
+    from gpu_util import (abs_sums, assert_bitexact, assert_exact_inputs, assert_within_bound, device_inputs,
+                          oracle_full, run, say)
 
 
 def _wl(name, bias=None):
@@ -96,14 +98,28 @@ def test_integer_inputs_exact(dtype, M, N, K):
             assert_bitexact(run(d, grid_cap=g, tile=tile, policy=policy), C, f"{dtype} {tile} {policy} {g}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8"])
+@pytest.mark.parametrize("dtype", ["mxfp6_e2m3", "mxfp6_e3m2", "mxfp4_mxfp8", "mxfp8_mxfp4"])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 32), (100, 72, 96), (300, 200, 512), (64, 384, 1056)])
+def test_exact_mx_inputs(dtype, M, N, K):
+    """MXFP6 and mixed MXFP4 x MXFP8 on exact inputs: every tile shape, three policies."""
+    x = exact_inputs(dtype, M, N, K, bias=True, seed=M + N + K)
+    assert_exact_inputs(x)
+    d = device_inputs(x)
+    C, _ = oracle_full(x)
+    for tile in [None, (64, 64), (128, 128), (256, 256), (16, 256)]:
+        for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 5), (pg.PURE_DP, 2)]:
+            say(f"{dtype} exact {M}x{N}x{K} tile {tile} policy {policy} grid {g}")
+            assert_bitexact(run(d, grid_cap=g, tile=tile, policy=policy), C, f"{dtype} {tile} {policy} {g}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp8", "mxfp6_e2m3", "mxfp6_e3m2"])
 def test_random_within_bound_and_repeatable(dtype):
     M, N, K = 513, 388, 1056
     kw = {"fp8_scales": (0.5, 3.0)} if dtype == "fp8" else {}
     x = make_inputs(dtype, M, N, K, bias=True, seed=77, **kw)
     d = device_inputs(x)
     C, D = oracle_full(x)
-    S = oracle.abs_product_sums(dtype, x["A"], x["B"], x["SA"], x["SB"])
+    S = abs_sums(x)
     for tile in [None, (64, 64), (128, 128), (256, 256)]:
         for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 9)]:
             say(f"{dtype} random {M}x{N}x{K} tile {tile} policy {policy} grid {g}")
@@ -115,7 +131,9 @@ def test_random_within_bound_and_repeatable(dtype):
 
 # ---------------------------------------------------------------- every compiled kernel
 
-_DTYPES = {0: "mxfp4", 1: "bf16", 2: "fp8", 3: "mxfp8"}
+_DTYPES = {0: "mxfp4", 1: "bf16", 2: "fp8", 3: "mxfp8", 4: "mxfp6_e2m3", 5: "mxfp6_e3m2", 6: "mxfp4_mxfp8",
+           7: "mxfp8_mxfp4"}
+_MX = ["mxfp4", "mxfp8", "mxfp6_e2m3", "mxfp6_e3m2", "mxfp4_mxfp8", "mxfp8_mxfp4"]
 
 
 def _num_variants():
@@ -135,12 +153,10 @@ def test_every_variant_exact(index):
     v = pg.variants()[index]
     dtype, bm, bn = _DTYPES[v["dtype"]], v["tile_m"], v["tile_n"]
     M = 2 * bm + 7
-    ragged_k = {"mxfp4": 448, "bf16": 200, "fp8": 208, "mxfp8": 224}[dtype]   # the ABI needs K % 32, % 8, % 16
+    ragged_k = {"bf16": 200, "fp8": 208, "mxfp4": 448}.get(dtype, 224)   # the ABI needs K % 8, % 16, % 32
     for N, K in [(2 * bn + 16, 512 if dtype == "mxfp4" else 256), (bn + 13, ragged_k)]:
-        if dtype == "mxfp4":
-            x = make_inputs(dtype, M, N, K, bias=True, seed=3000 + index)
-        else:
-            x = integer_inputs(dtype, M, N, K, bias=True, seed=3000 + index)
+        x = exact_inputs(dtype, M, N, K, bias=True, seed=3000 + index)
+        assert_exact_inputs(x)
         d = device_inputs(x)
         C, _ = oracle_full(x)
         for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 7), (pg.PURE_DP, 3)]:
@@ -149,7 +165,7 @@ def test_every_variant_exact(index):
             assert_bitexact(got, C, f"variant {index} {M}x{N}x{K} policy {policy} grid {g}")
 
 
-@pytest.mark.parametrize("dtype", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("dtype", _MX)
 def test_direct_scale_reads(dtype):
     """MX kernels of up to 128-row tiles read the scales straight from the caller's
     [rows][K/32] arrays when K is a whole number of k-steps and the arrays are
@@ -161,10 +177,8 @@ def test_direct_scale_reads(dtype):
         if _DTYPES[v["dtype"]] != dtype or v["tile_m"] > 128:
             continue
         M, N, K = 2 * v["tile_m"] + 3, 2 * v["tile_n"] + 8, 1024
-        if dtype == "mxfp4":
-            x = make_inputs(dtype, M, N, K, bias=True, seed=3500 + index)
-        else:
-            x = integer_inputs(dtype, M, N, K, bias=True, seed=3500 + index)
+        x = exact_inputs(dtype, M, N, K, bias=True, seed=3500 + index)
+        assert_exact_inputs(x)
         d = device_inputs(x)
         C, _ = oracle_full(x)
         for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 7), (pg.PURE_DP, 3)]:
