@@ -45,15 +45,21 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MXFP4 Stream-K GEMM TFLOP/s and % of dense FP4 MFMA peak, 1 MI355X"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
-# (a product with one E4M3 operand runs at the fp8 rate)
-PEAK_TFLOPS = {"mxfp4": 10100.0, "fp8": 5000.0, "mxfp8": 5000.0, "mxfp4_mxfp8": 5000.0, "bf16": 2500.0}
+# (FP6 runs at the FP4 rate; a product with one E4M3 operand at the fp8 rate)
+PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp6_e2m3": 10100.0, "mxfp6_e3m2": 10100.0, "fp8": 5000.0, "mxfp8": 5000.0,
+               "mxfp4_mxfp8": 5000.0, "mxfp8_mxfp4": 5000.0, "bf16": 2500.0}
+# bits per element of A and of B
+ELEMENT_BITS = {"mxfp4": (4, 4), "mxfp6_e2m3": (6, 6), "mxfp6_e3m2": (6, 6), "mxfp8": (8, 8), "fp8": (8, 8),
+                "mxfp4_mxfp8": (4, 8), "mxfp8_mxfp4": (8, 4), "bf16": (16, 16)}
+MIXED = {"mxfp4_mxfp8": ("mxfp4", "mxfp8"), "mxfp8_mxfp4": ("mxfp8", "mxfp4")}
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "mxfp4_addmm_8192"
 
 
 # the sources that decide the forward GEMM kernels and their launch (the
-# backward and the E2M1 widening pass live in files of their own)
-GEMM_SOURCES = ("sk_api.cpp", "sk_common.h", "sk_kernels.hip", "sk_tuning_table.inc")
+# backward helpers live in a file of their own)
+GEMM_SOURCES = ("sk_api.cpp", "sk_common.h", "sk_kernel.h", "sk_kernels.hip", "sk_kernels_mx.hip",
+                "sk_tuning_table.inc")
 
 
 def source_hash() -> str:
@@ -147,16 +153,12 @@ def algorithmic_bytes(w) -> int:
     if w.op == "backward":
         # reads dC, A, B; writes dA, dB, dbias
         return 2 * (M * N + M * K + N * K) + 2 * (M * K + N * K) + 2 * N
-    if w.dtype == "mxfp4":
-        b = (M + N) * (K // 2) + (M + N) * (K // 32)
-    elif w.dtype == "mxfp8":
-        b = (M + N) * K + (M + N) * (K // 32)
-    elif w.dtype == "mxfp4_mxfp8":
-        b = M * (K // 2) + N * K + (M + N) * (K // 32)
-    elif w.dtype == "bf16":
-        b = (M + N) * K * 2
-    else:
-        b = (M + N) * K + 8
+    ba, bb = ELEMENT_BITS[w.dtype]
+    b = (M * K * ba + N * K * bb) // 8
+    if w.dtype == "fp8":
+        b += 8                                  # the two per-tensor fp32 scales
+    elif w.dtype != "bf16":
+        b += (M + N) * (K // 32)                # E8M0 block scales
     return b + (2 * N if w.bias else 0) + 2 * M * N
 
 
@@ -166,8 +168,8 @@ def cpu_baseline(w, x, budget_s: float = 10.0) -> dict:
     if w.op == "backward":
         run_once = lambda: oracle.bf16_backward(x["dC"], x["A"], x["B"])
         what = "decode, two matrix products and a column sum"
-    elif w.dtype == "mxfp4_mxfp8":
-        run_once = lambda: oracle.gemm_mx("mxfp4", "mxfp8", x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=w.K)
+    elif w.dtype in MIXED:
+        run_once = lambda: oracle.gemm_mx(*MIXED[w.dtype], x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=w.K)
         what = "decode, one matrix product"
     else:
         run_once = lambda: oracle.gemm(w.dtype, x["A"], x["B"], x["SA"], x["SB"], x["bias"], K=w.K)
@@ -308,6 +310,9 @@ def vendor(args, w, copies, C, ours) -> int:
     vendor's MX call takes no bias here, so both run without one)."""
     import torch
     d0 = copies[0]
+    if w.dtype not in ("mxfp4", "mxfp8", "fp8", "bf16"):
+        print(f"--vendor: torch has no {w.dtype} product to compare with", file=sys.stderr)
+        return 2
     if w.dtype in ("mxfp4", "mxfp8"):
         el = torch.float4_e2m1fn_x2 if w.dtype == "mxfp4" else torch.float8_e4m3fn
         vs = [(c["A"].view(el), c["B"].view(el).t(), c["SA"].view(torch.float8_e8m0fnu),
@@ -371,23 +376,22 @@ def pg_call(w, c, bias, C):
 def device_inputs(torch, w, x, dev) -> dict:
     """Host arrays of one forward workload -> device tensors for the binding."""
     d = {}
-    if w.dtype == "mxfp4":
-        for k in ("A", "B", "SA", "SB"):
-            d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
-    elif w.dtype == "mxfp8":
-        for k in ("A", "B"):
-            d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
-        for k in ("SA", "SB"):
-            d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
-    elif w.dtype == "bf16":
-        for k in ("A", "B"):
-            d[k] = torch.from_numpy(x[k].view(np.int16)).view(torch.bfloat16).to(dev)
+    for op, fmt in zip(("A", "B"), MIXED.get(w.dtype, (w.dtype, w.dtype))):
+        t = np.ascontiguousarray(x[op])
+        if fmt == "bf16":
+            d[op] = torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to(dev)
+        elif fmt in ("mxfp8", "fp8"):
+            d[op] = torch.from_numpy(t).view(torch.float8_e4m3fn).to(dev)
+        else:  # packed E2M1 or FP6 bytes
+            d[op] = torch.from_numpy(t).to(dev)
+    if w.dtype == "bf16":
         d["SA"] = d["SB"] = None
-    else:
-        for k in ("A", "B"):
-            d[k] = torch.from_numpy(x[k]).view(torch.float8_e4m3fn).to(dev)
+    elif w.dtype == "fp8":
         d["SA"] = torch.tensor([x["SA"]], dtype=torch.float32, device=dev)
         d["SB"] = torch.tensor([x["SB"]], dtype=torch.float32, device=dev)
+    else:
+        for k in ("SA", "SB"):
+            d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
     d["bias"] = None if x["bias"] is None else torch.from_numpy(x["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
     return d
 
@@ -603,19 +607,12 @@ def main() -> int:
 
         def step(i):
             pg.gemm_bf16_backward(d["dC"], d["A"], d["B"], grid_cap=cap)
-    elif w.dtype == "mxfp4_mxfp8":
-        from persistent_gemm_amd.inputs import mixed_inputs
-        x = mixed_inputs("mxfp4", "mxfp8", w.M, w.N, w.K, bias=w.bias, seed=w.seed)
-        d = {"A": torch.from_numpy(x["A"]).to(dev), "B": torch.from_numpy(x["B"]).view(torch.float8_e4m3fn).to(dev),
-             "SA": torch.from_numpy(x["SA"]).to(dev), "SB": torch.from_numpy(x["SB"]).to(dev),
-             "bias": torch.from_numpy(x["bias"].view(np.int16)).view(torch.bfloat16).to(dev)}
-        C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
-        p = pg.plan("mxfp8", w.M, w.N, w.K, grid_cap=cap, policy=policy)   # the kernel that runs
-
-        def step(i):
-            pg.gemm_mx("mxfp4", "mxfp8", d["A"], d["B"], d["SA"], d["SB"], d["bias"], C, grid_cap=cap)
     else:
-        x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
+        if w.dtype in MIXED:
+            from persistent_gemm_amd.inputs import mixed_inputs
+            x = mixed_inputs(*MIXED[w.dtype], w.M, w.N, w.K, bias=w.bias, seed=w.seed)
+        else:
+            x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
         if args.co_schedule:
             return co_schedule(args, w, device_inputs(torch, w, x, dev), tile, policy)
 
@@ -666,7 +663,7 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(w, x)
     if args.workload == DEFAULT_WORKLOAD and default_launch and not args.no_others:
         del step
-        if w.op == "forward" and w.dtype != "mxfp4_mxfp8":
+        if w.op == "forward":
             del copies, C
         torch.cuda.empty_cache()
         out["other_configs"] = other_configs(torch, pg, dev, args.steps, args.warmup, not args.no_cpu)

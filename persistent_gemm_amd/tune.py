@@ -43,7 +43,10 @@ ROOT = os.path.dirname(HERE)
 TABLE = os.path.join(HERE, "csrc", "sk_tuning_table.inc")
 SUMMARY = os.path.join(ROOT, "profiles", "tuning_table.md")
 
-DTYPE_CODE = {"mxfp4": pg.MXFP4, "bf16": pg.BF16, "fp8": pg.FP8, "mxfp8": pg.MXFP8}
+DTYPE_CODE = {"mxfp4": pg.MXFP4, "bf16": pg.BF16, "fp8": pg.FP8, "mxfp8": pg.MXFP8, "mxfp6_e2m3": pg.MXFP6_E2M3,
+              "mxfp6_e3m2": pg.MXFP6_E3M2, "mxfp4_mxfp8": pg.MXFP4_MXFP8, "mxfp8_mxfp4": pg.MXFP8_MXFP4}
+# element format of A and of B
+FORMATS = {"mxfp4_mxfp8": ("mxfp4", "mxfp8"), "mxfp8_mxfp4": ("mxfp8", "mxfp4")}
 POLICIES = {"hybrid": pg.HYBRID, "sk": pg.PURE_SK, "dp": pg.PURE_DP}
 MARGIN = 0.03
 RUNOFF = 0.08
@@ -56,6 +59,10 @@ def _buffers(dtype: str, rows: int, K: int, g: torch.Generator):
     """Operand bytes and scales for `rows` rows of K elements, on the device."""
     if dtype == "mxfp4":
         x = torch.randint(0, 256, (rows, K // 2), generator=g, dtype=torch.uint8)
+        s = torch.full((rows, K // 32), 127, dtype=torch.uint8)
+        return x.cuda(), s.cuda()
+    if dtype.startswith("mxfp6"):
+        x = torch.randint(0, 256, (rows, 3 * K // 4), generator=g, dtype=torch.uint8)
         s = torch.full((rows, K // 32), 127, dtype=torch.uint8)
         return x.cuda(), s.cuda()
     if dtype == "mxfp8":
@@ -86,13 +93,15 @@ def sweep(dtype: str, reps: int):
     kernels = [i for i, v in enumerate(pg.variants()) if v["dtype"] == code]
     g = torch.Generator().manual_seed(2024)
     Kmax, Mmax, Nmax = max(KS), max(MS), max(NS)
-    A, SA = _buffers(dtype, Mmax, Kmax, g)
-    B, SB = _buffers(dtype, Nmax, Kmax, g)
+    fa, fb = FORMATS.get(dtype, (dtype, dtype))
+    A, SA = _buffers(fa, Mmax, Kmax, g)
+    B, SB = _buffers(fb, Nmax, Kmax, g)
     C = torch.empty(Mmax * Nmax, dtype=torch.bfloat16, device="cuda")
     rows = []
     for M, N, K in itertools.product(MS, NS, KS):
-        kb = K // 2 if dtype == "mxfp4" else K
-        a = A.view(-1)[: M * kb].view(M, kb)
+        row = {"mxfp4": K // 2, "mxfp6_e2m3": 3 * K // 4, "mxfp6_e3m2": 3 * K // 4}
+        ka, kb = row.get(fa, K), row.get(fb, K)
+        a = A.view(-1)[: M * ka].view(M, ka)
         b = B.view(-1)[: N * kb].view(N, kb)
         sa = None if SA is None else SA.view(-1)[: M * (K // 32)].view(M, K // 32)
         sb = None if SB is None else SB.view(-1)[: N * (K // 32)].view(N, K // 32)

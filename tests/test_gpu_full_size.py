@@ -13,12 +13,12 @@ import torch
 
 import oracle
 import persistent_gemm_amd as pg
-from persistent_gemm_amd.inputs import WORKLOADS, make_inputs
+from persistent_gemm_amd.inputs import WORKLOADS, make_inputs, mixed_inputs
 
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from gpu_util import assert_bitexact, assert_within_bound, device_inputs, oracle_full, run, say
+    from gpu_util import abs_sums, assert_bitexact, assert_within_bound, device_inputs, oracle_full, run, say
 
 
 def _wl(name):
@@ -140,3 +140,25 @@ def test_mxfp8_addmm_8192_sampled_within_bound():
     assert ok.all(), f"{(~ok).sum()} of {ok.size} sampled elements outside the bound"
     say("8192^3 mxfp8 addmm, repeat")
     assert np.array_equal(run(d), got)
+
+
+@pytest.mark.parametrize("name", ["mxfp6_e2m3_addmm_8192", "mxfp6_e3m2_addmm_8192", "mxfp4_mxfp8_addmm_8192"])
+def test_other_mx_addmm_8192_within_bound(name):
+    """MXFP6 (both element types) and mixed MXFP4 x MXFP8 at 8192^3, the plain launch (AUTO):
+    the whole output within the bound, then a bit-identical repeat.  Random codes over the
+    whole range and scales 2**-2 .. 2**2 make the sums inexact in fp32, hence the bound."""
+    w = WORKLOADS[name]
+    if w.dtype == "mxfp4_mxfp8":
+        x = mixed_inputs("mxfp4", "mxfp8", w.M, w.N, w.K, bias=w.bias, seed=w.seed)
+    else:
+        x = make_inputs(w.dtype, w.M, w.N, w.K, bias=w.bias, seed=w.seed)
+    d = device_inputs(x)
+    p = pg.plan(w.dtype, w.M, w.N, w.K, policy=pg.AUTO)
+    say(f"8192^3 {w.dtype} addmm, AUTO (kernel {p.variant}, grid {p.grid}, policy {p.policy})")
+    got = run(d, policy=pg.AUTO)
+    say(f"8192^3 {w.dtype} oracle")
+    C, D = oracle_full(x)
+    S = abs_sums(x)
+    assert_within_bound(got, C, D, S, f"{name} AUTO")
+    say(f"8192^3 {w.dtype} repeat")
+    assert np.array_equal(run(d, policy=pg.AUTO), got)
