@@ -396,15 +396,31 @@ def device_inputs(torch, w, x, dev) -> dict:
     return d
 
 
+# Untimed calls after the warm-up steps, until this much wall time has passed: under
+# load the device raises its shader clock over the first several milliseconds (a
+# 260 us call runs at about 320 us for its first twenty-odd repetitions), so a short
+# warm-up would time the ramp instead of the steady state.
+SETTLE_MS = 50.0
+
+
 def time_steps(torch, pg, step, steps: int, warmup: int) -> dict:
-    """Wall time per step over `steps` timed steps (after `warmup`), HIP events around
-    each call, and the device time per call: the same steps again between two
-    events on the launch stream, with a spin kernel queued first so that the host
-    stays ahead and the calls run back to back."""
+    """Wall time per step over `steps` timed steps (after `warmup` steps and the settle
+    calls), HIP events around each call, and the device time per call: the same steps
+    again between two events on the launch stream, with a spin kernel queued first so
+    that the host stays ahead and the calls run back to back."""
     for i in range(warmup):
         step(i)
     pg.check()
     torch.cuda.synchronize()
+    t_settle, n_settle = time.perf_counter(), 0
+    while (time.perf_counter() - t_settle) * 1e3 < SETTLE_MS:
+        step(warmup + n_settle)
+        n_settle += 1
+        if n_settle % 8 == 0:
+            torch.cuda.synchronize()   # keep the queue short: the loop measures device time, not enqueue time
+    torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    pg.check()
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -427,7 +443,8 @@ def time_steps(torch, pg, step, steps: int, warmup: int) -> dict:
     d1.record(stream)
     torch.cuda.synchronize()
     pg.check()
-    return {"ms_per_step": wall / steps * 1e3, "call_ms": call_ms, "dev_ms": d0.elapsed_time(d1) / steps}
+    return {"ms_per_step": wall / steps * 1e3, "call_ms": call_ms, "dev_ms": d0.elapsed_time(d1) / steps,
+            "settle": {"calls": n_settle, "ms": round(settle_ms, 1)}}
 
 
 def roofline_of(w, p, dev_ms: float, call_ms, traffic, cap_scaled: bool) -> dict:
@@ -495,7 +512,7 @@ def other_configs(torch, pg, dev, steps: int, warmup: int, cpu: bool) -> list:
             # a capped call takes up to 256/cap times longer (about 10 ms at cap 1): fewer repetitions there
             n = max(3, min(steps, steps * p.grid // 256)) if w.caps else steps
             t = time_steps(torch, pg, step, n, min(warmup, n))
-            r = {"grid_cap": cap, "steps": n, "ms_per_step": round(t["ms_per_step"], 5),
+            r = {"grid_cap": cap, "steps": n, "settle": t["settle"], "ms_per_step": round(t["ms_per_step"], 5),
                  "value": round(float(w.flops) / (t["ms_per_step"] / 1e3) / 1e12, 3), "unit": "TFLOP/s",
                  "config": plan_config(pg, p),
                  "roofline": roofline_of(w, p, t["dev_ms"], t["call_ms"], None, bool(w.caps))}
@@ -647,6 +664,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {**t["settle"], "why": f"untimed calls after the warm-up until {SETTLE_MS:.0f} ms have passed: "
+                                         "the device raises its clock over the first milliseconds under load"},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
