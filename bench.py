@@ -532,6 +532,48 @@ def other_configs(torch, pg, dev, steps: int, warmup: int, cpu: bool) -> list:
     return out
 
 
+def ceiling(args) -> int:
+    """The device's own ceilings for the roofline, from libskprobe.so: MFMA-only rates on the
+    whole device with fixed, rotating random and zero operands (FP4, E4M3, bf16), and the
+    rotating-operand FP4 rate with direct-to-LDS loads of random bytes interleaved, from an
+    L2-sized and a memory-sized span per workgroup.  One JSON line."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "persistent_gemm_amd", "libskprobe.so"))
+    lib.skp_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                                  ctypes.POINTER(ctypes.c_double)]
+    lib.skp_mfma_dma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int,
+                                 ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double)]
+    torch.cuda.set_device(0)
+    ms, flop, nbytes = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
+    rows = []
+    kinds = [("fp4 scaled 32x32x64", 0, PEAK_TFLOPS["mxfp4"], 80000), ("e4m3 scaled 32x32x64", 1, PEAK_TFLOPS["fp8"], 50000),
+             ("bf16 32x32x16", 2, PEAK_TFLOPS["bf16"], 100000)]
+    for name, kind, peak, iters in kinds:
+        for mode, what in ((0, "fixed operands"), (1, "rotating random operands"), (2, "zero operands")):
+            if lib.skp_mfma_rate(kind, mode, iters, ctypes.byref(ms), ctypes.byref(flop)) != 0:
+                raise RuntimeError("skp_mfma_rate failed")
+            tf = flop.value / (ms.value / 1e3) / 1e12
+            rows.append({"probe": "mfma only", "mfma": name, "data": what, "ms": round(ms.value, 3),
+                         "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)})
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (256 << 20,), dtype=torch.int32, device="cuda")   # 1 GiB of random bytes
+    for span, where in ((64 << 10, "64 KiB per workgroup (L2)"), (4 << 20, "4 MiB per workgroup (memory)")):
+        for loads in (0, 1, 2, 4):
+            if lib.skp_mfma_dma(loads, src.data_ptr(), span, 60000, ctypes.byref(ms), ctypes.byref(flop),
+                                ctypes.byref(nbytes)) != 0:
+                raise RuntimeError("skp_mfma_dma failed")
+            s = ms.value / 1e3
+            rows.append({"probe": "fp4 mfma + direct-to-LDS loads", "loads_per_8_mfma": loads, "span": where,
+                         "ms": round(ms.value, 3), "tflops": round(flop.value / s / 1e12, 1),
+                         "gbs_per_cu_into_lds": round(nbytes.value / s / 1e9 / 256, 1)})
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"ceiling": rows, "how": "256 workgroups of 8 waves (2 per SIMD), back-to-back MFMAs into 8 "
+                      "accumulators per wave; one timed launch after a shorter warm-up launch"}), flush=True)
+    return 0
+
+
 def trace_calls(args, torch, pg, w, copies, C, cap, policy, tile, p) -> int:
     """The launch's phase trace on `args.trace` calls (after the warm-ups), one JSON line each."""
     buf = torch.zeros(32 * p.grid, dtype=torch.int64, device=C.device)
@@ -583,6 +625,12 @@ def main() -> int:
                     help="instead of timing, run CALLS calls of the launch with the library's phase trace and "
                          "print each call's phase summary (per-workgroup 100 MHz stamps: ramp, streaming, "
                          "fixup waits, epilogues) as one JSON line")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="instead of the GEMM, run the device-ceiling probes (libskprobe.so): MFMA-only rates by "
+                         "operand data and with direct-to-LDS loads interleaved")
+    ap.add_argument("--zero-data", action="store_true",
+                    help="time the workload with all-zero A and B (same kernel and launch): the power the "
+                         "operand bits draw sets the clock; its own JSON line, never the headline")
     ap.add_argument("--traffic-summary", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV output (no GPU)")
@@ -599,6 +647,8 @@ def main() -> int:
 
     if args.copy_calibration > 0:
         return copy_calibration(args)
+    if args.ceiling:
+        return ceiling(args)
 
     import torch
 
@@ -634,6 +684,9 @@ def main() -> int:
             return co_schedule(args, w, device_inputs(torch, w, x, dev), tile, policy)
 
         copies = [device_inputs(torch, w, x, dev)]
+        if args.zero_data:
+            copies[0]["A"].zero_()
+            copies[0]["B"].zero_()
         for i in range(1, max(1, args.rotate or w.rotate)):
             copies.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in copies[0].items()})
         C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
@@ -652,7 +705,8 @@ def main() -> int:
     t = time_steps(torch, pg, step, args.steps, args.warmup)
     ms_per_step = t["ms_per_step"]
     value = float(w.flops) / (ms_per_step / 1e3) / 1e12
-    default_launch = args.cap is None and args.tile is None and policy == pg.AUTO and args.variant is None
+    default_launch = (args.cap is None and args.tile is None and policy == pg.AUTO and args.variant is None
+                      and not args.zero_data)
     tag = "" if default_launch else "_nondefault"
     traffic = traffic_for(args.workload, tag, p.variant)
     out = {
@@ -671,7 +725,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic",
+        "data": "synthetic, A and B all zero (--zero-data)" if args.zero_data else "synthetic",
         "config": {"workload": args.workload, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias,
                    "input_copies": max(1, args.rotate or w.rotate), **plan_config(pg, p),
                    "policy_requested": args.policy, "parallelism": "stream-k, 1 GPU"},

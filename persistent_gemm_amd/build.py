@@ -9,6 +9,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libskgemm.so")
+# device-ceiling probes for the roofline (bench.py --ceiling), a library of their own
+PROBE_LIB = os.path.join(HERE, "libskprobe.so")
+PROBE_SOURCES = ["sk_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["sk_kernels.hip", "sk_kernels_mx.hip", "sk_backward.hip", "sk_api.cpp"]
@@ -20,10 +23,10 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link the shared library; returns its path."""
+    """Compile every source (in parallel) and link the shared libraries; returns the GEMM library's path."""
     from concurrent.futures import ThreadPoolExecutor
     objs, cmds = [], []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
@@ -34,9 +37,11 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(len(cmds), 5)) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    n = len(SOURCES)
+    for lib, lib_objs in ((LIB, objs[:n]), (PROBE_LIB, objs[n:])):
+        tmp = lib + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *lib_objs, "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -811,20 +811,32 @@ struct Kernel {
       __hip_atomic_store(a.locks + w, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // Wait until workgroup v has published; false if the spin limit ran out.
-  static __device__ __forceinline__ bool wait_for(const KArgs& a, int v, int* s_flag) {
-    if (threadIdx.x == 0) {
+  // Wait until workgroups first .. w-1 have all published; false if the spin
+  // limit ran out.  Wave 0 polls up to 64 of the flags at once, one per lane,
+  // so that the round trips of device-scope loads overlap instead of adding
+  // up one contributor after another.
+  static __device__ __forceinline__ bool wait_all(const KArgs& a, int first, int w, int* s_flag) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       int ok = 1;
-      while (__hip_atomic_load(a.locks + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
-        __builtin_amdgcn_s_sleep(2);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > a.spin_limit) {
-          ok = 0;
-          break;
+      for (int b = first; b < w && ok; b += 64) {
+        const int v = b + lane;
+        bool done = v >= w;
+        for (;;) {
+          if (!done) done = __hip_atomic_load(a.locks + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+          if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+          __builtin_amdgcn_s_sleep(2);
+          if (__builtin_amdgcn_s_memrealtime() - t0 > a.spin_limit) {
+            ok = 0;
+            break;
+          }
         }
       }
-      if (!ok) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *s_flag = ok;
+      if (lane == 0) {
+        if (!ok) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = ok;
+      }
     }
     __syncthreads();
     // The flag is the same for every lane; saying so keeps the work loop (and
@@ -950,10 +962,40 @@ struct Kernel {
     // (8 runs in flight, 4 for eight-wave tiles, whose register file is half)
     constexpr int CHK_RUNS = C::NW >= 8 ? 4 : 8;
     constexpr int CHK = CHK_RUNS / C::NQ > 0 ? CHK_RUNS / C::NQ : 1;
+    // Wave tiles of at most 4 runs: the partials of the first PRE contributors
+    // (w-1 .. w-PRE), every run of every block, are loaded up front in one
+    // batch (at most 16 runs in flight), so the blocks do not each wait a round
+    // trip; the rest, if any, follow in chunks as above.
+    constexpr int RUNS = C::FM * C::FN * C::NQ;
+    constexpr int PRE = RUNS <= 4 ? 16 / RUNS : 0;
+    v4u pre[PRE > 0 ? PRE : 1][PRE > 0 ? RUNS : 1];
+    if constexpr (PRE > 0) {
+#pragma unroll
+      for (int c = 0; c < PRE; ++c)
+        if (w - 1 - c >= first) {
+          const uint32_t base = slot_off(w - 1 - c);
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+              for (int q = 0; q < C::NQ; ++q)
+                pre[c][(i * C::FN + j) * C::NQ + q] =
+                    __builtin_amdgcn_raw_buffer_load_b128(rp, base + run_off(i, j, q), 0, kDeviceScope);
+        }
+    }
     auto block_sums = [&](const typename Acc<C>::T& blk, int i, int j, v4f x[C::NQ]) {
 #pragma unroll
       for (int q = 0; q < C::NQ; ++q) x[q] = read_run(blk, q);
-      for (int v0 = w - 1; v0 >= first; v0 -= CHK) {
+      if constexpr (PRE > 0) {
+#pragma unroll
+        for (int c = 0; c < PRE; ++c)
+          if (w - 1 - c >= first) {
+#pragma unroll
+            for (int q = 0; q < C::NQ; ++q) x[q] += __builtin_bit_cast(v4f, pre[c][(i * C::FN + j) * C::NQ + q]);
+          }
+      }
+      for (int v0 = w - 1 - PRE; v0 >= first; v0 -= CHK) {
         v4u p[CHK][C::NQ];
 #pragma unroll
         for (int c = 0; c < CHK; ++c)
@@ -1256,11 +1298,7 @@ struct Kernel {
         if (ic.mode == WORK_OWNER) {
           // every contributor has published before any partial is read
           first = ic.first;
-          for (int v = w - 1; v >= first; --v)
-            if (!wait_for(kargs(), v, s_flag)) {
-              ok = false;
-              break;
-            }
+          ok = wait_all(kargs(), first, w, s_flag);
         }
         stamp(2);
         if (ok) {

@@ -282,3 +282,11 @@ def test_auto_choice_cache_keeps_answers_apart():
     with ThreadPoolExecutor(max_workers=4) as ex:
         got = list(ex.map(answer, queries * 8))
     assert got == [want[q] for q in queries * 8]
+
+
+def test_probe_library_exports_its_probes():
+    """libskprobe.so (bench.py --ceiling) is built beside the GEMM library and exports its two probes."""
+    import os
+    path = os.path.join(os.path.dirname(pg.library_path()), "libskprobe.so")
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "skp_mfma_rate") and hasattr(lib, "skp_mfma_dma")
