@@ -592,7 +592,7 @@ def trace_calls(args, torch, pg, w, copies, C, cap, policy, tile, p) -> int:
                    variant=args.variant, trace=buf)
         e1.record()
         pg.check()
-        summ = pg.phase_summary(buf.cpu().numpy(), p.grid)
+        summ = pg.phase_summary(buf.cpu().numpy(), p.grid, p)
         print(json.dumps({"workload": args.workload, "call": i, "event_us": round(e0.elapsed_time(e1) * 1e3, 2),
                           "config": plan_config(pg, p), "input_copies": len(copies), "phases": summ}), flush=True)
     return 0

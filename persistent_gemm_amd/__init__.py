@@ -412,9 +412,11 @@ def gemm_ex(dtype, A, B, A_scale=None, B_scale=None, bias=None, C=None, *, grid_
     return C
 
 
-def phase_summary(words, grid: int) -> dict:
+def phase_summary(words, grid: int, plan: "Plan | None" = None) -> dict:
     """Phase durations (microseconds) from a launch's trace words (host int array of 32 * grid):
-    min / median / max over the workgroups of each phase, relative to the earliest entry."""
+    min / median / max over the workgroups of each phase, relative to the earliest entry.
+    Given the launch's plan, each item's phases are also split by the item's role
+    (whole tile, contributor, owner) from the host's copy of the work lists."""
     import numpy as np
     t = np.asarray(words, dtype=np.int64).reshape(-1, 32)[:grid]
     t0 = t[:, 0].min()
@@ -425,12 +427,31 @@ def phase_summary(words, grid: int) -> dict:
            "prologue_args_us": f(us(t[:, 29] - t[:, 0])), "prologue_issue_us": f(us(t[:, 28] - t[:, 29])),
            "prologue_land_us": f(us(t[:, 27] - t[:, 28])), "items": []}
     n = t[:, 30]
+    roles = None
+    if plan is not None:
+        names = {0: "whole", 1: "contributor", 2: "owner"}
+        lists = [plan_wg_work(plan, w) for w in range(grid)]
+        roles = [[names[x[3]] for x in lst] for lst in lists]
     for j in range(min(int(n.max()), 6)):
         has = n > j
         st, ke, fx, en = (t[has, 1 + 4 * j + i] for i in range(4))
-        out["items"].append({"item": j, "workgroups": int(has.sum()), "start_us": f(us(st - t0)),
-                             "ksteps_us": f(us(ke - st)), "publish_or_wait_us": f(us(fx - ke)),
-                             "epilogue_us": f(us(en - fx)), "end_us": f(us(en - t0))})
+        item = {"item": j, "workgroups": int(has.sum()), "start_us": f(us(st - t0)),
+                "ksteps_us": f(us(ke - st)), "publish_or_wait_us": f(us(fx - ke)),
+                "epilogue_us": f(us(en - fx)), "end_us": f(us(en - t0))}
+        if roles is not None:
+            idx = np.nonzero(has)[0]
+            by = {}
+            for w in idx:
+                if j < len(roles[w]):
+                    by.setdefault(roles[w][j], []).append(w)
+            item["by_role"] = {}
+            for role, ws in by.items():
+                r = t[ws]
+                st2, ke2, fx2, en2 = (r[:, 1 + 4 * j + i] for i in range(4))
+                item["by_role"][role] = {"workgroups": len(ws), "ksteps_end_us": f(us(ke2 - t0)),
+                                         "publish_or_wait_us": f(us(fx2 - ke2)), "epilogue_us": f(us(en2 - fx2)),
+                                         "end_us": f(us(en2 - t0))}
+        out["items"].append(item)
     return out
 
 
