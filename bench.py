@@ -405,9 +405,11 @@ SETTLE_MS = 50.0
 
 def time_steps(torch, pg, step, steps: int, warmup: int) -> dict:
     """Wall time per step over `steps` timed steps (after `warmup` steps and the settle
-    calls), HIP events around each call, and the device time per call: the same steps
-    again between two events on the launch stream, with a spin kernel queued first so
-    that the host stays ahead and the calls run back to back."""
+    calls), with nothing but the steps between the two synchronisations; then the device
+    time per call: the same steps again between two events on the launch stream, with a
+    spin kernel queued first so that the host stays ahead and the calls run back to back;
+    then, for information, HIP events around each call of a third pass (events recorded
+    between calls lengthen a short call's wall time, so the timed loop has none)."""
     for i in range(warmup):
         step(i)
     pg.check()
@@ -422,19 +424,13 @@ def time_steps(torch, pg, step, steps: int, warmup: int) -> dict:
     settle_ms = (time.perf_counter() - t_settle) * 1e3
     pg.check()
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        starts[i].record(stream)
         step(i)
-        ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     pg.check()
-    call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-    torch.cuda.synchronize()
     hold_device(torch, 200_000 * steps)
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     d0.record(stream)
@@ -443,6 +439,15 @@ def time_steps(torch, pg, step, steps: int, warmup: int) -> dict:
     d1.record(stream)
     torch.cuda.synchronize()
     pg.check()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    pg.check()
+    call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     return {"ms_per_step": wall / steps * 1e3, "call_ms": call_ms, "dev_ms": d0.elapsed_time(d1) / steps,
             "settle": {"calls": n_settle, "ms": round(settle_ms, 1)}}
 
@@ -463,7 +468,7 @@ def roofline_of(w, p, dev_ms: float, call_ms, traffic, cap_scaled: bool) -> dict
                        "how": "device time per call, back-to-back calls between two HIP events"},
          "call_ms": {"mean": round(float(np.mean(call_ms)), 5), "min": round(float(np.min(call_ms)), 5),
                      "median": round(float(np.median(call_ms)), 5), "max": round(float(np.max(call_ms)), 5),
-                     "how": "HIP events around each call of the timed loop"},
+                     "how": "HIP events around each call of a pass after the timed ones"},
          "algorithmic_bytes": ab, "hbm_gbs_at_algorithmic_bytes": round(ab / s / 1e9, 1)}
     if w.dtype == "mxfp4" and w.M <= 16:
         r.update({"bound": "hbm", "achieved": round(ab / s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
