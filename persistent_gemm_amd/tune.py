@@ -52,7 +52,7 @@ MARGIN = 0.03
 RUNOFF = 0.08
 MS = (16, 128, 1024, 4096, 8192)
 NS = (1024, 4096, 8192)
-KS = (1024, 8192)
+KS = (1024, 4096, 8192)
 
 
 def _buffers(dtype: str, rows: int, K: int, g: torch.Generator):
