@@ -192,6 +192,11 @@ struct Cfg {
   static constexpr int A_PT = cdiv(A_GROUPS, NW), B_PT = cdiv(B_GROUPS, NW);
   static constexpr int SA_PT = cdiv(SA_INST, NW), SB_PT = cdiv(SB_INST, NW);
   static constexpr int LOADS_PER_STAGE_S = A_PT + B_PT + SA_PT + SB_PT;
+  // Eight-wave kernels whose operand fragments take 8 VGPRs (E4M3 and the
+  // six-bit types, NCH == 2) refill A's fragments in place and double-buffer
+  // only B's: two full sets of operands would not fit beside the
+  // accumulators in the 128 VGPRs such a wave has.
+  static constexpr bool INPLACE = NW >= 8 && NCH == 2;
   static constexpr int P_SLOT = BM * BN;                // floats per scratch slot
   static constexpr int P_WAVE = FM * FN * ACC * 64;     // floats per wave in a slot
   static constexpr int NQ = ACC / 4;                    // 4-column runs per block per lane
@@ -729,6 +734,34 @@ struct Kernel {
     }
   }
 
+  // MFMA slot B of sub-step U with A's fragments from oa and B's from ob.
+  template <int U, int B>
+  static __device__ __forceinline__ void mfma_ab(const Ops& oa, const Ops& ob, const Scales& sc, Acc<C>& acc) {
+    constexpr BlockIJ bij = block_of(B);
+    constexpr int i = bij.i, j = bij.j;
+    constexpr int ba = C::MX ? sbyte(i, U) : 0, bb = C::MX ? sbyte(j, U) : 0;
+    mfma<C, ba % 4, bb % 4>(acc.v[i][j], oa.a[i], ob.b[j], (int)sc.a[ba / 4], (int)sc.b[bb / 4]);
+  }
+  // The slot of sub-step order in which A's fragment I is used for the last time.
+  static constexpr int last_use_a(int i) {
+    int l = -1;
+    for (int b = 0; b < C::FM * C::FN; ++b)
+      if (block_of(b).i == i) l = b;
+    return l;
+  }
+  // A's fragment I (both halves) / B's fragment J of sub-step U, from the stage at byte offset so.
+  template <int U, int I>
+  static __device__ __forceinline__ void read_a(int so, const LdsPtrs& p, Ops& o) {
+    static_for<C::NCH>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      read_chunk<C::FA, h>(o.a[I][h], p.a + so + p.slot_a[U * C::NCH + h] + I * C::MF * C::KB);
+    });
+  }
+  template <int U, int J, int H>
+  static __device__ __forceinline__ void read_b(int so, const LdsPtrs& p, Ops& o) {
+    read_chunk<C::FB, H>(o.b[J][H], p.b + so + p.slot_b[U * C::NCH + H] + J * C::MF * C::KB);
+  }
+
   template <int U, int B>
   static __device__ __forceinline__ void mfma_one(const Ops& o, const Scales& sc, Acc<C>& acc) {
     constexpr BlockIJ bij = block_of(B);
@@ -1258,6 +1291,75 @@ struct Kernel {
       advance_issue();
     };
 
+    // INPLACE kernels: A's fragments live in o0.a and are refilled one by one
+    // right after the MFMA that uses each for the last time in a sub-step; B's
+    // alternate between o0.b (even sub-steps) and o1.b (odd), read early in
+    // the sub-step before.  In the last sub-step the refills come from the
+    // next stage, so those whose slot falls before the barrier wait for it,
+    // as do B's fragments and the scales of the next k-step.
+    auto kstep_inplace = [&](int d, auto& o0, auto& o1, Scales& sc0, Scales& sc1, Acc<C>& acc) {
+      static_assert(!C::INPLACE || PRE > 0, "the in-place schedule issues its loads before the barrier");
+      const int cur = d % S, nxt = (d + 1) % S;
+      const DmaCtx dc = dma_ctx();
+      constexpr int NBR = C::FN * C::NCH;   // B reads per sub-step
+      static_for<C::NU>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        constexpr bool last = u + 1 == C::NU;
+        auto& bnow = (u & 1) ? o1 : o0;
+        auto& bnxt = (u & 1) ? o0 : o1;
+        static_for<NB>([&](auto bc) {
+          constexpr int b = decltype(bc)::value;
+          constexpr int slot = u * NB + b;
+          if constexpr (last && b == HB) {
+            wait_vmcnt_n<(S - 2) * PER_STAGE>();
+            lds_barrier();
+            const lds_u8* st = stage_ptr(smem, nxt);
+            if constexpr (C::MX) read_scale_a(st, lp, sc1);
+            static_for<C::FM>([&](auto ic) {
+              constexpr int i = decltype(ic)::value;
+              if constexpr (last_use_a(i) < HB) read_a<0, i>(nxt * C::STAGE, lp, o0);
+            });
+            if constexpr (C::MX) read_scale_b(st, lp, sc1);
+            static_for<NBR>([&](auto rc) {
+              constexpr int r = decltype(rc)::value;
+              read_b<0, r / C::NCH, r % C::NCH>(nxt * C::STAGE, lp, bnxt);
+            });
+          }
+          mfma_ab<u, b>(o0, bnow, sc0, acc);
+          static_for<C::FM>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (last_use_a(i) == b) {
+              if constexpr (!last) read_a<u + 1, i>(cur * C::STAGE, lp, o0);
+              else if constexpr (b >= HB) read_a<0, i>(nxt * C::STAGE, lp, o0);
+            }
+          });
+          if constexpr (!last) {
+            static_for<NBR>([&](auto rc) {
+              constexpr int r = decltype(rc)::value;
+              if constexpr ((NBR <= NB ? r : r * NB / NBR) == b) read_b<u + 1, r / C::NCH, r % C::NCH>(cur * C::STAGE, lp, bnxt);
+            });
+          }
+          if constexpr (slot < PRE) {
+            static_for<PER_STAGE>([&](auto pc) {
+              constexpr int pp = decltype(pc)::value;
+              if constexpr (pp * DMA_SPAN / PER_STAGE == slot) dma_piece<pp>(dc, lo, row_bytes, row_bytes_b);
+            });
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        anchor(acc);
+      });
+      sc0 = sc1;
+      if constexpr ((C::NU & 1) == 1) {
+        // the next k-step's B went to o1 (its sub-step 0 reads o0)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int h = 0; h < C::NCH; ++h) o0.b[j][h] = o1.b[j][h];
+      }
+      advance_issue();
+    };
+
     static_for<S - 1>([&](auto) {
       const DmaCtx dc = dma_ctx();
       static_for<PER_STAGE>([&](auto pc) { dma_piece<decltype(pc)::value>(dc, lo, row_bytes, row_bytes_b); });
@@ -1282,7 +1384,8 @@ struct Kernel {
       int n = ic.k1 - ic.k0;   // at least one k-step per item
       stamp(0);
       do {
-        kstep_interleaved(done, o0, o1, sc0, sc1, acc);
+        if constexpr (C::INPLACE) kstep_inplace(done, o0, o1, sc0, sc1, acc);
+        else kstep_interleaved(done, o0, o1, sc0, sc1, acc);
         ++done;
       } while (--n > 0);
 
