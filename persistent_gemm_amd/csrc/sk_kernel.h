@@ -315,9 +315,17 @@ __device__ __forceinline__ v2u round_run(const float t[4], const float b[4]) {
       : "=&v"(dn[0]), "=&v"(dn[1]), "=&v"(dn[2]), "=&v"(dn[3]), "=&v"(up[0]), "=&v"(up[1]), "=&v"(up[2]),
         "=&v"(up[3])
       : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+  // the odd one of the two: a mask of the low bit of the rounded-down sum
+  // (all ones when it is odd), then a bitfield select (two VALU ops)
   float o[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) o[k] = (__float_as_uint(dn[k]) & 1u) ? dn[k] : up[k];
+  for (int k = 0; k < 4; ++k) {
+    // (written out: the compiler would turn the plain form back into a compare and a select)
+    uint32_t m, r;
+    asm("v_bfe_i32 %0, %1, 0, 1" : "=v"(m) : "v"(dn[k]));
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(dn[k]), "v"(up[k]));
+    o[k] = __uint_as_float(r);
+  }
   v2u h;
   h[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{o[0], o[1]}), v2bf));
   h[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{o[2], o[3]}), v2bf));
