@@ -19,10 +19,13 @@ namespace sk {
 // sub-step; so a lane's NB * NU bytes for a k-step are contiguous.  127 (a
 // scale of 1) stands for rows past `rows` and bytes past s_pitch (a ragged last
 // k-step).  All the factors are powers of two, given as shifts.  One
-// workgroup moves a tile's rows for 64 / SPR k-steps (64 bytes of each row)
+// workgroup moves a tile's rows for RB / SPR k-steps (RB bytes of each row)
 // through LDS: rows are read 16 bytes at a time when aligned, each k-step's
-// block is written 16 bytes at a time.  The LDS rows are 68 bytes apart (17
-// banks), since the lanes of a wave gather bytes from rows a few apart.
+// block is written 16 bytes at a time.  The LDS rows are RB + 4 bytes apart
+// (an odd number of banks), since the lanes of a wave gather bytes from rows
+// a few apart.  RB = 16 gives four small workgroups per CU at 8192^3, whose
+// loads and stores overlap; a pass of few large workgroups waits out one
+// memory round trip after another.
 struct RelayoutOp {
   const uint8_t* src;
   uint8_t* dst;
@@ -30,11 +33,12 @@ struct RelayoutOp {
   int tr, mf_s, ng_s, nb_s, nu_s;      // TR, and log2 of MF, NG, NB, NU
 };
 
-template <int SPR>
+template <int SPR, int RB>
 __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutOp b, int s_pitch, int ksteps) {
-  constexpr int KT = 64 / SPR;                 // k-steps per workgroup
-  constexpr int PITCH = 68;                    // LDS bytes per tile row
-  __shared__ __attribute__((aligned(16))) uint8_t t8[256 * PITCH];   // [tile row][64 bytes + 4]
+  constexpr int KT = RB / SPR;                 // k-steps per workgroup
+  constexpr int PITCH = RB + 4;                // LDS bytes per tile row
+  constexpr int PR = RB / 16;                  // 16-byte pieces per row
+  __shared__ __attribute__((aligned(16))) uint8_t t8[256 * PITCH];   // [tile row][RB bytes + 4]
   const bool is_a = (int)blockIdx.x < a.blocks;
   const RelayoutOp o = is_a ? a : b;
   const int tb = is_a ? (int)blockIdx.x : (int)blockIdx.x - a.blocks;
@@ -43,8 +47,8 @@ __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutO
   const uint8_t* __restrict__ src = o.src;
   if (o.vec16) {
     // s_pitch % 16 == 0: a 16-byte piece is wholly inside the row or past its end
-    for (int pc = tid; pc < o.tr * 4; pc += 256) {
-      const int r = pc >> 2, q = pc & 3, row = r0 + r, col = k0 * SPR + q * 16;
+    for (int pc = tid; pc < o.tr * PR; pc += 256) {
+      const int r = pc / PR, q = pc % PR, row = r0 + r, col = k0 * SPR + q * 16;
       v4u v = v4u{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
       if (row < o.rows && col < s_pitch) v = *(const v4u*)(src + (int64_t)row * s_pitch + col);
       uint32_t* d = (uint32_t*)(t8 + r * PITCH + q * 16);
@@ -54,8 +58,8 @@ __global__ __launch_bounds__(256) void sk_scale_relayout(RelayoutOp a, RelayoutO
       d[3] = v[3];
     }
   } else {
-    for (int bi = tid; bi < o.tr * 64; bi += 256) {
-      const int r = bi >> 6, c = bi & 63, row = r0 + r, col = k0 * SPR + c;
+    for (int bi = tid; bi < o.tr * RB; bi += 256) {
+      const int r = bi / RB, c = bi % RB, row = r0 + r, col = k0 * SPR + c;
       t8[r * PITCH + c] = (row < o.rows && col < s_pitch) ? src[(int64_t)row * s_pitch + col] : (uint8_t)127;
     }
   }
@@ -118,10 +122,11 @@ hipError_t launch_scale_relayout(const uint8_t* src_a, uint8_t* dst_a, const Sca
       return hipErrorInvalidValue;
   }
   const RelayoutOp a = op(src_a, dst_a, la), b = op(src_b, dst_b, lb);
-  const dim3 grid((unsigned)(a.blocks + b.blocks), (unsigned)((ksteps + 64 / spr - 1) / (64 / spr)));
-  if (spr == 2) hipLaunchKernelGGL(sk_scale_relayout<2>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
-  else if (spr == 4) hipLaunchKernelGGL(sk_scale_relayout<4>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
-  else hipLaunchKernelGGL(sk_scale_relayout<8>, grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  constexpr int RB = 16;
+  const dim3 grid((unsigned)(a.blocks + b.blocks), (unsigned)((ksteps + RB / spr - 1) / (RB / spr)));
+  if (spr == 2) hipLaunchKernelGGL((sk_scale_relayout<2, RB>), grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  else if (spr == 4) hipLaunchKernelGGL((sk_scale_relayout<4, RB>), grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
+  else hipLaunchKernelGGL((sk_scale_relayout<8, RB>), grid, dim3(256), 0, s, a, b, s_pitch, ksteps);
   return hipGetLastError();
 }
 
