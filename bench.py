@@ -558,7 +558,8 @@ def ceiling(args) -> int:
     ms, flop, nbytes = ctypes.c_float(), ctypes.c_double(), ctypes.c_double()
     rows = []
     kinds = [("fp4 scaled 32x32x64", 0, PEAK_TFLOPS["mxfp4"], 80000), ("e4m3 scaled 32x32x64", 1, PEAK_TFLOPS["fp8"], 50000),
-             ("bf16 32x32x16", 2, PEAK_TFLOPS["bf16"], 100000)]
+             ("bf16 32x32x16", 2, PEAK_TFLOPS["bf16"], 100000),
+             ("fp4 scaled 16x16x128", 3, PEAK_TFLOPS["mxfp4"], 160000), ("bf16 16x16x32", 4, PEAK_TFLOPS["bf16"], 200000)]
     for name, kind, peak, iters in kinds:
         for mode, what in ((0, "fixed operands"), (1, "rotating random operands"), (2, "zero operands")):
             if lib.skp_mfma_rate(kind, mode, iters, ctypes.byref(ms), ctypes.byref(flop)) != 0:

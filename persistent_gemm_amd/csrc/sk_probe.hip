@@ -19,6 +19,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
@@ -58,7 +59,18 @@ __device__ __forceinline__ void operands(v8i (&a)[8], v8i (&b)[8]) {
     }
 }
 
-// KIND 0: scaled FP4 (E2M1) 32x32x64; 1: scaled E4M3 32x32x64; 2: bf16 32x32x16.
+// KIND 0: scaled FP4 (E2M1) 32x32x64; 1: scaled E4M3 32x32x64; 2: bf16 32x32x16;
+// 3: scaled FP4 16x16x128; 4: bf16 16x16x32 (the 16x16 forms accumulate into 4 floats).
+template <int KIND>
+__device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  if constexpr (KIND == 3) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+  else {
+    const v8bf x = __builtin_bit_cast(v8bf, int4{a[0], a[1], a[2], a[3]});
+    const v8bf y = __builtin_bit_cast(v8bf, int4{b[0], b[1], b[2], b[3]});
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+  }
+}
+
 template <int KIND>
 __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, v16f c, int sa, int sb) {
   if constexpr (KIND == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
@@ -68,6 +80,26 @@ __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, v16f c, int sa,
     const v8bf y = __builtin_bit_cast(v8bf, int4{b[0], b[1], b[2], b[3]});
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
   }
+}
+
+template <int KIND, int MODE>
+__global__ __launch_bounds__(kThreads) void mfma_rate16(int iters, float* out) {
+  v4f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4f{};
+  v8i a[8], b[8];
+  operands<KIND == 4 ? 2 : 0, MODE>(a, b);
+  const uint32_t lane = blockIdx.x * kThreads + threadIdx.x;
+  const int sa = MODE == 1 ? 125 + (int)(mix32(lane) % 5) : 127;
+  const int sb = MODE == 1 ? 125 + (int)(mix32(lane + 99u) % 5) : 127;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = mfma16<KIND>(a[i], b[(i + 3) & 7], acc[i], sa, sb);
+  }
+  float s = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][3];
+  out[blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
 template <int KIND, int MODE>
@@ -135,7 +167,8 @@ typedef void (*RateKernel)(int, float*);
 
 template <int KIND>
 RateKernel rate_kernel(int mode) {
-  return mode == 0 ? mfma_rate<KIND, 0> : mode == 1 ? mfma_rate<KIND, 1> : mfma_rate<KIND, 2>;
+  if constexpr (KIND >= 3) return mode == 0 ? mfma_rate16<KIND, 0> : mode == 1 ? mfma_rate16<KIND, 1> : mfma_rate16<KIND, 2>;
+  else return mode == 0 ? mfma_rate<KIND, 0> : mode == 1 ? mfma_rate<KIND, 1> : mfma_rate<KIND, 2>;
 }
 
 // Milliseconds of one launch of `launch` (after one launch of warm-up work).
@@ -151,8 +184,8 @@ int time_launch(F&& launch, float* ms) {
   if (!rc && (hipEventRecord(e1) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)) rc = 1;
   if (!rc && hipEventElapsedTime(ms, e0, e1) != hipSuccess) rc = 1;
   if (!rc && hipGetLastError() != hipSuccess) rc = 1;
-  hipEventDestroy(e0);
-  hipEventDestroy(e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
   return rc;
 }
 
@@ -161,19 +194,21 @@ int time_launch(F&& launch, float* ms) {
 extern "C" {
 
 // Whole-device MFMA-only rate: kind 0 scaled FP4 32x32x64, 1 scaled E4M3
-// 32x32x64, 2 bf16 32x32x16; mode 0 fixed operands, 1 rotating random
-// operands, 2 zero operands.  256 workgroups of 8 waves, `iters` x 8 MFMAs per
+// 32x32x64, 2 bf16 32x32x16, 3 scaled FP4 16x16x128, 4 bf16 16x16x32; mode 0
+// fixed operands, 1 rotating random operands, 2 zero operands.  256 workgroups of 8 waves, `iters` x 8 MFMAs per
 // wave.  Writes the launch's milliseconds and FLOP; returns 0, or 1 on error.
 int skp_mfma_rate(int kind, int mode, int iters, float* ms, double* flop) {
-  if (kind < 0 || kind > 2 || mode < 0 || mode > 2 || iters < 1 || !ms || !flop) return 1;
+  if (kind < 0 || kind > 4 || mode < 0 || mode > 2 || iters < 1 || !ms || !flop) return 1;
   float* out = nullptr;
   if (hipMalloc(&out, (size_t)kGrid * kThreads * sizeof(float)) != hipSuccess) return 1;
-  RateKernel k = kind == 0 ? rate_kernel<0>(mode) : kind == 1 ? rate_kernel<1>(mode) : rate_kernel<2>(mode);
+  RateKernel k = kind == 0 ? rate_kernel<0>(mode) : kind == 1 ? rate_kernel<1>(mode) : kind == 2 ? rate_kernel<2>(mode)
+               : kind == 3 ? rate_kernel<3>(mode) : rate_kernel<4>(mode);
   const int rc = time_launch(
       [&](bool warm) { hipLaunchKernelGGL(k, dim3(kGrid), dim3(kThreads), 0, 0, warm ? iters / 4 + 1 : iters, out); },
       ms);
-  hipFree(out);
-  const double per = kind == 2 ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 64;
+  (void)hipFree(out);
+  const double per = kind == 2 ? 2.0 * 32 * 32 * 16 : kind == 3 ? 2.0 * 16 * 16 * 128 : kind == 4 ? 2.0 * 16 * 16 * 32
+                                                                                     : 2.0 * 32 * 32 * 64;
   *flop = per * 8.0 * iters * (kThreads / 64) * kGrid;
   return rc;
 }
@@ -196,7 +231,7 @@ int skp_mfma_dma(int loads, const void* src, uint32_t span, int iters, float* ms
                            warm ? iters / 4 + 1 : iters, out);
       },
       ms);
-  hipFree(out);
+  (void)hipFree(out);
   *flop = 2.0 * 32 * 32 * 64 * 8.0 * iters * (kThreads / 64) * kGrid;
   *bytes = 1024.0 * loads * iters * (kThreads / 64) * kGrid;
   return rc;
