@@ -59,7 +59,7 @@ DEFAULT_WORKLOAD = "mxfp4_addmm_8192"
 # the sources that decide the forward GEMM kernels and their launch (the
 # backward helpers live in a file of their own)
 GEMM_SOURCES = ("sk_api.cpp", "sk_common.h", "sk_kernel.h", "sk_kernels.hip", "sk_kernels_mx.hip",
-                "sk_tuning_table.inc")
+                "sk_kernels_ksplit.hip", "sk_tuning_table.inc")
 
 
 def source_hash() -> str:

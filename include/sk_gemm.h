@@ -269,7 +269,8 @@ typedef struct sk_gemm_args {
   uint32_t delay_seed;      /* with SK_DEBUG_DELAY */
   int32_t drop_signal_wg;   /* with SK_DEBUG_DROP_SIGNAL */
   int32_t variant;          /* 0: automatic; k > 0: compiled kernel k-1 (see sk_variant_info), which must
-                               match dtype (SK_ERR_UNSUPPORTED otherwise); overrides tile_m, tile_n */
+                               match dtype and, for a direct-only kernel, the call (sk_variant_k_split);
+                               SK_ERR_UNSUPPORTED otherwise; overrides tile_m, tile_n */
   uint64_t spin_limit_ticks;/* owner wait limit in ticks of the 100 MHz device clock; 0 = 2e8 (2 s) */
   uint64_t* trace;          /* NULL, or a device buffer of 32 uint64 per workgroup of the launch (sk_plan's
                                grid): a phase trace.  Wave 0 of workgroup w writes 100 MHz timestamps
@@ -389,6 +390,17 @@ sk_status sk_stream_cu_count(void* stream, int32_t* count);
 int32_t sk_num_variants(void);
 sk_status sk_variant_info(int32_t index, int32_t* dtype, int32_t* tile_m, int32_t* tile_n, int32_t* tile_k,
                           int32_t* threads, int32_t* lds_bytes);
+/* How kernel `index` covers K (host-only; either pointer may be NULL).  *k_slices
+ * > 1: each MAC iteration of tile_k elements is split into that many k-slices,
+ * each multiplied by its own group of waves into accumulators of their own,
+ * which are added once per tile (skinny problems: a 16 x 32 tile still keeps
+ * four waves' loads in flight).  *direct_only = 1: the kernel reads MX scales
+ * only straight from the caller's arrays, so it runs only where K is a
+ * multiple of tile_k, both scale arrays are 4-byte aligned and
+ * SK_DEBUG_RELAYOUT is not set; elsewhere the automatic choice passes it
+ * over, and choosing it by index (sk_gemm_args.variant) gives
+ * SK_ERR_UNSUPPORTED.  SK_ERR_ARG for an index out of range. */
+sk_status sk_variant_k_split(int32_t index, int32_t* k_slices, int32_t* direct_only);
 
 const char* sk_status_string(sk_status s);
 

@@ -149,6 +149,7 @@ def load():
     lib.sk_debug_poison_workspace.argtypes = [vp, i64]
     lib.sk_num_variants.argtypes = []
     lib.sk_variant_info.argtypes = [ctypes.c_int32] + [ctypes.POINTER(ctypes.c_int32)] * 6
+    lib.sk_variant_k_split.argtypes = [ctypes.c_int32] + [ctypes.POINTER(ctypes.c_int32)] * 2
     lib.sk_stream_create_cu_masked.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
                                                ctypes.POINTER(ctypes.c_void_p)]
     lib.sk_stream_destroy.argtypes = [vp]
@@ -157,7 +158,7 @@ def load():
     lib.sk_status_string.restype = ctypes.c_char_p
     for name in ("sk_gemm_mxfp4", "sk_gemm_mxfp4_noalloc", "sk_gemm_mxfp8", "sk_gemm_bf16", "sk_gemm_bf16_backward", "sk_gemm_mx", "sk_gemm_fp8", "sk_addmm", "sk_gemm_ex", "sk_plan",
                  "sk_plan_wg_range", "sk_plan_wg_work", "sk_check", "sk_debug_poison_workspace", "sk_variant_info",
-                 "sk_stream_create_cu_masked", "sk_stream_destroy", "sk_stream_cu_count"):
+                 "sk_variant_k_split", "sk_stream_create_cu_masked", "sk_stream_destroy", "sk_stream_cu_count"):
         getattr(lib, name).restype = ctypes.c_int
     lib.sk_num_variants.restype = ctypes.c_int32
     _LIB = lib
@@ -511,13 +512,16 @@ def poison_workspace(scratch_bytes: int, stream=None):
 
 
 def variants():
-    """Compiled kernel shapes: list of dicts (dtype, tile_m, tile_n, tile_k, threads, lds_bytes)."""
+    """Compiled kernel shapes: list of dicts (dtype, tile_m, tile_n, tile_k, threads,
+    lds_bytes, k_slices, direct_only)."""
     lib = load()
     out = []
     for i in range(lib.sk_num_variants()):
-        v = [ctypes.c_int32() for _ in range(6)]
-        _ok(lib.sk_variant_info(i, *[ctypes.byref(x) for x in v]), "sk_variant_info")
-        out.append(dict(zip(("dtype", "tile_m", "tile_n", "tile_k", "threads", "lds_bytes"), [x.value for x in v])))
+        v = [ctypes.c_int32() for _ in range(8)]
+        _ok(lib.sk_variant_info(i, *[ctypes.byref(x) for x in v[:6]]), "sk_variant_info")
+        _ok(lib.sk_variant_k_split(i, *[ctypes.byref(x) for x in v[6:]]), "sk_variant_k_split")
+        out.append(dict(zip(("dtype", "tile_m", "tile_n", "tile_k", "threads", "lds_bytes", "k_slices", "direct_only"),
+                            [x.value for x in v])))
     return out
 
 

@@ -14,7 +14,7 @@ PROBE_LIB = os.path.join(HERE, "libskprobe.so")
 PROBE_SOURCES = ["sk_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sk_kernels.hip", "sk_kernels_mx.hip", "sk_backward.hip", "sk_api.cpp"]
+SOURCES = ["sk_kernels.hip", "sk_kernels_mx.hip", "sk_kernels_ksplit.hip", "sk_backward.hip", "sk_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # keep hipcc from emitting packed-fp32 arithmetic on its own

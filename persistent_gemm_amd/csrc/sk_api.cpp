@@ -208,10 +208,11 @@ int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n, int fo
     const Variant* v = sk::variant(forced - 1);
     return (v && v->dtype == dtype) ? forced - 1 : -1;
   }
+  // (kernels that read only the caller's scales are taken from the tuned table, or by index)
   auto find = [&](int bm, int bn) {
     for (int i = 0; i < nv; ++i) {
       const Variant* v = sk::variant(i);
-      if (v->dtype == dtype && v->bm == bm && v->bn == bn) return i;
+      if (v->dtype == dtype && v->bm == bm && v->bn == bn && v->launch) return i;
     }
     return -1;
   };
@@ -231,22 +232,41 @@ int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n, int fo
   return find(256, 256);
 }
 
+// Whether a call can read the MX scales straight from the caller's arrays
+// with variant v: K a whole number of the kernel's k-steps (no k-step reads
+// past a row's last scale byte); `aligned`: the scale arrays are 4-byte
+// aligned (dword loads) and the caller did not ask for the re-laid copy.
+bool direct_fits(const Variant* v, int64_t K, bool aligned) {
+  if (!v->launch_direct || !aligned) return false;
+  const int64_t spr = v->dtype == SK_MXFP4 ? v->kb / 16 : v->kb / 32;   // scale bytes per row per k-step
+  return (K / 32) % spr == 0;
+}
+
+// `direct_ok`: direct_fits' `aligned` for the call (a plan query assumes it).
+// A kernel that reads only the caller's scales (no re-layout launcher) is
+// used only where direct_fits; the tuned table's choice is then skipped, and
+// an explicitly chosen kernel is SK_ERR_UNSUPPORTED.
 sk_status make_plan(int dtype, int policy, int64_t M, int64_t N, int64_t K, int grid_cap, int tile_m, int tile_n,
-                    int forced, int num_cus, sk_plan_info* p) {
+                    int forced, int num_cus, sk_plan_info* p, bool direct_ok = true) {
   if (!dtype_ok(dtype)) return SK_ERR_ARG;
   if (policy < SK_POLICY_HYBRID || policy > SK_POLICY_AUTO) return SK_ERR_ARG;
   if (M < 1 || N < 1 || K < 1 || M >= kMaxM || N > kMaxN || K > kMaxK) return SK_ERR_ARG;
   if (num_cus < 1) return SK_ERR_ARG;
   if (forced < 0) return SK_ERR_ARG;
+  auto usable = [&](const Variant* v) { return v->launch || direct_fits(v, K, direct_ok); };
   if (policy == SK_POLICY_AUTO) {
     // measured (kernel, policy) unless the caller fixed the kernel; else HYBRID
     int tv = -1, tp = SK_POLICY_HYBRID;
-    if (forced == 0 && tile_m <= 0 && tile_n <= 0 && tuned_choice(dtype, M, N, K, &tv, &tp)) forced = tv + 1;
+    if (forced == 0 && tile_m <= 0 && tile_n <= 0 && tuned_choice(dtype, M, N, K, &tv, &tp)) {
+      if (usable(sk::variant(tv))) forced = tv + 1;
+      else tp = SK_POLICY_HYBRID;
+    }
     policy = tp;
   }
   const int vi = pick_variant(dtype, M, N, tile_m, tile_n, forced);
   if (vi < 0) return SK_ERR_UNSUPPORTED;
   const Variant* v = sk::variant(vi);
+  if (!usable(v)) return SK_ERR_UNSUPPORTED;
   std::memset(p, 0, sizeof(*p));
   p->tile_m = v->bm;
   p->tile_n = v->bn;
@@ -470,12 +490,13 @@ sk_status run(const sk_gemm_args& g, bool fixed = false) {
   // The grid is sized to the compute units the stream may use, so on a
   // CU-masked stream the cap is a partition of the device, not a count.
   const int cus = stream_cus(dev, (hipStream_t)g.stream, info.cus);
-  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, cus, &p);
+  const bool direct_ok = !(g.debug_flags & SK_DEBUG_RELAYOUT) && !(((uintptr_t)g.A_scale | (uintptr_t)g.B_scale) & 3);
+  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, cus, &p, direct_ok);
   if (st != SK_OK) return st;
   if (fixed && (uint64_t)p.scratch_bytes > kStaticDataBytes) {
     // The same kernel over whole tiles needs no partial tiles.  Only MXFP4 takes
     // this path, whose fp32 sums are exact in any order: the bits are the same.
-    st = make_plan(g.dtype, SK_POLICY_PURE_DP, g.M, g.N, g.K, g.grid_cap, 0, 0, p.variant + 1, cus, &p);
+    st = make_plan(g.dtype, SK_POLICY_PURE_DP, g.M, g.N, g.K, g.grid_cap, 0, 0, p.variant + 1, cus, &p, direct_ok);
     if (st != SK_OK) return st;
   }
   hipStream_t stream = (hipStream_t)g.stream;
@@ -493,8 +514,8 @@ sk_status run(const sk_gemm_args& g, bool fixed = false) {
   // arrays, saving the re-layout launch: when K is whole k-steps (so no
   // k-step reads past a row's last scale byte) and the scale arrays are
   // 4-byte aligned (dword loads).
-  const bool direct = is_mx(g.dtype) && v->launch_direct != nullptr && !(g.debug_flags & SK_DEBUG_RELAYOUT) &&
-                      (g.K / 32) % spr == 0 && !(((uintptr_t)g.A_scale | (uintptr_t)g.B_scale) & 3);
+  const bool direct = is_mx(g.dtype) && direct_fits(v, g.K, direct_ok);
+  if (!direct && !v->launch) return SK_ERR_UNSUPPORTED;   // (make_plan has ruled this out)
   int64_t sa_bytes = 0, sb_bytes = 0, rows_a = 0, rows_b = 0;
   if (is_mx(g.dtype) && !direct) {
     rows_a = cdiv(g.M, v->bm) * v->bm;
@@ -839,6 +860,14 @@ sk_status sk_variant_info(int32_t index, int32_t* dtype, int32_t* tile_m, int32_
   if (tile_k) *tile_k = v->bk;
   if (threads) *threads = v->threads;
   if (lds_bytes) *lds_bytes = v->lds;
+  return SK_OK;
+}
+
+sk_status sk_variant_k_split(int32_t index, int32_t* k_slices, int32_t* direct_only) {
+  const Variant* v = sk::variant(index);
+  if (!v) return SK_ERR_ARG;
+  if (k_slices) *k_slices = v->wk;
+  if (direct_only) *direct_only = v->launch == nullptr;
   return SK_OK;
 }
 

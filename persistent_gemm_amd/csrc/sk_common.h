@@ -165,13 +165,16 @@ struct WorkIter {
 struct Variant {
   int dtype;
   int bm, bn;       // output tile
-  int kb;           // bytes of each operand row per MAC iteration
+  int kb;           // LDS bytes of each operand row per MAC iteration (k-step)
   int bk;           // K elements per MAC iteration
   int mfma;         // 32 (32x32 MFMA) or 16 (16x16 MFMA)
   int threads;
   int lds;
   int wm, wn;       // waves along M and N
-  int ng, nu;       // MFMA lane groups, MFMAs per block per k-step
+  int ng, nu;       // MFMA lane groups, MFMAs per block per k-slice
+  int wk;           // k-slices per k-step, each multiplied by its own group of waves
+  // The kernel reading MX scales from the re-laid copy (and the non-MX
+  // kernels), or nullptr for a kernel that only reads the caller's scales.
   hipError_t (*launch)(int grid, const KArgs& a, hipStream_t s);
   // The same kernel reading MX scales straight from the caller's row-major
   // [rows][K/32] arrays (no re-layout pass), or nullptr where not compiled.

@@ -136,11 +136,20 @@ constexpr int fmt_of_b(int dt) {
 }
 constexpr int fmt_bits(int f) { return f == FMT_E4M3 ? 8 : f == FMT_E2M1 ? 4 : f == FMT_BF16 ? 16 : 6; }
 
-template <int DT_, int BM_, int BN_, int KB_, int MF_, int WM_, int WN_, int STAGES_>
+// WK > 1 splits each k-step among WK groups of waves: a k-step then covers WK
+// consecutive k-slices of KB bytes per row, slice s held in sub-stage s of the
+// stage (each laid out as a whole stage of a WK = 1 kernel), and the waves of
+// group s multiply slice s into accumulators of their own.  Their sums are
+// added once per tile.  A tile too small to give every wave its own output
+// block (16 x 32) still gets several waves' loads in flight, and each k-step
+// reads WK * KB contiguous bytes of every row.
+template <int DT_, int BM_, int BN_, int KB_, int MF_, int WM_, int WN_, int STAGES_, int WK_ = 1>
 struct Cfg {
   static constexpr int DT = DT_, BM = BM_, BN = BN_, KB = KB_, MF = MF_, WM = WM_, WN = WN_;
   static constexpr int STAGES = STAGES_;
-  static constexpr int NW = WM * WN;
+  static constexpr int WK = WK_;
+  static constexpr int OW = WM * WN;                   // waves over the output tile (group 0: waves 0 .. OW-1)
+  static constexpr int NW = OW * WK;
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // per-wave tile
   static constexpr int FM = WTM / MF, FN = WTN / MF;   // MFMA blocks per wave
@@ -157,11 +166,13 @@ struct Cfg {
   static constexpr int U = WIDE ? 32 : 16;             // LDS bytes per lane per MFMA
   static constexpr int NU = LB / U;                    // MFMAs per block per k-step
   static constexpr int NCH = U / 16;                   // 16-byte chunks per lane per MFMA
-  static constexpr int SPR = DT == DT_MXFP4 ? KB / 16 : (MX ? KB / 32 : 0);  // scale bytes per row per k-step
-  static constexpr int BK = DT == DT_MXFP4 ? 2 * KB : (DT == DT_BF16 ? KB / 2 : KB);
-  // bytes of one row's k-step in memory (the LDS image of a WIDE block may be padded)
-  static constexpr int KBG_A = WIDE ? BK * fmt_bits(FA) / 8 : KB;
-  static constexpr int KBG_B = WIDE ? BK * fmt_bits(FB) / 8 : KB;
+  static constexpr int SPR = DT == DT_MXFP4 ? KB / 16 : (MX ? KB / 32 : 0);  // scale bytes per row per k-slice
+  static constexpr int BKS = DT == DT_MXFP4 ? 2 * KB : (DT == DT_BF16 ? KB / 2 : KB);   // K per k-slice
+  static constexpr int BK = WK * BKS;                  // K per k-step
+  // bytes of one row's k-slice in memory (the LDS image of a WIDE block may be padded)
+  static constexpr int KBG_A = WIDE ? BKS * fmt_bits(FA) / 8 : KB;
+  static constexpr int KBG_B = WIDE ? BKS * fmt_bits(FB) / 8 : KB;
+  static constexpr int KSA = WK * KBG_A, KSB = WK * KBG_B;   // ... and of its k-step
   static constexpr int ACC = MF == 32 ? 16 : 4;        // fp32 accumulators per block per lane
   // MX scale bytes a lane reads per k-step: its lane group's NU bytes of each
   // of its FM (FN) blocks, stored contiguously by the scale pre-pass
@@ -176,16 +187,20 @@ struct Cfg {
   // same chunk of 16 consecutive rows hit 16 different 16-byte bank groups.
   static constexpr int RG = 1024 / KB;
   static constexpr int CPR = KB / 16;                  // chunks per row
-  static constexpr int A_GROUPS = BM / RG, B_GROUPS = BN / RG;
-  // Scale bytes of a k-step, [row][SPR], filled by dword loads of 64 lanes
+  static constexpr int A_GRP = BM / RG, B_GRP = BN / RG;             // row groups per sub-stage
+  static constexpr int A_GROUPS = WK * A_GRP, B_GROUPS = WK * B_GRP;  // ... per stage
+  // Scale bytes of a k-slice, [row][SPR], filled by dword loads of 64 lanes
   // (256 bytes per instruction), so each area is a whole number of 256 B.
-  static constexpr int SA_INST = MX ? cdiv(BM * SPR, 256) : 0;
-  static constexpr int SB_INST = MX ? cdiv(BN * SPR, 256) : 0;
+  static constexpr int SA_I = MX ? cdiv(BM * SPR, 256) : 0;
+  static constexpr int SB_I = MX ? cdiv(BN * SPR, 256) : 0;
+  static constexpr int SA_INST = WK * SA_I, SB_INST = WK * SB_I;
+  // a sub-stage: A rows, B rows, A's scales, B's scales
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * KB;
   static constexpr int SA_OFF = (BM + BN) * KB;
-  static constexpr int SB_OFF = SA_OFF + SA_INST * 256;
-  static constexpr int STAGE = SB_OFF + SB_INST * 256;
+  static constexpr int SB_OFF = SA_OFF + SA_I * 256;
+  static constexpr int SUB = SB_OFF + SB_I * 256;
+  static constexpr int STAGE = WK * SUB;
   static constexpr int LDS = STAGES * STAGE;
   // Direct loads per wave per k-step; a wave with nothing left repeats a
   // group (same bytes to the same place), so every wave issues the same count.
@@ -202,10 +217,16 @@ struct Cfg {
   static constexpr int NQ = ACC / 4;                    // 4-column runs per block per lane
   // Output staging (epilogue): per wave, MF rows x SC columns of bf16 in the
   // stage freed by a tile's last k-step, read back as 16-byte row chunks.
+  // (wave tiles narrower than 32 columns are stored from registers instead)
+  static constexpr bool STAGED = WTN % 32 == 0;
   static constexpr int SC = WTN % 64 == 0 ? 64 : 32;
   static constexpr int SCH = SC / 8;                    // 16-byte chunks per staged row
   static constexpr int SRP = 64 / SCH;                  // staged rows per wave store
   static constexpr int STG_WAVE = MF * SC * 2;
+  // WK > 1: the accumulators of waves OW .. NW-1, [wave - OW][P_WAVE floats],
+  // passed to group 0 in the same freed stage, after the output staging
+  static constexpr int RED_OFF = OW * STG_WAVE;
+  static constexpr int RED_BYTES = (WK - 1) * OW * P_WAVE * 4;
   static constexpr int BIAS_OFF = STAGES * STAGE;       // bf16 bias of the current tile
   static constexpr int LDS_TOTAL = BIAS_OFF + BN * 2;
 
@@ -221,8 +242,9 @@ struct Cfg {
   static_assert((STAGES - 2) * LOADS_PER_STAGE_S <= 63, "vmcnt range");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS");
   static_assert(BN <= NT, "one bias element per thread");
-  static_assert(NW * STG_WAVE <= STAGE, "output staging fits in one stage");
-  static_assert(WTN % SC == 0 && SC % MF == 0 && MF % SRP == 0, "output staging windows");
+  static_assert(RED_OFF + RED_BYTES <= STAGE, "output staging and the k-split sums fit in one stage");
+  static_assert(WK == 1 || WK == 2 || WK == 4, "k-split");
+  static_assert(!STAGED || (WTN % SC == 0 && SC % MF == 0 && MF % SRP == 0), "output staging windows");
 };
 
 template <class C>
@@ -385,21 +407,24 @@ template <class C, bool DIRECT = false>
 struct Kernel {
   static constexpr int NT = C::NT;
   static_assert(!DIRECT || (C::MX && C::SPR >= 4), "direct scale reads need MX scales, at least 4 bytes per row");
+  static_assert(C::WK == 1 || DIRECT, "k-split kernels read the caller's scales (the re-laid copy has one k-slice per k-step)");
 
   struct TileCtx {
     v4u ra, rb, rsa, rsb;   // A, B and (MXFP4) their scales, from the tile's first row
   };
 
   // Per-lane 32-bit buffer offsets of this wave's direct-to-LDS loads, fixed
-  // for a launch.  Lane j of a data load fills slot j % CPR of row
-  // (group*RG + j / CPR), so it fetches that row's chunk (j % CPR) ^ swz(row);
-  // lane j of a scale load takes bytes [inst*256 + 4j, +4) of the k-step's
-  // scale block ([row][SPR]).  Rows past M or N lie outside the tile's buffer
-  // resource and read as zero.
+  // for a launch.  Row group g of a stage is group g % A_GRP of sub-stage
+  // g / A_GRP (B likewise), which holds k-slice g / A_GRP of the k-step.  Lane
+  // j of a data load fills slot j % CPR of row (group*RG + j / CPR), so it
+  // fetches that row's chunk (j % CPR) ^ swz(row) of the k-slice; lane j of a
+  // scale load takes bytes [inst*256 + 4j, +4) of the k-slice's scale block
+  // ([row][SPR]).  Rows past M or N lie outside the tile's buffer resource and
+  // read as zero.
   struct LoadOffs {
     uint32_t a[C::A_PT];     // lane's row offset plus chunk offset, per load
     uint32_t b[C::B_PT];
-    uint32_t ca[C::A_PT];    // lane's chunk byte offset inside the k-step, per load
+    uint32_t ca[C::A_PT];    // lane's chunk byte offset inside the k-step (kNone: padding), per load
     uint32_t cb[C::B_PT];
     uint32_t sa[C::SA_PT > 0 ? C::SA_PT : 1];
     uint32_t sb[C::SB_PT > 0 ? C::SB_PT : 1];
@@ -472,31 +497,40 @@ struct Kernel {
     LoadOffs o;
 #pragma unroll
     for (int i = 0; i < C::A_PT; ++i) {
-      const int row = ((wave + i * C::NW) % C::A_GROUPS) * C::RG + rr;
-      o.ca[i] = gchunk<C::FA>(p ^ swz(row));
-      o.a[i] = o.ca[i] == kNone ? kOob : (uint32_t)row * (uint32_t)a.row_bytes + o.ca[i];
+      const int grp = (wave + i * C::NW) % C::A_GROUPS;
+      const int row = (grp % C::A_GRP) * C::RG + rr;
+      const uint32_t c = gchunk<C::FA>(p ^ swz(row));
+      o.ca[i] = c == kNone ? kNone : (uint32_t)(grp / C::A_GRP) * C::KBG_A + c;
+      o.a[i] = c == kNone ? kOob : (uint32_t)row * (uint32_t)a.row_bytes + o.ca[i];
     }
 #pragma unroll
     for (int i = 0; i < C::B_PT; ++i) {
-      const int row = ((wave + i * C::NW) % C::B_GROUPS) * C::RG + rr;
-      o.cb[i] = gchunk<C::FB>(p ^ swz(row));
-      o.b[i] = o.cb[i] == kNone ? kOob : (uint32_t)row * (uint32_t)a.row_bytes_b + o.cb[i];
+      const int grp = (wave + i * C::NW) % C::B_GROUPS;
+      const int row = (grp % C::B_GRP) * C::RG + rr;
+      const uint32_t c = gchunk<C::FB>(p ^ swz(row));
+      o.cb[i] = c == kNone ? kNone : (uint32_t)(grp / C::B_GRP) * C::KBG_B + c;
+      o.b[i] = c == kNone ? kOob : (uint32_t)row * (uint32_t)a.row_bytes_b + o.cb[i];
     }
     if constexpr (C::MX) {
-      // the k-step's scale bytes of the tile's rows are contiguous ([row][SPR])
-      // (DIRECT: byte `byte` of the [row][SPR] block is byte byte % SPR of
-      // the k-step's scales in row byte / SPR of the caller's array)
+      // the k-slice's scale bytes of the tile's rows are contiguous ([row][SPR])
+      // (DIRECT: byte `byte` of the [row][SPR] block of k-slice s is byte
+      // s * SPR + byte % SPR of the k-step's scales in row byte / SPR of the
+      // caller's array)
 #pragma unroll
       for (int i = 0; i < C::SA_PT; ++i) {
-        const int byte = ((wave + i * C::NW) % C::SA_INST) * 256 + lane * 4;
-        const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch + (uint32_t)(byte % C::SPR)
+        const int ins = (wave + i * C::NW) % C::SA_INST;
+        const int byte = (ins % C::SA_I) * 256 + lane * 4;
+        const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch +
+                                          (uint32_t)((ins / C::SA_I) * C::SPR + byte % C::SPR)
                                     : (uint32_t)byte;
         o.sa[i] = byte < C::BM * C::SPR ? src : kOob;
       }
 #pragma unroll
       for (int i = 0; i < C::SB_PT; ++i) {
-        const int byte = ((wave + i * C::NW) % C::SB_INST) * 256 + lane * 4;
-        const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch + (uint32_t)(byte % C::SPR)
+        const int ins = (wave + i * C::NW) % C::SB_INST;
+        const int byte = (ins % C::SB_I) * 256 + lane * 4;
+        const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch +
+                                          (uint32_t)((ins / C::SB_I) * C::SPR + byte % C::SPR)
                                     : (uint32_t)byte;
         o.sb[i] = byte < C::BN * C::SPR ? src : kOob;
       }
@@ -513,7 +547,8 @@ struct Kernel {
 
   static __device__ __forceinline__ LdsPtrs lds_ptrs(const lds_u8* smem) {
     const int lane = threadIdx.x & 63, wave = wave_id();
-    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int ow = wave % C::OW, wk = wave / C::OW;   // output wave, k-slice
+    const int wm = ow / C::WN, wn = ow % C::WN;
     const int lr = lane % C::MF, g = lane / C::MF;
     LdsPtrs p;
     // Block rows start at multiples of 16, so the lane's permutation is swz(lr).
@@ -539,12 +574,13 @@ struct Kernel {
         p.slot_a[u * C::NCH + h] = (chunk(C::FA, u, h) ^ x) * 16;
         p.slot_b[u * C::NCH + h] = (chunk(C::FB, u, h) ^ x) * 16;
       }
-    p.a = smem + C::A_OFF + (wm * C::WTM + lr) * C::KB;
-    p.b = smem + C::B_OFF + (wn * C::WTN + lr) * C::KB;
+    // the wave's k-slice is sub-stage wk of every stage
+    p.a = smem + wk * C::SUB + C::A_OFF + (wm * C::WTM + lr) * C::KB;
+    p.b = smem + wk * C::SUB + C::B_OFF + (wn * C::WTN + lr) * C::KB;
     if constexpr (DIRECT) {
       // [row][SPR]: the lane's row in block 0, its lane group's NU bytes
-      p.sa = C::SA_OFF + (wm * C::WTM + lr) * C::SPR + g * C::NU;
-      p.sb = C::SB_OFF + (wn * C::WTN + lr) * C::SPR + g * C::NU;
+      p.sa = wk * C::SUB + C::SA_OFF + (wm * C::WTM + lr) * C::SPR + g * C::NU;
+      p.sb = wk * C::SUB + C::SB_OFF + (wn * C::WTN + lr) * C::SPR + g * C::NU;
     } else {
       // packed order of a tile's k-step scales: [wave row][lane row][lane group][block][sub-step]
       p.sa = C::SA_OFF + ((wm * C::MF + lr) * C::NG + g) * C::NSA;
@@ -779,7 +815,8 @@ struct Kernel {
   }
 
   // One direct-to-LDS load of a k-step, by its index P among the k-step's
-  // LOADS_PER_STAGE_S loads (A row groups, then B, then the two scale areas).
+  // LOADS_PER_STAGE_S loads (A row groups, then B, then the two scale areas;
+  // each into the sub-stage of its k-slice).
   // d.valid false issues the same load with every lane out of range: it
   // writes zeros into a stage nobody reads, so that every k-step issues the
   // same number of loads.
@@ -798,20 +835,20 @@ struct Kernel {
       constexpr int i = P;
       const int grp = (wave + i * C::NW) % C::A_GROUPS;
       const bool kin = d.valid && (!d.ragged_a || d.kbyte_a + o.ca[i] < (uint32_t)row_bytes_a);
-      dma_load16(d.t.ra, kin ? o.a[i] : kOob, d.kbyte_a, d.lds + C::A_OFF + grp * 1024);
+      dma_load16(d.t.ra, kin ? o.a[i] : kOob, d.kbyte_a, d.lds + (grp / C::A_GRP) * C::SUB + C::A_OFF + (grp % C::A_GRP) * 1024);
     } else if constexpr (P < C::A_PT + C::B_PT) {
       constexpr int i = P - C::A_PT;
       const int grp = (wave + i * C::NW) % C::B_GROUPS;
       const bool kin = d.valid && (!d.ragged_b || d.kbyte_b + o.cb[i] < (uint32_t)row_bytes_b);
-      dma_load16(d.t.rb, kin ? o.b[i] : kOob, d.kbyte_b, d.lds + C::B_OFF + grp * 1024);
+      dma_load16(d.t.rb, kin ? o.b[i] : kOob, d.kbyte_b, d.lds + (grp / C::B_GRP) * C::SUB + C::B_OFF + (grp % C::B_GRP) * 1024);
     } else if constexpr (P < C::A_PT + C::B_PT + C::SA_PT) {
       constexpr int i = P - C::A_PT - C::B_PT;
       const int ins = (wave + i * C::NW) % C::SA_INST;
-      dma_load4(d.rsa, d.valid ? o.sa[i] : kOob, 0u, d.lds + C::SA_OFF + ins * 256);
+      dma_load4(d.rsa, d.valid ? o.sa[i] : kOob, 0u, d.lds + (ins / C::SA_I) * C::SUB + C::SA_OFF + (ins % C::SA_I) * 256);
     } else {
       constexpr int i = P - C::A_PT - C::B_PT - C::SA_PT;
       const int ins = (wave + i * C::NW) % C::SB_INST;
-      dma_load4(d.rsb, d.valid ? o.sb[i] : kOob, 0u, d.lds + C::SB_OFF + ins * 256);
+      dma_load4(d.rsb, d.valid ? o.sb[i] : kOob, 0u, d.lds + (ins / C::SB_I) * C::SUB + C::SB_OFF + (ins % C::SB_I) * 256);
     }
   }
 
@@ -893,7 +930,7 @@ struct Kernel {
   // [wave][block][accumulator quad][lane][4 floats].
   static __device__ __forceinline__ uint32_t slot_off(int w) {
     return (uint32_t)w * (uint32_t)(C::P_SLOT * 4) +
-           (uint32_t)(wave_id() * C::P_WAVE + (threadIdx.x & 63) * 4) * 4u;
+           (uint32_t)((wave_id() % C::OW) * C::P_WAVE + (threadIdx.x & 63) * 4) * 4u;
   }
 
   // Four accumulators (one run of four output columns) copied out of AGPRs.
@@ -940,18 +977,55 @@ struct Kernel {
         }
   }
 
+  // WK > 1: the waves of k-slices 1 .. WK-1 hand their accumulators to the
+  // wave of slice 0 with the same output block (through `red`, a free stage),
+  // which adds them to its own in slice order; only slice 0's waves then hold
+  // the item's sums.  Every wave takes part (one barrier).
+  static __device__ __forceinline__ void reduce_k(Acc<C>& acc, lds_u8* red) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int ow = wave % C::OW, wk = wave / C::OW;
+    typedef __attribute__((address_space(3))) v4f* PV;
+    mfma_read_hazard();
+    if (wk > 0) {
+      lds_u8* const mine = red + ((wk - 1) * C::OW + ow) * (C::P_WAVE * 4) + lane * 16;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < C::NQ; ++q) *(PV)(mine + run_off(i, j, q)) = read_run(acc.v[i][j], q);
+    }
+    lds_barrier();
+    if (wk == 0) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < C::NQ; ++q) {
+            v4f x = read_run(acc.v[i][j], q);
+#pragma unroll
+            for (int s = 1; s < C::WK; ++s)
+              x += *(const PV)(red + ((s - 1) * C::OW + ow) * (C::P_WAVE * 4) + lane * 16 + run_off(i, j, q));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc.v[i][j][4 * q + k] = x[k];
+          }
+    }
+  }
+
   // Finishes one tile: C = round(sigma * (acc + P[w-1] + ... + P[first]) + bias),
   // the partials of the lower workgroups added in descending order (none when
   // first >= w).  Each lane holds, per block and run, four consecutive
   // columns of one row.  When N % 8 == 0 the wave rounds MF rows x SC columns
   // at a time into its part of the LDS stage `stg` (free while a tile is
   // finished) and writes them back as 16-byte pieces of whole rows, so each
-  // store instruction fills entire 128-byte lines; otherwise elements are
-  // stored one by one.  The tile's bias was staged in LDS (as -0 when there
-  // is none).
+  // store instruction fills entire 128-byte lines; otherwise (and for wave
+  // tiles narrower than 32 columns) each lane stores its runs of four
+  // columns, as one 8-byte piece when N % 4 == 0, else element by element.
+  // The tile's bias was staged in LDS (as -0 when there is none).
   static __device__ __forceinline__ void epilogue(const KArgs& a, int tile, const Acc<C>& acc, const lds_u8* smem,
                                                   lds_u8* stg, int w, int first) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int lane = threadIdx.x & 63, wave = wave_id() % C::OW;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int lr = lane % C::MF, g = lane / C::MF;
     const int tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
@@ -966,7 +1040,7 @@ struct Kernel {
       sigma = x * y;
     }
     const int N = a.N;
-    const bool staged = (N & 7) == 0;
+    const bool staged = C::STAGED && (N & 7) == 0;
     lds_u8* sw = stg + wave * C::STG_WAVE;
     // The bias of every column this lane touches (the same for all block
     // rows), read from LDS once: FN blocks x NQ runs of four bf16.
@@ -1061,7 +1135,7 @@ struct Kernel {
       constexpr int i = decltype(ic_)::value;
       const uint32_t row0 = (uint32_t)(wm * C::WTM + i * C::MF);     // first row of the block row, in the tile
       if (staged) {
-        static_for<C::WTN / C::SC>([&](auto cwc) {
+        if constexpr (C::STAGED) static_for<C::WTN / C::SC>([&](auto cwc) {
           constexpr int cw = decltype(cwc)::value;
           static_for<C::SC / C::MF>([&](auto jjc) {
             constexpr int jj = decltype(jjc)::value;
@@ -1106,10 +1180,15 @@ struct Kernel {
             const v2u h = run_bits(j, q, x[q]);
             const int col = n0 + wn * C::WTN + j * C::MF + (C::MF == 32 ? 8 * q + 4 * g : 4 * g);
             const uint32_t coff = ((row0 + lr) * (uint32_t)N + (uint32_t)col) * 2u;
-            const uint32_t hv[4] = {h[0] & 0xffffu, h[0] >> 16, h[1] & 0xffffu, h[1] >> 16};
+            if ((N & 3) == 0) {
+              // the run's four columns are all inside N or all past it
+              __builtin_amdgcn_raw_buffer_store_b64(h, rc, col < N ? coff : kOob, 0, 0);
+            } else {
+              const uint32_t hv[4] = {h[0] & 0xffffu, h[0] >> 16, h[1] & 0xffffu, h[1] >> 16};
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv[k], rc, col + k < N ? coff + 2u * k : kOob, 0, 0);
+              for (int k = 0; k < 4; ++k)
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv[k], rc, col + k < N ? coff + 2u * k : kOob, 0, 0);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -1217,14 +1296,14 @@ struct Kernel {
       DmaCtx d;
       d.t = ti;
       d.valid = have_i;
-      d.kbyte_a = have_i ? (uint32_t)ki * C::KBG_A : 0u;
-      d.kbyte_b = have_i ? (uint32_t)ki * C::KBG_B : 0u;
+      d.kbyte_a = have_i ? (uint32_t)ki * C::KSA : 0u;
+      d.kbyte_b = have_i ? (uint32_t)ki * C::KSB : 0u;
       if constexpr (C::MX) {
         d.rsa = rsrc_plus(ti.rsa, have_i ? (uint32_t)ki * sa_kstride : 0u);
         d.rsb = rsrc_plus(ti.rsb, have_i ? (uint32_t)ki * sb_kstride : 0u);
       }
-      d.ragged_a = d.kbyte_a + C::KBG_A > (uint32_t)row_bytes;
-      d.ragged_b = d.kbyte_b + C::KBG_B > (uint32_t)row_bytes_b;
+      d.ragged_a = d.kbyte_a + C::KSA > (uint32_t)row_bytes;
+      d.ragged_b = d.kbyte_b + C::KSB > (uint32_t)row_bytes_b;
       d.lds = (uint32_t)(uintptr_t)stage_ptr(smem, issued % S);
       return d;
     };
@@ -1399,8 +1478,12 @@ struct Kernel {
 
       // ---- the item is complete
       stamp(1);
+      // the stage of the item's last k-step is free until the next k-step issues into it
+      lds_u8* const freed = stage_ptr(smem, (done + S - 1) % S);
+      if constexpr (C::WK > 1) reduce_k(acc, freed + C::RED_OFF);
+      const bool holds = C::WK == 1 || wave_id() < C::OW;   // a wave with the item's sums
       if (ic.mode == WORK_CONTRIB) {
-        store_partial(kargs(), w, acc);
+        if (holds) store_partial(kargs(), w, acc);
         publish(kargs(), w);
         stamp(2);
       } else {
@@ -1416,9 +1499,8 @@ struct Kernel {
           lds_barrier();   // every wave is done with the previous tile's bias
           if (tid < C::BN) *(__attribute__((address_space(3))) uint16_t*)(smem + C::BIAS_OFF + tid * 2) = (uint16_t)bias_h;
           lds_barrier();
-          // the stage of the item's last k-step is free until the next k-step issues into it
-          epilogue(kargs(), ic.tile, acc, smem, stage_ptr(smem, (done + S - 1) % S), w, first);
-          lds_barrier();   // ... which must wait until every wave is done staging output there
+          if (holds) epilogue(kargs(), ic.tile, acc, smem, freed, w, first);
+          lds_barrier();   // the next k-step's loads into `freed` wait until every wave is done with it
         }
       }
       stamp(3);
@@ -1473,9 +1555,20 @@ constexpr Launcher direct_launcher() {
   Variant {                                                                                              \
     DT, BM, BN, KB, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::BK, MF, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NT, \
         SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::LDS_TOTAL, WM, WN,                                       \
-        SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NG, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NU,          \
+        SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NG, SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST)::NU, 1,       \
         &launch_variant<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC, false>,                             \
         direct_launcher<SK_CFG(DT, BM, BN, KB, MF, WM, WN, ST), OCC>()                                   \
+  }
+
+// A k-split kernel (WK groups of waves): direct scale reads only, so no
+// re-layout launcher.  Its k-step is WK k-slices of KB bytes per row.
+#define SK_CFG_WK(DT, BM, BN, KB, MF, WM, WN, ST, WK) Cfg<DT, BM, BN, KB, MF, WM, WN, ST, WK>
+#define SK_VARIANT_WK(DT, BM, BN, KB, MF, WM, WN, ST, WK, OCC)                                               \
+  Variant {                                                                                                  \
+    DT, BM, BN, (WK) * (KB), SK_CFG_WK(DT, BM, BN, KB, MF, WM, WN, ST, WK)::BK, MF,                           \
+        SK_CFG_WK(DT, BM, BN, KB, MF, WM, WN, ST, WK)::NT, SK_CFG_WK(DT, BM, BN, KB, MF, WM, WN, ST, WK)::LDS_TOTAL, \
+        WM, WN, SK_CFG_WK(DT, BM, BN, KB, MF, WM, WN, ST, WK)::NG, SK_CFG_WK(DT, BM, BN, KB, MF, WM, WN, ST, WK)::NU, \
+        WK, nullptr, &launch_variant<SK_CFG_WK(DT, BM, BN, KB, MF, WM, WN, ST, WK), OCC, true>                 \
   }
 
 }  // namespace sk

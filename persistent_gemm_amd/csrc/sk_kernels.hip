@@ -172,23 +172,28 @@ static const Variant kVariants[] = {
     SK_VARIANT(DT_MXFP4, 16, 32, 128, 16, 1, 1, 8, 1),
 };
 
-// sk_kernels_mx.hip: the MXFP6 and mixed-format kernels, numbered after these.
+// sk_kernels_mx.hip: the MXFP6 and mixed-format kernels, numbered after these;
+// sk_kernels_ksplit.hip: the k-split kernels, numbered after those.
 const Variant* wide_variants(int* count);
+const Variant* split_variants(int* count);
 
 namespace {
 constexpr int kBase = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 }
 
 int num_variants() {
-  int n = 0;
-  wide_variants(&n);
-  return kBase + n;
+  int nw = 0, ns = 0;
+  wide_variants(&nw);
+  split_variants(&ns);
+  return kBase + nw + ns;
 }
 const Variant* variant(int index) {
   if (index >= 0 && index < kBase) return &kVariants[index];
-  int n = 0;
-  const Variant* w = wide_variants(&n);
-  return (index >= kBase && index < kBase + n) ? &w[index - kBase] : nullptr;
+  int nw = 0, ns = 0;
+  const Variant* w = wide_variants(&nw);
+  if (index >= kBase && index < kBase + nw) return &w[index - kBase];
+  const Variant* x = split_variants(&ns);
+  return (index >= kBase + nw && index < kBase + nw + ns) ? &x[index - kBase - nw] : nullptr;
 }
 
 }  // namespace sk

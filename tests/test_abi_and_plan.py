@@ -255,11 +255,41 @@ def test_auto_policy_takes_the_measured_choice():
         assert (v["dtype"], v["tile_m"], v["tile_n"], v["threads"]) == (dtype, bm, bn, threads)
         p = pg.plan(dtype, M, N, K, policy=pg.AUTO, num_cus=256)
         assert (p.variant, p.policy) == (vi, pol), (dtype, M, N, K)
-        # a shape a little off the grid takes the same entry
-        q = pg.plan(dtype, M + 8, N - 8, K + 32, policy=pg.AUTO, num_cus=256)
+        # a shape a little off the grid takes the same entry (for a direct-only
+        # kernel, K whole k-steps; one that is not falls back to the choice by shape)
+        dk = v["tile_k"] if v["direct_only"] else 32
+        q = pg.plan(dtype, M + 8, N - 8, K + dk, policy=pg.AUTO, num_cus=256)
         assert (q.variant, q.policy) == (vi, pol), (dtype, M, N, K)
+        if v["direct_only"]:
+            q = pg.plan(dtype, M, N, K + 32, policy=pg.AUTO, num_cus=256)
+            assert not vs[q.variant]["direct_only"] and q.policy == pg.HYBRID, (dtype, M, N, K)
     p = pg.plan(pg.MXFP4, 8192, 8192, 8192, policy=pg.AUTO, tile=(128, 128), num_cus=256)
     assert (p.tile_m, p.tile_n, p.policy) == (128, 128, pg.HYBRID)
+
+
+def test_direct_only_kernels_need_whole_k_steps():
+    """A k-split kernel reads only the caller's scales: it plans where K is a
+    whole number of its k-steps and is refused elsewhere; a choice by tile
+    shape never lands on it."""
+    vs = pg.variants()
+    split = [i for i, v in enumerate(vs) if v["direct_only"]]
+    assert split, "k-split kernels are compiled"
+    for i in split:
+        v = vs[i]
+        assert v["k_slices"] > 1 and v["dtype"] == pg.MXFP4
+        p = pg.plan(pg.MXFP4, 16, 8192, 4 * v["tile_k"], variant=i, num_cus=256)
+        assert (p.variant, p.tile_k, p.iters_per_tile) == (i, v["tile_k"], 4)
+        for K in (4 * v["tile_k"] + 32, v["tile_k"] // 2):
+            with pytest.raises(pg.SkError) as e:
+                pg.plan(pg.MXFP4, 16, 8192, K, variant=i, num_cus=256)
+            assert e.value.name == "SK_ERR_UNSUPPORTED"
+        tile = (v["tile_m"], v["tile_n"])
+        if any((x["dtype"], x["tile_m"], x["tile_n"]) == (pg.MXFP4, *tile) and not x["direct_only"] for x in vs):
+            p = pg.plan(pg.MXFP4, 16, 8192, 8192, tile=tile, num_cus=256)
+            assert not vs[p.variant]["direct_only"]
+        else:
+            with pytest.raises(pg.SkError):
+                pg.plan(pg.MXFP4, 16, 8192, 8192, tile=tile, num_cus=256)
 
 
 def test_auto_choice_cache_keeps_answers_apart():

@@ -148,13 +148,19 @@ def test_every_variant_exact(index):
     """Each compiled kernel, chosen by index, on exact inputs spanning several
     tiles with ragged M, N and K tails, under all three policies.  N is once a
     multiple of 8 (whole 16-byte output pieces) and once not (element
-    stores); K is once whole k-steps and once a ragged last k-step (for the
-    MX types, one whose scale block is only partly inside K)."""
+    stores) and once a multiple of 4 but not of 8 (8-byte runs, or the staged
+    path's ragged last chunk); K is once whole k-steps and once a ragged last
+    k-step (for the MX types, one whose scale block is only partly inside K)."""
     v = pg.variants()[index]
     dtype, bm, bn = _DTYPES[v["dtype"]], v["tile_m"], v["tile_n"]
     M = 2 * bm + 7
     ragged_k = {"bf16": 200, "fp8": 208, "mxfp4": 448}.get(dtype, 224)   # the ABI needs K % 8, % 16, % 32
-    for N, K in [(2 * bn + 16, 512 if dtype == "mxfp4" else 256), (bn + 13, ragged_k)]:
+    whole_k = 512 if dtype == "mxfp4" else 256
+    shapes = [(2 * bn + 16, whole_k), (bn + 13, ragged_k), (bn + 12, whole_k)]
+    if v["direct_only"]:
+        # whole k-steps only (each of k_slices k-slices); K of one k-step and of three
+        shapes = [(2 * bn + 16, v["tile_k"]), (bn + 13, 3 * v["tile_k"]), (bn + 12, v["tile_k"])]
+    for N, K in shapes:
         x = exact_inputs(dtype, M, N, K, bias=True, seed=3000 + index)
         assert_exact_inputs(x)
         d = device_inputs(x)
@@ -181,8 +187,10 @@ def test_direct_scale_reads(dtype):
         assert_exact_inputs(x)
         d = device_inputs(x)
         C, _ = oracle_full(x)
+        # a direct-only kernel has no re-laid path: asked for one, it is refused
+        flag_set = (0,) if v["direct_only"] else (0, pg.DEBUG_RELAYOUT)
         for policy, g in [(pg.HYBRID, 0), (pg.PURE_SK, 7), (pg.PURE_DP, 3)]:
-            for flags in (0, pg.DEBUG_RELAYOUT):
+            for flags in flag_set:
                 say(f"variant {index} ({dtype} {v['tile_m']}x{v['tile_n']}) {M}x{N}x{K} policy {policy} flags {flags}")
                 got = run(d, grid_cap=g, policy=policy, variant=index, debug_flags=flags)
                 assert_bitexact(got, C, f"variant {index} policy {policy} flags {flags}")
@@ -194,8 +202,21 @@ def test_direct_scale_reads(dtype):
                 buf[shift:shift + t.numel()] = t.reshape(-1)
                 e[k] = buf[shift:shift + t.numel()].view(t.shape)
             say(f"variant {index} scale arrays at offset {shift}")
+            if v["direct_only"] and shift == 1:
+                continue
             got = run(e, grid_cap=0, policy=pg.HYBRID, variant=index)
             assert_bitexact(got, C, f"variant {index} scales at offset {shift}")
+        if v["direct_only"]:
+            for why, kw, e in [("relayout flag", {"debug_flags": pg.DEBUG_RELAYOUT}, d), ("unaligned scales", {}, None)]:
+                if e is None:
+                    e = dict(d)
+                    for k in ("SA", "SB"):
+                        buf = torch.zeros(d[k].numel() + 16, dtype=torch.uint8, device=d[k].device)
+                        e[k] = buf[1:1 + d[k].numel()].view(d[k].shape)
+                say(f"variant {index}: refused with {why}")
+                with pytest.raises(pg.SkError) as ei:
+                    run(e, grid_cap=0, policy=pg.HYBRID, variant=index, **kw)
+                assert ei.value.name == "SK_ERR_UNSUPPORTED"
 
 
 def _midpoint_inputs(M, N, K):
