@@ -870,6 +870,8 @@ struct Kernel {
   // partials are stored and loaded with the device-scope cache policy (sc1),
   // and the flags are device-scope atomics.
   static constexpr int kDeviceScope = 16;   // buffer cache policy: sc1
+  // s_waitcnt vmcnt(0) with the other counters left alone (expcnt 7, lgkmcnt 15)
+  static constexpr int kWaitVmcnt0 = 0x0F70;
 
   // Publish this workgroup's partial: every wave waits until its own
   // device-scope stores of the partial have completed, then the barrier, then
@@ -1023,6 +1025,11 @@ struct Kernel {
   // tiles narrower than 32 columns) each lane stores its runs of four
   // columns, as one 8-byte piece when N % 4 == 0, else element by element.
   // The tile's bias was staged in LDS (as -0 when there is none).
+  // PARTIALS: first < w (an owner with contributors).  The tiles a workgroup
+  // finishes alone take the copy without any partial-tile code: the compiler
+  // waits for every outstanding load before using a conditionally loaded
+  // partial, which would also wait for the next item's operand loads.
+  template <bool PARTIALS>
   static __device__ __forceinline__ void epilogue(const KArgs& a, int tile, const Acc<C>& acc, const lds_u8* smem,
                                                   lds_u8* stg, int w, int first) {
     const int lane = threadIdx.x & 63, wave = wave_id() % C::OW;
@@ -1084,7 +1091,7 @@ struct Kernel {
     constexpr int RUNS = C::FM * C::FN * C::NQ;
     constexpr int PRE = RUNS <= 4 ? 16 / RUNS : 0;
     v4u pre[PRE > 0 ? PRE : 1][PRE > 0 ? RUNS : 1];
-    if constexpr (PRE > 0) {
+    if constexpr (PARTIALS && PRE > 0) {
 #pragma unroll
       for (int c = 0; c < PRE; ++c)
         if (w - 1 - c >= first) {
@@ -1102,6 +1109,7 @@ struct Kernel {
     auto block_sums = [&](const typename Acc<C>::T& blk, int i, int j, v4f x[C::NQ]) {
 #pragma unroll
       for (int q = 0; q < C::NQ; ++q) x[q] = read_run(blk, q);
+      if constexpr (!PARTIALS) return;
       if constexpr (PRE > 0) {
 #pragma unroll
         for (int c = 0; c < PRE; ++c)
@@ -1194,6 +1202,15 @@ struct Kernel {
         });
       }
     });
+    if constexpr (PARTIALS) {
+      // The partials are loaded and added under the same conditions, which
+      // the compiler does not pair up: it takes a load that was issued and
+      // never used as possibly still in flight, and then waits for every
+      // outstanding load (the next item's operand stages included) before
+      // the first register write of each later k-step.  A wait it can see,
+      // once per owner tile, tells it they have all landed.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
   }
 
   // Position in a workgroup's work list: the WorkIter fields that change as
@@ -1499,7 +1516,10 @@ struct Kernel {
           lds_barrier();   // every wave is done with the previous tile's bias
           if (tid < C::BN) *(__attribute__((address_space(3))) uint16_t*)(smem + C::BIAS_OFF + tid * 2) = (uint16_t)bias_h;
           lds_barrier();
-          if (holds) epilogue(kargs(), ic.tile, acc, smem, freed, w, first);
+          if (holds) {
+            if (first < w) epilogue<true>(kargs(), ic.tile, acc, smem, freed, w, first);
+            else epilogue<false>(kargs(), ic.tile, acc, smem, freed, w, first);
+          }
           lds_barrier();   // the next k-step's loads into `freed` wait until every wave is done with it
         }
       }

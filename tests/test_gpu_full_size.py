@@ -29,7 +29,7 @@ def _wl(name):
 # The kernels the tuned table picks for the timed workloads (variant indices as in
 # sk_variant_info); the tests assert them so that a retuned table cannot leave
 # the timed kernel unchecked.
-BENCHED = {"mxfp4_addmm_8192": 23, "bf16_addmm_4096": 25, "mxfp4_gemm_16x8192x8192": 28}
+BENCHED = {"mxfp4_addmm_8192": 23, "bf16_addmm_4096": 25, "mxfp4_gemm_16x8192x8192": 53}
 
 
 def _auto_plan(w):
@@ -60,6 +60,12 @@ def test_skinny_mxfp4_16x8192x8192_bitexact():
                             ((16, 256), pg.PURE_DP, 0), ((64, 64), pg.HYBRID, 0)]:
         say(f"skinny 16x8192x8192 tile {tile} policy {policy} grid {g}")
         assert_bitexact(run(d, tile=tile, policy=policy, grid_cap=g), C, f"{tile} {policy} {g}")
+    # the 16 x 128 kernel with 128-byte k-steps, each tile split four ways (the
+    # Stream-K fixup at this shape), and the k-split kernel split by MAC
+    # iteration too (its waves' sums added before a partial tile is published)
+    for variant, policy, g in [(28, pg.HYBRID, 0), (p.variant, pg.PURE_SK, 100), (p.variant, pg.HYBRID, 200)]:
+        say(f"skinny 16x8192x8192 kernel {variant} policy {policy} grid {g}")
+        assert_bitexact(run(d, variant=variant, policy=policy, grid_cap=g), C, f"kernel {variant} {policy} {g}")
 
 
 def test_large_mxfp4_addmm_8192_bitexact():
