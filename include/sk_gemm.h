@@ -396,7 +396,7 @@ sk_status sk_variant_info(int32_t index, int32_t* dtype, int32_t* tile_m, int32_
  * which are added once per tile (skinny problems: a 16 x 32 tile still keeps
  * four waves' loads in flight).  *direct_only = 1: the kernel reads MX scales
  * only straight from the caller's arrays, so it runs only where K is a
- * multiple of tile_k, both scale arrays are 4-byte aligned and
+ * multiple of tile_k, both scale arrays are 16-byte aligned and
  * SK_DEBUG_RELAYOUT is not set; elsewhere the automatic choice passes it
  * over, and choosing it by index (sk_gemm_args.variant) gives
  * SK_ERR_UNSUPPORTED.  SK_ERR_ARG for an index out of range. */

@@ -234,26 +234,36 @@ int pick_variant(int dtype, int64_t M, int64_t N, int tile_m, int tile_n, int fo
 
 // Whether a call can read the MX scales straight from the caller's arrays
 // with variant v: K a whole number of the kernel's k-steps (no k-step reads
-// past a row's last scale byte); `aligned`: the scale arrays are 4-byte
-// aligned (dword loads) and the caller did not ask for the re-laid copy.
-bool direct_fits(const Variant* v, int64_t K, bool aligned) {
-  if (!v->launch_direct || !aligned) return false;
+// past a row's last scale byte), and the scale arrays aligned for the
+// kernel's loads (4 bytes; 16 for the k-split kernels, whose loads take 16
+// bytes of a row at a time).  `align`: the alignment both scale arrays share
+// (a power of two up to 16), 0 when the caller asked for the re-laid copy.
+bool direct_fits(const Variant* v, int64_t K, int align) {
+  if (!v->launch_direct || align < (v->wk > 1 ? 16 : 4)) return false;
   const int64_t spr = v->dtype == SK_MXFP4 ? v->kb / 16 : v->kb / 32;   // scale bytes per row per k-step
   return (K / 32) % spr == 0;
 }
 
-// `direct_ok`: direct_fits' `aligned` for the call (a plan query assumes it).
+int scale_alignment(const sk_gemm_args& g) {
+  if (g.debug_flags & SK_DEBUG_RELAYOUT) return 0;
+  const uintptr_t x = (uintptr_t)g.A_scale | (uintptr_t)g.B_scale;
+  int a = 1;
+  while (a < 16 && !(x & (uintptr_t)a)) a *= 2;
+  return a;
+}
+
+// `scale_align`: direct_fits' `align` for the call (a plan query assumes 16).
 // A kernel that reads only the caller's scales (no re-layout launcher) is
 // used only where direct_fits; the tuned table's choice is then skipped, and
 // an explicitly chosen kernel is SK_ERR_UNSUPPORTED.
 sk_status make_plan(int dtype, int policy, int64_t M, int64_t N, int64_t K, int grid_cap, int tile_m, int tile_n,
-                    int forced, int num_cus, sk_plan_info* p, bool direct_ok = true) {
+                    int forced, int num_cus, sk_plan_info* p, int scale_align = 16) {
   if (!dtype_ok(dtype)) return SK_ERR_ARG;
   if (policy < SK_POLICY_HYBRID || policy > SK_POLICY_AUTO) return SK_ERR_ARG;
   if (M < 1 || N < 1 || K < 1 || M >= kMaxM || N > kMaxN || K > kMaxK) return SK_ERR_ARG;
   if (num_cus < 1) return SK_ERR_ARG;
   if (forced < 0) return SK_ERR_ARG;
-  auto usable = [&](const Variant* v) { return v->launch || direct_fits(v, K, direct_ok); };
+  auto usable = [&](const Variant* v) { return v->launch || direct_fits(v, K, scale_align); };
   if (policy == SK_POLICY_AUTO) {
     // measured (kernel, policy) unless the caller fixed the kernel; else HYBRID
     int tv = -1, tp = SK_POLICY_HYBRID;
@@ -490,13 +500,13 @@ sk_status run(const sk_gemm_args& g, bool fixed = false) {
   // The grid is sized to the compute units the stream may use, so on a
   // CU-masked stream the cap is a partition of the device, not a count.
   const int cus = stream_cus(dev, (hipStream_t)g.stream, info.cus);
-  const bool direct_ok = !(g.debug_flags & SK_DEBUG_RELAYOUT) && !(((uintptr_t)g.A_scale | (uintptr_t)g.B_scale) & 3);
-  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, cus, &p, direct_ok);
+  const int scale_align = scale_alignment(g);
+  st = make_plan(g.dtype, g.policy, g.M, g.N, g.K, g.grid_cap, g.tile_m, g.tile_n, g.variant, cus, &p, scale_align);
   if (st != SK_OK) return st;
   if (fixed && (uint64_t)p.scratch_bytes > kStaticDataBytes) {
     // The same kernel over whole tiles needs no partial tiles.  Only MXFP4 takes
     // this path, whose fp32 sums are exact in any order: the bits are the same.
-    st = make_plan(g.dtype, SK_POLICY_PURE_DP, g.M, g.N, g.K, g.grid_cap, 0, 0, p.variant + 1, cus, &p, direct_ok);
+    st = make_plan(g.dtype, SK_POLICY_PURE_DP, g.M, g.N, g.K, g.grid_cap, 0, 0, p.variant + 1, cus, &p, scale_align);
     if (st != SK_OK) return st;
   }
   hipStream_t stream = (hipStream_t)g.stream;
@@ -511,10 +521,8 @@ sk_status run(const sk_gemm_args& g, bool fixed = false) {
   // scale bytes.
   const int64_t spr = g.dtype == SK_MXFP4 ? v->kb / 16 : v->kb / 32, ksteps = p.iters_per_tile;
   // Kernels of at most 128-row tiles instead gather the scales straight from the caller's
-  // arrays, saving the re-layout launch: when K is whole k-steps (so no
-  // k-step reads past a row's last scale byte) and the scale arrays are
-  // 4-byte aligned (dword loads).
-  const bool direct = is_mx(g.dtype) && direct_fits(v, g.K, direct_ok);
+  // arrays, saving the re-layout launch, where direct_fits.
+  const bool direct = is_mx(g.dtype) && direct_fits(v, g.K, scale_align);
   if (!direct && !v->launch) return SK_ERR_UNSUPPORTED;   // (make_plan has ruled this out)
   int64_t sa_bytes = 0, sb_bytes = 0, rows_a = 0, rows_b = 0;
   if (is_mx(g.dtype) && !direct) {

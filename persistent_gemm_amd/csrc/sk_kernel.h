@@ -190,22 +190,34 @@ struct Cfg {
   static constexpr int A_GRP = BM / RG, B_GRP = BN / RG;             // row groups per sub-stage
   static constexpr int A_GROUPS = WK * A_GRP, B_GROUPS = WK * B_GRP;  // ... per stage
   // Scale bytes of a k-slice, [row][SPR], filled by dword loads of 64 lanes
-  // (256 bytes per instruction), so each area is a whole number of 256 B.
-  static constexpr int SA_I = MX ? cdiv(BM * SPR, 256) : 0;
-  static constexpr int SB_I = MX ? cdiv(BN * SPR, 256) : 0;
-  static constexpr int SA_INST = WK * SA_I, SB_INST = WK * SB_I;
-  // a sub-stage: A rows, B rows, A's scales, B's scales
+  // (256 bytes per instruction), so each area is a whole number of 256 B; a
+  // sub-stage is then A rows, B rows, A's scales, B's scales.  SW (k-split
+  // kernels): the scale bytes of all WK k-slices of every row, [row][WK *
+  // SPR], once per stage after the sub-stages, filled by 16-byte loads (a
+  // whole number of 1 KiB per area): a quarter of the load requests, each
+  // row's bytes of a k-step being contiguous in the caller's array.
+  static constexpr bool SW = WK > 1;
+  static constexpr int SROW = SW ? WK * SPR : SPR;     // bytes per row of a scale area
+  static constexpr int SUNIT = SW ? 1024 : 256;        // bytes per scale load instruction
+  static constexpr int SA_I = MX ? cdiv(BM * SROW, SUNIT) : 0;
+  static constexpr int SB_I = MX ? cdiv(BN * SROW, SUNIT) : 0;
+  static constexpr int SA_INST = SW ? SA_I : WK * SA_I, SB_INST = SW ? SB_I : WK * SB_I;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = BM * KB;
-  static constexpr int SA_OFF = (BM + BN) * KB;
-  static constexpr int SB_OFF = SA_OFF + SA_I * 256;
-  static constexpr int SUB = SB_OFF + SB_I * 256;
-  static constexpr int STAGE = WK * SUB;
+  static constexpr int SUB = (BM + BN) * KB + (SW ? 0 : (SA_I + SB_I) * SUNIT);
+  static constexpr int SA_OFF = SW ? WK * SUB : (BM + BN) * KB;   // SW: in the stage; else in each sub-stage
+  static constexpr int SB_OFF = SA_OFF + SA_I * SUNIT;
+  // SW: A's and B's scale loads share one count per wave; a wave past the
+  // last of them issues one with every lane out of range (it writes zeros)
+  // into a spare kilobyte of the stage, so every wave issues the same count.
+  static constexpr int SPT = SW ? cdiv(SA_INST + SB_INST, NW) : 0;
+  static constexpr int JUNK_OFF = SB_OFF + SB_I * SUNIT;
+  static constexpr int STAGE = SW ? JUNK_OFF + (SPT * NW > SA_INST + SB_INST ? 1024 : 0) : WK * SUB;
   static constexpr int LDS = STAGES * STAGE;
   // Direct loads per wave per k-step; a wave with nothing left repeats a
   // group (same bytes to the same place), so every wave issues the same count.
   static constexpr int A_PT = cdiv(A_GROUPS, NW), B_PT = cdiv(B_GROUPS, NW);
-  static constexpr int SA_PT = cdiv(SA_INST, NW), SB_PT = cdiv(SB_INST, NW);
+  static constexpr int SA_PT = SW ? SPT : cdiv(SA_INST, NW), SB_PT = SW ? 0 : cdiv(SB_INST, NW);
   static constexpr int LOADS_PER_STAGE_S = A_PT + B_PT + SA_PT + SB_PT;
   // Eight-wave kernels whose operand fragments take 8 VGPRs (E4M3 and the
   // six-bit types, NCH == 2) refill A's fragments in place and double-buffer
@@ -244,6 +256,7 @@ struct Cfg {
   static_assert(BN <= NT, "one bias element per thread");
   static_assert(RED_OFF + RED_BYTES <= STAGE, "output staging and the k-split sums fit in one stage");
   static_assert(WK == 1 || WK == 2 || WK == 4, "k-split");
+  static_assert(!SW || !MX || SROW % 16 == 0, "16-byte scale loads cover whole row segments");
   static_assert(!STAGED || (WTN % SC == 0 && SC % MF == 0 && MF % SRP == 0), "output staging windows");
 };
 
@@ -516,23 +529,34 @@ struct Kernel {
       // (DIRECT: byte `byte` of the [row][SPR] block of k-slice s is byte
       // s * SPR + byte % SPR of the k-step's scales in row byte / SPR of the
       // caller's array)
+      // (SW: byte `byte` of the [row][SROW] area is byte byte % SROW of the
+      // k-step's scales in row byte / SROW, 16 bytes per lane)
+      auto scale_src = [&](int ins, int rows, int per) -> uint32_t {
+        if constexpr (C::SW) {
+          const int byte = ins * 1024 + lane * 16;
+          return byte < rows * C::SROW ? (uint32_t)(byte / C::SROW) * (uint32_t)a.s_pitch + (uint32_t)(byte % C::SROW)
+                                       : kOob;
+        } else {
+          const int byte = (ins % per) * 256 + lane * 4;
+          const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch +
+                                            (uint32_t)((ins / per) * C::SPR + byte % C::SPR)
+                                      : (uint32_t)byte;
+          return byte < rows * C::SPR ? src : kOob;
+        }
+      };
+      if constexpr (C::SW) {
+        // scale load i of this wave: A's instruction wave + i*NW, else B's, else none
 #pragma unroll
-      for (int i = 0; i < C::SA_PT; ++i) {
-        const int ins = (wave + i * C::NW) % C::SA_INST;
-        const int byte = (ins % C::SA_I) * 256 + lane * 4;
-        const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch +
-                                          (uint32_t)((ins / C::SA_I) * C::SPR + byte % C::SPR)
-                                    : (uint32_t)byte;
-        o.sa[i] = byte < C::BM * C::SPR ? src : kOob;
-      }
+        for (int i = 0; i < C::SA_PT; ++i) {
+          const int idx = wave + i * C::NW;
+          o.sa[i] = idx < C::SA_INST ? scale_src(idx, C::BM, 0)
+                  : idx < C::SA_INST + C::SB_INST ? scale_src(idx - C::SA_INST, C::BN, 0) : kOob;
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < C::SB_PT; ++i) {
-        const int ins = (wave + i * C::NW) % C::SB_INST;
-        const int byte = (ins % C::SB_I) * 256 + lane * 4;
-        const uint32_t src = DIRECT ? (uint32_t)(byte / C::SPR) * (uint32_t)a.s_pitch +
-                                          (uint32_t)((ins / C::SB_I) * C::SPR + byte % C::SPR)
-                                    : (uint32_t)byte;
-        o.sb[i] = byte < C::BN * C::SPR ? src : kOob;
+        for (int i = 0; i < C::SA_PT; ++i) o.sa[i] = scale_src((wave + i * C::NW) % C::SA_INST, C::BM, C::SA_I);
+#pragma unroll
+        for (int i = 0; i < C::SB_PT; ++i) o.sb[i] = scale_src((wave + i * C::NW) % C::SB_INST, C::BN, C::SB_I);
       }
     }
     return o;
@@ -579,8 +603,10 @@ struct Kernel {
     p.b = smem + wk * C::SUB + C::B_OFF + (wn * C::WTN + lr) * C::KB;
     if constexpr (DIRECT) {
       // [row][SPR]: the lane's row in block 0, its lane group's NU bytes
-      p.sa = wk * C::SUB + C::SA_OFF + (wm * C::WTM + lr) * C::SPR + g * C::NU;
-      p.sb = wk * C::SUB + C::SB_OFF + (wn * C::WTN + lr) * C::SPR + g * C::NU;
+      // [row][SROW]: the lane's row in block 0, its k-slice's bytes, its lane group's NU bytes
+      const int slice = C::SW ? wk * C::SPR : wk * C::SUB;
+      p.sa = slice + C::SA_OFF + (wm * C::WTM + lr) * C::SROW + g * C::NU;
+      p.sb = slice + C::SB_OFF + (wn * C::WTN + lr) * C::SROW + g * C::NU;
     } else {
       // packed order of a tile's k-step scales: [wave row][lane row][lane group][block][sub-step]
       p.sa = C::SA_OFF + ((wm * C::MF + lr) * C::NG + g) * C::NSA;
@@ -616,7 +642,7 @@ struct Kernel {
     for (int k = 0; k < NW; ++k) w[k] = 0;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const lds_u8* q = p + i * C::MF * C::SPR;
+      const lds_u8* q = p + i * C::MF * C::SROW;
       uint32_t x;
       if constexpr (C::NU == 1) x = *q;
       else if constexpr (C::NU == 2) x = *(const __attribute__((address_space(3))) uint16_t*)q;
@@ -843,8 +869,16 @@ struct Kernel {
       dma_load16(d.t.rb, kin ? o.b[i] : kOob, d.kbyte_b, d.lds + (grp / C::B_GRP) * C::SUB + C::B_OFF + (grp % C::B_GRP) * 1024);
     } else if constexpr (P < C::A_PT + C::B_PT + C::SA_PT) {
       constexpr int i = P - C::A_PT - C::B_PT;
-      const int ins = (wave + i * C::NW) % C::SA_INST;
-      dma_load4(d.rsa, d.valid ? o.sa[i] : kOob, 0u, d.lds + (ins / C::SA_I) * C::SUB + C::SA_OFF + (ins % C::SA_I) * 256);
+      if constexpr (C::SW) {
+        const int idx = wave + i * C::NW;
+        if (idx < C::SA_INST) dma_load16(d.rsa, d.valid ? o.sa[i] : kOob, 0u, d.lds + C::SA_OFF + idx * 1024);
+        else if (idx < C::SA_INST + C::SB_INST)
+          dma_load16(d.rsb, d.valid ? o.sa[i] : kOob, 0u, d.lds + C::SB_OFF + (idx - C::SA_INST) * 1024);
+        else dma_load16(d.rsa, kOob, 0u, d.lds + C::JUNK_OFF);
+      } else {
+        const int ins = (wave + i * C::NW) % C::SA_INST;
+        dma_load4(d.rsa, d.valid ? o.sa[i] : kOob, 0u, d.lds + (ins / C::SA_I) * C::SUB + C::SA_OFF + (ins % C::SA_I) * 256);
+      }
     } else {
       constexpr int i = P - C::A_PT - C::B_PT - C::SA_PT;
       const int ins = (wave + i * C::NW) % C::SB_INST;

@@ -202,17 +202,19 @@ def test_direct_scale_reads(dtype):
                 buf[shift:shift + t.numel()] = t.reshape(-1)
                 e[k] = buf[shift:shift + t.numel()].view(t.shape)
             say(f"variant {index} scale arrays at offset {shift}")
-            if v["direct_only"] and shift == 1:
+            if v["direct_only"]:
+                # (16-byte scale loads: offsets 4 and 1 are refused, below)
                 continue
             got = run(e, grid_cap=0, policy=pg.HYBRID, variant=index)
             assert_bitexact(got, C, f"variant {index} scales at offset {shift}")
         if v["direct_only"]:
-            for why, kw, e in [("relayout flag", {"debug_flags": pg.DEBUG_RELAYOUT}, d), ("unaligned scales", {}, None)]:
-                if e is None:
-                    e = dict(d)
+            for why, kw, shift in [("relayout flag", {"debug_flags": pg.DEBUG_RELAYOUT}, 0),
+                                   ("scales 4 bytes off 16", {}, 4), ("scales 1 byte off", {}, 1)]:
+                e = dict(d)
+                if shift:
                     for k in ("SA", "SB"):
-                        buf = torch.zeros(d[k].numel() + 16, dtype=torch.uint8, device=d[k].device)
-                        e[k] = buf[1:1 + d[k].numel()].view(d[k].shape)
+                        buf = torch.zeros(d[k].numel() + 32, dtype=torch.uint8, device=d[k].device)
+                        e[k] = buf[shift:shift + d[k].numel()].view(d[k].shape)
                 say(f"variant {index}: refused with {why}")
                 with pytest.raises(pg.SkError) as ei:
                     run(e, grid_cap=0, policy=pg.HYBRID, variant=index, **kw)
