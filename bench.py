@@ -543,9 +543,10 @@ def other_configs(torch, pg, dev, steps: int, warmup: int, cpu: bool) -> list:
 
 def ceiling(args) -> int:
     """The device's own ceilings for the roofline, from libskprobe.so: MFMA-only rates on the
-    whole device with fixed, rotating random and zero operands (FP4, E4M3, bf16), and the
+    whole device with fixed, rotating random and zero operands (FP4, E4M3, bf16), the
     rotating-operand FP4 rate with direct-to-LDS loads of random bytes interleaved, from an
-    L2-sized and a memory-sized span per workgroup.  One JSON line."""
+    L2-sized and a memory-sized span per workgroup, and the cold read of 32 MiB by the
+    skinny call's row pattern and by plain loads.  One JSON line."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "persistent_gemm_amd", "libskprobe.so"))
@@ -579,6 +580,18 @@ def ceiling(args) -> int:
                          "ms": round(ms.value, 3), "tflops": round(flop.value / s / 1e12, 1),
                          "gbs_per_cu_into_lds": round(nbytes.value / s / 1e9 / 256, 1)})
             print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    # the cold read of the skinny call's 32 MiB of B: 15 launches, each on a region none before it read
+    lib.skp_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    times = (ctypes.c_float * 15)()
+    for pattern, what in ((0, "direct-to-LDS rows: 256 workgroups x 32 rows x 4 KiB, 128 B of each row per load"),
+                          (1, "plain 16-byte vector loads: 1024 workgroups, contiguous slices")):
+        if lib.skp_stream(pattern, src.data_ptr(), 15, times) != 0:
+            raise RuntimeError("skp_stream failed")
+        us = sorted(t * 1e3 for t in times)
+        rows.append({"probe": "cold read of 32 MiB", "pattern": what, "us_median": round(us[7], 2),
+                     "us_min": round(us[0], 2), "tbs_at_median": round((32 << 20) / (us[7] * 1e-6) / 1e12, 2),
+                     "how": "HIP events around each launch (its dispatch included)"})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
     print(json.dumps({"ceiling": rows, "how": "256 workgroups of 8 waves (2 per SIMD), back-to-back MFMAs into 8 "
                       "accumulators per wave; one timed launch after a shorter warm-up launch"}), flush=True)
     return 0

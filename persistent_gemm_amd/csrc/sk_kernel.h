@@ -1059,11 +1059,9 @@ struct Kernel {
   // tiles narrower than 32 columns) each lane stores its runs of four
   // columns, as one 8-byte piece when N % 4 == 0, else element by element.
   // The tile's bias was staged in LDS (as -0 when there is none).
-  // PARTIALS: first < w (an owner with contributors).  The tiles a workgroup
-  // finishes alone take the copy without any partial-tile code: the compiler
-  // waits for every outstanding load before using a conditionally loaded
-  // partial, which would also wait for the next item's operand loads.
-  template <bool PARTIALS>
+  // PARTIALS false: a copy without the partial-tile code, for tiles finished
+  // alone (first >= w), used by the k-split kernels (see the wait at the end).
+  template <bool PARTIALS = true>
   static __device__ __forceinline__ void epilogue(const KArgs& a, int tile, const Acc<C>& acc, const lds_u8* smem,
                                                   lds_u8* stg, int w, int first) {
     const int lane = threadIdx.x & 63, wave = wave_id() % C::OW;
@@ -1236,15 +1234,16 @@ struct Kernel {
         });
       }
     });
-    if constexpr (PARTIALS) {
-      // The partials are loaded and added under the same conditions, which
-      // the compiler does not pair up: it takes a load that was issued and
-      // never used as possibly still in flight, and then waits for every
-      // outstanding load (the next item's operand stages included) before
-      // the first register write of each later k-step.  A wait it can see,
-      // once per owner tile, tells it they have all landed.
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    }
+    // The partials are loaded and added under the same conditions, which the
+    // compiler does not pair up: it takes a load that was issued and never
+    // used as possibly still in flight, and then waits for every outstanding
+    // load (the next item's operand stages included) before the first
+    // register write of each later k-step.  A wait it can see, once per tile,
+    // tells it they have all landed.  The k-split kernels, whose registers
+    // are plentiful, also carry a copy without partials for the tiles they
+    // finish alone, which needs no such wait; in the 8-wave kernels the pair
+    // of copies raises the register pressure around them (more spills).
+    if constexpr (PARTIALS) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
   // Position in a workgroup's work list: the WorkIter fields that change as
@@ -1530,8 +1529,7 @@ struct Kernel {
       // ---- the item is complete
       stamp(1);
       // the stage of the item's last k-step is free until the next k-step issues into it
-      lds_u8* const freed = stage_ptr(smem, (done + S - 1) % S);
-      if constexpr (C::WK > 1) reduce_k(acc, freed + C::RED_OFF);
+      if constexpr (C::WK > 1) reduce_k(acc, stage_ptr(smem, (done + S - 1) % S) + C::RED_OFF);
       const bool holds = C::WK == 1 || wave_id() < C::OW;   // a wave with the item's sums
       if (ic.mode == WORK_CONTRIB) {
         if (holds) store_partial(kargs(), w, acc);
@@ -1551,8 +1549,9 @@ struct Kernel {
           if (tid < C::BN) *(__attribute__((address_space(3))) uint16_t*)(smem + C::BIAS_OFF + tid * 2) = (uint16_t)bias_h;
           lds_barrier();
           if (holds) {
-            if (first < w) epilogue<true>(kargs(), ic.tile, acc, smem, freed, w, first);
-            else epilogue<false>(kargs(), ic.tile, acc, smem, freed, w, first);
+            lds_u8* const stg = stage_ptr(smem, (done + S - 1) % S);
+            if (C::WK > 1 && first >= w) epilogue<false>(kargs(), ic.tile, acc, smem, stg, w, first);
+            else epilogue(kargs(), ic.tile, acc, smem, stg, w, first);
           }
           lds_barrier();   // the next k-step's loads into `freed` wait until every wave is done with it
         }

@@ -12,6 +12,11 @@
 //     random bytes interleaved (L loads of 1 KiB per wave per 8 MFMAs), from a
 //     span per workgroup small enough to stay in L2 or large enough to stream
 //     from memory.
+//   * The cold read of 32 MiB spread over the device, the skinny GEMM's B:
+//     direct-to-LDS loads of 32 rows x 4 KiB per workgroup, 128 bytes of each
+//     row per load as the GEMM's k-steps take them, or plain 16-byte vector
+//     loads of a contiguous slice per workgroup; each launch reads a region
+//     the launches before it did not touch, so none of it is in the MALL.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -163,6 +168,45 @@ __global__ __launch_bounds__(kThreads) void mfma_dma(const uint8_t* src, uint32_
   out[blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+// Direct-to-LDS row streaming: workgroup w reads rows [32 w, +32) of a
+// [8192][4096]-byte matrix, 128 bytes of every row per step (one load of 64
+// lanes x 16 bytes covers 8 rows), 12 loads in flight per wave; the bytes land
+// in a 64 KiB LDS ring and are not used.
+__global__ __launch_bounds__(256) void stream_rows(const uint8_t* src) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][16][1024];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint64_t tb = (uint64_t)(uintptr_t)(src + (uint64_t)blockIdx.x * 32 * 4096);
+  v4u rs = v4u{(uint32_t)tb, (uint32_t)(tb >> 32) & 0xffffu, 32u * 4096u, 0x00020000u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rs[i]);
+  int n = 0;
+  for (int k = 0; k < 4096 / 128; ++k) {
+    const int row = wave * 8 + lane / 8;   // 4 waves x 8 rows: the 32 rows
+    const uint32_t voff = (uint32_t)row * 4096u + (uint32_t)k * 128u + (uint32_t)(lane % 8) * 16u;
+    const uint32_t lds = (uint32_t)(uintptr_t)&ring[wave][n & 15][0];
+    ++n;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds\n\ts_waitcnt vmcnt(12)"
+                 :: "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(rs) : "memory", "m0");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Plain 16-byte vector loads: workgroup w reads the w-th of gridDim.x equal
+// contiguous slices of the n16 16-byte words, 8 loads in flight per thread.
+__global__ __launch_bounds__(256) void stream_plain(const v4u* src, uint64_t n16, uint32_t* out) {
+  const uint64_t per = n16 / gridDim.x;
+  const v4u* p = src + (uint64_t)blockIdx.x * per;
+  v4u acc = {0, 0, 0, 0};
+  for (uint64_t i = threadIdx.x; i < per; i += 256 * 8) {
+    v4u x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = i + u * 256 < per ? __builtin_nontemporal_load(p + i + u * 256) : v4u{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= x[u];
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x12345678u) out[threadIdx.x] = 1;   // keeps the loads
+}
+
 typedef void (*RateKernel)(int, float*);
 
 template <int KIND>
@@ -234,6 +278,35 @@ int skp_mfma_dma(int loads, const void* src, uint32_t span, int iters, float* ms
   (void)hipFree(out);
   *flop = 2.0 * 32 * 32 * 64 * 8.0 * iters * (kThreads / 64) * kGrid;
   *bytes = 1024.0 * loads * iters * (kThreads / 64) * kGrid;
+  return rc;
+}
+
+// The cold read of 32 MiB: pattern 0 direct-to-LDS rows (256 workgroups of
+// 4 waves), 1 plain vector loads (1024 workgroups of 4 waves).  src: device
+// memory of at least `regions` x 64 MiB; launch i reads the 32 MiB at i x
+// 64 MiB, so a region is read once.  Writes each launch's milliseconds (HIP
+// events around the launch, which include its dispatch) to ms[0 .. regions);
+// returns 0, or 1 on error.
+int skp_stream(int pattern, const void* src, int regions, float* ms) {
+  if ((pattern != 0 && pattern != 1) || !src || regions < 1 || regions > 64 || !ms) return 1;
+  uint32_t* out = nullptr;
+  if (hipMalloc(&out, 1024) != hipSuccess) return 1;
+  int rc = 0;
+  for (int r = 0; r < regions && !rc; ++r) {
+    const uint8_t* base = (const uint8_t*)src + (uint64_t)r * (64ull << 20);
+    rc = time_launch(
+        [&](bool warm) {
+          if (warm) {
+            hipLaunchKernelGGL(stream_plain, dim3(64), dim3(256), 0, 0, (const v4u*)out, (uint64_t)64, out);
+          } else if (pattern == 0) {
+            hipLaunchKernelGGL(stream_rows, dim3(256), dim3(256), 0, 0, base);
+          } else {
+            hipLaunchKernelGGL(stream_plain, dim3(1024), dim3(256), 0, 0, (const v4u*)base, (uint64_t)(32ull << 20) / 16, out);
+          }
+        },
+        &ms[r]);
+  }
+  (void)hipFree(out);
   return rc;
 }
 

@@ -315,8 +315,8 @@ def test_auto_choice_cache_keeps_answers_apart():
 
 
 def test_probe_library_exports_its_probes():
-    """libskprobe.so (bench.py --ceiling) is built beside the GEMM library and exports its two probes."""
+    """libskprobe.so (bench.py --ceiling) is built beside the GEMM library and exports its probes."""
     import os
     path = os.path.join(os.path.dirname(pg.library_path()), "libskprobe.so")
     lib = ctypes.CDLL(path)
-    assert hasattr(lib, "skp_mfma_rate") and hasattr(lib, "skp_mfma_dma")
+    assert hasattr(lib, "skp_mfma_rate") and hasattr(lib, "skp_mfma_dma") and hasattr(lib, "skp_stream")
