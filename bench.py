@@ -543,7 +543,7 @@ def other_configs(torch, pg, dev, steps: int, warmup: int, cpu: bool) -> list:
 
 def ceiling(args) -> int:
     """The device's own ceilings for the roofline, from libskprobe.so: MFMA-only rates on the
-    whole device with fixed, rotating random and zero operands (FP4, E4M3, bf16), the
+    whole device with fixed, rotating random and zero operands (FP4, FP6, E4M3, bf16), the
     rotating-operand FP4 rate with direct-to-LDS loads of random bytes interleaved, from an
     L2-sized and a memory-sized span per workgroup, and the cold read of 32 MiB by the
     skinny call's row pattern and by plain loads.  One JSON line."""
@@ -560,7 +560,8 @@ def ceiling(args) -> int:
     rows = []
     kinds = [("fp4 scaled 32x32x64", 0, PEAK_TFLOPS["mxfp4"], 80000), ("e4m3 scaled 32x32x64", 1, PEAK_TFLOPS["fp8"], 50000),
              ("bf16 32x32x16", 2, PEAK_TFLOPS["bf16"], 100000),
-             ("fp4 scaled 16x16x128", 3, PEAK_TFLOPS["mxfp4"], 160000), ("bf16 16x16x32", 4, PEAK_TFLOPS["bf16"], 200000)]
+             ("fp4 scaled 16x16x128", 3, PEAK_TFLOPS["mxfp4"], 160000), ("bf16 16x16x32", 4, PEAK_TFLOPS["bf16"], 200000),
+             ("fp6 e2m3 scaled 32x32x64", 5, PEAK_TFLOPS["mxfp6_e2m3"], 80000)]
     for name, kind, peak, iters in kinds:
         for mode, what in ((0, "fixed operands"), (1, "rotating random operands"), (2, "zero operands")):
             if lib.skp_mfma_rate(kind, mode, iters, ctypes.byref(ms), ctypes.byref(flop)) != 0:

@@ -65,7 +65,8 @@ __device__ __forceinline__ void operands(v8i (&a)[8], v8i (&b)[8]) {
 }
 
 // KIND 0: scaled FP4 (E2M1) 32x32x64; 1: scaled E4M3 32x32x64; 2: bf16 32x32x16;
-// 3: scaled FP4 16x16x128; 4: bf16 16x16x32 (the 16x16 forms accumulate into 4 floats).
+// 3: scaled FP4 16x16x128; 4: bf16 16x16x32 (the 16x16 forms accumulate into 4 floats);
+// 5: scaled FP6 (E2M3) 32x32x64 (every 6-bit code is a finite value).
 template <int KIND>
 __device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
   if constexpr (KIND == 3) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
@@ -80,6 +81,7 @@ template <int KIND>
 __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, v16f c, int sa, int sb) {
   if constexpr (KIND == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
   else if constexpr (KIND == 1) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  else if constexpr (KIND == 5) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, sa, 0, sb);
   else {
     const v8bf x = __builtin_bit_cast(v8bf, int4{a[0], a[1], a[2], a[3]});
     const v8bf y = __builtin_bit_cast(v8bf, int4{b[0], b[1], b[2], b[3]});
@@ -211,7 +213,7 @@ typedef void (*RateKernel)(int, float*);
 
 template <int KIND>
 RateKernel rate_kernel(int mode) {
-  if constexpr (KIND >= 3) return mode == 0 ? mfma_rate16<KIND, 0> : mode == 1 ? mfma_rate16<KIND, 1> : mfma_rate16<KIND, 2>;
+  if constexpr (KIND == 3 || KIND == 4) return mode == 0 ? mfma_rate16<KIND, 0> : mode == 1 ? mfma_rate16<KIND, 1> : mfma_rate16<KIND, 2>;
   else return mode == 0 ? mfma_rate<KIND, 0> : mode == 1 ? mfma_rate<KIND, 1> : mfma_rate<KIND, 2>;
 }
 
@@ -238,15 +240,16 @@ int time_launch(F&& launch, float* ms) {
 extern "C" {
 
 // Whole-device MFMA-only rate: kind 0 scaled FP4 32x32x64, 1 scaled E4M3
-// 32x32x64, 2 bf16 32x32x16, 3 scaled FP4 16x16x128, 4 bf16 16x16x32; mode 0
+// 32x32x64, 2 bf16 32x32x16, 3 scaled FP4 16x16x128, 4 bf16 16x16x32, 5 scaled
+// FP6 (E2M3) 32x32x64; mode 0
 // fixed operands, 1 rotating random operands, 2 zero operands.  256 workgroups of 8 waves, `iters` x 8 MFMAs per
 // wave.  Writes the launch's milliseconds and FLOP; returns 0, or 1 on error.
 int skp_mfma_rate(int kind, int mode, int iters, float* ms, double* flop) {
-  if (kind < 0 || kind > 4 || mode < 0 || mode > 2 || iters < 1 || !ms || !flop) return 1;
+  if (kind < 0 || kind > 5 || mode < 0 || mode > 2 || iters < 1 || !ms || !flop) return 1;
   float* out = nullptr;
   if (hipMalloc(&out, (size_t)kGrid * kThreads * sizeof(float)) != hipSuccess) return 1;
   RateKernel k = kind == 0 ? rate_kernel<0>(mode) : kind == 1 ? rate_kernel<1>(mode) : kind == 2 ? rate_kernel<2>(mode)
-               : kind == 3 ? rate_kernel<3>(mode) : rate_kernel<4>(mode);
+               : kind == 3 ? rate_kernel<3>(mode) : kind == 4 ? rate_kernel<4>(mode) : rate_kernel<5>(mode);
   const int rc = time_launch(
       [&](bool warm) { hipLaunchKernelGGL(k, dim3(kGrid), dim3(kThreads), 0, 0, warm ? iters / 4 + 1 : iters, out); },
       ms);
