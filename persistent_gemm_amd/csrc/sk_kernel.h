@@ -238,7 +238,7 @@ struct Cfg {
   // WK > 1: the accumulators of waves OW .. NW-1, [wave - OW][P_WAVE floats],
   // passed to group 0 in the same freed stage, after the output staging
   static constexpr int RED_OFF = OW * STG_WAVE;
-  static constexpr int RED_BYTES = (WK - 1) * OW * P_WAVE * 4;
+  static constexpr int RED_BYTES = WK > 1 ? WK * OW * P_WAVE * 4 : 0;   // (every wave's sums, for finish_split)
   static constexpr int BIAS_OFF = STAGES * STAGE;       // bf16 bias of the current tile
   static constexpr int LDS_TOTAL = BIAS_OFF + BN * 2;
 
@@ -1059,9 +1059,6 @@ struct Kernel {
   // tiles narrower than 32 columns) each lane stores its runs of four
   // columns, as one 8-byte piece when N % 4 == 0, else element by element.
   // The tile's bias was staged in LDS (as -0 when there is none).
-  // PARTIALS false: a copy without the partial-tile code, for tiles finished
-  // alone (first >= w), used by the k-split kernels (see the wait at the end).
-  template <bool PARTIALS = true>
   static __device__ __forceinline__ void epilogue(const KArgs& a, int tile, const Acc<C>& acc, const lds_u8* smem,
                                                   lds_u8* stg, int w, int first) {
     const int lane = threadIdx.x & 63, wave = wave_id() % C::OW;
@@ -1123,7 +1120,7 @@ struct Kernel {
     constexpr int RUNS = C::FM * C::FN * C::NQ;
     constexpr int PRE = RUNS <= 4 ? 16 / RUNS : 0;
     v4u pre[PRE > 0 ? PRE : 1][PRE > 0 ? RUNS : 1];
-    if constexpr (PARTIALS && PRE > 0) {
+    if constexpr (PRE > 0) {
 #pragma unroll
       for (int c = 0; c < PRE; ++c)
         if (w - 1 - c >= first) {
@@ -1141,7 +1138,6 @@ struct Kernel {
     auto block_sums = [&](const typename Acc<C>::T& blk, int i, int j, v4f x[C::NQ]) {
 #pragma unroll
       for (int q = 0; q < C::NQ; ++q) x[q] = read_run(blk, q);
-      if constexpr (!PARTIALS) return;
       if constexpr (PRE > 0) {
 #pragma unroll
         for (int c = 0; c < PRE; ++c)
@@ -1239,11 +1235,73 @@ struct Kernel {
     // used as possibly still in flight, and then waits for every outstanding
     // load (the next item's operand stages included) before the first
     // register write of each later k-step.  A wait it can see, once per tile,
-    // tells it they have all landed.  The k-split kernels, whose registers
-    // are plentiful, also carry a copy without partials for the tiles they
-    // finish alone, which needs no such wait; in the 8-wave kernels the pair
-    // of copies raises the register pressure around them (more spills).
-    if constexpr (PARTIALS) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // tells it they have all landed.  (A second copy of the epilogue without
+    // partials, for the tiles finished alone, would need no wait, but the
+    // pair raises the register pressure around it: more spills in the
+    // 8-wave kernels.  The k-split kernels finish such tiles in
+    // finish_split.)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+
+  // WK > 1, a tile the workgroup finishes alone (no partials): every wave
+  // writes its accumulators to `red` (a free stage), and after one barrier
+  // each wave takes an equal share of the tile's 4-column runs, adds the WK
+  // k-slices' sums of each in slice order (the order reduce_k uses), rounds
+  // them with the bias (staged in LDS before the barrier) and stores them:
+  // the work after the k-steps is spread over all the waves instead of
+  // waiting on slice 0's.  Each lane of a share stores its run as one
+  // 8-byte piece when N % 4 == 0, else element by element.
+  static __device__ __forceinline__ void finish_split(const KArgs& a, int tile, const Acc<C>& acc, lds_u8* red,
+                                                      const lds_u8* smem) {
+    typedef __attribute__((address_space(3))) v4f* PV;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    constexpr int RUNS = C::FM * C::FN * C::NQ;           // runs of one output wave, 64 lanes each
+    constexpr int TOTAL = C::OW * RUNS * 64;              // lane-runs of the tile
+    static_assert(TOTAL % C::NW == 0, "equal shares");
+    constexpr int SHARE = TOTAL / C::NW;
+    mfma_read_hazard();
+    lds_u8* const mine = red + wave * (C::P_WAVE * 4) + lane * 16;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < C::NQ; ++q) *(PV)(mine + run_off(i, j, q)) = read_run(acc.v[i][j], q);
+    lds_barrier();
+    const int tm = tile / a.tiles_n, tn = tile - tm * a.tiles_n;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int rows = min(C::BM, a.M - m0);
+    const int N = a.N;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C + (int64_t)m0 * N, (uint32_t)rows * (uint32_t)N * 2u);
+#pragma unroll
+    for (int x0 = 0; x0 < SHARE; x0 += 64) {
+      const int x = wave * SHARE + x0 + lane;              // lane-run of the tile
+      if (x0 + 64 > SHARE && x0 + lane >= SHARE) break;
+      const int ow = x / (RUNS * 64), run = (x / 64) % RUNS, l = x % 64;
+      v4f v = *(const PV)(red + ow * (C::P_WAVE * 4) + run * 1024 + l * 16);
+#pragma unroll
+      for (int k = 1; k < C::WK; ++k) v += *(const PV)(red + (k * C::OW + ow) * (C::P_WAVE * 4) + run * 1024 + l * 16);
+      // the run's place: block (i, j), accumulator quad q of output wave ow, lane l
+      const int q = run % C::NQ, ij = run / C::NQ, j = ij % C::FN, i = ij / C::FN;
+      const int wm = ow / C::WN, wn = ow % C::WN;
+      const int row = wm * C::WTM + i * C::MF + l % C::MF;
+      const int tcol = wn * C::WTN + j * C::MF + (C::MF == 32 ? 8 * q + 4 * (l / C::MF) : 4 * (l / C::MF));
+      const v2u bb = *(const __attribute__((address_space(3))) v2u*)(smem + C::BIAS_OFF + tcol * 2);
+      const float b4[4] = {__uint_as_float(bb[0] << 16), __uint_as_float(bb[0] & 0xffff0000u),
+                           __uint_as_float(bb[1] << 16), __uint_as_float(bb[1] & 0xffff0000u)};
+      const float t[4] = {v[0], v[1], v[2], v[3]};
+      const v2u h = round_run(t, b4);
+      const int col = n0 + tcol;
+      const uint32_t coff = ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u;
+      if ((N & 3) == 0) {
+        __builtin_amdgcn_raw_buffer_store_b64(h, rc, col < N ? coff : kOob, 0, 0);
+      } else {
+        const uint32_t hv[4] = {h[0] & 0xffffu, h[0] >> 16, h[1] & 0xffffu, h[1] >> 16};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv[k], rc, col + k < N ? coff + 2u * k : kOob, 0, 0);
+      }
+    }
   }
 
   // Position in a workgroup's work list: the WorkIter fields that change as
@@ -1529,7 +1587,10 @@ struct Kernel {
       // ---- the item is complete
       stamp(1);
       // the stage of the item's last k-step is free until the next k-step issues into it
-      if constexpr (C::WK > 1) reduce_k(acc, stage_ptr(smem, (done + S - 1) % S) + C::RED_OFF);
+      // (k-split kernels: a whole tile goes to finish_split, others add their slices here)
+      if constexpr (C::WK > 1) {
+        if (ic.mode != WORK_WHOLE) reduce_k(acc, stage_ptr(smem, (done + S - 1) % S) + C::RED_OFF);
+      }
       const bool holds = C::WK == 1 || wave_id() < C::OW;   // a wave with the item's sums
       if (ic.mode == WORK_CONTRIB) {
         if (holds) store_partial(kargs(), w, acc);
@@ -1547,13 +1608,14 @@ struct Kernel {
         if (ok) {
           lds_barrier();   // every wave is done with the previous tile's bias
           if (tid < C::BN) *(__attribute__((address_space(3))) uint16_t*)(smem + C::BIAS_OFF + tid * 2) = (uint16_t)bias_h;
-          lds_barrier();
-          if (holds) {
-            lds_u8* const stg = stage_ptr(smem, (done + S - 1) % S);
-            if (C::WK > 1 && first >= w) epilogue<false>(kargs(), ic.tile, acc, smem, stg, w, first);
-            else epilogue(kargs(), ic.tile, acc, smem, stg, w, first);
+          lds_u8* const stg = stage_ptr(smem, (done + S - 1) % S);
+          if (C::WK > 1 && ic.mode == WORK_WHOLE) {
+            finish_split(kargs(), ic.tile, acc, stg + C::RED_OFF, smem);   // (its barrier also publishes the bias)
+          } else {
+            lds_barrier();
+            if (holds) epilogue(kargs(), ic.tile, acc, smem, stg, w, first);
           }
-          lds_barrier();   // the next k-step's loads into `freed` wait until every wave is done with it
+          lds_barrier();   // the next k-step's loads into the freed stage wait until every wave is done with it
         }
       }
       stamp(3);
