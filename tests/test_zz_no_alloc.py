@@ -21,8 +21,11 @@ if torch.cuda.is_available():
 
 # largest first: 256x256 tiles whose tuned plan needs 64 MiB of partial tiles (so the
 # call runs data-parallel) with re-laid scales in the array; then 128x128 and 64x64
-# tiles with a Stream-K head, whose partial tiles (16 and 4 MiB) live in the array
-SHAPES = [(3072, 3072, 2048), (1024, 1024, 4096), (512, 512, 2048), (1024, 1024, 4096)]
+# tiles with a Stream-K head, whose partial tiles (16 and 4 MiB) live in the array;
+# then two skinny calls on the k-split kernel, data-parallel and with every tile
+# split four ways (its waves' sums added before a partial is published)
+SHAPES = [(3072, 3072, 2048), (1024, 1024, 4096), (512, 512, 2048), (1024, 1024, 4096), (16, 4096, 8192),
+          (16, 2048, 8192)]
 
 
 def _bits(t):
