@@ -235,10 +235,11 @@ struct Cfg {
   static constexpr int SCH = SC / 8;                    // 16-byte chunks per staged row
   static constexpr int SRP = 64 / SCH;                  // staged rows per wave store
   static constexpr int STG_WAVE = MF * SC * 2;
-  // WK > 1: the accumulators of waves OW .. NW-1, [wave - OW][P_WAVE floats],
-  // passed to group 0 in the same freed stage, after the output staging
+  // WK > 1: waves' accumulators passed between them in the same freed stage,
+  // after the output staging: [wave][P_WAVE floats] for finish_split (every
+  // wave), [wave - OW][P_WAVE floats] for reduce_k (waves OW .. NW-1)
   static constexpr int RED_OFF = OW * STG_WAVE;
-  static constexpr int RED_BYTES = WK > 1 ? WK * OW * P_WAVE * 4 : 0;   // (every wave's sums, for finish_split)
+  static constexpr int RED_BYTES = WK > 1 ? WK * OW * P_WAVE * 4 : 0;
   static constexpr int BIAS_OFF = STAGES * STAGE;       // bf16 bias of the current tile
   static constexpr int LDS_TOTAL = BIAS_OFF + BN * 2;
 
@@ -1013,10 +1014,11 @@ struct Kernel {
         }
   }
 
-  // WK > 1: the waves of k-slices 1 .. WK-1 hand their accumulators to the
-  // wave of slice 0 with the same output block (through `red`, a free stage),
-  // which adds them to its own in slice order; only slice 0's waves then hold
-  // the item's sums.  Every wave takes part (one barrier).
+  // WK > 1, an item of a split tile: the waves of k-slices 1 .. WK-1 hand their
+  // accumulators to the wave of slice 0 with the same output block (through
+  // `red`, a free stage), which adds them to its own in slice order; only slice
+  // 0's waves then hold the item's sums (to publish as a partial, or to finish
+  // with the other workgroups' partials).  Every wave takes part (one barrier).
   static __device__ __forceinline__ void reduce_k(Acc<C>& acc, lds_u8* red) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int ow = wave % C::OW, wk = wave / C::OW;
