@@ -85,13 +85,6 @@ __device__ __forceinline__ v4u rsrc_words(const void* base, uint32_t bytes) {
   return v4u{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
 }
 
-// The same resource with its base moved up by `off` bytes.  (The range check
-// covers the SGPR offset too, so offsets past the records cannot ride there.)
-__device__ __forceinline__ v4u rsrc_plus(const v4u& r, uint32_t off) {
-  const uint64_t b = (((uint64_t)(r[1] & 0xffffu) << 32) | r[0]) + off;
-  return v4u{(uint32_t)b, (r[1] & 0xffff0000u) | ((uint32_t)(b >> 32) & 0xffffu), r[2], r[3]};
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const v4u& r) {
   const uint64_t b = ((uint64_t)r[1] << 32) | r[0];
   return make_rsrc((const void*)(uintptr_t)b, r[2]);
@@ -438,8 +431,11 @@ struct Kernel {
   struct LoadOffs {
     uint32_t a[C::A_PT];     // lane's row offset plus chunk offset, per load
     uint32_t b[C::B_PT];
-    uint32_t ca[C::A_PT];    // lane's chunk byte offset inside the k-step (kNone: padding), per load
-    uint32_t cb[C::B_PT];
+    // per load: the k-step byte offsets k for which the lane's chunk lies
+    // inside the row, k < lim (a chunk at byte c of the k-step: lim = row bytes
+    // - c, or 0 for a padding chunk or one past the row at every k)
+    uint32_t lim_a[C::A_PT];
+    uint32_t lim_b[C::B_PT];
     uint32_t sa[C::SA_PT > 0 ? C::SA_PT : 1];
     uint32_t sb[C::SB_PT > 0 ? C::SB_PT : 1];
   };
@@ -472,18 +468,19 @@ struct Kernel {
     t.ra = rsrc_words(a.A + (int64_t)m0 * a.row_bytes, (uint32_t)(rows_a * a.row_bytes));
     t.rb = rsrc_words(a.B + (int64_t)n0 * a.row_bytes_b, (uint32_t)(rows_b * a.row_bytes_b));
     if constexpr (DIRECT) {
-      // the caller's scales: the tile's rows, [row][s_pitch]; a k-step moves
-      // the base by SPR bytes (see rsrc_plus), and since K is a whole number
-      // of k-steps every byte read lies inside the tile's rows
+      // the caller's scales: the tile's rows, [row][s_pitch]; k-step ks reads
+      // at scalar offset ks * sa_kstride (its first byte in a row), and since
+      // K is a whole number of k-steps every byte read lies inside the tile's rows
       t.rsa = rsrc_words(a.SA + (int64_t)m0 * a.s_pitch, (uint32_t)(rows_a * a.s_pitch));
       t.rsb = rsrc_words(a.SB + (int64_t)n0 * a.s_pitch, (uint32_t)(rows_b * a.s_pitch));
     } else if constexpr (C::MX) {
       // k-step-major scales, a tile's k-step block of BM * SPR bytes at
-      // SA + ks * sa_kstride + m0 * SPR in the packed lane order (the k-step's
-      // block is reached by moving the base, see rsrc_plus).  The scale copy
-      // holds whole tiles (rows past M carry 127), so the range is the block.
-      t.rsa = rsrc_words(a.SA + (int64_t)m0 * C::SPR, (uint32_t)(C::BM * C::SPR));
-      t.rsb = rsrc_words(a.SB + (int64_t)n0 * C::SPR, (uint32_t)(C::BN * C::SPR));
+      // SA + ks * sa_kstride + m0 * SPR in the packed lane order; k-step ks
+      // reads at scalar offset ks * sa_kstride.  The scale copy holds whole
+      // tiles (rows past M carry 127), so the range ends with the tile's block
+      // of the last k-step.
+      t.rsa = rsrc_words(a.SA + (int64_t)m0 * C::SPR, (uint32_t)(a.iters - 1) * a.sa_kstride + C::BM * C::SPR);
+      t.rsb = rsrc_words(a.SB + (int64_t)n0 * C::SPR, (uint32_t)(a.iters - 1) * a.sb_kstride + C::BN * C::SPR);
     } else {
       t.rsa = t.ra;
       t.rsb = t.rb;
@@ -514,16 +511,18 @@ struct Kernel {
       const int grp = (wave + i * C::NW) % C::A_GROUPS;
       const int row = (grp % C::A_GRP) * C::RG + rr;
       const uint32_t c = gchunk<C::FA>(p ^ swz(row));
-      o.ca[i] = c == kNone ? kNone : (uint32_t)(grp / C::A_GRP) * C::KBG_A + c;
-      o.a[i] = c == kNone ? kOob : (uint32_t)row * (uint32_t)a.row_bytes + o.ca[i];
+      const uint32_t ca = c == kNone ? kNone : (uint32_t)(grp / C::A_GRP) * C::KBG_A + c;
+      o.a[i] = c == kNone ? kOob : (uint32_t)row * (uint32_t)a.row_bytes + ca;
+      o.lim_a[i] = ca < (uint32_t)a.row_bytes ? (uint32_t)a.row_bytes - ca : 0u;
     }
 #pragma unroll
     for (int i = 0; i < C::B_PT; ++i) {
       const int grp = (wave + i * C::NW) % C::B_GROUPS;
       const int row = (grp % C::B_GRP) * C::RG + rr;
       const uint32_t c = gchunk<C::FB>(p ^ swz(row));
-      o.cb[i] = c == kNone ? kNone : (uint32_t)(grp / C::B_GRP) * C::KBG_B + c;
-      o.b[i] = c == kNone ? kOob : (uint32_t)row * (uint32_t)a.row_bytes_b + o.cb[i];
+      const uint32_t cb = c == kNone ? kNone : (uint32_t)(grp / C::B_GRP) * C::KBG_B + c;
+      o.b[i] = c == kNone ? kOob : (uint32_t)row * (uint32_t)a.row_bytes_b + cb;
+      o.lim_b[i] = cb < (uint32_t)a.row_bytes_b ? (uint32_t)a.row_bytes_b - cb : 0u;
     }
     if constexpr (C::MX) {
       // the k-slice's scale bytes of the tile's rows are contiguous ([row][SPR])
@@ -850,40 +849,41 @@ struct Kernel {
   struct DmaCtx {
     TileCtx t;
     uint32_t kbyte_a, kbyte_b;   // the k-step's byte offset in a row of A and of B
-    v4u rsa, rsb;                // the k-step's scale blocks
+    uint32_t kc_a, kc_b;         // ... compared with LoadOffs::lim (all ones when invalid: every lane out of range)
+    uint32_t ks_a, ks_b;         // scalar offsets of the k-step's scale bytes
     uint32_t lds;                // LDS address of the target stage
-    bool valid, ragged_a, ragged_b;
+    bool valid;
   };
   template <int P>
-  static __device__ __forceinline__ void dma_piece(const DmaCtx& d, const LoadOffs& o, int row_bytes_a,
-                                                   int row_bytes_b) {
-    const int wave = wave_id();
+  static __device__ __forceinline__ void dma_piece(const DmaCtx& d, const LoadOffs& o) {
+    const uint32_t wave = (uint32_t)wave_id();
+    __builtin_assume(wave < (uint32_t)C::NW);
     if constexpr (P < C::A_PT) {
       constexpr int i = P;
-      const int grp = (wave + i * C::NW) % C::A_GROUPS;
-      const bool kin = d.valid && (!d.ragged_a || d.kbyte_a + o.ca[i] < (uint32_t)row_bytes_a);
-      dma_load16(d.t.ra, kin ? o.a[i] : kOob, d.kbyte_a, d.lds + (grp / C::A_GRP) * C::SUB + C::A_OFF + (grp % C::A_GRP) * 1024);
+      const uint32_t grp = (wave + i * C::NW) % C::A_GROUPS;
+      dma_load16(d.t.ra, d.kc_a < o.lim_a[i] ? o.a[i] : kOob, d.kbyte_a,
+                 d.lds + (grp / C::A_GRP) * C::SUB + C::A_OFF + (grp % C::A_GRP) * 1024);
     } else if constexpr (P < C::A_PT + C::B_PT) {
       constexpr int i = P - C::A_PT;
-      const int grp = (wave + i * C::NW) % C::B_GROUPS;
-      const bool kin = d.valid && (!d.ragged_b || d.kbyte_b + o.cb[i] < (uint32_t)row_bytes_b);
-      dma_load16(d.t.rb, kin ? o.b[i] : kOob, d.kbyte_b, d.lds + (grp / C::B_GRP) * C::SUB + C::B_OFF + (grp % C::B_GRP) * 1024);
+      const uint32_t grp = (wave + i * C::NW) % C::B_GROUPS;
+      dma_load16(d.t.rb, d.kc_b < o.lim_b[i] ? o.b[i] : kOob, d.kbyte_b,
+                 d.lds + (grp / C::B_GRP) * C::SUB + C::B_OFF + (grp % C::B_GRP) * 1024);
     } else if constexpr (P < C::A_PT + C::B_PT + C::SA_PT) {
       constexpr int i = P - C::A_PT - C::B_PT;
       if constexpr (C::SW) {
-        const int idx = wave + i * C::NW;
-        if (idx < C::SA_INST) dma_load16(d.rsa, d.valid ? o.sa[i] : kOob, 0u, d.lds + C::SA_OFF + idx * 1024);
+        const uint32_t idx = wave + i * C::NW;
+        if (idx < C::SA_INST) dma_load16(d.t.rsa, d.valid ? o.sa[i] : kOob, d.ks_a, d.lds + C::SA_OFF + idx * 1024);
         else if (idx < C::SA_INST + C::SB_INST)
-          dma_load16(d.rsb, d.valid ? o.sa[i] : kOob, 0u, d.lds + C::SB_OFF + (idx - C::SA_INST) * 1024);
-        else dma_load16(d.rsa, kOob, 0u, d.lds + C::JUNK_OFF);
+          dma_load16(d.t.rsb, d.valid ? o.sa[i] : kOob, d.ks_b, d.lds + C::SB_OFF + (idx - C::SA_INST) * 1024);
+        else dma_load16(d.t.rsa, kOob, 0u, d.lds + C::JUNK_OFF);
       } else {
-        const int ins = (wave + i * C::NW) % C::SA_INST;
-        dma_load4(d.rsa, d.valid ? o.sa[i] : kOob, 0u, d.lds + (ins / C::SA_I) * C::SUB + C::SA_OFF + (ins % C::SA_I) * 256);
+        const uint32_t ins = (wave + i * C::NW) % C::SA_INST;
+        dma_load4(d.t.rsa, d.valid ? o.sa[i] : kOob, d.ks_a, d.lds + (ins / C::SA_I) * C::SUB + C::SA_OFF + (ins % C::SA_I) * 256);
       }
     } else {
       constexpr int i = P - C::A_PT - C::B_PT - C::SA_PT;
-      const int ins = (wave + i * C::NW) % C::SB_INST;
-      dma_load4(d.rsb, d.valid ? o.sb[i] : kOob, 0u, d.lds + (ins / C::SB_I) * C::SUB + C::SB_OFF + (ins % C::SB_I) * 256);
+      const uint32_t ins = (wave + i * C::NW) % C::SB_INST;
+      dma_load4(d.t.rsb, d.valid ? o.sb[i] : kOob, d.ks_b, d.lds + (ins / C::SB_I) * C::SUB + C::SB_OFF + (ins % C::SB_I) * 256);
     }
   }
 
@@ -1362,7 +1362,6 @@ struct Kernel {
     };
     const LoadOffs lo = load_offsets(kargs());
     const LdsPtrs lp = lds_ptrs(smem);
-    const int row_bytes = kargs().row_bytes, row_bytes_b = kargs().row_bytes_b;
     if (rec) tr[w * kTraceWords + 29] = __builtin_amdgcn_s_memrealtime();
     const uint32_t sa_kstride = kargs().sa_kstride, sb_kstride = kargs().sb_kstride;
 
@@ -1408,13 +1407,11 @@ struct Kernel {
       d.valid = have_i;
       d.kbyte_a = have_i ? (uint32_t)ki * C::KSA : 0u;
       d.kbyte_b = have_i ? (uint32_t)ki * C::KSB : 0u;
-      if constexpr (C::MX) {
-        d.rsa = rsrc_plus(ti.rsa, have_i ? (uint32_t)ki * sa_kstride : 0u);
-        d.rsb = rsrc_plus(ti.rsb, have_i ? (uint32_t)ki * sb_kstride : 0u);
-      }
-      d.ragged_a = d.kbyte_a + C::KSA > (uint32_t)row_bytes;
-      d.ragged_b = d.kbyte_b + C::KSB > (uint32_t)row_bytes_b;
-      d.lds = (uint32_t)(uintptr_t)stage_ptr(smem, issued % S);
+      d.kc_a = have_i ? d.kbyte_a : ~0u;
+      d.kc_b = have_i ? d.kbyte_b : ~0u;
+      d.ks_a = have_i ? (uint32_t)ki * sa_kstride : 0u;
+      d.ks_b = have_i ? (uint32_t)ki * sb_kstride : 0u;
+      d.lds = (uint32_t)(uintptr_t)stage_ptr(smem, (int)((uint32_t)issued % S));
       return d;
     };
     auto advance_issue = [&]() {
@@ -1438,10 +1435,10 @@ struct Kernel {
     // barrier, so they all go out in the first slots instead.
     constexpr int DMA_SPAN = S == 2 ? (PRE < PER_STAGE ? PRE : PER_STAGE) : PRE;
     auto kstep_interleaved = [&](int d, Ops& o0, Ops& o1, Scales& sc0, Scales& sc1, Acc<C>& acc) {
-      const int cur = d % S, nxt = (d + 1) % S;
+      const int cur = (int)((uint32_t)d % S), nxt = (int)((uint32_t)(d + 1) % S);
       const DmaCtx dc = dma_ctx();
       if constexpr (PRE == 0) {
-        static_for<PER_STAGE>([&](auto pc) { dma_piece<decltype(pc)::value>(dc, lo, row_bytes, row_bytes_b); });
+        static_for<PER_STAGE>([&](auto pc) { dma_piece<decltype(pc)::value>(dc, lo); });
       }
       static_for<C::NU>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
@@ -1461,7 +1458,7 @@ struct Kernel {
           }
           static_for<PER_STAGE>([&](auto pc) {
             constexpr int pp = decltype(pc)::value;
-            if constexpr (pp * DMA_SPAN / PER_STAGE == slot) dma_piece<pp>(dc, lo, row_bytes, row_bytes_b);
+            if constexpr (pp * DMA_SPAN / PER_STAGE == slot) dma_piece<pp>(dc, lo);
           });
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -1496,7 +1493,7 @@ struct Kernel {
     // as do B's fragments and the scales of the next k-step.
     auto kstep_inplace = [&](int d, auto& o0, auto& o1, Scales& sc0, Scales& sc1, Acc<C>& acc) {
       static_assert(!C::INPLACE || PRE > 0, "the in-place schedule issues its loads before the barrier");
-      const int cur = d % S, nxt = (d + 1) % S;
+      const int cur = (int)((uint32_t)d % S), nxt = (int)((uint32_t)(d + 1) % S);
       const DmaCtx dc = dma_ctx();
       constexpr int NBR = C::FN * C::NCH;   // B reads per sub-step
       static_for<C::NU>([&](auto uc) {
@@ -1539,7 +1536,7 @@ struct Kernel {
           if constexpr (slot < PRE) {
             static_for<PER_STAGE>([&](auto pc) {
               constexpr int pp = decltype(pc)::value;
-              if constexpr (pp * DMA_SPAN / PER_STAGE == slot) dma_piece<pp>(dc, lo, row_bytes, row_bytes_b);
+              if constexpr (pp * DMA_SPAN / PER_STAGE == slot) dma_piece<pp>(dc, lo);
             });
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -1559,7 +1556,7 @@ struct Kernel {
 
     static_for<S - 1>([&](auto) {
       const DmaCtx dc = dma_ctx();
-      static_for<PER_STAGE>([&](auto pc) { dma_piece<decltype(pc)::value>(dc, lo, row_bytes, row_bytes_b); });
+      static_for<PER_STAGE>([&](auto pc) { dma_piece<decltype(pc)::value>(dc, lo); });
       advance_issue();
     });
     uint32_t bias_h = load_bias(ic.tile);
@@ -1591,7 +1588,7 @@ struct Kernel {
       // the stage of the item's last k-step is free until the next k-step issues into it
       // (k-split kernels: a whole tile goes to finish_split, others add their slices here)
       if constexpr (C::WK > 1) {
-        if (ic.mode != WORK_WHOLE) reduce_k(acc, stage_ptr(smem, (done + S - 1) % S) + C::RED_OFF);
+        if (ic.mode != WORK_WHOLE) reduce_k(acc, stage_ptr(smem, (int)((uint32_t)(done + S - 1) % S)) + C::RED_OFF);
       }
       const bool holds = C::WK == 1 || wave_id() < C::OW;   // a wave with the item's sums
       if (ic.mode == WORK_CONTRIB) {
@@ -1610,7 +1607,7 @@ struct Kernel {
         if (ok) {
           lds_barrier();   // every wave is done with the previous tile's bias
           if (tid < C::BN) *(__attribute__((address_space(3))) uint16_t*)(smem + C::BIAS_OFF + tid * 2) = (uint16_t)bias_h;
-          lds_u8* const stg = stage_ptr(smem, (done + S - 1) % S);
+          lds_u8* const stg = stage_ptr(smem, (int)((uint32_t)(done + S - 1) % S));
           if (C::WK > 1 && ic.mode == WORK_WHOLE) {
             finish_split(kargs(), ic.tile, acc, stg + C::RED_OFF, smem);   // (its barrier also publishes the bias)
           } else {
