@@ -104,6 +104,18 @@ __device__ __forceinline__ void dma_load4(const v4u& rsrc, uint32_t voff, uint32
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, %3 offen lds"
                :: "v"(voff), "s"(lds), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+// The same with the LDS address given as a base plus a constant, added
+// straight into m0 (one scalar instruction instead of an add and a move).
+template <uint32_t IMM>
+__device__ __forceinline__ void dma_load16_at(const v4u& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %1, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+               :: "v"(voff), "s"(lds), "s"(rsrc), "s"(soff), "n"(IMM) : "memory", "m0", "scc");
+}
+template <uint32_t IMM>
+__device__ __forceinline__ void dma_load4_at(const v4u& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %1, %4\n\ts_nop 0\n\tbuffer_load_dword %0, %2, %3 offen lds"
+               :: "v"(voff), "s"(lds), "s"(rsrc), "s"(soff), "n"(IMM) : "memory", "m0", "scc");
+}
 
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -212,6 +224,12 @@ struct Cfg {
   static constexpr int A_PT = cdiv(A_GROUPS, NW), B_PT = cdiv(B_GROUPS, NW);
   static constexpr int SA_PT = SW ? SPT : cdiv(SA_INST, NW), SB_PT = SW ? 0 : cdiv(SB_INST, NW);
   static constexpr int LOADS_PER_STAGE_S = A_PT + B_PT + SA_PT + SB_PT;
+  // Loads whose LDS target is a constant plus 1 KiB (scales: 256 B) per wave:
+  // every wave has a group of its own in each load (no wrap-around) and a
+  // load's NW groups lie in one sub-stage.
+  static constexpr bool LIN_A = A_GROUPS % NW == 0 && A_GRP % NW == 0;
+  static constexpr bool LIN_B = B_GROUPS % NW == 0 && B_GRP % NW == 0;
+  static constexpr bool LIN_S = !SW && MX && SA_INST % NW == 0 && SA_I % NW == 0 && SB_INST % NW == 0 && SB_I % NW == 0;
   // Eight-wave kernels whose operand fragments take 8 VGPRs (E4M3 and the
   // six-bit types, NCH == 2) refill A's fragments in place and double-buffer
   // only B's: two full sets of operands would not fit beside the
@@ -842,48 +860,64 @@ struct Kernel {
 
   // One direct-to-LDS load of a k-step, by its index P among the k-step's
   // LOADS_PER_STAGE_S loads (A row groups, then B, then the two scale areas;
-  // each into the sub-stage of its k-slice).
-  // d.valid false issues the same load with every lane out of range: it
-  // writes zeros into a stage nobody reads, so that every k-step issues the
-  // same number of loads.
+  // each into the sub-stage of its k-slice).  Past the end of the work list
+  // the last k-step's loads are issued again, into a stage nobody reads, so
+  // that every k-step issues the same number of loads.
   struct DmaCtx {
     TileCtx t;
     uint32_t kbyte_a, kbyte_b;   // the k-step's byte offset in a row of A and of B
-    uint32_t kc_a, kc_b;         // ... compared with LoadOffs::lim (all ones when invalid: every lane out of range)
     uint32_t ks_a, ks_b;         // scalar offsets of the k-step's scale bytes
     uint32_t lds;                // LDS address of the target stage
-    bool valid;
+    uint32_t w16, w4;            // ... plus 1 KiB (256 B) per wave below this one (the LIN_ loads' base)
+    uint32_t wave;
   };
   template <int P>
   static __device__ __forceinline__ void dma_piece(const DmaCtx& d, const LoadOffs& o) {
-    const uint32_t wave = (uint32_t)wave_id();
-    __builtin_assume(wave < (uint32_t)C::NW);
+    const uint32_t wave = d.wave;
     if constexpr (P < C::A_PT) {
       constexpr int i = P;
-      const uint32_t grp = (wave + i * C::NW) % C::A_GROUPS;
-      dma_load16(d.t.ra, d.kc_a < o.lim_a[i] ? o.a[i] : kOob, d.kbyte_a,
-                 d.lds + (grp / C::A_GRP) * C::SUB + C::A_OFF + (grp % C::A_GRP) * 1024);
+      const uint32_t voff = d.kbyte_a < o.lim_a[i] ? o.a[i] : kOob;
+      if constexpr (C::LIN_A) {
+        constexpr uint32_t g0 = i * C::NW;   // wave 0's row group
+        dma_load16_at<(g0 / C::A_GRP) * C::SUB + C::A_OFF + (g0 % C::A_GRP) * 1024>(d.t.ra, voff, d.kbyte_a, d.w16);
+      } else {
+        const uint32_t grp = (wave + i * C::NW) % C::A_GROUPS;
+        dma_load16(d.t.ra, voff, d.kbyte_a, d.lds + (grp / C::A_GRP) * C::SUB + C::A_OFF + (grp % C::A_GRP) * 1024);
+      }
     } else if constexpr (P < C::A_PT + C::B_PT) {
       constexpr int i = P - C::A_PT;
-      const uint32_t grp = (wave + i * C::NW) % C::B_GROUPS;
-      dma_load16(d.t.rb, d.kc_b < o.lim_b[i] ? o.b[i] : kOob, d.kbyte_b,
-                 d.lds + (grp / C::B_GRP) * C::SUB + C::B_OFF + (grp % C::B_GRP) * 1024);
+      const uint32_t voff = d.kbyte_b < o.lim_b[i] ? o.b[i] : kOob;
+      if constexpr (C::LIN_B) {
+        constexpr uint32_t g0 = i * C::NW;
+        dma_load16_at<(g0 / C::B_GRP) * C::SUB + C::B_OFF + (g0 % C::B_GRP) * 1024>(d.t.rb, voff, d.kbyte_b, d.w16);
+      } else {
+        const uint32_t grp = (wave + i * C::NW) % C::B_GROUPS;
+        dma_load16(d.t.rb, voff, d.kbyte_b, d.lds + (grp / C::B_GRP) * C::SUB + C::B_OFF + (grp % C::B_GRP) * 1024);
+      }
     } else if constexpr (P < C::A_PT + C::B_PT + C::SA_PT) {
       constexpr int i = P - C::A_PT - C::B_PT;
       if constexpr (C::SW) {
         const uint32_t idx = wave + i * C::NW;
-        if (idx < C::SA_INST) dma_load16(d.t.rsa, d.valid ? o.sa[i] : kOob, d.ks_a, d.lds + C::SA_OFF + idx * 1024);
+        if (idx < C::SA_INST) dma_load16(d.t.rsa, o.sa[i], d.ks_a, d.lds + C::SA_OFF + idx * 1024);
         else if (idx < C::SA_INST + C::SB_INST)
-          dma_load16(d.t.rsb, d.valid ? o.sa[i] : kOob, d.ks_b, d.lds + C::SB_OFF + (idx - C::SA_INST) * 1024);
+          dma_load16(d.t.rsb, o.sa[i], d.ks_b, d.lds + C::SB_OFF + (idx - C::SA_INST) * 1024);
         else dma_load16(d.t.rsa, kOob, 0u, d.lds + C::JUNK_OFF);
+      } else if constexpr (C::LIN_S) {
+        constexpr uint32_t n0 = i * C::NW;   // wave 0's instruction
+        dma_load4_at<(n0 / C::SA_I) * C::SUB + C::SA_OFF + (n0 % C::SA_I) * 256>(d.t.rsa, o.sa[i], d.ks_a, d.w4);
       } else {
         const uint32_t ins = (wave + i * C::NW) % C::SA_INST;
-        dma_load4(d.t.rsa, d.valid ? o.sa[i] : kOob, d.ks_a, d.lds + (ins / C::SA_I) * C::SUB + C::SA_OFF + (ins % C::SA_I) * 256);
+        dma_load4(d.t.rsa, o.sa[i], d.ks_a, d.lds + (ins / C::SA_I) * C::SUB + C::SA_OFF + (ins % C::SA_I) * 256);
       }
     } else {
       constexpr int i = P - C::A_PT - C::B_PT - C::SA_PT;
-      const uint32_t ins = (wave + i * C::NW) % C::SB_INST;
-      dma_load4(d.t.rsb, d.valid ? o.sb[i] : kOob, d.ks_b, d.lds + (ins / C::SB_I) * C::SUB + C::SB_OFF + (ins % C::SB_I) * 256);
+      if constexpr (C::LIN_S) {
+        constexpr uint32_t n0 = i * C::NW;
+        dma_load4_at<(n0 / C::SB_I) * C::SUB + C::SB_OFF + (n0 % C::SB_I) * 256>(d.t.rsb, o.sb[i], d.ks_b, d.w4);
+      } else {
+        const uint32_t ins = (wave + i * C::NW) % C::SB_INST;
+        dma_load4(d.t.rsb, o.sb[i], d.ks_b, d.lds + (ins / C::SB_I) * C::SUB + C::SB_OFF + (ins % C::SB_I) * 256);
+      }
     }
   }
 
@@ -1389,8 +1423,8 @@ struct Kernel {
     };
 
     // ---- the direct path: one fixed, interleaved schedule per k-step.
-    // k-step d reads stage d % S and issues the loads of k-step d + S - 1 (or
-    // same-count dummies past the end of the list) into stage (d + S - 1) % S,
+    // k-step d reads stage d % S and issues the loads of k-step d + S - 1 (past
+    // the end of the list, the last k-step's again) into stage (d + S - 1) % S,
     // which the barrier of k-step d - 1 freed.  Because every k-step issues
     // PER_STAGE loads, the loads of stage d + 1 have landed once at most
     // (S - 2) * PER_STAGE loads are outstanding (loads complete in issue
@@ -1401,19 +1435,22 @@ struct Kernel {
     // stage d + 1 sits half-way through the last sub-step, after which that
     // stage's scales and first operands are read (inside an item) between the
     // remaining MFMAs.  sched_barrier(0) between slots keeps this order.
+    const uint32_t wv = (uint32_t)wave_id();
     auto dma_ctx = [&]() -> DmaCtx {
       DmaCtx d;
       d.t = ti;
-      d.valid = have_i;
-      d.kbyte_a = have_i ? (uint32_t)ki * C::KSA : 0u;
-      d.kbyte_b = have_i ? (uint32_t)ki * C::KSB : 0u;
-      d.kc_a = have_i ? d.kbyte_a : ~0u;
-      d.kc_b = have_i ? d.kbyte_b : ~0u;
-      d.ks_a = have_i ? (uint32_t)ki * sa_kstride : 0u;
-      d.ks_b = have_i ? (uint32_t)ki * sb_kstride : 0u;
+      d.kbyte_a = (uint32_t)ki * C::KSA;
+      d.kbyte_b = (uint32_t)ki * C::KSB;
+      d.ks_a = (uint32_t)ki * sa_kstride;
+      d.ks_b = (uint32_t)ki * sb_kstride;
       d.lds = (uint32_t)(uintptr_t)stage_ptr(smem, (int)((uint32_t)issued % S));
+      d.w16 = d.lds + wv * 1024u;
+      d.w4 = d.lds + wv * 256u;
+      d.wave = wv;
       return d;
     };
+    // (past the end of the list ki stays on the last k-step, whose loads are
+    // then issued again)
     auto advance_issue = [&]() {
       ++issued;
       if (have_i && ++ki == ki_end) {
@@ -1423,6 +1460,8 @@ struct Kernel {
           ki = x.k0;
           ki_end = x.k1;
           ti = tile_ctx(kargs(), x.tile);
+        } else {
+          ki = ki_end - 1;
         }
       }
     };
