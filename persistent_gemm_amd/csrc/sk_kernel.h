@@ -319,10 +319,19 @@ __device__ __forceinline__ void mfma(typename Acc<C>::T& acc, const v4u* a, cons
   } else {
     const v8i va = mfma_operand<C, C::FA>(a), vb = mfma_operand<C, C::FB>(b);
     // the first operand is B's block (the transposed product): its format comes first
-    if constexpr (C::MF == 32)
+    if constexpr (C::DT == DT_FP8) {
+      // no block scales: with both scale operands 0 (and op_sel 0) the
+      // compiler emits the unscaled f8f6f4 instruction, which multiplies by 1
+      // and leaves the two scale registers free
+      if constexpr (C::MF == 32)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc, C::FB, C::FA, 0, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vb, va, acc, C::FB, C::FA, 0, 0, 0, 0);
+    } else if constexpr (C::MF == 32) {
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb, va, acc, C::FB, C::FA, OPB, sb, OPA, sa);
-    else
+    } else {
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vb, va, acc, C::FB, C::FA, OPB, sb, OPA, sa);
+    }
   }
 }
 
