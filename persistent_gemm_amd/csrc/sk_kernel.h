@@ -230,6 +230,11 @@ struct Cfg {
   static constexpr bool LIN_A = A_GROUPS % NW == 0 && A_GRP % NW == 0;
   static constexpr bool LIN_B = B_GROUPS % NW == 0 && B_GRP % NW == 0;
   static constexpr bool LIN_S = !SW && MX && SA_INST % NW == 0 && SA_I % NW == 0 && SB_INST % NW == 0 && SB_I % NW == 0;
+  // ... and whose loads all give the lane the same chunk of its row (the NW
+  // row groups between two of a wave's loads are a whole number of 16-row
+  // swizzle periods), so they share one in-row limit
+  static constexpr bool LIM1_A = LIN_A && WK == 1 && (NW * RG) % 16 == 0;
+  static constexpr bool LIM1_B = LIN_B && WK == 1 && (NW * RG) % 16 == 0;
   // Eight-wave kernels whose operand fragments take 8 VGPRs (E4M3 and the
   // six-bit types, NCH == 2) refill A's fragments in place and double-buffer
   // only B's: two full sets of operands would not fit beside the
@@ -885,7 +890,7 @@ struct Kernel {
     const uint32_t wave = d.wave;
     if constexpr (P < C::A_PT) {
       constexpr int i = P;
-      const uint32_t voff = d.kbyte_a < o.lim_a[i] ? o.a[i] : kOob;
+      const uint32_t voff = d.kbyte_a < o.lim_a[C::LIM1_A ? 0 : i] ? o.a[i] : kOob;
       if constexpr (C::LIN_A) {
         constexpr uint32_t g0 = i * C::NW;   // wave 0's row group
         dma_load16_at<(g0 / C::A_GRP) * C::SUB + C::A_OFF + (g0 % C::A_GRP) * 1024>(d.t.ra, voff, d.kbyte_a, d.w16);
@@ -895,7 +900,7 @@ struct Kernel {
       }
     } else if constexpr (P < C::A_PT + C::B_PT) {
       constexpr int i = P - C::A_PT;
-      const uint32_t voff = d.kbyte_b < o.lim_b[i] ? o.b[i] : kOob;
+      const uint32_t voff = d.kbyte_b < o.lim_b[C::LIM1_B ? 0 : i] ? o.b[i] : kOob;
       if constexpr (C::LIN_B) {
         constexpr uint32_t g0 = i * C::NW;
         dma_load16_at<(g0 / C::B_GRP) * C::SUB + C::B_OFF + (g0 % C::B_GRP) * 1024>(d.t.rb, voff, d.kbyte_b, d.w16);
